@@ -1,0 +1,177 @@
+/*
+ * rq.h - C ABI of the ResidualQuant decode library (librq.so), AMD MI355X (gfx950).
+ *
+ * ResidualQuant stores the KV cache of a looped Transformer per anchor group of
+ * loops: the last loop of the group ("anchor") as INT4 codes, every earlier loop as
+ * a 2-bit residual r = R (kv_l - c * anchor_hat) with one BF16 least-squares
+ * coefficient c per key or value vector, a fixed orthogonal rotation R per
+ * (KV head, K|V), and an FP8-E4M3 offset and scale per group of contiguous
+ * channels.  Decode attention rebuilds c * anchor_hat + R^T r_hat on chip.
+ *
+ * Sources: "ResidualQuant ... cross-loop KV residual quantization" explainer
+ * (learnaivisually.com): paragraph on the master print and overlays (anchor,
+ * residual, c, rotation, on-chip rebuild), paragraph "Which print is the master"
+ * (shared vs chained reads, BF16 pending token), "Worked example" (4-bit anchor,
+ * 2-bit residuals, FP8 scale and offset, BF16 c); arXiv digest (ai4snews),
+ * Figure 1 caption (g = 32) and the paragraph on Huginn-3.5B's 8 groups of 4 loops.
+ *
+ * Conventions for every entry point:
+ *  - Pointers named "device" are device memory owned by the caller; the library
+ *    never allocates, frees or synchronises, and only enqueues work on `stream`.
+ *  - BF16 tensors are passed as their 16-bit patterns (uint16_t).
+ *  - All argument checks run on the host before anything is launched; a failing
+ *    check returns its status and enqueues nothing.  A launch failure returns
+ *    RQ_ERR_HIP.  Values inside device buffers (ctx_len, pos) are not visible to
+ *    the host: the kernels clamp them as documented instead.
+ *  - Calls that share a workspace must not overlap in time (same stream is fine).
+ */
+#ifndef RQ_H_
+#define RQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rq_status {
+    RQ_OK = 0,
+    RQ_ERR_INVALID_ARG = 1,   /* null pointer, size out of range, inconsistent shape */
+    RQ_ERR_UNSUPPORTED = 2,   /* configuration tuple without a compiled kernel */
+    RQ_ERR_MISALIGNED = 3,    /* device pointer not 16-byte aligned */
+    RQ_ERR_WORKSPACE = 4,     /* workspace missing or smaller than required */
+    RQ_ERR_HIP = 5            /* the HIP runtime reported an error at launch */
+} rq_status;
+
+/* Shape of one layer's compressed cache.  Supported tuples: head_dim 64 or 128;
+ * group 16 or 32 (dividing head_dim); anchor_bits 4 or 2; resid_bits 2;
+ * loops_per_group 2..8; n_groups >= 1; n_q_heads a multiple (1..8) of n_kv_heads. */
+typedef struct rq_config {
+    int32_t head_dim;         /* d */
+    int32_t group;            /* g: channels per quantization group */
+    int32_t anchor_bits;      /* code width of the anchor (last) loop of a group */
+    int32_t resid_bits;       /* code width of the residual loops */
+    int32_t loops_per_group;  /* L: loops sharing one anchor; loop L-1 of the group is the anchor */
+    int32_t n_groups;         /* anchor groups; total loops = L * n_groups */
+    int32_t chained;          /* 0: every loop references the anchor; 1: loop l references rebuilt loop l+1 */
+    int32_t n_kv_heads;
+    int32_t n_q_heads;        /* query head hq reads KV head hq / (n_q_heads / n_kv_heads) */
+    int32_t max_batch;
+    int32_t max_ctx;          /* token slots per sequence; storage is rounded up to 64-token tiles */
+} rq_config;
+
+/* Byte layout of the cache (one flat, 16-byte-aligned device buffer):
+ * [batch][KV head][K|V] blocks; each block holds the n_groups*L planes in global loop
+ * order (the anchor plane is the last of its group); each plane is ceil(max_ctx/64)
+ * tiles of 64 tokens; a tile holds
+ *   codes: 64 rows of d*bits/8 bytes, channel i at bit i*bits of its row (little-endian);
+ *   meta : 64 rows of 2*(d/g) bytes: E4M3 offset then E4M3 scale of each channel group;
+ *   c    : residual planes only, 64 BF16 coefficients.
+ * At d=128, g=32, INT4/INT2 a token costs 72 B (anchor) + 42 B (each residual) per
+ * KV head per K|V.  Returns 0 for an invalid or unsupported configuration. */
+size_t rq_cache_bytes(const rq_config* cfg);
+
+/* Bytes of scratch that rq_decode_attention needs for `cfg` (split-K partial results
+ * and one arrival counter per (batch row, query head)).  The caller allocates it and
+ * zero-fills it ONCE before first use; every call leaves the counters at zero again. */
+size_t rq_workspace_bytes(const rq_config* cfg);
+
+/* Shape of one loop's uncompressed BF16 cache for the baseline decode kernel. */
+typedef struct rq_bf16_config {
+    int32_t head_dim;         /* 64 or 128 */
+    int32_t n_kv_heads;
+    int32_t n_q_heads;        /* multiple of n_kv_heads */
+    int32_t max_batch;
+    int32_t t_cap;            /* token slots per sequence in k_cache/v_cache */
+} rq_bf16_config;
+
+/* Workspace bytes for rq_bf16_decode_attention (same contract as rq_workspace_bytes). */
+size_t rq_bf16_workspace_bytes(const rq_bf16_config* cfg);
+
+const char* rq_status_str(rq_status status);
+
+/* rq_quantize_token - quantize finished tokens of one anchor group into the cache.
+ * Explainer, "Which print is the master": a token's K/V stay BF16 in a temporary
+ * buffer until the group's last loop has run, and are quantized only then.  For
+ * each (token, batch row b, KV head, K|V) and the L loops x_0..x_{L-1} of group
+ * `group_idx`:
+ *   anchor  : x_{L-1} quantized per group of g channels at anchor_bits;
+ *   loop l<L-1 (shared): c = BF16(<x_l,a>/<a,a>) with a the dequantized anchor
+ *             (c = 0 if a = 0), r = R (x_l - c a), r quantized per group at resid_bits;
+ *   chained : same with a replaced by the rebuilt loop l+1 (c_{l+1} a' + R^T r_hat_{l+1}).
+ * Quantizer: offset z = largest E4M3 value <= group min; scale s = smallest E4M3
+ * value >= 2^-9 with z + (2^bits-1) s >= group max; code = round-half-even((x-z)/s)
+ * clamped to [0, 2^bits-1].  All of this is computed in float64.
+ *   cfg       : host pointer.
+ *   cache     : device, rq_cache_bytes(cfg) bytes; written at the token slots only.
+ *   pending   : device BF16 values of x, element (t, b, l, X, h, i) at
+ *               t*st[0] + b*st[1] + l*st[2] + X*st[3] + h*st[4] + i (X: 0 = K, 1 = V).
+ *   pending_strides : host array of 5 element strides, or NULL for the contiguous
+ *               [n_tokens][batch][L][2][n_kv_heads][head_dim] layout.
+ *   group_idx : anchor group 0..n_groups-1 the loops belong to.
+ *   pos       : device int32[batch]; token t of row b goes to slot pos[b] + t.  Slots
+ *               outside [0, max_ctx) are skipped (nothing is written).
+ *   rot       : device float32 [n_kv_heads][2][head_dim][head_dim], row-major R.
+ *   batch     : rows 1..max_batch;  n_tokens : tokens per row, >= 1.
+ * Inputs must be finite with |x| small enough that every group range fits E4M3
+ * (offset >= -448, scale <= 448); other inputs give unspecified codes. */
+rq_status rq_quantize_token(const rq_config* cfg, void* cache, const uint16_t* pending,
+                            const int64_t* pending_strides, int32_t group_idx,
+                            const int32_t* pos, const float* rot, int32_t batch,
+                            int32_t n_tokens, hipStream_t stream);
+
+/* rq_decode_attention - one loop-step of fused decode attention over the packed cache.
+ * Explainer, paragraph on the master print: each loop's KV is rebuilt as
+ * c * anchor + residual tile by tile on chip and never written back; with a shared
+ * anchor a loop reads two planes (anchor + its residual), chained loop l reads the
+ * anchor and the residual planes l..L-2.  The kernel never rebuilds K/V explicitly:
+ * score_j = C_j (q . a_j) + sum_k gamma_jk (R_K q) . r_jk and the output accumulates
+ * sum p_j C_j a_j and sum p_j gamma_jk r_jk separately, applying R_V^T once.  The
+ * current token (not yet quantized) is the last attention entry, in BF16.
+ * For each batch row b and query head hq (KV head h = hq / (Hq/Hkv)):
+ *   out[b][hq] = softmax over j in [0, ctx_len[b]) and the current token of
+ *                sm_scale * q . k_j, applied to the rebuilt values v_j.
+ *   cfg       : host pointer.   cache : device, as written by rq_quantize_token.
+ *   loop      : global loop index 0..L*n_groups-1 (group = loop / L).
+ *   q         : device [batch][n_q_heads][head_dim], float32 (q_is_bf16 = 0) or BF16 (1).
+ *   k_cur, v_cur : device BF16 [batch][n_kv_heads][head_dim], the current token's K/V of this loop.
+ *   pending   : device or NULL.  If set, k_cur/v_cur are also stored into the pending
+ *               buffer [batch][L][2][n_kv_heads][head_dim] at local loop loop % L (the
+ *               buffer rq_quantize_token later reads).
+ *   ctx_len   : device int32[batch], tokens already in the cache (clamped to [0, ctx_bound]).
+ *   ctx_bound : host upper bound of every ctx_len[b], 0..max_ctx; sizes the launch.
+ *   rot       : device float32 [n_kv_heads][2][head_dim][head_dim].
+ *   out       : device float32 [batch][n_q_heads][head_dim].
+ *   workspace : device, >= rq_workspace_bytes(cfg) bytes, zero-filled once before first use.
+ *   n_splits  : split-K factor 1..64, or 0 to let the library choose.
+ * Alignment: cache, q, k_cur, v_cur, pending, out, rot and workspace 16-byte aligned. */
+rq_status rq_decode_attention(const rq_config* cfg, const void* cache, int32_t loop,
+                              const void* q, int32_t q_is_bf16,
+                              const uint16_t* k_cur, const uint16_t* v_cur, uint16_t* pending,
+                              const int32_t* ctx_len, int32_t ctx_bound, const float* rot,
+                              float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                              int32_t batch, int32_t n_splits, hipStream_t stream);
+
+/* rq_bf16_decode_attention - the same decode attention over an uncompressed BF16
+ * cache (the baseline the arXiv digest's section 5.3 compares against: BF16
+ * FlashAttention decode over each loop's own KV).
+ *   cfg       : host pointer.
+ *   k_cache, v_cache : device BF16 [max_batch][n_kv_heads][t_cap][head_dim] of one loop.
+ *   append    : if nonzero, k_cur/v_cur are also stored at slot ctx_len[b] (when < t_cap).
+ *   ctx_bound : host upper bound of every ctx_len[b], 0..t_cap.
+ *   workspace : >= rq_bf16_workspace_bytes(cfg) bytes, zero-filled once before first use.
+ * Other arguments as for rq_decode_attention. */
+rq_status rq_bf16_decode_attention(const rq_bf16_config* cfg, uint16_t* k_cache, uint16_t* v_cache,
+                                   const void* q, int32_t q_is_bf16,
+                                   const uint16_t* k_cur, const uint16_t* v_cur, int32_t append,
+                                   const int32_t* ctx_len, int32_t ctx_bound, float sm_scale,
+                                   float* out, void* workspace, size_t workspace_bytes,
+                                   int32_t batch, int32_t n_splits, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RQ_H_ */

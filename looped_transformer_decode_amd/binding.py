@@ -1,0 +1,149 @@
+"""Thin Python binding of librq.so (argument marshalling only).
+
+Every function has the name of the C entry point it calls (see include/rq.h) and
+takes torch tensors that already live on the GPU; it passes their device pointers
+and sizes through ctypes and raises RQError on a non-zero status.  No computation
+happens here: if the library is missing the import fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librq.so")
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is not built; run __graft_entry__.build() or "
+                      "python -m looped_transformer_decode_amd.build")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+EXPORTS = ("rq_cache_bytes", "rq_workspace_bytes", "rq_bf16_workspace_bytes", "rq_status_str",
+           "rq_quantize_token", "rq_decode_attention", "rq_bf16_decode_attention")
+
+
+class rq_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "head_dim", "group", "anchor_bits", "resid_bits", "loops_per_group", "n_groups", "chained",
+        "n_kv_heads", "n_q_heads", "max_batch", "max_ctx")]
+
+
+class rq_bf16_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("head_dim", "n_kv_heads", "n_q_heads", "max_batch", "t_cap")]
+
+
+class RQError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {rq_status_str(status)} (status {status})")
+        self.status = status
+
+
+_vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+_cfgp = ctypes.POINTER(rq_config)
+_bcfgp = ctypes.POINTER(rq_bf16_config)
+
+_lib.rq_cache_bytes.argtypes = [_cfgp]
+_lib.rq_cache_bytes.restype = _sz
+_lib.rq_workspace_bytes.argtypes = [_cfgp]
+_lib.rq_workspace_bytes.restype = _sz
+_lib.rq_bf16_workspace_bytes.argtypes = [_bcfgp]
+_lib.rq_bf16_workspace_bytes.restype = _sz
+_lib.rq_status_str.argtypes = [_i32]
+_lib.rq_status_str.restype = ctypes.c_char_p
+_lib.rq_quantize_token.argtypes = [_cfgp, _vp, _vp, ctypes.POINTER(ctypes.c_int64), _i32, _vp, _vp,
+                                   _i32, _i32, _vp]
+_lib.rq_quantize_token.restype = _i32
+_lib.rq_decode_attention.argtypes = [_cfgp, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _f32,
+                                     _vp, _vp, _sz, _i32, _i32, _vp]
+_lib.rq_decode_attention.restype = _i32
+_lib.rq_bf16_decode_attention.argtypes = [_bcfgp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _f32,
+                                          _vp, _vp, _sz, _i32, _i32, _vp]
+_lib.rq_bf16_decode_attention.restype = _i32
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise RQError(fn, status)
+
+
+def rq_status_str(status: int) -> str:
+    return _lib.rq_status_str(int(status)).decode()
+
+
+def rq_cache_bytes(cfg: rq_config) -> int:
+    return int(_lib.rq_cache_bytes(ctypes.byref(cfg)))
+
+
+def rq_workspace_bytes(cfg: rq_config) -> int:
+    return int(_lib.rq_workspace_bytes(ctypes.byref(cfg)))
+
+
+def rq_bf16_workspace_bytes(cfg: rq_bf16_config) -> int:
+    return int(_lib.rq_bf16_workspace_bytes(ctypes.byref(cfg)))
+
+
+def rq_quantize_token(cfg: rq_config, cache: torch.Tensor, pending: torch.Tensor, group_idx: int,
+                      pos: torch.Tensor, rot: torch.Tensor, batch: int, n_tokens: int = 1,
+                      pending_strides: Optional[Sequence[int]] = None, stream=None) -> None:
+    st = None
+    if pending_strides is not None:
+        st = (ctypes.c_int64 * 5)(*[int(s) for s in pending_strides])
+    _check("rq_quantize_token", _lib.rq_quantize_token(
+        ctypes.byref(cfg), _ptr(cache), _ptr(pending), st, group_idx, _ptr(pos), _ptr(rot),
+        batch, n_tokens, _stream(stream)))
+
+
+def rq_decode_attention(cfg: rq_config, cache: torch.Tensor, loop: int, q: torch.Tensor,
+                        k_cur: torch.Tensor, v_cur: torch.Tensor, pending: Optional[torch.Tensor],
+                        ctx_len: torch.Tensor, ctx_bound: int, rot: torch.Tensor, sm_scale: float,
+                        out: torch.Tensor, workspace: torch.Tensor, batch: int, n_splits: int = 0,
+                        stream=None) -> None:
+    q_bf16 = 1 if q.dtype == torch.bfloat16 else 0
+    _check("rq_decode_attention", _lib.rq_decode_attention(
+        ctypes.byref(cfg), _ptr(cache), loop, _ptr(q), q_bf16, _ptr(k_cur), _ptr(v_cur), _ptr(pending),
+        _ptr(ctx_len), ctx_bound, _ptr(rot), sm_scale, _ptr(out), _ptr(workspace), _nbytes(workspace),
+        batch, n_splits, _stream(stream)))
+
+
+def rq_bf16_decode_attention(cfg: rq_bf16_config, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                             q: torch.Tensor, k_cur: torch.Tensor, v_cur: torch.Tensor, append: bool,
+                             ctx_len: torch.Tensor, ctx_bound: int, sm_scale: float, out: torch.Tensor,
+                             workspace: torch.Tensor, batch: int, n_splits: int = 0, stream=None) -> None:
+    q_bf16 = 1 if q.dtype == torch.bfloat16 else 0
+    _check("rq_bf16_decode_attention", _lib.rq_bf16_decode_attention(
+        ctypes.byref(cfg), _ptr(k_cache), _ptr(v_cache), _ptr(q), q_bf16, _ptr(k_cur), _ptr(v_cur),
+        1 if append else 0, _ptr(ctx_len), ctx_bound, sm_scale, _ptr(out), _ptr(workspace),
+        _nbytes(workspace), batch, n_splits, _stream(stream)))
+
+
+def config_for(wl, chained: Optional[bool] = None, max_batch: Optional[int] = None,
+               max_ctx: Optional[int] = None) -> rq_config:
+    """rq_config for a synth.Workload (capacity: its batch, context + the current token)."""
+    return rq_config(wl.head_dim, wl.group, wl.anchor_bits, wl.resid_bits, wl.loops_per_group,
+                     wl.n_groups, int(wl.chained if chained is None else chained), wl.n_kv_heads,
+                     wl.n_q_heads, max_batch or wl.batch, max_ctx or wl.ctx + 1)
+
+
+def bf16_config_for(wl, max_batch: Optional[int] = None, t_cap: Optional[int] = None) -> rq_bf16_config:
+    return rq_bf16_config(wl.head_dim, wl.n_kv_heads, wl.n_q_heads, max_batch or wl.batch,
+                          t_cap or wl.ctx + 1)

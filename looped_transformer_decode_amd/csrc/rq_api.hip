@@ -1,0 +1,234 @@
+// C ABI of librq.so: argument validation on the host, then kernel launches.
+#include <string.h>
+
+#include "rq_args.hpp"
+
+namespace rq {
+
+
+bool make_geom(const rq_config* c, Geom* g) {
+    if (c == nullptr) return false;
+    const int d = c->head_dim, gs = c->group;
+    if (d != 64 && d != 128) return false;
+    if ((gs != 16 && gs != 32) || d % gs != 0) return false;
+    if (c->anchor_bits != 4 && c->anchor_bits != 2) return false;
+    if (c->resid_bits != 2) return false;
+    if (c->loops_per_group < 2 || c->loops_per_group > kMaxLoops) return false;
+    if (c->n_groups < 1 || c->n_groups > 64) return false;
+    if (c->chained != 0 && c->chained != 1) return false;
+    if (c->chained && c->loops_per_group > 4) return false;     // kernels read at most 3 residual planes
+    if (c->n_kv_heads < 1 || c->n_q_heads < c->n_kv_heads || c->n_q_heads % c->n_kv_heads != 0) return false;
+    if (c->n_q_heads / c->n_kv_heads > 8) return false;
+    if (c->max_batch < 1 || c->max_ctx < 1 || c->max_ctx > (1 << 24)) return false;
+    g->d = d;
+    g->g = gs;
+    g->ba = c->anchor_bits;
+    g->br = c->resid_bits;
+    g->L = c->loops_per_group;
+    g->n_groups = c->n_groups;
+    g->chained = c->chained;
+    g->hkv = c->n_kv_heads;
+    g->hq = c->n_q_heads;
+    g->max_batch = c->max_batch;
+    g->max_ctx = c->max_ctx;
+    g->n_tiles = (c->max_ctx + kTile - 1) / kTile;
+    g->a_row = d * g->ba / 8;
+    g->r_row = d * g->br / 8;
+    g->m_row = 2 * (d / gs);
+    g->a_tile = (int64_t)kTile * (g->a_row + g->m_row);
+    g->r_tile = (int64_t)kTile * (g->r_row + g->m_row + 2);
+    g->group_bytes = (int64_t)g->n_tiles * (g->a_tile + (int64_t)(g->L - 1) * g->r_tile);
+    g->block_bytes = (int64_t)g->n_groups * g->group_bytes;
+    g->total = (int64_t)g->max_batch * g->hkv * 2 * g->block_bytes;
+    return true;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static int auto_splits(int batch, int hq, int n_tiles) {
+    if (n_tiles <= 0) return 1;
+    // aim for >= 8 tiles (512 tokens) per split and enough workgroups to fill 256 CUs
+    int s = (n_tiles + 7) / 8;
+    const int heads = batch * hq;
+    while (s > 1 && heads * s > 4096) --s;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return s < 1 ? 1 : s;
+}
+
+}  // namespace rq
+
+using namespace rq;
+
+extern "C" {
+
+size_t rq_cache_bytes(const rq_config* cfg) {
+    Geom g;
+    if (!make_geom(cfg, &g)) return 0;
+    return (size_t)g.total;
+}
+
+size_t rq_workspace_bytes(const rq_config* cfg) {
+    Geom g;
+    if (!make_geom(cfg, &g)) return 0;
+    return workspace_bytes(g.max_batch, g.hq, g.d);
+}
+
+static bool bf16_cfg_ok(const rq_bf16_config* c) {
+    return c != nullptr && (c->head_dim == 64 || c->head_dim == 128) && c->n_kv_heads >= 1 &&
+           c->n_q_heads >= c->n_kv_heads && c->n_q_heads % c->n_kv_heads == 0 && c->max_batch >= 1 &&
+           c->t_cap >= 1 && c->t_cap <= (1 << 24);
+}
+
+size_t rq_bf16_workspace_bytes(const rq_bf16_config* cfg) {
+    if (!bf16_cfg_ok(cfg)) return 0;
+    return workspace_bytes(cfg->max_batch, cfg->n_q_heads, cfg->head_dim);
+}
+
+const char* rq_status_str(rq_status s) {
+    switch (s) {
+        case RQ_OK: return "ok";
+        case RQ_ERR_INVALID_ARG: return "invalid argument";
+        case RQ_ERR_UNSUPPORTED: return "unsupported configuration";
+        case RQ_ERR_MISALIGNED: return "device pointer not 16-byte aligned";
+        case RQ_ERR_WORKSPACE: return "workspace missing or too small";
+        case RQ_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+rq_status rq_quantize_token(const rq_config* cfg, void* cache, const uint16_t* pending,
+                            const int64_t* pending_strides, int32_t group_idx, const int32_t* pos,
+                            const float* rot, int32_t batch, int32_t n_tokens, hipStream_t stream) {
+    Geom g;
+    if (cfg == nullptr) return RQ_ERR_INVALID_ARG;
+    if (!make_geom(cfg, &g)) return RQ_ERR_UNSUPPORTED;
+    if (!cache || !pending || !pos || !rot) return RQ_ERR_INVALID_ARG;
+    if (batch < 1 || batch > g.max_batch || n_tokens < 1) return RQ_ERR_INVALID_ARG;
+    if (group_idx < 0 || group_idx >= g.n_groups) return RQ_ERR_INVALID_ARG;
+    if ((int64_t)n_tokens * batch * g.hkv * 2 > 0x7FFFFFFFLL) return RQ_ERR_INVALID_ARG;
+    if (!aligned16(cache) || !aligned16(rot) || (reinterpret_cast<uintptr_t>(pending) & 1u))
+        return RQ_ERR_MISALIGNED;
+    PackArgs a;
+    memset(&a, 0, sizeof(a));
+    a.geo = g;
+    a.cache = static_cast<uint8_t*>(cache);
+    a.pending = pending;
+    if (pending_strides) {
+        for (int i = 0; i < 5; ++i) {
+            if (pending_strides[i] < 0) return RQ_ERR_INVALID_ARG;
+            a.st[i] = pending_strides[i];
+        }
+    } else {
+        a.st[4] = g.d;
+        a.st[3] = (int64_t)g.hkv * g.d;
+        a.st[2] = 2 * a.st[3];
+        a.st[1] = (int64_t)g.L * a.st[2];
+        a.st[0] = (int64_t)batch * a.st[1];
+    }
+    a.pos = pos;
+    a.rot = rot;
+    a.group_idx = group_idx;
+    a.batch = batch;
+    a.n_tokens = n_tokens;
+    return launch_pack(a, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
+}
+
+rq_status rq_decode_attention(const rq_config* cfg, const void* cache, int32_t loop, const void* q,
+                              int32_t q_is_bf16, const uint16_t* k_cur, const uint16_t* v_cur,
+                              uint16_t* pending, const int32_t* ctx_len, int32_t ctx_bound,
+                              const float* rot, float sm_scale, float* out, void* workspace,
+                              size_t workspace_bytes_, int32_t batch, int32_t n_splits,
+                              hipStream_t stream) {
+    Geom g;
+    if (cfg == nullptr) return RQ_ERR_INVALID_ARG;
+    if (!make_geom(cfg, &g)) return RQ_ERR_UNSUPPORTED;
+    if (!cache || !q || !k_cur || !v_cur || !ctx_len || !rot || !out) return RQ_ERR_INVALID_ARG;
+    if (batch < 1 || batch > g.max_batch) return RQ_ERR_INVALID_ARG;
+    if (loop < 0 || loop >= g.L * g.n_groups) return RQ_ERR_INVALID_ARG;
+    if (ctx_bound < 0 || ctx_bound > g.max_ctx) return RQ_ERR_INVALID_ARG;
+    if (n_splits < 0 || n_splits > kMaxSplits) return RQ_ERR_INVALID_ARG;
+    if (q_is_bf16 != 0 && q_is_bf16 != 1) return RQ_ERR_INVALID_ARG;
+    if (!(sm_scale > 0.f) || sm_scale != sm_scale) return RQ_ERR_INVALID_ARG;
+    if (!aligned16(cache) || !aligned16(q) || !aligned16(k_cur) || !aligned16(v_cur) ||
+        !aligned16(out) || !aligned16(rot) || (pending && !aligned16(pending)) ||
+        (workspace && !aligned16(workspace)))
+        return RQ_ERR_MISALIGNED;
+    const size_t need = workspace_bytes(g.max_batch, g.hq, g.d);
+    if (!workspace || workspace_bytes_ < need) return RQ_ERR_WORKSPACE;
+    const int lloc = loop % g.L;
+    const int nres = (lloc == g.L - 1) ? 0 : (g.chained ? g.L - 1 - lloc : 1);
+    const int n_tiles = (ctx_bound + kTile - 1) / kTile;
+    int S = n_splits ? n_splits : auto_splits(batch, g.hq, n_tiles);
+    if (n_tiles > 0 && S > n_tiles) S = n_tiles;
+    if (S < 1) S = 1;
+    DecodeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.geo = g;
+    a.cache = static_cast<const uint8_t*>(cache);
+    a.loop = loop;
+    a.q = q;
+    a.k_cur = k_cur;
+    a.v_cur = v_cur;
+    a.pending = pending;
+    a.ctx_len = ctx_len;
+    a.ctx_bound = ctx_bound;
+    a.rot = rot;
+    a.sm_scale = sm_scale;
+    a.out = out;
+    a.partials = static_cast<float*>(workspace);
+    a.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) +
+                                             workspace_counter_offset(g.max_batch, g.hq, g.d));
+    a.batch = batch;
+    a.n_splits = S;
+    a.tiles_per_split = n_tiles > 0 ? (n_tiles + S - 1) / S : 0;
+    return launch_decode(a, nres, q_is_bf16 != 0, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
+}
+
+rq_status rq_bf16_decode_attention(const rq_bf16_config* cfg, uint16_t* k_cache, uint16_t* v_cache,
+                                   const void* q, int32_t q_is_bf16, const uint16_t* k_cur,
+                                   const uint16_t* v_cur, int32_t append, const int32_t* ctx_len,
+                                   int32_t ctx_bound, float sm_scale, float* out, void* workspace,
+                                   size_t workspace_bytes_, int32_t batch, int32_t n_splits,
+                                   hipStream_t stream) {
+    if (cfg == nullptr) return RQ_ERR_INVALID_ARG;
+    if (!bf16_cfg_ok(cfg)) return RQ_ERR_UNSUPPORTED;
+    const int head_dim = cfg->head_dim, n_q_heads = cfg->n_q_heads;
+    if (!k_cache || !v_cache || !q || !k_cur || !v_cur || !ctx_len || !out) return RQ_ERR_INVALID_ARG;
+    if (batch < 1 || batch > cfg->max_batch || ctx_bound < 0 || ctx_bound > cfg->t_cap) return RQ_ERR_INVALID_ARG;
+    if (n_splits < 0 || n_splits > kMaxSplits) return RQ_ERR_INVALID_ARG;
+    if (q_is_bf16 != 0 && q_is_bf16 != 1) return RQ_ERR_INVALID_ARG;
+    if (!(sm_scale > 0.f) || sm_scale != sm_scale) return RQ_ERR_INVALID_ARG;
+    if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(k_cur) ||
+        !aligned16(v_cur) || !aligned16(out) || (workspace && !aligned16(workspace)))
+        return RQ_ERR_MISALIGNED;
+    const size_t need = workspace_bytes(cfg->max_batch, n_q_heads, head_dim);
+    if (!workspace || workspace_bytes_ < need) return RQ_ERR_WORKSPACE;
+    const int n_tiles = (ctx_bound + kTile - 1) / kTile;
+    int S = n_splits ? n_splits : auto_splits(batch, n_q_heads, n_tiles);
+    if (n_tiles > 0 && S > n_tiles) S = n_tiles;
+    if (S < 1) S = 1;
+    Bf16Args a;
+    memset(&a, 0, sizeof(a));
+    a.k = k_cache;
+    a.v = v_cache;
+    a.t_cap = cfg->t_cap;
+    a.hkv = cfg->n_kv_heads;
+    a.hq = n_q_heads;
+    a.q = q;
+    a.k_cur = k_cur;
+    a.v_cur = v_cur;
+    a.append = append ? 1 : 0;
+    a.ctx_len = ctx_len;
+    a.ctx_bound = ctx_bound;
+    a.sm_scale = sm_scale;
+    a.out = out;
+    a.partials = static_cast<float*>(workspace);
+    a.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) +
+                                             workspace_counter_offset(cfg->max_batch, n_q_heads, head_dim));
+    a.batch = batch;
+    a.n_splits = S;
+    a.tiles_per_split = n_tiles > 0 ? (n_tiles + S - 1) / S : 0;
+    return launch_bf16(a, head_dim, q_is_bf16 != 0, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Internal definitions shared by the ResidualQuant HIP kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rq.h"
+
+namespace rq {
+
+constexpr int kTile = 64;          // tokens per cache tile
+constexpr int kMaxSplits = 64;     // split-K upper bound (sizes the workspace)
+constexpr int kMaxLoops = 8;       // loops per anchor group
+constexpr int kWave = 64;
+
+// Byte geometry of the packed cache, derived from rq_config on the host and passed
+// to kernels by value.
+struct Geom {
+    int d, g, ba, br, L, n_groups, chained, hkv, hq, max_batch, max_ctx;
+    int n_tiles;
+    int a_row, r_row, m_row;           // bytes per token row: anchor codes, residual codes, meta
+    int64_t a_tile, r_tile;            // bytes per tile
+    int64_t group_bytes, block_bytes, total;
+
+    __host__ __device__ int64_t plane_offset(int b, int h, int x, int loop) const {
+        const int k = loop / L, l = loop % L;
+        return ((int64_t)(b * hkv + h) * 2 + x) * block_bytes + (int64_t)k * group_bytes +
+               (int64_t)l * n_tiles * r_tile;
+    }
+};
+
+// Returns false if the configuration is outside the supported tuples.
+bool make_geom(const rq_config* cfg, Geom* g);
+
+// Workspace layout for split-K decode: per (batch row, query head, split) a record of
+// acc_a[d], acc_r[d], m, l (+2 pad); then one uint32 arrival counter per (row, query head).
+__host__ __device__ inline int partial_stride(int d) { return 2 * d + 4; }
+inline size_t workspace_bytes(int max_batch, int hq, int d) {
+    size_t rec = (size_t)max_batch * hq * kMaxSplits * partial_stride(d) * sizeof(float);
+    size_t cnt = (size_t)max_batch * hq * sizeof(uint32_t);
+    return ((rec + 255) & ~(size_t)255) + ((cnt + 255) & ~(size_t)255);
+}
+inline size_t workspace_counter_offset(int max_batch, int hq, int d) {
+    size_t rec = (size_t)max_batch * hq * kMaxSplits * partial_stride(d) * sizeof(float);
+    return (rec + 255) & ~(size_t)255;
+}
+
+// ---------------------------------------------------------------- number formats
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// OCP FP8 E4M3FN byte -> float (finite patterns; 0x7F/0xFF are never stored by the pack).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    float mag = (e == 0) ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+    return (b & 0x80u) ? -mag : mag;
+}
+
+// ---------------------------------------------------------------- block mapping
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).
+// Remap so that consecutive logical indices (the splits of one query head, and the
+// query heads of one KV head) run on the same XCD.
+__device__ __forceinline__ int xcd_logical_block(int bid, int nblocks) {
+    constexpr int kXcd = 8;
+    const int per = nblocks / kXcd, rem = nblocks % kXcd;
+    const int xcd = bid % kXcd, local = bid / kXcd;
+    return (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+// ---------------------------------------------------------------- cross-lane helpers
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+__device__ __forceinline__ double shfl_xor_d(double v, int m) {
+    int2 p = *reinterpret_cast<int2*>(&v);
+    p.x = __shfl_xor(p.x, m, kWave);
+    p.y = __shfl_xor(p.y, m, kWave);
+    return *reinterpret_cast<double*>(&p);
+}
+
+}  // namespace rq

@@ -1,0 +1,210 @@
+// rq_pack: quantize finished tokens of one anchor group into the packed cache.
+//
+// ResidualQuant explainer, paragraph on the master print: the last loop is the INT4
+// anchor, each earlier loop stores residual = KV(loop) - c * anchor with a per-vector
+// least-squares c, rotated before 2-bit quantization; paragraph "Which print is the
+// master": the current token stays BF16 until its final loop and is quantized only
+// then (this kernel is that drain step).  Group quantizer with FP8 offset and scale:
+// "Worked example" of the same page and the arXiv digest's Figure 1 caption (g = 32).
+//
+// All arithmetic is float64 so that the integer decisions (codes, FP8 metadata, BF16
+// rounding of c) are taken exactly like a float64 reference would take them.
+#include "rq_args.hpp"
+
+namespace rq {
+
+
+// ---- FP8 E4M3FN on the float64 grid (exact: every step is a power-of-two scaling,
+// floor/ceil or a comparison)
+
+// largest grid value <= a, for 0 <= a (values above 448 give 448)
+__device__ inline double e4m3_down_mag(double a) {
+    if (a >= 448.0) return 448.0;
+    if (a < 0x1p-6) return floor(a * 512.0) * 0x1p-9;        // subnormal spacing 2^-9
+    const int e = ilogb(a);                                    // 2^e <= a < 2^(e+1)
+    const double q = ldexp(1.0, e - 3);                        // 3 mantissa bits
+    return floor(a / q) * q;
+}
+
+// smallest grid value >= a, for 0 <= a <= 448
+__device__ inline double e4m3_up_mag(double a) {
+    if (a <= 0x1p-6) return ceil(a * 512.0) * 0x1p-9;
+    const int e = ilogb(a);
+    const double q = ldexp(1.0, e - 3);
+    return ceil(a / q) * q;
+}
+
+__device__ inline double e4m3_floor(double v) {
+    return v >= 0.0 ? e4m3_down_mag(v) : -e4m3_up_mag(fmin(-v, 448.0));
+}
+
+__device__ inline uint32_t e4m3_bits(double v) {          // v on the grid
+    const uint32_t sign = v < 0.0 ? 0x80u : 0u;
+    const double a = fabs(v);
+    if (a == 0.0) return 0u;
+    if (a < 0x1p-6) return sign | (uint32_t)(a * 512.0);
+    const int e = ilogb(a);
+    const uint32_t man = (uint32_t)(a * ldexp(1.0, 3 - e)) - 8u;
+    return sign | ((uint32_t)(e + 7) << 3) | man;
+}
+
+__device__ inline double e4m3_pos_value(uint32_t b) {     // 0 < b <= 0x7E
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    return e == 0 ? m * 0x1p-9 : ldexp(1.0 + m * 0.125, (int)e - 7);
+}
+
+// BF16 round-to-nearest-even of a float64 value, in one rounding step.
+__device__ inline double bf16_round(double v) {
+    if (v == 0.0) return 0.0;
+    int e = ilogb(v);
+    if (e < -126) e = -126;
+    const double q = ldexp(1.0, e - 7);
+    return rint(v / q) * q;
+}
+
+struct QOut {
+    uint32_t code;
+    double z, s;
+    uint32_t zb, sb;
+};
+
+// Group quantizer: every lane holds one channel; groups are `g` consecutive lanes.
+__device__ inline QOut quantize_lane(double x, int bits, int g) {
+    double lo = x, hi = x;
+    for (int off = g >> 1; off >= 1; off >>= 1) {
+        lo = fmin(lo, shfl_xor_d(lo, off));
+        hi = fmax(hi, shfl_xor_d(hi, off));
+    }
+    QOut o;
+    const double n = (double)((1 << bits) - 1);
+    o.z = e4m3_floor(lo);
+    // smallest scale s >= 2^-9 on the grid with z + n*s >= hi (the sum is exact)
+    double need = (hi - o.z) / n;
+    if (need < 0x1p-9) need = 0x1p-9;
+    uint32_t sb = e4m3_bits(e4m3_up_mag(fmin(need, 448.0)));
+    while (sb > 1u && o.z + n * e4m3_pos_value(sb - 1u) >= hi) --sb;
+    while (sb < 0x7Eu && o.z + n * e4m3_pos_value(sb) < hi) ++sb;
+    o.s = e4m3_pos_value(sb);
+    o.sb = sb;
+    o.zb = e4m3_bits(o.z);
+    double t = rint((x - o.z) / o.s);
+    t = fmin(fmax(t, 0.0), n);
+    o.code = (uint32_t)t;
+    return o;
+}
+
+template <int D>
+__device__ inline double block_sum(double v, double* red) {
+    for (int off = 32; off >= 1; off >>= 1) v += shfl_xor_d(v, off);
+    constexpr int W = D / 64;
+    if (W == 1) return v;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    double s = 0.0;
+    for (int i = 0; i < W; ++i) s += red[i];
+    return s;
+}
+
+// Pack `bits`-wide codes of consecutive lanes into 32-bit words and store them.
+__device__ inline void store_codes(uint8_t* row, uint32_t code, int bits) {
+    const int per = 32 / bits;
+    const int i = threadIdx.x;
+    uint32_t v = code << ((i % per) * bits);
+    for (int off = 1; off < per; off <<= 1) v |= (uint32_t)__shfl_xor((int)v, off, kWave);
+    if (i % per == 0) reinterpret_cast<uint32_t*>(row)[i / per] = v;
+}
+
+__device__ inline void store_meta(uint8_t* row, const QOut& q, int g) {
+    const int i = threadIdx.x;
+    if (i % g == 0) reinterpret_cast<uint16_t*>(row)[i / g] = (uint16_t)(q.zb | (q.sb << 8));
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void rq_pack_kernel(PackArgs a) {
+    const Geom& G = a.geo;
+    const int i = threadIdx.x;
+    int wg = blockIdx.x;
+    const int x = wg & 1;
+    wg >>= 1;
+    const int h = wg % G.hkv;
+    wg /= G.hkv;
+    const int b = wg % a.batch;
+    const int t = wg / a.batch;
+    const int slot = a.pos[b] + t;
+    if (slot < 0 || slot >= G.max_ctx) return;       // same for the whole workgroup
+    const int tile = slot / kTile, jj = slot % kTile;
+    const int L = G.L;
+
+    __shared__ double sh_v[D];
+    __shared__ double red[D / 64];
+
+    double xv[kMaxLoops];
+    const uint16_t* src = a.pending + t * a.st[0] + b * a.st[1] + x * a.st[3] + h * a.st[4] + i;
+#pragma unroll
+    for (int l = 0; l < kMaxLoops; ++l)
+        if (l < L) xv[l] = (double)bf16_to_f32(src[l * a.st[2]]);
+
+    // anchor: the group's last loop
+    const int loop0 = a.group_idx * L;
+    const QOut qa = quantize_lane(xv[L - 1], G.ba, G.g);
+    {
+        uint8_t* p = a.cache + G.plane_offset(b, h, x, loop0 + L - 1) + tile * G.a_tile;
+        store_codes(p + jj * G.a_row, qa.code, G.ba);
+        store_meta(p + kTile * G.a_row + jj * G.m_row, qa, G.g);
+    }
+    double ref = qa.z + qa.code * qa.s;                 // dequantized anchor (exact)
+    const float* R = a.rot + (int64_t)(h * 2 + x) * D * D;
+
+    for (int l = L - 2; l >= 0; --l) {
+        const double num = block_sum<D>(xv[l] * ref, red);
+        const double den = block_sum<D>(ref * ref, red);
+        const double c = bf16_round(den > 0.0 ? num / den : 0.0);
+        const double y = xv[l] - c * ref;
+        __syncthreads();
+        sh_v[i] = y;
+        __syncthreads();
+        // r = R y : lane i takes row i of R
+        double r = 0.0;
+        const float4* Rrow = reinterpret_cast<const float4*>(R + (int64_t)i * D);
+#pragma unroll 8
+        for (int k4 = 0; k4 < D / 4; ++k4) {
+            const float4 rv = Rrow[k4];
+            r += (double)rv.x * sh_v[4 * k4 + 0];
+            r += (double)rv.y * sh_v[4 * k4 + 1];
+            r += (double)rv.z * sh_v[4 * k4 + 2];
+            r += (double)rv.w * sh_v[4 * k4 + 3];
+        }
+        const QOut qr = quantize_lane(r, G.br, G.g);
+        uint8_t* p = a.cache + G.plane_offset(b, h, x, loop0 + l) + tile * G.r_tile;
+        store_codes(p + jj * G.r_row, qr.code, G.br);
+        store_meta(p + kTile * G.r_row + jj * G.m_row, qr, G.g);
+        if (i == 0) {
+            const uint32_t cb = __float_as_uint((float)c) >> 16;    // c is a BF16 value
+            reinterpret_cast<uint16_t*>(p + kTile * (G.r_row + G.m_row))[jj] = (uint16_t)cb;
+        }
+        if (G.chained) {
+            // rebuilt loop l = c * ref + R^T r_hat becomes the reference of loop l-1
+            const double rhat = qr.z + qr.code * qr.s;
+            __syncthreads();
+            sh_v[i] = rhat;
+            __syncthreads();
+            double tcol = 0.0;
+#pragma unroll 8
+            for (int k = 0; k < D; ++k) tcol += (double)R[(int64_t)k * D + i] * sh_v[k];
+            ref = c * ref + tcol;
+        }
+    }
+}
+
+hipError_t launch_pack(const PackArgs& a, hipStream_t stream) {
+    const int nwg = a.n_tokens * a.batch * a.geo.hkv * 2;
+    if (a.geo.d == 128)
+        hipLaunchKernelGGL(rq_pack_kernel<128>, dim3(nwg), dim3(128), 0, stream, a);
+    else
+        hipLaunchKernelGGL(rq_pack_kernel<64>, dim3(nwg), dim3(64), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace rq

@@ -1,0 +1,148 @@
+"""Host-side checks of librq.so that need no GPU: every symbol declared in include/rq.h
+is exported, the size queries agree with the oracle's byte layout, and invalid
+arguments are rejected on the host with the documented status (nothing launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from looped_transformer_decode_amd import synth
+from oracle import residualquant as RQ
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "looped_transformer_decode_amd", "librq.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="librq.so not built")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from looped_transformer_decode_amd import binding
+    return binding
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "rq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(B):
+    lib = ctypes.CDLL(LIB)
+    declared = _declared_symbols()
+    assert len(declared) >= 7
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(B.EXPORTS)
+
+
+def _oracle_cfg(wl, chained):
+    return RQ.Config(wl.head_dim, wl.group, wl.anchor_bits, wl.resid_bits, wl.loops_per_group,
+                     wl.n_groups, chained, wl.n_kv_heads, wl.n_q_heads, wl.batch, wl.ctx + 1)
+
+
+@pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
+@pytest.mark.parametrize("chained", [False, True])
+def test_cache_bytes_match_oracle_layout(B, name, chained):
+    wl = synth.WORKLOADS[name]
+    if chained and wl.loops_per_group > 4:
+        pytest.skip("chained needs L <= 4")
+    cfg = B.config_for(wl, chained=chained)
+    assert B.rq_cache_bytes(cfg) == RQ.Layout(_oracle_cfg(wl, chained)).total_bytes
+    assert B.rq_workspace_bytes(cfg) > 0
+
+
+def test_invalid_configs_have_no_size(B):
+    wl = synth.WORKLOADS["ouro_b4_t8192"]
+    for field, bad in (("head_dim", 96), ("group", 24), ("anchor_bits", 3), ("resid_bits", 4),
+                       ("loops_per_group", 1), ("n_q_heads", 17), ("max_batch", 0), ("max_ctx", 0)):
+        cfg = B.config_for(wl)
+        setattr(cfg, field, bad)
+        assert B.rq_cache_bytes(cfg) == 0, field
+        assert B.rq_workspace_bytes(cfg) == 0, field
+    cfg = B.config_for(wl.with_(loops_per_group=8), chained=True)
+    assert B.rq_cache_bytes(cfg) == 0                    # chained reads at most 3 residual planes
+    assert B.rq_bf16_workspace_bytes(B.rq_bf16_config(96, 1, 1, 1, 64)) == 0
+
+
+def test_status_strings(B):
+    assert B.rq_status_str(0) == "ok"
+    assert "workspace" in B.rq_status_str(4)
+
+
+# Fake, 256-byte aligned device addresses: every call below must fail its host checks
+# before touching them.
+A = 0x7F0000000000
+
+
+def _decode(B, cfg, **kw):
+    args = dict(cache=A, loop=0, q=A, q_bf16=1, k_cur=A, v_cur=A, pending=None, ctx_len=A, ctx_bound=64,
+                rot=A, sm_scale=0.1, out=A, ws=A, ws_bytes=1 << 40, batch=1, n_splits=0)
+    args.update(kw)
+    return B._lib.rq_decode_attention(ctypes.byref(cfg), args["cache"], args["loop"], args["q"],
+                                      args["q_bf16"], args["k_cur"], args["v_cur"], args["pending"],
+                                      args["ctx_len"], args["ctx_bound"], args["rot"], args["sm_scale"],
+                                      args["out"], args["ws"], args["ws_bytes"], args["batch"],
+                                      args["n_splits"], None)
+
+
+def test_decode_attention_rejects_bad_arguments(B):
+    wl = synth.WORKLOADS["ouro_b4_t8192"]
+    cfg = B.config_for(wl)
+    need = B.rq_workspace_bytes(cfg)
+    assert _decode(B, B.rq_config()) == 2                # all-zero config: unsupported
+    assert _decode(B, cfg, cache=None) == 1
+    assert _decode(B, cfg, loop=4) == 1
+    assert _decode(B, cfg, loop=-1) == 1
+    assert _decode(B, cfg, batch=5) == 1
+    assert _decode(B, cfg, ctx_bound=wl.ctx + 2) == 1
+    assert _decode(B, cfg, n_splits=65) == 1
+    assert _decode(B, cfg, sm_scale=0.0) == 1
+    assert _decode(B, cfg, q_bf16=2) == 1
+    assert _decode(B, cfg, q=A + 8) == 3
+    assert _decode(B, cfg, pending=A + 4) == 3
+    assert _decode(B, cfg, ws=None) == 4
+    assert _decode(B, cfg, ws_bytes=need - 1) == 4
+
+
+def test_quantize_token_rejects_bad_arguments(B):
+    wl = synth.WORKLOADS["ouro_b4_t8192"]
+    cfg = B.config_for(wl)
+    f = B._lib.rq_quantize_token
+    ok = dict(cache=A, pending=A, st=None, grp=0, pos=A, rot=A, batch=4, n=1)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(ctypes.byref(cfg), a["cache"], a["pending"], a["st"], a["grp"], a["pos"], a["rot"],
+                 a["batch"], a["n"], None)
+
+    assert call(cache=None) == 1
+    assert call(grp=1) == 1
+    assert call(batch=0) == 1
+    assert call(batch=5) == 1
+    assert call(n=0) == 1
+    assert call(cache=A + 8) == 3
+    assert call(pending=A + 1) == 3
+    bad = (ctypes.c_int64 * 5)(1, 1, -1, 1, 1)
+    assert call(st=bad) == 1
+    cfg2 = B.config_for(wl)
+    cfg2.head_dim = 96
+    assert f(ctypes.byref(cfg2), A, A, None, 0, A, A, 1, 1, None) == 2
+
+
+def test_bf16_decode_rejects_bad_arguments(B):
+    cfg = B.rq_bf16_config(128, 16, 16, 4, 8193)
+    need = B.rq_bf16_workspace_bytes(cfg)
+    f = B._lib.rq_bf16_decode_attention
+
+    def call(cfg=cfg, k=A, v=A, q=A, ctx_bound=8192, ws=A, ws_bytes=1 << 40, batch=4):
+        return f(ctypes.byref(cfg), k, v, q, 1, A, A, 0, A, ctx_bound, 0.1, A, ws, ws_bytes, batch, 0, None)
+
+    assert call(k=None) == 1
+    assert call(ctx_bound=8194) == 1
+    assert call(batch=5) == 1
+    assert call(q=A + 2) == 3
+    assert call(ws_bytes=need - 1) == 4
+    assert call(cfg=B.rq_bf16_config(128, 16, 24, 4, 8193)) == 2

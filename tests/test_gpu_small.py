@@ -1,0 +1,202 @@
+"""GPU parity at sizes the oracle finishes in seconds: several 64-token tiles, ragged
+tails, empty context, every loop of every anchor group, split-count variants, shared and
+chained layouts, GQA, float32 and BF16 queries.  Everything goes through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+from looped_transformer_decode_amd import synth
+from oracle import residualquant as RQ
+
+from _support import (assert_stats, check_encoding, check_pack_block, close, device_block, gpu_pack,
+                      new_stats, oracle_cfg, say, slice_enc, sub_cache)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    from looped_transformer_decode_amd import binding
+    return binding
+
+
+W = synth.WORKLOADS
+CASES = {
+    # name: (workload, chained, batch, ctx_len per row, n_kv_heads override, n_q_heads override)
+    "tiny": (W["tiny_d64_t256"], False, 1, [256], None, None),
+    "tiny_chained": (W["tiny_d64_t256"], True, 1, [256], None, None),
+    "d128g32_ragged": (W["ouro_b4_t8192"], False, 4, [0, 1, 64, 300], 2, 2),
+    "d128g16int2_ragged": (W["int2g16_b4_t16384"], False, 3, [65, 200, 127], 2, 2),
+    "d128g16int2_chained": (W["int2g16_b4_t16384"], True, 3, [65, 200, 127], 2, 2),
+    "gqa4_two_groups": (W["huginn_gqa4_b8_t8192"].with_(n_groups=2), False, 2, [190, 77], 2, 8),
+    "d64_bf16q_ragged": (W["tiny_d64_t256"].with_(q_dtype="bf16"), False, 2, [129, 63], None, None),
+}
+
+
+def _setup(B, name, seed=1234):
+    wl, chained, batch, ctx, hkv, hq = CASES[name]
+    T = max(ctx)
+    wl = wl.with_(batch=batch, ctx=T, chained=chained,
+                  n_kv_heads=hkv or wl.n_kv_heads, n_q_heads=hq or wl.n_q_heads)
+    inp = synth.generate(wl, seed=seed, device="cuda")
+    cfg = B.config_for(wl)
+    ocfg = oracle_cfg(wl)
+    return wl, inp, cfg, ocfg, ctx, T
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_pack_context_parity(B, name):
+    wl, inp, cfg, ocfg, ctx, T = _setup(B, name)
+    say(f"[pack] case={name} T={T} batch={wl.batch}")
+    cache = gpu_pack(B, cfg, inp.kv, inp.rot, T)
+    torch.cuda.synchronize()
+    kv = inp.kv.double().cpu().numpy()
+    rot = inp.rot.double().cpu().numpy()
+    stats = new_stats()
+    for b in range(wl.batch):
+        for h in range(wl.n_kv_heads):
+            block = device_block(cache, ocfg, b, h)
+            _, sub = sub_cache(np.zeros(0, np.uint8), ocfg, 0, 0)
+            xs = [[kv[k, :, x, b, h, :T] for x in range(2)] for k in range(wl.n_groups)]
+            check_pack_block(block, sub, xs, rot[h], T, stats)
+    say(f"[pack] case={name} stats={stats}")
+    assert_stats(stats)
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_decode_step_parity(B, name):
+    """One decode step through every loop: attention at each loop (with the current token
+    written to the pending buffer), then the finished token packed from that buffer."""
+    wl, inp, cfg, ocfg, ctx, T = _setup(B, name, seed=99)
+    say(f"[decode] case={name} T={T} ctx={ctx}")
+    dev = inp.kv.device
+    L, d, Hq, Hkv = wl.loops_per_group, wl.head_dim, wl.n_q_heads, wl.n_kv_heads
+    cache = gpu_pack(B, cfg, inp.kv, inp.rot, T)
+    ctx_len = torch.tensor(ctx, dtype=torch.int32, device=dev)
+    ws = torch.zeros(B.rq_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    pending = torch.zeros(wl.batch, L, 2, Hkv, d, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    cache_np = cache.cpu().numpy()
+    kv = inp.kv.double().cpu().numpy()
+    rot = inp.rot.double().cpu().numpy()
+    own = RQ.pack_context(kv, rot, ocfg, T)
+    lay = RQ.Layout(ocfg)
+    sc = synth.sm_scale(d)
+    n_tiles = -(-T // 64)
+    for loop in range(wl.n_loops):
+        grp, l = divmod(loop, L)
+        k_cur = inp.kv[grp, l, 0, :, :, T].contiguous()
+        v_cur = inp.kv[grp, l, 1, :, :, T].contiguous()
+        q = inp.q[loop].contiguous()
+        ref_gpu = RQ.decode_attention(cache_np, lay, loop, q.double().cpu().numpy(), kv[grp, l, 0, :, :, T],
+                                      kv[grp, l, 1, :, :, T], ctx, rot, sc)
+        ref_own = RQ.decode_attention(own, lay, loop, q.double().cpu().numpy(), kv[grp, l, 0, :, :, T],
+                                      kv[grp, l, 1, :, :, T], ctx, rot, sc)
+        for ns in sorted({0, 1, min(3, n_tiles), n_tiles}):
+            out = torch.full((wl.batch, Hq, d), float("nan"), dtype=torch.float32, device=dev)
+            say(f"[decode] case={name} loop={loop} n_splits={ns}")
+            B.rq_decode_attention(cfg, cache, loop, q, k_cur, v_cur, pending, ctx_len, T, inp.rot, sc, out,
+                                  ws, wl.batch, n_splits=ns)
+            torch.cuda.synchronize()
+            o = out.double().cpu().numpy()
+            assert np.all(np.isfinite(o))
+            e1, e2 = close(o, ref_gpu), close(o, ref_own)
+            say(f"    err/bound vs oracle(gpu cache)={e1:.3f} vs oracle(own cache)={e2:.3f}")
+            assert e1 <= 1.0 and e2 <= 1.0
+        if l == L - 1:
+            # pending now holds the current token of every loop of this group
+            want = inp.kv[grp, :, :, :, :, T].permute(2, 0, 1, 3, 4)
+            assert torch.equal(pending, want)
+            say(f"[decode] case={name} pack finished token of group {grp}")
+            B.rq_quantize_token(cfg, cache, pending, grp, ctx_len, inp.rot, wl.batch, 1)
+            torch.cuda.synchronize()
+            cache_np = cache.cpu().numpy()
+            stats = new_stats()
+            for b in range(wl.batch):
+                for h in range(Hkv):
+                    block, sub = sub_cache(cache_np, ocfg, b, h)
+                    for x in range(2):
+                        enc = RQ.read_tokens(block, RQ.Layout(sub), 0, 0, x, grp, ctx[b] + 1)
+                        check_encoding(slice_enc(enc, slice(ctx[b], ctx[b] + 1)),
+                                       kv[grp, :, x, b, h, T:T + 1], rot[h, x], sub, stats)
+            assert_stats(stats)
+
+
+@pytest.mark.parametrize("name", ["tiny", "d128g32_ragged", "gqa4_two_groups"])
+def test_bf16_decode_parity(B, name):
+    wl, inp, cfg, ocfg, ctx, T = _setup(B, name, seed=7)
+    say(f"[bf16] case={name} ctx={ctx}")
+    dev = inp.kv.device
+    d, Hq, Hkv = wl.head_dim, wl.n_q_heads, wl.n_kv_heads
+    bcfg = B.bf16_config_for(wl)
+    ws = torch.zeros(B.rq_bf16_workspace_bytes(bcfg), dtype=torch.uint8, device=dev)
+    ctx_len = torch.tensor(ctx, dtype=torch.int32, device=dev)
+    kv = inp.kv.double().cpu().numpy()
+    sc = synth.sm_scale(d)
+    gqa = Hq // Hkv
+    for loop in range(min(wl.n_loops, 4)):
+        grp, l = divmod(loop, wl.loops_per_group)
+        K = inp.kv[grp, l, 0]
+        V = inp.kv[grp, l, 1]
+        k_cur = K[:, :, T].contiguous()
+        v_cur = V[:, :, T].contiguous()
+        q = inp.q[loop].contiguous()
+        qn = q.double().cpu().numpy()
+        ref = np.zeros((wl.batch, Hq, d))
+        for b in range(wl.batch):
+            for hq in range(Hq):
+                h = hq // gqa
+                keys = np.concatenate([kv[grp, l, 0, b, h, :ctx[b]], kv[grp, l, 0, b, h, T][None]])
+                vals = np.concatenate([kv[grp, l, 1, b, h, :ctx[b]], kv[grp, l, 1, b, h, T][None]])
+                ref[b, hq] = RQ.attention(qn[b, hq], keys, vals, sc)
+        for ns in (0, 1):
+            out = torch.full((wl.batch, Hq, d), float("nan"), dtype=torch.float32, device=dev)
+            say(f"[bf16] case={name} loop={loop} n_splits={ns}")
+            B.rq_bf16_decode_attention(bcfg, K.contiguous(), V.contiguous(), q, k_cur, v_cur, False, ctx_len, T,
+                                       sc, out, ws, wl.batch, n_splits=ns)
+            torch.cuda.synchronize()
+            e = close(out.double().cpu().numpy(), ref)
+            say(f"    err/bound={e:.3f}")
+            assert e <= 1.0
+
+
+def test_bf16_append_writes_current_token(B):
+    wl, inp, cfg, ocfg, ctx, T = _setup(B, "d128g32_ragged", seed=8)
+    dev = inp.kv.device
+    bcfg = B.bf16_config_for(wl)
+    ws = torch.zeros(B.rq_bf16_workspace_bytes(bcfg), dtype=torch.uint8, device=dev)
+    ctx_len = torch.tensor(ctx, dtype=torch.int32, device=dev)
+    K = inp.kv[0, 0, 0].clone()
+    V = inp.kv[0, 0, 1].clone()
+    k_cur = torch.randn(wl.batch, wl.n_kv_heads, wl.head_dim, device=dev).to(torch.bfloat16)
+    v_cur = torch.randn(wl.batch, wl.n_kv_heads, wl.head_dim, device=dev).to(torch.bfloat16)
+    out = torch.empty(wl.batch, wl.n_q_heads, wl.head_dim, device=dev)
+    say("[bf16-append]")
+    B.rq_bf16_decode_attention(bcfg, K, V, inp.q[0].contiguous(), k_cur, v_cur, True, ctx_len, T,
+                               0.1, out, ws, wl.batch)
+    torch.cuda.synchronize()
+    for b, n in enumerate(ctx):
+        assert torch.equal(K[b, :, n], k_cur[b]) and torch.equal(V[b, :, n], v_cur[b])
+        assert torch.equal(K[b, :, :n], inp.kv[0, 0, 0, b, :, :n])
+
+
+def test_workspace_counters_return_to_zero(B):
+    wl, inp, cfg, ocfg, ctx, T = _setup(B, "d128g32_ragged", seed=9)
+    dev = inp.kv.device
+    cache = gpu_pack(B, cfg, inp.kv, inp.rot, T)
+    ws = torch.zeros(B.rq_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    ctx_len = torch.tensor(ctx, dtype=torch.int32, device=dev)
+    out = torch.empty(wl.batch, wl.n_q_heads, wl.head_dim, device=dev)
+    k_cur = inp.kv[0, 0, 0, :, :, T].contiguous()
+    v_cur = inp.kv[0, 0, 1, :, :, T].contiguous()
+    outs = []
+    say("[counters]")
+    for rep in range(3):
+        B.rq_decode_attention(cfg, cache, 0, inp.q[0].contiguous(), k_cur, v_cur, None, ctx_len, T, inp.rot, 0.1,
+                              out, ws, wl.batch, n_splits=3)
+        torch.cuda.synchronize()
+        outs.append(out.clone())
+    n_rec = wl.batch * wl.n_q_heads * 64 * (2 * wl.head_dim + 4) * 4
+    off = (n_rec + 255) // 256 * 256
+    assert int(ws[off:].count_nonzero()) == 0
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
