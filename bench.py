@@ -1,0 +1,261 @@
+"""Benchmark of the ResidualQuant decode hot path on one MI355X.
+
+One step = one layer's decode step of one token through every loop of the workload:
+for each loop, fused RQ decode attention (which also writes the current token into the
+BF16 pending buffer); after each anchor loop, rq_quantize_token packs the finished token
+of that anchor group.  Inputs (packed context, queries, current-token K/V) are resident
+in HBM before the timed region.  The BF16 decode kernel is timed on the same K/V.
+
+To measure HBM rather than the 256 MB Infinity Cache, every loop-step reads its own
+replica of the packed cache (replicas rotate; the same replica comes back only after
+more than 256 MB of other reads), which is what a multi-layer model sees between two
+loops of one layer.  Warm (single replica) figures are reported separately.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "ouro_b4_t8192"
+
+
+def algorithmic_bytes(wl, loop_local: int, chained: bool) -> int:
+    """Compressed bytes one loop-step must read: codes + FP8 metadata + BF16 c of every
+    plane the loop needs, for K and V, for all context tokens of all (row, KV head)."""
+    d, g = wl.head_dim, wl.group
+    A = d * wl.anchor_bits // 8 + 2 * d // g
+    R = d * wl.resid_bits // 8 + 2 * d // g + 2
+    L = wl.loops_per_group
+    n_res = 0 if loop_local == L - 1 else (L - 1 - loop_local if chained else 1)
+    return 2 * (A + n_res * R) * wl.batch * wl.ctx * wl.n_kv_heads
+
+
+def bf16_bytes(wl) -> int:
+    return 2 * 2 * wl.head_dim * wl.batch * wl.ctx * wl.n_kv_heads
+
+
+def cpu_baseline(wl, budget_s: float = 12.0):
+    """Time the float64 oracle (as it is) on a bounded sample of the same workload:
+    one residual loop-step of decode attention for single (row, KV head) pairs at the
+    full context, repeated until the time budget is used."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from looped_transformer_decode_amd import synth
+    from oracle import residualquant as RQ
+
+    T = wl.ctx
+    small = wl.with_(batch=1, n_kv_heads=1, n_q_heads=wl.n_q_heads // wl.n_kv_heads)
+    inp = synth.generate(small, seed=11, device="cpu")
+    cfg = RQ.Config(small.head_dim, small.group, small.anchor_bits, small.resid_bits,
+                    small.loops_per_group, small.n_groups, small.chained, 1, small.n_q_heads, 1, T + 1)
+    kv = inp.kv.double().numpy()
+    rot = inp.rot.double().numpy()
+    cache = RQ.pack_context(kv, rot, cfg, T)
+    lay = RQ.Layout(cfg)
+    q = inp.q.double().numpy()
+    sc = synth.sm_scale(small.head_dim)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        RQ.decode_attention(cache, lay, 0, q[0], kv[0, 0, 0, :, :, T], kv[0, 0, 1, :, :, T], [T], rot, sc)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    per_head_bytes = algorithmic_bytes(small, 0, small.chained)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {
+        "value": round(per_head_bytes * reps / el / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{reps} residual loop-steps of float64 oracle decode attention for one (row, KV head) "
+                  f"at {T} context tokens ({el:.1f} s)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--chained", action="store_true")
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--replicas", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decode hot path has no cross-GPU step here "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from looped_transformer_decode_amd import binding as B
+    from looped_transformer_decode_amd import synth
+
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[args.workload]
+    if args.chained:
+        wl = wl.with_(chained=True)
+    L, d, T, Bt = wl.loops_per_group, wl.head_dim, wl.ctx, wl.batch
+    print(f"[bench] workload={wl.name} chained={wl.chained}: generating inputs", file=sys.stderr, flush=True)
+    inp = synth.generate(wl, seed=20261202, device=dev)
+    cfg = B.config_for(wl)
+    cache_bytes = B.rq_cache_bytes(cfg)
+    cache = torch.zeros(cache_bytes, dtype=torch.uint8, device=dev)
+    pos0 = torch.zeros(Bt, dtype=torch.int32, device=dev)
+    for grp in range(wl.n_groups):
+        st = inp.kv[grp].stride()
+        B.rq_quantize_token(cfg, cache, inp.kv[grp], grp, pos0, inp.rot, Bt, T,
+                            pending_strides=(st[4], st[2], st[0], st[1], st[3]))
+    torch.cuda.synchronize()
+    n_rep = args.replicas or max(2, min(16, math.ceil(1.6e9 / cache_bytes)))
+    caches = [cache] + [cache.clone() for _ in range(n_rep - 1)]
+    print(f"[bench] packed context ({cache_bytes/1e6:.1f} MB), {n_rep} replicas", file=sys.stderr, flush=True)
+
+    q = [inp.q[i].contiguous() for i in range(wl.n_loops)]
+    k_cur = [inp.kv[i // L, i % L, 0, :, :, T].contiguous() for i in range(wl.n_loops)]
+    v_cur = [inp.kv[i // L, i % L, 1, :, :, T].contiguous() for i in range(wl.n_loops)]
+    ctx_len = torch.full((Bt,), T, dtype=torch.int32, device=dev)
+    pending = torch.zeros(Bt, L, 2, wl.n_kv_heads, d, dtype=torch.bfloat16, device=dev)
+    ws = torch.zeros(B.rq_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    out = torch.empty(Bt, wl.n_q_heads, d, dtype=torch.float32, device=dev)
+    sc = synth.sm_scale(d)
+    stream = torch.cuda.current_stream()
+    n_loops = wl.n_loops
+    ev = {}
+
+    def step(s, timed):
+        for loop in range(n_loops):
+            c = caches[(s * n_loops + loop) % n_rep]
+            if timed:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            B.rq_decode_attention(cfg, c, loop, q[loop], k_cur[loop], v_cur[loop], pending, ctx_len, T, inp.rot,
+                                  sc, out, ws, Bt, n_splits=args.splits, stream=stream)
+            if timed:
+                e1.record(stream)
+                ev.setdefault(("dec", loop % L), []).append((e0, e1))
+            if loop % L == L - 1:
+                if timed:
+                    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    p0.record(stream)
+                B.rq_quantize_token(cfg, c, pending, loop // L, ctx_len, inp.rot, Bt, 1, stream=stream)
+                if timed:
+                    p1.record(stream)
+                    ev.setdefault(("pack",), []).append((p0, p1))
+
+    for s in range(args.warmup):
+        step(s, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(args.warmup + s, True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    def avg_ms(key):
+        v = [a.elapsed_time(b) for a, b in ev[key]]
+        return sum(v) / len(v)
+
+    per_loop = {l: avg_ms(("dec", l)) for l in range(L)}
+    pack_ms = avg_ms(("pack",))
+    step_bytes = sum(algorithmic_bytes(wl, l % L, wl.chained) for l in range(n_loops))
+    res_loops = [l for l in range(L - 1)]
+    res_ms = sum(per_loop[l] for l in res_loops) / len(res_loops)
+    res_bytes = algorithmic_bytes(wl, 0, False)
+    anchor_bytes = algorithmic_bytes(wl, L - 1, False)
+    res_gbps = res_bytes / (res_ms * 1e-3) / 1e9
+
+    # warm: single replica, residual loop 0 repeated
+    for _ in range(3):
+        B.rq_decode_attention(cfg, cache, 0, q[0], k_cur[0], v_cur[0], None, ctx_len, T, inp.rot, sc, out, ws, Bt,
+                              n_splits=args.splits, stream=stream)
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    for _ in range(10):
+        B.rq_decode_attention(cfg, cache, 0, q[0], k_cur[0], v_cur[0], None, ctx_len, T, inp.rot, sc, out, ws, Bt,
+                              n_splits=args.splits, stream=stream)
+    w1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) / 10
+
+    # BF16 baseline on the same K/V: every loop of one anchor group (own K/V per loop)
+    bcfg = B.bf16_config_for(wl)
+    bws = torch.zeros(B.rq_bf16_workspace_bytes(bcfg), dtype=torch.uint8, device=dev)
+    Ks = [inp.kv[0, l, 0] for l in range(L)]
+    Vs = [inp.kv[0, l, 1] for l in range(L)]
+    for l in range(L):
+        B.rq_bf16_decode_attention(bcfg, Ks[l], Vs[l], q[l], k_cur[l], v_cur[l], False, ctx_len, T, sc, out, bws,
+                                   Bt, n_splits=args.splits, stream=stream)
+    bev = []
+    for s in range(max(3, args.steps // 2)):
+        for l in range(L):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            B.rq_bf16_decode_attention(bcfg, Ks[l], Vs[l], q[l], k_cur[l], v_cur[l], False, ctx_len, T, sc, out,
+                                       bws, Bt, n_splits=args.splits, stream=stream)
+            e1.record(stream)
+            bev.append((e0, e1))
+    torch.cuda.synchronize()
+    bf16_ms = sum(a.elapsed_time(b) for a, b in bev) / len(bev)
+    bf16_gbps = bf16_bytes(wl) / (bf16_ms * 1e-3) / 1e9
+
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    result = {
+        "metric": "RQ decode-attn HBM GB/s (% of peak) & KV-tokens/s read, vs BF16 decode",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded stand-in for Ouro/Huginn K/V: anchor N(0,1) with x8 key outliers, "
+                "loops a_l*anchor + 0.15 N(0,1) + drift), random orthogonal rotations",
+        "config": {"workload": wl.name, "batch": Bt, "ctx": T, "n_q_heads": wl.n_q_heads,
+                   "n_kv_heads": wl.n_kv_heads, "head_dim": d, "loops": wl.n_loops,
+                   "loops_per_group": L, "group": wl.group, "anchor_bits": wl.anchor_bits,
+                   "resid_bits": wl.resid_bits, "chained": wl.chained, "cache_replicas": n_rep},
+        "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "kv_tokens_per_s": round(Bt * T / (res_ms * 1e-3), 1),
+        "step": {"bytes": step_bytes, "ms_wall": round(ms_step, 4),
+                 "ms_per_loop_step": {str(l): round(v, 4) for l, v in per_loop.items()},
+                 "ms_pack": round(pack_ms, 4)},
+        "residual_loop_step": {"bytes": res_bytes, "ms": round(res_ms, 4), "gbps": round(res_gbps, 1),
+                               "warm_single_replica_ms": round(warm_ms, 4)},
+        "anchor_loop_step": {"bytes": anchor_bytes, "ms": round(per_loop[L - 1], 4),
+                             "gbps": round(anchor_bytes / (per_loop[L - 1] * 1e-3) / 1e9, 1)},
+        "bf16": {"bytes": bf16_bytes(wl), "ms_per_loop_step": round(bf16_ms, 4), "gbps": round(bf16_gbps, 1),
+                 "speedup_rq_residual_vs_bf16": round(bf16_ms / res_ms, 3),
+                 "speedup_rq_step_vs_bf16_step": round(bf16_ms * n_loops / ms_step, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(res_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(res_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "rq_decode_kernel (residual loop-step)"},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -73,9 +73,9 @@ typedef struct rq_config {
  * KV head per K|V.  Returns 0 for an invalid or unsupported configuration. */
 size_t rq_cache_bytes(const rq_config* cfg);
 
-/* Bytes of scratch that rq_decode_attention needs for `cfg` (split-K partial results
- * and one arrival counter per (batch row, query head)).  The caller allocates it and
- * zero-fills it ONCE before first use; every call leaves the counters at zero again. */
+/* Bytes of scratch that rq_decode_attention needs for `cfg`: one split-K partial record
+ * (unnormalised output, running max, denominator) per (batch row, query head, split).
+ * The caller allocates it; its contents need no initialisation and are not kept. */
 size_t rq_workspace_bytes(const rq_config* cfg);
 
 /* Shape of one loop's uncompressed BF16 cache for the baseline decode kernel. */
@@ -128,7 +128,7 @@ rq_status rq_quantize_token(const rq_config* cfg, void* cache, const uint16_t* p
  * anchor a loop reads two planes (anchor + its residual), chained loop l reads the
  * anchor and the residual planes l..L-2.  The kernel never rebuilds K/V explicitly:
  * score_j = C_j (q . a_j) + sum_k gamma_jk (R_K q) . r_jk and the output accumulates
- * sum p_j C_j a_j and sum p_j gamma_jk r_jk separately, applying R_V^T once.  The
+ * sum p_j C_j a_j and sum p_j gamma_jk r_jk separately, applying R_V^T once per split.  The
  * current token (not yet quantized) is the last attention entry, in BF16.
  * For each batch row b and query head hq (KV head h = hq / (Hq/Hkv)):
  *   out[b][hq] = softmax over j in [0, ctx_len[b]) and the current token of
@@ -144,7 +144,7 @@ rq_status rq_quantize_token(const rq_config* cfg, void* cache, const uint16_t* p
  *   ctx_bound : host upper bound of every ctx_len[b], 0..max_ctx; sizes the launch.
  *   rot       : device float32 [n_kv_heads][2][head_dim][head_dim].
  *   out       : device float32 [batch][n_q_heads][head_dim].
- *   workspace : device, >= rq_workspace_bytes(cfg) bytes, zero-filled once before first use.
+ *   workspace : device, >= rq_workspace_bytes(cfg) bytes of scratch.
  *   n_splits  : split-K factor 1..64, or 0 to let the library choose.
  * Alignment: cache, q, k_cur, v_cur, pending, out, rot and workspace 16-byte aligned. */
 rq_status rq_decode_attention(const rq_config* cfg, const void* cache, int32_t loop,
@@ -161,7 +161,7 @@ rq_status rq_decode_attention(const rq_config* cfg, const void* cache, int32_t l
  *   k_cache, v_cache : device BF16 [max_batch][n_kv_heads][t_cap][head_dim] of one loop.
  *   append    : if nonzero, k_cur/v_cur are also stored at slot ctx_len[b] (when < t_cap).
  *   ctx_bound : host upper bound of every ctx_len[b], 0..t_cap.
- *   workspace : >= rq_bf16_workspace_bytes(cfg) bytes, zero-filled once before first use.
+ *   workspace : >= rq_bf16_workspace_bytes(cfg) bytes of scratch.
  * Other arguments as for rq_decode_attention. */
 rq_status rq_bf16_decode_attention(const rq_bf16_config* cfg, uint16_t* k_cache, uint16_t* v_cache,
                                    const void* q, int32_t q_is_bf16,

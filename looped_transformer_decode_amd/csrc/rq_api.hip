@@ -167,21 +167,30 @@ rq_status rq_decode_attention(const rq_config* cfg, const void* cache, int32_t l
     a.cache = static_cast<const uint8_t*>(cache);
     a.loop = loop;
     a.q = q;
-    a.k_cur = k_cur;
-    a.v_cur = v_cur;
-    a.pending = pending;
     a.ctx_len = ctx_len;
     a.ctx_bound = ctx_bound;
     a.rot = rot;
     a.sm_scale = sm_scale;
-    a.out = out;
     a.partials = static_cast<float*>(workspace);
-    a.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) +
-                                             workspace_counter_offset(g.max_batch, g.hq, g.d));
     a.batch = batch;
     a.n_splits = S;
     a.tiles_per_split = n_tiles > 0 ? (n_tiles + S - 1) / S : 0;
-    return launch_decode(a, nres, q_is_bf16 != 0, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
+    if (launch_decode(a, nres, q_is_bf16 != 0, stream) != hipSuccess) return RQ_ERR_HIP;
+    CombineArgs c;
+    memset(&c, 0, sizeof(c));
+    c.partials = a.partials;
+    c.n_splits = S;
+    c.q = q;
+    c.k_cur = k_cur;
+    c.v_cur = v_cur;
+    c.hkv = g.hkv;
+    c.hq = g.hq;
+    c.sm_scale = sm_scale;
+    c.out = out;
+    c.pending = pending;
+    c.L = g.L;
+    c.lloc = lloc;
+    return launch_combine(c, g.d, q_is_bf16 != 0, batch, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 
 rq_status rq_bf16_decode_attention(const rq_bf16_config* cfg, uint16_t* k_cache, uint16_t* v_cache,
@@ -215,20 +224,33 @@ rq_status rq_bf16_decode_attention(const rq_bf16_config* cfg, uint16_t* k_cache,
     a.hkv = cfg->n_kv_heads;
     a.hq = n_q_heads;
     a.q = q;
-    a.k_cur = k_cur;
-    a.v_cur = v_cur;
-    a.append = append ? 1 : 0;
     a.ctx_len = ctx_len;
     a.ctx_bound = ctx_bound;
     a.sm_scale = sm_scale;
-    a.out = out;
     a.partials = static_cast<float*>(workspace);
-    a.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) +
-                                             workspace_counter_offset(cfg->max_batch, n_q_heads, head_dim));
     a.batch = batch;
     a.n_splits = S;
     a.tiles_per_split = n_tiles > 0 ? (n_tiles + S - 1) / S : 0;
-    return launch_bf16(a, head_dim, q_is_bf16 != 0, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
+    if (launch_bf16(a, head_dim, q_is_bf16 != 0, stream) != hipSuccess) return RQ_ERR_HIP;
+    CombineArgs c;
+    memset(&c, 0, sizeof(c));
+    c.partials = a.partials;
+    c.n_splits = S;
+    c.q = q;
+    c.k_cur = k_cur;
+    c.v_cur = v_cur;
+    c.hkv = cfg->n_kv_heads;
+    c.hq = n_q_heads;
+    c.sm_scale = sm_scale;
+    c.out = out;
+    if (append) {
+        c.k_app = k_cache;
+        c.v_app = v_cache;
+        c.t_cap = cfg->t_cap;
+        c.ctx_len = ctx_len;
+        c.ctx_bound = ctx_bound;
+    }
+    return launch_combine(c, head_dim, q_is_bf16 != 0, batch, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 
 }  // extern "C"

@@ -22,41 +22,51 @@ struct DecodeArgs {
     const uint8_t* cache;
     int loop;
     const void* q;
-    const uint16_t* k_cur;
-    const uint16_t* v_cur;
-    uint16_t* pending;
     const int32_t* ctx_len;
     int ctx_bound;
     const float* rot;
     float sm_scale;
-    float* out;
     float* partials;
-    uint32_t* counters;
     int batch;
     int n_splits;
     int tiles_per_split;
 };
 
 struct Bf16Args {
-    uint16_t* k;
-    uint16_t* v;
+    const uint16_t* k;
+    const uint16_t* v;
     int t_cap, hkv, hq;
     const void* q;
-    const uint16_t* k_cur;
-    const uint16_t* v_cur;
-    int append;
     const int32_t* ctx_len;
     int ctx_bound;
     float sm_scale;
-    float* out;
     float* partials;
-    uint32_t* counters;
     int batch;
     int n_splits;
     int tiles_per_split;
 };
 
+// Merge of the split-K partial records of one loop-step, plus the current token.
+struct CombineArgs {
+    const float* partials;      // [batch * hq][kMaxSplits][d + 4]
+    int n_splits;
+    const void* q;
+    const uint16_t* k_cur;      // [batch][hkv][d]
+    const uint16_t* v_cur;
+    int hkv, hq;
+    float sm_scale;
+    float* out;                 // [batch][hq][d]
+    uint16_t* pending;          // ResidualQuant: [batch][L][2][hkv][d] or null
+    int L, lloc;
+    uint16_t* k_app;            // BF16 baseline append target [batch][hkv][t_cap][d] or null
+    uint16_t* v_app;
+    int t_cap;
+    const int32_t* ctx_len;
+    int ctx_bound;
+};
+
 hipError_t launch_pack(const PackArgs& a, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, int d, bool qbf16, int batch, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int nres, bool qbf16, hipStream_t st);
 hipError_t launch_bf16(const Bf16Args& a, int d, bool qbf16, hipStream_t st);
 

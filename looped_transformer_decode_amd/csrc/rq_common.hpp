@@ -33,16 +33,10 @@ struct Geom {
 bool make_geom(const rq_config* cfg, Geom* g);
 
 // Workspace layout for split-K decode: per (batch row, query head, split) a record of
-// acc_a[d], acc_r[d], m, l (+2 pad); then one uint32 arrival counter per (row, query head).
-__host__ __device__ inline int partial_stride(int d) { return 2 * d + 4; }
+// o[d] (unnormalised output), m (running max), l (denominator), 2 floats of padding.
+__host__ __device__ inline int partial_stride(int d) { return d + 4; }
 inline size_t workspace_bytes(int max_batch, int hq, int d) {
-    size_t rec = (size_t)max_batch * hq * kMaxSplits * partial_stride(d) * sizeof(float);
-    size_t cnt = (size_t)max_batch * hq * sizeof(uint32_t);
-    return ((rec + 255) & ~(size_t)255) + ((cnt + 255) & ~(size_t)255);
-}
-inline size_t workspace_counter_offset(int max_batch, int hq, int d) {
-    size_t rec = (size_t)max_batch * hq * kMaxSplits * partial_stride(d) * sizeof(float);
-    return (rec + 255) & ~(size_t)255;
+    return (size_t)max_batch * hq * kMaxSplits * partial_stride(d) * sizeof(float);
 }
 
 // ---------------------------------------------------------------- number formats

@@ -44,6 +44,15 @@ __device__ __forceinline__ uint32_t load_meta(const uint8_t* p) {
     else return *reinterpret_cast<const uint32_t*>(p);
 }
 
+// Raw bytes of one token-pass for one lane: K and V words of the anchor plane and of the
+// NR residual planes, with their metadata and coefficients.
+template <int AW, int NR>
+struct Frame {
+    uint32_t ka[AW], kam, va[AW], vam;
+    uint32_t kr[NR][2], krm[NR], kc[NR];
+    uint32_t vr[NR][2], vrm[NR], vc[NR];
+};
+
 // D: head dim; GS: group size; BA: anchor bits; NRES: residual planes read (0 = anchor loop).
 template <int D, int GS, int BA, int NRES, bool QBF16>
 __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
@@ -52,31 +61,76 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
     constexpr int PPT = kTile / SLOTS;     // passes per tile
     constexpr int GPL = 32 / GS;           // quantization groups per lane
     constexpr int AB = 32 * BA / 8;        // anchor code bytes per lane
+    constexpr int AW = AB / 4;
+    constexpr int NR = NRES ? NRES : 1;
     constexpr int NV = NRES ? 64 : 32;
 
     const Geom& G = a.geo;
-    const int nwg = gridDim.x;
-    const int lb = xcd_logical_block(blockIdx.x, nwg);
+    const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
     const int split = lb % a.n_splits;
     const int bh = lb / a.n_splits;        // b * Hq + hq
     const int hq = bh % G.hq;
     const int b = bh / G.hq;
-    const int gqa = G.hq / G.hkv;
-    const int h = hq / gqa;
+    const int h = hq / (G.hq / G.hkv);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int chunk = lane % LPT, slot = lane / LPT;
 
     __shared__ float sq[D];
     __shared__ float su[D];
-    __shared__ EpilogueSmem<D> sm;
+    __shared__ SplitSmem<D> sm;
 
     int n = a.ctx_len[b];
     n = n < 0 ? 0 : (n > a.ctx_bound ? a.ctx_bound : n);
     const int n_tiles = (n + kTile - 1) / kTile;
     const int t_begin = split * a.tiles_per_split;
     const int t_end = min(n_tiles, t_begin + a.tiles_per_split);
+    const int first = t_begin + w;
+    const int my_tiles = first < t_end ? (t_end - first + kWaves - 1) / kWaves : 0;
+    const int n_it = my_tiles * PPT;
 
-    // ---- prologue: q and u = R_K q
+    // ---- plane bases
+    const int L = G.L;
+    const int aloop = (a.loop / L) * L + L - 1;
+    const uint8_t* aK = a.cache + G.plane_offset(b, h, 0, aloop);
+    const uint8_t* aV = a.cache + G.plane_offset(b, h, 1, aloop);
+    const uint8_t* rK[NR];
+    const uint8_t* rV[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        rK[k] = a.cache + G.plane_offset(b, h, 0, a.loop + k);
+        rV[k] = a.cache + G.plane_offset(b, h, 1, a.loop + k);
+    }
+    const int a_meta = kTile * G.a_row;
+    const int r_meta = kTile * G.r_row;
+    const int r_cblk = kTile * (G.r_row + G.m_row);
+
+    auto load = [&](Frame<AW, NR>& f, int it) {
+        const int tile = first + kWaves * (it / PPT);
+        const int jj = (it % PPT) * SLOTS + slot;
+        const int64_t ta = (int64_t)tile * G.a_tile + jj * G.a_row + chunk * AB;
+        const int64_t tm = (int64_t)tile * G.a_tile + a_meta + jj * G.m_row + chunk * GPL * 2;
+        load_words<AB>(f.ka, aK + ta);
+        load_words<AB>(f.va, aV + ta);
+        f.kam = load_meta<GPL>(aK + tm);
+        f.vam = load_meta<GPL>(aV + tm);
+        if constexpr (NRES > 0) {
+            const int64_t tr = (int64_t)tile * G.r_tile;
+#pragma unroll
+            for (int k = 0; k < NRES; ++k) {
+                load_words<8>(f.kr[k], rK[k] + tr + jj * G.r_row + chunk * 8);
+                load_words<8>(f.vr[k], rV[k] + tr + jj * G.r_row + chunk * 8);
+                f.krm[k] = load_meta<GPL>(rK[k] + tr + r_meta + jj * G.m_row + chunk * GPL * 2);
+                f.vrm[k] = load_meta<GPL>(rV[k] + tr + r_meta + jj * G.m_row + chunk * GPL * 2);
+                f.kc[k] = *reinterpret_cast<const uint16_t*>(rK[k] + tr + r_cblk + jj * 2);
+                f.vc[k] = *reinterpret_cast<const uint16_t*>(rV[k] + tr + r_cblk + jj * 2);
+            }
+        }
+    };
+
+    Frame<AW, NR> fa, fb;
+    if (n_it > 0) load(fa, 0);
+
+    // ---- prologue (overlaps the first loads): q and u = R_K q
     for (int i = threadIdx.x; i < D; i += kThreads) {
         float qv;
         if constexpr (QBF16)
@@ -86,8 +140,8 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
         sq[i] = qv;
     }
     __syncthreads();
-    const float* RK = a.rot + (int64_t)(h * 2 + 0) * D * D;
     if constexpr (NRES > 0) {
+        const float* RK = a.rot + (int64_t)(h * 2 + 0) * D * D;
         constexpr int TPR = kThreads / D;          // threads per row
         constexpr int COLS = D / TPR;
         const int row = threadIdx.x / TPR, part = threadIdx.x % TPR;
@@ -123,23 +177,6 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
         Ug[gg] = s2;
     }
 
-    // ---- plane bases
-    const int L = G.L;
-    const int grp = a.loop / L, lloc = a.loop % L;
-    const int aloop = grp * L + L - 1;
-    const uint8_t* aK = a.cache + G.plane_offset(b, h, 0, aloop);
-    const uint8_t* aV = a.cache + G.plane_offset(b, h, 1, aloop);
-    const uint8_t* rK[NRES ? NRES : 1];
-    const uint8_t* rV[NRES ? NRES : 1];
-#pragma unroll
-    for (int k = 0; k < NRES; ++k) {
-        rK[k] = a.cache + G.plane_offset(b, h, 0, a.loop + k);
-        rV[k] = a.cache + G.plane_offset(b, h, 1, a.loop + k);
-    }
-    const int a_meta = kTile * G.a_row;
-    const int r_meta = kTile * G.r_row;
-    const int r_cblk = kTile * (G.r_row + G.m_row);
-
     float accA[32], accR[NRES ? 32 : 1], offA[GPL], offR[GPL];
 #pragma unroll
     for (int i = 0; i < 32; ++i) accA[i] = 0.f;
@@ -150,99 +187,90 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
     float m_run = -INFINITY, l_lane = 0.f;
     const float sm_scale = a.sm_scale;
 
-    for (int tile = t_begin + w; tile < t_end; tile += kWaves) {
-        const int64_t ta = (int64_t)tile * G.a_tile, tr = (int64_t)tile * G.r_tile;
-#pragma unroll 1
-        for (int p = 0; p < PPT; ++p) {
-            const int jj = p * SLOTS + slot;
-            const bool valid = tile * kTile + jj < n;
-            // ---------------- keys
-            uint32_t wa[AB / 4];
-            load_words<AB>(wa, aK + ta + jj * G.a_row + chunk * AB);
-            const uint32_t ma = load_meta<GPL>(aK + ta + a_meta + jj * G.m_row + chunk * GPL * 2);
-            float part_a = 0.f;
+    auto compute = [&](const Frame<AW, NR>& f, int it) {
+        const int tile = first + kWaves * (it / PPT);
+        const int jj = (it % PPT) * SLOTS + slot;
+        const bool valid = tile * kTile + jj < n;
+        // ---------------- keys
+        float part_a = 0.f;
+#pragma unroll
+        for (int gg = 0; gg < GPL; ++gg) {
+            const float z = e4m3_to_f32((f.kam >> (16 * gg)) & 0xFF);
+            const float s = e4m3_to_f32((f.kam >> (16 * gg + 8)) & 0xFF);
+            float dot = 0.f;
+#pragma unroll
+            for (int i = 0; i < GS; ++i) dot += qr[gg * GS + i] * code_f<BA>(f.ka, gg * GS + i);
+            part_a += z * Qg[gg] + s * dot;
+        }
+        float coef = 1.f, part_r = 0.f;
+#pragma unroll
+        for (int k = 0; k < NRES; ++k) {
+            float pr = 0.f;
 #pragma unroll
             for (int gg = 0; gg < GPL; ++gg) {
-                const float z = e4m3_to_f32((ma >> (16 * gg)) & 0xFF);
-                const float s = e4m3_to_f32((ma >> (16 * gg + 8)) & 0xFF);
+                const float z = e4m3_to_f32((f.krm[k] >> (16 * gg)) & 0xFF);
+                const float s = e4m3_to_f32((f.krm[k] >> (16 * gg + 8)) & 0xFF);
                 float dot = 0.f;
 #pragma unroll
-                for (int i = 0; i < GS; ++i) dot += qr[gg * GS + i] * code_f<BA>(wa, gg * GS + i);
-                part_a += z * Qg[gg] + s * dot;
+                for (int i = 0; i < GS; ++i) dot += ur[gg * GS + i] * code_f<2>(f.kr[k], gg * GS + i);
+                pr += z * Ug[gg] + s * dot;
             }
-            float coef = 1.f, part_r = 0.f;
+            part_r += coef * pr;
+            coef *= valid ? bf16_to_f32(f.kc[k]) : 0.f;
+        }
+        float score = chunk_sum<LPT>(coef * part_a + part_r) * sm_scale;
+        score = valid ? score : -INFINITY;
+        const float pmax = slot_max<LPT>(score);
+        if (pmax > m_run) {                         // uniform across the wave
+            const float fs = __expf(m_run - pmax);
 #pragma unroll
-            for (int k = 0; k < NRES; ++k) {
-                uint32_t wr[2];
-                load_words<8>(wr, rK[k] + tr + jj * G.r_row + chunk * 8);
-                const uint32_t mr = load_meta<GPL>(rK[k] + tr + r_meta + jj * G.m_row + chunk * GPL * 2);
-                const uint32_t cb = *reinterpret_cast<const uint16_t*>(rK[k] + tr + r_cblk + jj * 2);
-                float pr = 0.f;
+            for (int i = 0; i < 32; ++i) accA[i] *= fs;
 #pragma unroll
-                for (int gg = 0; gg < GPL; ++gg) {
-                    const float z = e4m3_to_f32((mr >> (16 * gg)) & 0xFF);
-                    const float s = e4m3_to_f32((mr >> (16 * gg + 8)) & 0xFF);
-                    float dot = 0.f;
+            for (int i = 0; i < (NRES ? 32 : 1); ++i) accR[i] *= fs;
 #pragma unroll
-                    for (int i = 0; i < GS; ++i) dot += ur[gg * GS + i] * code_f<2>(wr, gg * GS + i);
-                    pr += z * Ug[gg] + s * dot;
-                }
-                part_r += coef * pr;
-                coef *= valid ? bf16_to_f32(cb) : 0.f;
+            for (int gg = 0; gg < GPL; ++gg) { offA[gg] *= fs; offR[gg] *= fs; }
+            l_lane *= fs;
+            m_run = pmax;
+        }
+        const float pw = valid ? __expf(score - m_run) : 0.f;
+        l_lane += pw;
+        // ---------------- values
+        float wv = pw;
+#pragma unroll
+        for (int k = 0; k < NRES; ++k) {
+#pragma unroll
+            for (int gg = 0; gg < GPL; ++gg) {
+                const float z = e4m3_to_f32((f.vrm[k] >> (16 * gg)) & 0xFF);
+                const float s = e4m3_to_f32((f.vrm[k] >> (16 * gg + 8)) & 0xFF);
+                offR[gg] += wv * z;
+                const float ws = wv * s;
+#pragma unroll
+                for (int i = 0; i < GS; ++i) accR[gg * GS + i] += ws * code_f<2>(f.vr[k], gg * GS + i);
             }
-            float score = chunk_sum<LPT>(coef * part_a + part_r) * sm_scale;
-            score = valid ? score : -INFINITY;
-            const float pmax = slot_max<LPT>(score);
-            if (pmax > m_run) {                         // uniform across the wave
-                const float f = __expf(m_run - pmax);
+            wv *= valid ? bf16_to_f32(f.vc[k]) : 0.f;
+        }
 #pragma unroll
-                for (int i = 0; i < 32; ++i) accA[i] *= f;
+        for (int gg = 0; gg < GPL; ++gg) {
+            const float z = e4m3_to_f32((f.vam >> (16 * gg)) & 0xFF);
+            const float s = e4m3_to_f32((f.vam >> (16 * gg + 8)) & 0xFF);
+            offA[gg] += wv * z;
+            const float ws = wv * s;
 #pragma unroll
-                for (int i = 0; i < (NRES ? 32 : 1); ++i) accR[i] *= f;
-#pragma unroll
-                for (int gg = 0; gg < GPL; ++gg) { offA[gg] *= f; offR[gg] *= f; }
-                l_lane *= f;
-                m_run = pmax;
-            }
-            const float pw = valid ? __expf(score - m_run) : 0.f;
-            l_lane += pw;
-            // ---------------- values
-            float wv = pw;
-#pragma unroll
-            for (int k = 0; k < NRES; ++k) {
-                uint32_t wr[2];
-                load_words<8>(wr, rV[k] + tr + jj * G.r_row + chunk * 8);
-                const uint32_t mr = load_meta<GPL>(rV[k] + tr + r_meta + jj * G.m_row + chunk * GPL * 2);
-                const uint32_t cb = *reinterpret_cast<const uint16_t*>(rV[k] + tr + r_cblk + jj * 2);
-#pragma unroll
-                for (int gg = 0; gg < GPL; ++gg) {
-                    const float z = e4m3_to_f32((mr >> (16 * gg)) & 0xFF);
-                    const float s = e4m3_to_f32((mr >> (16 * gg + 8)) & 0xFF);
-                    offR[gg] += wv * z;
-                    const float ws = wv * s;
-#pragma unroll
-                    for (int i = 0; i < GS; ++i) accR[gg * GS + i] += ws * code_f<2>(wr, gg * GS + i);
-                }
-                wv *= valid ? bf16_to_f32(cb) : 0.f;
-            }
-            {
-                uint32_t wv_a[AB / 4];
-                load_words<AB>(wv_a, aV + ta + jj * G.a_row + chunk * AB);
-                const uint32_t mv = load_meta<GPL>(aV + ta + a_meta + jj * G.m_row + chunk * GPL * 2);
-#pragma unroll
-                for (int gg = 0; gg < GPL; ++gg) {
-                    const float z = e4m3_to_f32((mv >> (16 * gg)) & 0xFF);
-                    const float s = e4m3_to_f32((mv >> (16 * gg + 8)) & 0xFF);
-                    offA[gg] += wv * z;
-                    const float ws = wv * s;
-#pragma unroll
-                    for (int i = 0; i < GS; ++i) accA[gg * GS + i] += ws * code_f<BA>(wv_a, gg * GS + i);
-                }
-            }
+            for (int i = 0; i < GS; ++i) accA[gg * GS + i] += ws * code_f<BA>(f.va, gg * GS + i);
+        }
+    };
+
+    // ---- main loop, two frames in flight
+    for (int it = 0; it < n_it; it += 2) {
+        if (it + 1 < n_it) load(fb, it + 1);
+        compute(fa, it);
+        if (it + 1 < n_it) {
+            if (it + 2 < n_it) load(fa, it + 2);
+            compute(fb, it + 1);
         }
     }
 
-    // ---- fold group offsets, reduce, write the partial record
+    // ---- fold group offsets, merge the waves, apply R_V^T to the residual part
     float v[NV];
 #pragma unroll
     for (int i = 0; i < 32; ++i) v[i] = accA[i] + offA[i / GS];
@@ -250,46 +278,35 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) v[32 + i] = accR[i] + offR[i / GS];
     }
-    float* recs = a.partials + (int64_t)bh * kMaxSplits * partial_stride(D);
-    const bool last = splitk_epilogue<D, NV>(v, m_run, l_lane, recs + (int64_t)split * partial_stride(D),
-                                            a.counters + bh, a.n_splits, sm);
-    if (!last) return;
-
-    // ---- final merge (last workgroup of this row and query head)
-    const uint16_t* kc = a.k_cur + ((int64_t)b * G.hkv + h) * D;
-    const uint16_t* vc = a.v_cur + ((int64_t)b * G.hkv + h) * D;
-    float pc = 0.f;
-    for (int i = threadIdx.x; i < D; i += kThreads) pc += sq[i] * bf16_to_f32(kc[i]);
-    const float s_cur = block_reduce_sum<kThreads>(pc, sm.red) * sm_scale;
-    const MergeOut mo = splitk_merge_weights<D>(recs, a.n_splits, s_cur, sm);
-    // merged anchor part (thread t < D) and residual part (D <= t < 2D)
-    float merged = 0.f;
-    if (threadIdx.x < (NRES ? 2 * D : D)) {
-        for (int s = 0; s < a.n_splits; ++s)
-            merged += sm.wsplit[s] * recs[(int64_t)s * partial_stride(D) + threadIdx.x];
-    }
+    const float2 ml = splitk_merge_waves<D, NV>(v, m_run, l_lane, sm);
+    float* rec = a.partials + ((int64_t)bh * kMaxSplits + split) * partial_stride(D);
     if constexpr (NRES > 0) {
-        if (threadIdx.x >= D && threadIdx.x < 2 * D) sm.vec[threadIdx.x - D] = merged;
+        // o_i = A_i + sum_k R_V[k][i] * Rr_k ; TPR threads per output, k split in parts
+        const float* RV = a.rot + (int64_t)(h * 2 + 1) * D * D;
+        constexpr int PARTS = kThreads / D;
+        constexpr int KP = D / PARTS;
+        const int i = threadIdx.x % D, part = threadIdx.x / D;
+        float t0 = 0.f, t1 = 0.f;
+#pragma unroll 8
+        for (int k = part * KP; k < (part + 1) * KP; k += 2) {
+            t0 += RV[(int64_t)k * D + i] * sm.sum[D + k];
+            t1 += RV[(int64_t)(k + 1) * D + i] * sm.sum[D + k + 1];
+        }
+        sm.acc[part][i] = t0 + t1;                 // wave scratch is free again
         __syncthreads();
-    }
-    if (threadIdx.x < D) {
-        const int i = threadIdx.x;
-        float o = merged;
-        if constexpr (NRES > 0) {
-            const float* RV = a.rot + (int64_t)(h * 2 + 1) * D * D;
-            float t = 0.f;
-            for (int k = 0; k < D; ++k) t += RV[(int64_t)k * D + i] * sm.vec[k];
-            o += t;
+        if (threadIdx.x < D) {
+            float o = sm.sum[i];
+#pragma unroll
+            for (int p = 0; p < PARTS; ++p) o += sm.acc[p][i];
+            rec[i] = o;
         }
-        o += mo.p_cur * bf16_to_f32(vc[i]);
-        a.out[(int64_t)bh * D + i] = o / mo.denom;
-        if (a.pending != nullptr && hq % gqa == 0) {
-            uint16_t* pd = a.pending + (((int64_t)b * L + lloc) * 2 * G.hkv + h) * D;
-            pd[i] = kc[i];
-            pd[(int64_t)G.hkv * D + i] = vc[i];
-        }
+    } else {
+        if (threadIdx.x < D) rec[threadIdx.x] = sm.sum[threadIdx.x];
     }
-    if (threadIdx.x == 0) a.counters[bh] = 0u;
+    if (threadIdx.x == 0) {
+        rec[D] = ml.x;
+        rec[D + 1] = ml.y;
+    }
 }
 
 template <int D, int GS, int BA, bool QB>
@@ -311,6 +328,9 @@ static hipError_t launch_q(const DecodeArgs& a, int nres, bool qbf16, dim3 grid,
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int nres, bool qbf16, hipStream_t st) {
+    if (!a.cache || !a.q || !a.ctx_len || !a.rot || !a.partials || a.batch < 1 || a.n_splits < 1 ||
+        a.n_splits > kMaxSplits)
+        return hipErrorInvalidValue;
     const dim3 grid(a.batch * a.geo.hq * a.n_splits);
     const int d = a.geo.d, g = a.geo.g, ba = a.geo.ba;
     if (d == 128 && g == 32 && ba == 4) return launch_q<128, 32, 4>(a, nres, qbf16, grid, st);

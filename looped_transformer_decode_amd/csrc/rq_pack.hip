@@ -199,6 +199,7 @@ __global__ __launch_bounds__(D) void rq_pack_kernel(PackArgs a) {
 }
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t stream) {
+    if (!a.cache || !a.pending || !a.pos || !a.rot || a.batch < 1 || a.n_tokens < 1) return hipErrorInvalidValue;
     const int nwg = a.n_tokens * a.batch * a.geo.hkv * 2;
     if (a.geo.d == 128)
         hipLaunchKernelGGL(rq_pack_kernel<128>, dim3(nwg), dim3(128), 0, stream, a);

@@ -40,10 +40,11 @@ def oracle_cfg(wl, chained=None, max_batch=None, max_ctx=None, n_kv_heads=None, 
 
 
 def pending_strides(kv: torch.Tensor):
-    """Strides (token, batch, loop, K|V, head) of one group slice kv[grp] of the
-    generator's [G][L][2][B][Hkv][T+1][d] tensor."""
+    """Strides (token, batch, loop, K|V, head) of one group slice kv[grp], shaped
+    [L][2][B][Hkv][T+1][d], of the generator's K/V tensor."""
+    assert kv.dim() == 6
     st = kv.stride()
-    return (st[5], st[3], st[1], st[2], st[4])
+    return (st[4], st[2], st[0], st[1], st[3])
 
 
 def gpu_pack(B, cfg, kv: torch.Tensor, rot: torch.Tensor, n_tokens: int, cache=None, pos0=0):

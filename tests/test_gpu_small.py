@@ -180,23 +180,22 @@ def test_bf16_append_writes_current_token(B):
         assert torch.equal(K[b, :, :n], inp.kv[0, 0, 0, b, :, :n])
 
 
-def test_workspace_counters_return_to_zero(B):
+def test_repeated_calls_are_deterministic(B):
+    """The workspace holds only per-call scratch: repeated calls give identical outputs."""
     wl, inp, cfg, ocfg, ctx, T = _setup(B, "d128g32_ragged", seed=9)
     dev = inp.kv.device
     cache = gpu_pack(B, cfg, inp.kv, inp.rot, T)
-    ws = torch.zeros(B.rq_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    ws = torch.full((B.rq_workspace_bytes(cfg),), 255, dtype=torch.uint8, device=dev)   # garbage is fine
     ctx_len = torch.tensor(ctx, dtype=torch.int32, device=dev)
     out = torch.empty(wl.batch, wl.n_q_heads, wl.head_dim, device=dev)
     k_cur = inp.kv[0, 0, 0, :, :, T].contiguous()
     v_cur = inp.kv[0, 0, 1, :, :, T].contiguous()
     outs = []
-    say("[counters]")
+    say("[repeat]")
     for rep in range(3):
         B.rq_decode_attention(cfg, cache, 0, inp.q[0].contiguous(), k_cur, v_cur, None, ctx_len, T, inp.rot, 0.1,
                               out, ws, wl.batch, n_splits=3)
         torch.cuda.synchronize()
         outs.append(out.clone())
-    n_rec = wl.batch * wl.n_q_heads * 64 * (2 * wl.head_dim + 4) * 4
-    off = (n_rec + 255) // 256 * 256
-    assert int(ws[off:].count_nonzero()) == 0
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+    assert bool(torch.isfinite(outs[0]).all())
