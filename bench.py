@@ -135,11 +135,11 @@ def main():
     ws = torch.zeros(B.rq_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
     out = torch.empty(Bt, wl.n_q_heads, d, dtype=torch.float32, device=dev)
     sc = synth.sm_scale(d)
-    stream = torch.cuda.current_stream()
     n_loops = wl.n_loops
     ev = {}
 
     def step(s, timed):
+        stream = torch.cuda.current_stream()
         for loop in range(n_loops):
             c = caches[(s * n_loops + loop) % n_rep]
             if timed:
@@ -159,15 +159,32 @@ def main():
                     p1.record(stream)
                     ev.setdefault(("pack",), []).append((p0, p1))
 
+    # per-kernel durations: eager steps with events around each call
     for s in range(args.warmup):
         step(s, False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for s in range(args.steps):
         step(args.warmup + s, True)
     torch.cuda.synchronize()
+
+    # whole-step time: each step replayed from a HIP graph (one graph per replica pattern)
+    n_pat = n_rep // math.gcd(n_rep, n_loops)
+    graphs = []
+    for p_ in range(n_pat):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(p_, False)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for s in range(args.warmup):
+        graphs[s % n_pat].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        graphs[s % n_pat].replay()
+    torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
+    stream = torch.cuda.current_stream()
 
     def avg_ms(key):
         v = [a.elapsed_time(b) for a, b in ev[key]]
@@ -237,7 +254,7 @@ def main():
                    "resid_bits": wl.resid_bits, "chained": wl.chained, "cache_replicas": n_rep},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "kv_tokens_per_s": round(Bt * T / (res_ms * 1e-3), 1),
-        "step": {"bytes": step_bytes, "ms_wall": round(ms_step, 4),
+        "step": {"bytes": step_bytes, "ms_wall": round(ms_step, 4), "launch": "hip graph replay",
                  "ms_per_loop_step": {str(l): round(v, 4) for l, v in per_loop.items()},
                  "ms_pack": round(pack_ms, 4)},
         "residual_loop_step": {"bytes": res_bytes, "ms": round(res_ms, 4), "gbps": round(res_gbps, 1),

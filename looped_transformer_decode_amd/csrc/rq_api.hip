@@ -45,12 +45,15 @@ bool make_geom(const rq_config* c, Geom* g) {
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Split-K factor: about two workgroups per CU (4 waves each) in flight, and at least four
+// 64-token tiles per workgroup so that its prologue (queries, R_K q) and epilogue (wave
+// merge, R_V^T) stay small next to its stream.
 static int auto_splits(int batch, int hq, int n_tiles) {
     if (n_tiles <= 0) return 1;
-    // aim for >= 8 tiles (512 tokens) per split and enough workgroups to fill 256 CUs
-    int s = (n_tiles + 7) / 8;
-    const int heads = batch * hq;
-    while (s > 1 && heads * s > 4096) --s;
+    constexpr int kTargetWorkgroups = 512;
+    int s = (kTargetWorkgroups + batch * hq - 1) / (batch * hq);
+    const int by_tiles = n_tiles / 4 > 0 ? n_tiles / 4 : 1;
+    if (s > by_tiles) s = by_tiles;
     if (s > kMaxSplits) s = kMaxSplits;
     return s < 1 ? 1 : s;
 }
@@ -130,6 +133,7 @@ rq_status rq_quantize_token(const rq_config* cfg, void* cache, const uint16_t* p
     a.group_idx = group_idx;
     a.batch = batch;
     a.n_tokens = n_tokens;
+    a.tokens_per_wg = n_tokens <= 8 ? 1 : 32;
     return launch_pack(a, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 
@@ -167,9 +171,9 @@ rq_status rq_decode_attention(const rq_config* cfg, const void* cache, int32_t l
     a.cache = static_cast<const uint8_t*>(cache);
     a.loop = loop;
     a.q = q;
+    a.rot = rot;
     a.ctx_len = ctx_len;
     a.ctx_bound = ctx_bound;
-    a.rot = rot;
     a.sm_scale = sm_scale;
     a.partials = static_cast<float*>(workspace);
     a.batch = batch;
@@ -190,6 +194,7 @@ rq_status rq_decode_attention(const rq_config* cfg, const void* cache, int32_t l
     c.pending = pending;
     c.L = g.L;
     c.lloc = lloc;
+    c.rot_v = nres > 0 ? rot + (size_t)g.d * g.d : nullptr;      // R of (KV head 0, V)
     return launch_combine(c, g.d, q_is_bf16 != 0, batch, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 

@@ -15,16 +15,17 @@ struct PackArgs {
     int group_idx;
     int batch;
     int n_tokens;
+    int tokens_per_wg;          // tokens handled by one workgroup (it keeps its row of R)
 };
 
 struct DecodeArgs {
     Geom geo;
     const uint8_t* cache;
     int loop;
-    const void* q;
+    const void* q;              // [batch][hq][d], float32 or BF16
+    const float* rot;           // [hkv][2][d][d]
     const int32_t* ctx_len;
     int ctx_bound;
-    const float* rot;
     float sm_scale;
     float* partials;
     int batch;
@@ -32,6 +33,7 @@ struct DecodeArgs {
     int tiles_per_split;
 };
 
+// BF16 baseline split kernel: K and V caches [batch][hkv][t_cap][d].
 struct Bf16Args {
     const uint16_t* k;
     const uint16_t* v;
@@ -58,6 +60,7 @@ struct CombineArgs {
     float* out;                 // [batch][hq][d]
     uint16_t* pending;          // ResidualQuant: [batch][L][2][hkv][d] or null
     int L, lloc;
+    const float* rot_v;         // ResidualQuant residual loops: R_V of KV head h at rot_v + h*2*d*d, else null
     uint16_t* k_app;            // BF16 baseline append target [batch][hkv][t_cap][d] or null
     uint16_t* v_app;
     int t_cap;

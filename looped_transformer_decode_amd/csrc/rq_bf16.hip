@@ -40,14 +40,17 @@ __global__ __launch_bounds__(kThreads) void rq_bf16_decode_kernel(Bf16Args a) {
     const uint16_t* K = a.k + base;
     const uint16_t* V = a.v + base;
 
-    struct F { uint4 k[4], v[4]; };
+    struct F { u32x4 k[4], v[4]; };
     auto load = [&](F& f, int it) {
         const int j = (first + kWaves * (it / PPT)) * kTile + (it % PPT) * SLOTS + slot;
         const int jl = j < n ? j : 0;             // tail slots of the last tile read token 0
-        const uint4* kp = reinterpret_cast<const uint4*>(K + (int64_t)jl * D + 32 * chunk);
-        const uint4* vp = reinterpret_cast<const uint4*>(V + (int64_t)jl * D + 32 * chunk);
+        const u32x4* kp = reinterpret_cast<const u32x4*>(K + (int64_t)jl * D + 32 * chunk);
+        const u32x4* vp = reinterpret_cast<const u32x4*>(V + (int64_t)jl * D + 32 * chunk);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) { f.k[c] = kp[c]; f.v[c] = vp[c]; }
+        for (int c = 0; c < 4; ++c) {
+            f.k[c] = kp[c];
+            f.v[c] = vp[c];
+        }
     };
     F fa, fb;
     if (n_it > 0) load(fa, 0);
@@ -81,15 +84,15 @@ __global__ __launch_bounds__(kThreads) void rq_bf16_decode_kernel(Bf16Args a) {
                 part += qr[8 * c + 2 * e + 1] * bf16hi(ws[e]);
             }
         }
-        float score = chunk_sum<LPT>(part) * a.sm_scale;
+        float score = group_sum_dpp<LPT>(part) * a.sm_scale;
         score = valid ? score : -INFINITY;
-        const float pmax = slot_max<LPT>(score);
-        if (pmax > m_run) {
-            const float fs = __expf(m_run - pmax);
+        if (wave_any(score > m_run + kRescaleSlack)) {      // rare: raise the reference
+            const float m_new = wave_max_uniform(score);
+            const float fs = __expf(m_run - m_new);
 #pragma unroll
             for (int i = 0; i < 32; ++i) acc[i] *= fs;
             l_lane *= fs;
-            m_run = pmax;
+            m_run = m_new;
         }
         const float pw = valid ? __expf(score - m_run) : 0.f;
         l_lane += pw;
@@ -117,8 +120,8 @@ __global__ __launch_bounds__(kThreads) void rq_bf16_decode_kernel(Bf16Args a) {
     float* rec = a.partials + ((int64_t)bh * kMaxSplits + split) * partial_stride(D);
     if (threadIdx.x < D) rec[threadIdx.x] = sm.sum[threadIdx.x];
     if (threadIdx.x == 0) {
-        rec[D] = ml.x;
-        rec[D + 1] = ml.y;
+        rec[2 * D] = ml.x;
+        rec[2 * D + 1] = ml.y;
     }
 }
 

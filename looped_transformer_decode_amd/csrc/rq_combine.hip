@@ -36,8 +36,10 @@ __device__ __forceinline__ float cb_max(float v, float* red) {
     return s;
 }
 
-// one workgroup of D threads per (batch row, query head); thread i owns channel i
-template <int D, bool QBF16>
+// one workgroup of D threads per (batch row, query head); thread i owns channel i.
+// RES: the records carry a residual part acc_r that still has to be rotated back, once
+// per head: o = sum_s w_s acc_a_s + R_V^T (sum_s w_s acc_r_s) + p_cur v_cur.
+template <int D, bool QBF16, bool RES>
 __global__ __launch_bounds__(D) void rq_combine_kernel(CombineArgs a) {
     static_assert(D >= kMaxSplits, "one thread per split record");
     const int bh = blockIdx.x;
@@ -47,6 +49,7 @@ __global__ __launch_bounds__(D) void rq_combine_kernel(CombineArgs a) {
     const int i = threadIdx.x;
     __shared__ float red[D / 64 > 0 ? D / 64 : 1];
     __shared__ float wsplit[kMaxSplits];
+    __shared__ float rvec[RES ? D : 1];
 
     const float qv = QBF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[(int64_t)bh * D + i])
                            : reinterpret_cast<const float*>(a.q)[(int64_t)bh * D + i];
@@ -57,8 +60,8 @@ __global__ __launch_bounds__(D) void rq_combine_kernel(CombineArgs a) {
     const float* recs = a.partials + (int64_t)bh * kMaxSplits * partial_stride(D);
     float ms = -INFINITY, ls = 0.f;
     if (i < a.n_splits) {
-        ms = recs[(int64_t)i * partial_stride(D) + D];
-        ls = recs[(int64_t)i * partial_stride(D) + D + 1];
+        ms = recs[(int64_t)i * partial_stride(D) + 2 * D];
+        ls = recs[(int64_t)i * partial_stride(D) + 2 * D + 1];
     }
     const float m_f = fmaxf(cb_max<D>(ls > 0.f ? ms : -INFINITY, red), s_cur);
     const float wsv = (ls > 0.f) ? __expf(ms - m_f) : 0.f;
@@ -66,17 +69,45 @@ __global__ __launch_bounds__(D) void rq_combine_kernel(CombineArgs a) {
     const float ltot = cb_sum<D>(wsv * ls, red);
     __syncthreads();
     float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+    float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
     const float* r = recs + i;
+    const int64_t ps = partial_stride(D);
     int s = 0;
     for (; s + 4 <= a.n_splits; s += 4) {
-        o0 += wsplit[s] * r[(int64_t)s * partial_stride(D)];
-        o1 += wsplit[s + 1] * r[(int64_t)(s + 1) * partial_stride(D)];
-        o2 += wsplit[s + 2] * r[(int64_t)(s + 2) * partial_stride(D)];
-        o3 += wsplit[s + 3] * r[(int64_t)(s + 3) * partial_stride(D)];
+        o0 += wsplit[s] * r[s * ps];
+        o1 += wsplit[s + 1] * r[(s + 1) * ps];
+        o2 += wsplit[s + 2] * r[(s + 2) * ps];
+        o3 += wsplit[s + 3] * r[(s + 3) * ps];
+        if constexpr (RES) {
+            r0 += wsplit[s] * r[s * ps + D];
+            r1 += wsplit[s + 1] * r[(s + 1) * ps + D];
+            r2 += wsplit[s + 2] * r[(s + 2) * ps + D];
+            r3 += wsplit[s + 3] * r[(s + 3) * ps + D];
+        }
     }
-    for (; s < a.n_splits; ++s) o0 += wsplit[s] * r[(int64_t)s * partial_stride(D)];
+    for (; s < a.n_splits; ++s) {
+        o0 += wsplit[s] * r[s * ps];
+        if constexpr (RES) r0 += wsplit[s] * r[s * ps + D];
+    }
+    float o_acc = (o0 + o1) + (o2 + o3);
+    if constexpr (RES) {
+        rvec[i] = (r0 + r1) + (r2 + r3);
+        __syncthreads();
+        // column i of R_V: R_V[k][i], coalesced across threads; all loads in flight together
+        const float* rv = a.rot_v + (int64_t)h * 2 * D * D + i;
+        float rk[D];
+#pragma unroll
+        for (int k = 0; k < D; ++k) rk[k] = rv[(int64_t)k * D];
+        float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+        for (int k = 0; k < D; k += 2) {
+            t0 += rk[k] * rvec[k];
+            t1 += rk[k + 1] * rvec[k + 1];
+        }
+        o_acc += t0 + t1;
+    }
     const float p_cur = __expf(s_cur - m_f);
-    const float o = ((o0 + o1) + (o2 + o3) + p_cur * bf16_to_f32(vc)) / (ltot + p_cur);
+    const float o = (o_acc + p_cur * bf16_to_f32(vc)) / (ltot + p_cur);
     a.out[(int64_t)bh * D + i] = o;
     if (hq % gqa == 0) {
         if (a.pending != nullptr) {
@@ -96,17 +127,23 @@ __global__ __launch_bounds__(D) void rq_combine_kernel(CombineArgs a) {
     }
 }
 
+template <int D, bool QB>
+static void launch_c(const CombineArgs& a, dim3 grid, hipStream_t st) {
+    if (a.rot_v) hipLaunchKernelGGL((rq_combine_kernel<D, QB, true>), grid, dim3(D), 0, st, a);
+    else hipLaunchKernelGGL((rq_combine_kernel<D, QB, false>), grid, dim3(D), 0, st, a);
+}
+
 hipError_t launch_combine(const CombineArgs& a, int d, bool qbf16, int batch, hipStream_t st) {
     if (!a.partials || !a.q || !a.k_cur || !a.v_cur || !a.out || batch < 1 || a.n_splits < 1 ||
         a.n_splits > kMaxSplits || (a.k_app && (!a.v_app || !a.ctx_len)))
         return hipErrorInvalidValue;
     const dim3 grid(batch * a.hq);
     if (d == 128) {
-        if (qbf16) hipLaunchKernelGGL((rq_combine_kernel<128, true>), grid, dim3(128), 0, st, a);
-        else hipLaunchKernelGGL((rq_combine_kernel<128, false>), grid, dim3(128), 0, st, a);
+        if (qbf16) launch_c<128, true>(a, grid, st);
+        else launch_c<128, false>(a, grid, st);
     } else if (d == 64) {
-        if (qbf16) hipLaunchKernelGGL((rq_combine_kernel<64, true>), grid, dim3(64), 0, st, a);
-        else hipLaunchKernelGGL((rq_combine_kernel<64, false>), grid, dim3(64), 0, st, a);
+        if (qbf16) launch_c<64, true>(a, grid, st);
+        else launch_c<64, false>(a, grid, st);
     } else {
         return hipErrorInvalidValue;
     }

@@ -12,6 +12,7 @@ constexpr int kTile = 64;          // tokens per cache tile
 constexpr int kMaxSplits = 64;     // split-K upper bound (sizes the workspace)
 constexpr int kMaxLoops = 8;       // loops per anchor group
 constexpr int kWave = 64;
+constexpr int kStageDepth = 3;     // LDS ring slots per wave in the decode kernel (passes)
 
 // Byte geometry of the packed cache, derived from rq_config on the host and passed
 // to kernels by value.
@@ -33,11 +34,15 @@ struct Geom {
 bool make_geom(const rq_config* cfg, Geom* g);
 
 // Workspace layout for split-K decode: per (batch row, query head, split) a record of
-// o[d] (unnormalised output), m (running max), l (denominator), 2 floats of padding.
-__host__ __device__ inline int partial_stride(int d) { return d + 4; }
+// acc_a[d] (anchor part, or the whole output of the BF16 kernel), acc_r[d] (residual part,
+// before R_V^T), m (running max), l (denominator), 2 floats of padding.
+__host__ __device__ inline int partial_stride(int d) { return 2 * d + 4; }
 inline size_t workspace_bytes(int max_batch, int hq, int d) {
     return (size_t)max_batch * hq * kMaxSplits * partial_stride(d) * sizeof(float);
 }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- number formats
 
@@ -73,6 +78,49 @@ __device__ __forceinline__ double shfl_xor_d(double v, int m) {
     p.x = __shfl_xor(p.x, m, kWave);
     p.y = __shfl_xor(p.y, m, kWave);
     return *reinterpret_cast<double*>(&p);
+}
+
+// ---------------------------------------------------------------- DPP reductions
+// quad_perm patterns: [1,0,3,2] swaps neighbours, [2,3,0,1] swaps pairs.
+constexpr int kDppQuadXor1 = 0xB1;
+constexpr int kDppQuadXor2 = 0x4E;
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr3 = 0x113;
+constexpr int kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROWMASK = 0xF, int BANKMASK = 0xF>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROWMASK,
+                                                      BANKMASK, false));
+}
+
+// Sum over aligned groups of N = 1, 2 or 4 lanes; every lane of the group gets the sum.
+template <int N>
+__device__ __forceinline__ float group_sum_dpp(float v) {
+    if constexpr (N >= 2) v += dpp_f<kDppQuadXor1>(v, v);
+    if constexpr (N >= 4) v += dpp_f<kDppQuadXor2>(v, v);
+    static_assert(N <= 4, "group of at most 4 lanes");
+    return v;
+}
+
+// Online softmax keeps a running reference m and weights p = exp(s - m).  The reference
+// only has to bound the scores well enough that p cannot overflow, so it is raised only
+// when a score exceeds it by more than this slack (natural-log units; p <= e^8).
+constexpr float kRescaleSlack = 8.0f;
+
+// True in every lane if any lane of the wave has pred set.
+__device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
+
+// Maximum over the 64 lanes of the wave, returned as a wave-uniform value.
+__device__ __forceinline__ float wave_max_uniform(float v) {
+    v = fmaxf(v, dpp_f<kDppRowShr1>(v, v));
+    v = fmaxf(v, dpp_f<kDppRowShr2>(v, v));
+    v = fmaxf(v, dpp_f<kDppRowShr3>(v, v));
+    v = fmaxf(v, dpp_f<kDppRowShr4, 0xF, 0xE>(v, v));
+    v = fmaxf(v, dpp_f<kDppRowShr8, 0xF, 0xC>(v, v));
+    v = fmaxf(v, dpp_f<kDppRowBcast15, 0xA>(v, v));
+    v = fmaxf(v, dpp_f<kDppRowBcast31, 0xC>(v, v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 }  // namespace rq

@@ -20,38 +20,152 @@
 namespace rq {
 
 
-template <int BITS, int NW>
-__device__ __forceinline__ float code_f(const uint32_t (&w)[NW], int idx) {
-    constexpr uint32_t mask = (1u << BITS) - 1u;
-    return (float)((w[(idx * BITS) >> 5] >> ((idx * BITS) & 31)) & mask);
+// ---- staging: the cache stream goes global -> LDS by DMA (global_load_lds_dwordx4), one
+// 16-byte chunk per lane, without passing through registers.  The compiler does not
+// track these LDS writes, so each wave waits for its own DMAs explicitly (vmcnt) before
+// reading a staged pass; no other vector-memory instruction is issued inside the loop.
+__device__ __forceinline__ void dma16(uint32_t voff, const uint8_t* sbase, uint32_t lds_addr) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
 }
 
-template <int NB>
-__device__ __forceinline__ void load_words(uint32_t (&w)[NB / 4], const uint8_t* p) {
-    if constexpr (NB == 16) {
-        const uint4 v = *reinterpret_cast<const uint4*>(p);
-        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+// copy BYTES (multiple of 16, at most 1024) from sbase + goff to LDS lds_addr
+template <int BYTES>
+__device__ __forceinline__ void stage(const uint8_t* sbase, uint32_t goff, uint32_t lds_addr, int lane) {
+    static_assert(BYTES % 16 == 0 && BYTES <= 1024, "one DMA instruction per block");
+    if (BYTES == 1024 || lane < BYTES / 16) dma16(goff + 16u * lane, sbase, lds_addr);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// ---- keys: exact integer dot products on the packed codes
+//
+// q is written per quantization group as 24-bit fixed point Q_i = rint(q_i / delta),
+// delta = 2^(e-21) with 2^e <= max|q_i|, split into six balanced base-16 digits d_k in
+// [-8, 7] (Q = sum_k 16^k d_k).  u = R_K q multiplies the 2-bit residual codes (0..3,
+// with small scales) and uses 16-bit fixed point, delta = 2^(e-13), four digits.  A digit word holds the
+// digits of the 8 channels whose codes share one 32-bit code word, at the same nibble
+// positions, so v_dot8_i32_i4 multiplies codes by digits without unpacking: 4-bit codes
+// are first offset to signed c - 8 (xor 0x8 per nibble; the offset is added back as
+// 8 * sum Q), 2-bit codes are split into even/odd channels (c in 0..3 fits a signed nibble).
+// sum_i q_i c_i = delta * sum_k 16^k dot_k (+ 8 delta sum Q for 4-bit codes).
+
+__device__ __forceinline__ int sdot8(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot8((int)a, (int)b, c, false);
+}
+
+// nibble words of a lane's 32 channels: 4 of them, in digit-word order
+template <int BITS>
+__device__ __forceinline__ void code_nibbles(uint32_t (&nib)[4], const uint32_t* w) {
+    if constexpr (BITS == 4) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) nib[k] = w[k] ^ 0x88888888u;
     } else {
-        const uint2 v = *reinterpret_cast<const uint2*>(p);
-        w[0] = v.x; w[1] = v.y;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            nib[2 * k] = w[k] & 0x33333333u;
+            nib[2 * k + 1] = (w[k] >> 2) & 0x33333333u;
+        }
     }
 }
 
-// metadata of this lane's GPL groups: byte pairs (z, s)
-template <int GPL>
-__device__ __forceinline__ uint32_t load_meta(const uint8_t* p) {
-    if constexpr (GPL == 1) return *reinterpret_cast<const uint16_t*>(p);
-    else return *reinterpret_cast<const uint32_t*>(p);
+// sum_k 16^k dot_k over the nibble words [w0, w0 + NW) of one group, ND = 6 or 4 digits
+template <int NW, int ND>
+__device__ __forceinline__ float digit_dot(const uint32_t (&nib)[4], const uint32_t (&dg)[ND][4], int w0) {
+    int acc[ND];
+#pragma unroll
+    for (int k = 0; k < ND; ++k) acc[k] = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int k = 0; k < ND; ++k) acc[k] = sdot8(nib[w0 + w], dg[k][w0 + w], acc[k]);
+    if constexpr (ND == 6) {
+        const int t0 = acc[0] + (acc[1] << 4) + (acc[2] << 8);
+        const int t1 = acc[3] + (acc[4] << 4) + (acc[5] << 8);
+        return (float)t0 + 4096.f * (float)t1;
+    } else {
+        const int t0 = acc[0] + (acc[1] << 4);
+        const int t1 = acc[2] + (acc[3] << 4);
+        return (float)t0 + 256.f * (float)t1;
+    }
 }
 
-// Raw bytes of one token-pass for one lane: K and V words of the anchor plane and of the
-// NR residual planes, with their metadata and coefficients.
-template <int AW, int NR>
-struct Frame {
-    uint32_t ka[AW], kam, va[AW], vam;
-    uint32_t kr[NR][2], krm[NR], kc[NR];
-    uint32_t vr[NR][2], vrm[NR], vc[NR];
-};
+// ---- values: FP16 magic numbers
+//
+// OR-ing a code into the mantissa of FP16 1024.0 (0x6400) gives 1024 + m*c exactly, where
+// m = 2^(bit position) of the code inside the half; v_fma_mix_f32 then accumulates
+// w * (1024 + m c) in fp32.  Per channel: sum_j w_j c_j = (acc - 1024 * sum_j w_j) / m.
+__device__ __forceinline__ void fma_pair(float& a0, float& a1, uint32_t pk, float w) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 h = __builtin_bit_cast(h2, pk);
+    a0 = fmaf((float)h.x, w, a0);
+    a1 = fmaf((float)h.y, w, a1);
+}
+
+constexpr uint32_t kMagic = 0x64006400u;
+
+// (x & mask) | magic in one v_and_or_b32 (mask as a scalar operand, magic in a register)
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(magic));
+    return r;
+}
+
+// 4-bit word: channels 0..7 of the word at nibbles 0..7
+__device__ __forceinline__ void v_acc4(float* acc, uint32_t w, float wt, uint32_t mg) {
+    const uint32_t w8 = w >> 8;
+    fma_pair(acc[0], acc[4], and_or(w, 0x000F000Fu, mg), wt);
+    fma_pair(acc[1], acc[5], and_or(w, 0x00F000F0u, mg), wt);
+    fma_pair(acc[2], acc[6], and_or(w8, 0x000F000Fu, mg), wt);
+    fma_pair(acc[3], acc[7], and_or(w8, 0x00F000F0u, mg), wt);
+}
+__host__ __device__ constexpr float mult4(int ch) { return (ch & 1) ? 16.f : 1.f; }
+
+// 2-bit word: channels 0..15 of the word at bits 2c
+__device__ __forceinline__ void v_acc2(float* acc, uint32_t w, float wt, uint32_t mg) {
+    const uint32_t w10 = w >> 10;
+    fma_pair(acc[0], acc[8], and_or(w, 0x00030003u, mg), wt);
+    fma_pair(acc[1], acc[9], and_or(w, 0x000C000Cu, mg), wt);
+    fma_pair(acc[2], acc[10], and_or(w, 0x00300030u, mg), wt);
+    fma_pair(acc[3], acc[11], and_or(w, 0x00C000C0u, mg), wt);
+    fma_pair(acc[4], acc[12], and_or(w, 0x03000300u, mg), wt);
+    fma_pair(acc[5], acc[13], and_or(w10, 0x00030003u, mg), wt);
+    fma_pair(acc[6], acc[14], and_or(w10, 0x000C000Cu, mg), wt);
+    fma_pair(acc[7], acc[15], and_or(w10, 0x00300030u, mg), wt);
+}
+__host__ __device__ constexpr float mult2(int ch) {
+    return (float)(1 << (2 * ((ch & 7) < 5 ? (ch & 7) : (ch & 7) - 5)));
+}
+
+template <int BITS>
+__device__ __forceinline__ void v_acc(float* acc, const uint32_t* w, float wt, int g0, int ng, uint32_t mg) {
+    // accumulate the channels of code words [g0, g0 + ng)
+    if constexpr (BITS == 4) {
+        for (int k = g0; k < g0 + ng; ++k) v_acc4(acc + 8 * k, w[k], wt, mg);
+    } else {
+        for (int k = g0; k < g0 + ng; ++k) v_acc2(acc + 16 * k, w[k], wt, mg);
+    }
+}
+
+template <int BITS>
+__host__ __device__ constexpr float inv_mult(int ch) {
+    return BITS == 4 ? 1.f / mult4(ch % 8) : 1.f / mult2(ch % 16);
+}
+
+__device__ __forceinline__ float fp8(uint32_t word, int byte) {
+    switch (byte) {
+        case 0: return __builtin_amdgcn_cvt_f32_fp8((int)word, 0);
+        case 1: return __builtin_amdgcn_cvt_f32_fp8((int)word, 1);
+        case 2: return __builtin_amdgcn_cvt_f32_fp8((int)word, 2);
+        default: return __builtin_amdgcn_cvt_f32_fp8((int)word, 3);
+    }
+}
 
 // D: head dim; GS: group size; BA: anchor bits; NRES: residual planes read (0 = anchor loop).
 template <int D, int GS, int BA, int NRES, bool QBF16>
@@ -61,9 +175,18 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
     constexpr int PPT = kTile / SLOTS;     // passes per tile
     constexpr int GPL = 32 / GS;           // quantization groups per lane
     constexpr int AB = 32 * BA / 8;        // anchor code bytes per lane
-    constexpr int AW = AB / 4;
+    constexpr int AW = AB / 4;             // anchor code words per lane
     constexpr int NR = NRES ? NRES : 1;
     constexpr int NV = NRES ? 64 : 32;
+    constexpr int NG = D / GS;             // groups per head vector
+    // bytes of one pass (SLOTS tokens) per block; each block is one DMA instruction
+    constexpr int AC = SLOTS * D * BA / 8;         // anchor codes
+    constexpr int AM = SLOTS * 2 * D / GS;         // FP8 offset/scale pairs
+    constexpr int RC = SLOTS * D * 2 / 8;          // residual codes
+    constexpr int CC = SLOTS * 2;                  // BF16 coefficients
+    constexpr int PASS = 2 * (AC + AM + NRES * (RC + AM + CC));
+    constexpr int NB = kStageDepth;                // ring slots per wave
+    constexpr int NDMA = 2 * (2 + 3 * NRES);       // DMA instructions per pass
 
     const Geom& G = a.geo;
     const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -75,9 +198,11 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int chunk = lane % LPT, slot = lane / LPT;
 
-    __shared__ float sq[D];
-    __shared__ float su[D];
     __shared__ SplitSmem<D> sm;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][NB][PASS];
+    __shared__ float sv[2][D];                         // q and u = R_K q
+    __shared__ uint32_t s_dig[10 * (D / 8)];           // digit words: q [6][D/8], u [4][D/8]
+    __shared__ float s_f[5][NG];                       // delta_q, corr_q, sum_q, delta_u, sum_u
 
     int n = a.ctx_len[b];
     n = n < 0 ? 0 : (n > a.ctx_bound ? a.ctx_bound : n);
@@ -86,7 +211,12 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
     const int t_end = min(n_tiles, t_begin + a.tiles_per_split);
     const int first = t_begin + w;
     const int my_tiles = first < t_end ? (t_end - first + kWaves - 1) / kWaves : 0;
-    const int n_it = my_tiles * PPT;
+    // passes: full tiles, except that only the globally last tile can be partial
+    int n_it = my_tiles * PPT;
+    if (my_tiles > 0 && first + kWaves * (my_tiles - 1) == n_tiles - 1) {
+        const int rem = n - (n_tiles - 1) * kTile;                 // 1..64 tokens in the last tile
+        n_it -= PPT - (rem + SLOTS - 1) / SLOTS;
+    }
 
     // ---- plane bases
     const int L = G.L;
@@ -104,133 +234,244 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
     const int r_meta = kTile * G.r_row;
     const int r_cblk = kTile * (G.r_row + G.m_row);
 
-    auto load = [&](Frame<AW, NR>& f, int it) {
-        const int tile = first + kWaves * (it / PPT);
-        const int jj = (it % PPT) * SLOTS + slot;
-        const int64_t ta = (int64_t)tile * G.a_tile + jj * G.a_row + chunk * AB;
-        const int64_t tm = (int64_t)tile * G.a_tile + a_meta + jj * G.m_row + chunk * GPL * 2;
-        load_words<AB>(f.ka, aK + ta);
-        load_words<AB>(f.va, aV + ta);
-        f.kam = load_meta<GPL>(aK + tm);
-        f.vam = load_meta<GPL>(aV + tm);
-        if constexpr (NRES > 0) {
-            const int64_t tr = (int64_t)tile * G.r_tile;
+    // Stage pass `it` (SLOTS consecutive tokens of one tile) of every plane into ring slot
+    // it % NB of this wave.  LDS slot layout: K then V, each [anchor codes][anchor meta]
+    // then per residual plane [codes][meta][c].
+    const uint32_t ring_base = __builtin_amdgcn_readfirstlane(lds_addr_of(&ring[w][0][0]));
+    auto issue = [&](int it) {
+        const uint32_t tile = first + kWaves * (it / PPT);
+        const uint32_t p = it % PPT;
+        uint32_t dst = ring_base + (uint32_t)(it % NB) * PASS;
+        const uint32_t ta = tile * (uint32_t)G.a_tile;
 #pragma unroll
-            for (int k = 0; k < NRES; ++k) {
-                load_words<8>(f.kr[k], rK[k] + tr + jj * G.r_row + chunk * 8);
-                load_words<8>(f.vr[k], rV[k] + tr + jj * G.r_row + chunk * 8);
-                f.krm[k] = load_meta<GPL>(rK[k] + tr + r_meta + jj * G.m_row + chunk * GPL * 2);
-                f.vrm[k] = load_meta<GPL>(rV[k] + tr + r_meta + jj * G.m_row + chunk * GPL * 2);
-                f.kc[k] = *reinterpret_cast<const uint16_t*>(rK[k] + tr + r_cblk + jj * 2);
-                f.vc[k] = *reinterpret_cast<const uint16_t*>(rV[k] + tr + r_cblk + jj * 2);
+        for (int x = 0; x < 2; ++x) {
+            const uint8_t* ap = x ? aV : aK;
+            stage<AC>(ap, ta + p * AC, dst, lane);
+            stage<AM>(ap, ta + a_meta + p * AM, dst + AC, lane);
+            dst += AC + AM;
+            if constexpr (NRES > 0) {
+                const uint32_t tr = tile * (uint32_t)G.r_tile;
+#pragma unroll
+                for (int k = 0; k < NRES; ++k) {
+                    const uint8_t* rp = x ? rV[k] : rK[k];
+                    stage<RC>(rp, tr + p * RC, dst, lane);
+                    stage<AM>(rp, tr + r_meta + p * AM, dst + RC, lane);
+                    stage<CC>(rp, tr + r_cblk + p * CC, dst + RC + AM, lane);
+                    dst += RC + AM + CC;
+                }
             }
         }
     };
-
-    Frame<AW, NR> fa, fb;
-    if (n_it > 0) load(fa, 0);
-
-    // ---- prologue (overlaps the first loads): q and u = R_K q
-    for (int i = threadIdx.x; i < D; i += kThreads) {
-        float qv;
-        if constexpr (QBF16)
-            qv = bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[(int64_t)bh * D + i]);
-        else
-            qv = reinterpret_cast<const float*>(a.q)[(int64_t)bh * D + i];
-        sq[i] = qv;
+    // wait until pass `it` has landed while `ahead` later passes stay in flight
+    auto wait_pass = [&](int ahead) {
+        if constexpr (NB >= 3) {
+            if (ahead >= 2) { wait_vm<2 * NDMA>(); return; }
+        }
+        if (ahead >= 1) wait_vm<NDMA>();
+        else wait_vm<0>();
+    };
+    // ---- prologue, one load round: every thread loads the R_K row segment and the q
+    // segment its part of u = R_K q needs (plus q_t itself) before the stream DMAs are
+    // issued, so all of it is in flight together.
+    constexpr int TPR = kThreads / D;                  // threads per row of R_K
+    constexpr int COLS = D / TPR;
+    const int prow = threadIdx.x / TPR, ppart = threadIdx.x % TPR;
+    float4 rseg[NRES ? COLS / 4 : 1];
+    float qseg[NRES ? COLS : 1];
+    float qown = 0.f;
+    {
+        const int64_t qo = (int64_t)bh * D;
+        if (threadIdx.x < D) {
+            qown = QBF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qo + threadIdx.x])
+                         : reinterpret_cast<const float*>(a.q)[qo + threadIdx.x];
+        }
+        if constexpr (NRES > 0) {
+            const float4* rr = reinterpret_cast<const float4*>(a.rot + (int64_t)(h * 2) * D * D +
+                                                               (int64_t)prow * D + ppart * COLS);
+#pragma unroll
+            for (int k4 = 0; k4 < COLS / 4; ++k4) rseg[k4] = rr[k4];
+#pragma unroll
+            for (int k = 0; k < COLS; ++k) {
+                const int c = ppart * COLS + k;
+                qseg[k] = QBF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qo + c])
+                                : reinterpret_cast<const float*>(a.q)[qo + c];
+            }
+        }
     }
-    __syncthreads();
+    for (int k = 0; k < NB - 1 && k < n_it; ++k) issue(k);
+    for (int i = threadIdx.x; i < 10 * (D / 8); i += kThreads) s_dig[i] = 0u;
+    if (threadIdx.x < D) sv[0][threadIdx.x] = qown;
     if constexpr (NRES > 0) {
-        const float* RK = a.rot + (int64_t)(h * 2 + 0) * D * D;
-        constexpr int TPR = kThreads / D;          // threads per row
-        constexpr int COLS = D / TPR;
-        const int row = threadIdx.x / TPR, part = threadIdx.x % TPR;
-        const float4* rr = reinterpret_cast<const float4*>(RK + (int64_t)row * D + part * COLS);
         float acc = 0.f;
 #pragma unroll
         for (int k4 = 0; k4 < COLS / 4; ++k4) {
-            const float4 r4 = rr[k4];
-            const int c0 = part * COLS + 4 * k4;
-            acc += r4.x * sq[c0] + r4.y * sq[c0 + 1] + r4.z * sq[c0 + 2] + r4.w * sq[c0 + 3];
+            acc += rseg[k4].x * qseg[4 * k4] + rseg[k4].y * qseg[4 * k4 + 1] +
+                   rseg[k4].z * qseg[4 * k4 + 2] + rseg[k4].w * qseg[4 * k4 + 3];
         }
 #pragma unroll
         for (int m = 1; m < TPR; m <<= 1) acc += shfl_xor_f(acc, m);
-        if (part == 0) su[row] = acc;
-        __syncthreads();
+        if (ppart == 0) sv[1][prow] = acc;
     }
-    float qr[32], ur[NRES ? 32 : 1], Qg[GPL], Ug[GPL];
+    __syncthreads();
+    // fixed-point digits (see the comment above digit_dot): q in the anchor-code layout,
+    // u in the 2-bit layout
+    if (threadIdx.x < (NRES ? 2 : 1) * D) {
+        const int which = threadIdx.x / D, i = threadIdx.x % D;
+        const float val = sv[which][i];
+        const bool four = (which == 0) && (BA == 4);
+        float amax = fabsf(val), vsum = val;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) qr[i] = sq[32 * chunk + i];
-    if constexpr (NRES > 0) {
+        for (int m = 1; m < GS; m <<= 1) {
+            amax = fmaxf(amax, shfl_xor_f(amax, m));
+            vsum += shfl_xor_f(vsum, m);
+        }
+        const int e = amax > 0.f ? ilogbf(amax) : 0;
+        const int fb = which ? 13 : 21;                    // |Q| <= 2^(fb + 1)
+        int Q = (int)rintf(val * ldexpf(1.f, fb - e));     // exact power-of-two scaling
+        int qsum = Q;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) ur[i] = su[32 * chunk + i];
+        for (int m = 1; m < GS; m <<= 1) qsum += __shfl_xor(qsum, m, kWave);
+        const int shift = four ? 4 * (i % 8) : 4 * ((i % 16) / 2);
+        const int widx = four ? i / 8 : (i / 16) * 2 + (i & 1);
+        const int nd = which ? 4 : 6;
+        const int base = which ? 6 * (D / 8) : 0;
+#pragma unroll
+        for (int k = 0; k < 6; ++k) {
+            if (k < nd) {
+                const int d = ((Q + 8) & 15) - 8;
+                Q = (Q - d) >> 4;
+                atomicOr(&s_dig[base + k * (D / 8) + widx], (uint32_t)(d & 15) << shift);
+            }
+        }
+        if (i % GS == 0) {
+            const int gi = i / GS;
+            if (which == 0) {
+                s_f[0][gi] = ldexpf(1.f, e - fb);
+                s_f[1][gi] = four ? 8.f * (float)qsum : 0.f;
+                s_f[2][gi] = vsum;
+            } else {
+                s_f[3][gi] = ldexpf(1.f, e - fb);
+                s_f[4][gi] = vsum;
+            }
+        }
+    }
+    __syncthreads();
+    uint32_t dq[6][4], du[4][4];
+    float dlq[GPL], crq[GPL], Qg[GPL], dlu[GPL], Ug[GPL];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+#pragma unroll
+        for (int k = 0; k < 6; ++k) dq[k][x] = s_dig[k * (D / 8) + 4 * chunk + x];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) du[k][x] = NRES ? s_dig[6 * (D / 8) + k * (D / 8) + 4 * chunk + x] : 0u;
     }
 #pragma unroll
     for (int gg = 0; gg < GPL; ++gg) {
-        float s1 = 0.f, s2 = 0.f;
-#pragma unroll
-        for (int i = 0; i < GS; ++i) {
-            s1 += qr[gg * GS + i];
-            if constexpr (NRES > 0) s2 += ur[gg * GS + i];
-        }
-        Qg[gg] = s1;
-        Ug[gg] = s2;
+        const int gi = chunk * GPL + gg;
+        dlq[gg] = s_f[0][gi];
+        crq[gg] = s_f[1][gi];
+        Qg[gg] = s_f[2][gi];
+        dlu[gg] = NRES ? s_f[3][gi] : 0.f;
+        Ug[gg] = NRES ? s_f[4][gi] : 0.f;
     }
 
-    float accA[32], accR[NRES ? 32 : 1], offA[GPL], offR[GPL];
+    float accA[32], accR[NRES ? 32 : 1], wA[GPL], wR[GPL], zA[GPL], zR[GPL];
 #pragma unroll
     for (int i = 0; i < 32; ++i) accA[i] = 0.f;
 #pragma unroll
     for (int i = 0; i < (NRES ? 32 : 1); ++i) accR[i] = 0.f;
 #pragma unroll
-    for (int gg = 0; gg < GPL; ++gg) offA[gg] = offR[gg] = 0.f;
+    for (int gg = 0; gg < GPL; ++gg) wA[gg] = wR[gg] = zA[gg] = zR[gg] = 0.f;
     float m_run = -INFINITY, l_lane = 0.f;
     const float sm_scale = a.sm_scale;
+    constexpr int DW = 4 / GPL;            // digit/nibble words per group
+    const uint32_t magic = kMagic;
 
-    auto compute = [&](const Frame<AW, NR>& f, int it) {
+    auto compute = [&](int it) {
         const int tile = first + kWaves * (it / PPT);
         const int jj = (it % PPT) * SLOTS + slot;
         const bool valid = tile * kTile + jj < n;
+        const int row = valid ? slot : 0;          // tail slots read the pass's first (valid) token
+        const uint8_t* sp = &ring[w][it % NB][0];
+        // lane's words: anchor codes, metadata (GPL pairs), per residual plane codes/meta/c
+        uint32_t ka[AW], va[AW], kr[NR][2], vr[NR][2], krm[NR], vrm[NR], kc[NR], vc[NR];
+        uint32_t kam, vam;
+        {
+            const uint8_t* kp = sp;
+            const uint8_t* vp = sp + (PASS / 2);
+#pragma unroll
+            for (int q4 = 0; q4 < AW; ++q4) {
+                ka[q4] = reinterpret_cast<const uint32_t*>(kp + row * (AC / SLOTS) + chunk * AB)[q4];
+                va[q4] = reinterpret_cast<const uint32_t*>(vp + row * (AC / SLOTS) + chunk * AB)[q4];
+            }
+            if constexpr (GPL == 1) {
+                kam = *reinterpret_cast<const uint16_t*>(kp + AC + row * (AM / SLOTS) + chunk * 2);
+                vam = *reinterpret_cast<const uint16_t*>(vp + AC + row * (AM / SLOTS) + chunk * 2);
+            } else {
+                kam = *reinterpret_cast<const uint32_t*>(kp + AC + row * (AM / SLOTS) + chunk * 4);
+                vam = *reinterpret_cast<const uint32_t*>(vp + AC + row * (AM / SLOTS) + chunk * 4);
+            }
+#pragma unroll
+            for (int k = 0; k < NRES; ++k) {
+                const int o = AC + AM + k * (RC + AM + CC);
+                kr[k][0] = reinterpret_cast<const uint32_t*>(kp + o + row * (RC / SLOTS) + chunk * 8)[0];
+                kr[k][1] = reinterpret_cast<const uint32_t*>(kp + o + row * (RC / SLOTS) + chunk * 8)[1];
+                vr[k][0] = reinterpret_cast<const uint32_t*>(vp + o + row * (RC / SLOTS) + chunk * 8)[0];
+                vr[k][1] = reinterpret_cast<const uint32_t*>(vp + o + row * (RC / SLOTS) + chunk * 8)[1];
+                if constexpr (GPL == 1) {
+                    krm[k] = *reinterpret_cast<const uint16_t*>(kp + o + RC + row * (AM / SLOTS) + chunk * 2);
+                    vrm[k] = *reinterpret_cast<const uint16_t*>(vp + o + RC + row * (AM / SLOTS) + chunk * 2);
+                } else {
+                    krm[k] = *reinterpret_cast<const uint32_t*>(kp + o + RC + row * (AM / SLOTS) + chunk * 4);
+                    vrm[k] = *reinterpret_cast<const uint32_t*>(vp + o + RC + row * (AM / SLOTS) + chunk * 4);
+                }
+                kc[k] = *reinterpret_cast<const uint16_t*>(kp + o + RC + AM + row * 2);
+                vc[k] = *reinterpret_cast<const uint16_t*>(vp + o + RC + AM + row * 2);
+            }
+        }
         // ---------------- keys
         float part_a = 0.f;
+        {
+            uint32_t nib[4];
+            code_nibbles<BA>(nib, ka);
 #pragma unroll
-        for (int gg = 0; gg < GPL; ++gg) {
-            const float z = e4m3_to_f32((f.kam >> (16 * gg)) & 0xFF);
-            const float s = e4m3_to_f32((f.kam >> (16 * gg + 8)) & 0xFF);
-            float dot = 0.f;
-#pragma unroll
-            for (int i = 0; i < GS; ++i) dot += qr[gg * GS + i] * code_f<BA>(f.ka, gg * GS + i);
-            part_a += z * Qg[gg] + s * dot;
+            for (int gg = 0; gg < GPL; ++gg) {
+                const float dot = dlq[gg] * (digit_dot<DW, 6>(nib, dq, gg * DW) + crq[gg]);
+                part_a += fp8(kam, 2 * gg) * Qg[gg] + fp8(kam, 2 * gg + 1) * dot;
+            }
         }
         float coef = 1.f, part_r = 0.f;
 #pragma unroll
         for (int k = 0; k < NRES; ++k) {
+            uint32_t nib[4];
+            code_nibbles<2>(nib, kr[k]);
             float pr = 0.f;
 #pragma unroll
             for (int gg = 0; gg < GPL; ++gg) {
-                const float z = e4m3_to_f32((f.krm[k] >> (16 * gg)) & 0xFF);
-                const float s = e4m3_to_f32((f.krm[k] >> (16 * gg + 8)) & 0xFF);
-                float dot = 0.f;
-#pragma unroll
-                for (int i = 0; i < GS; ++i) dot += ur[gg * GS + i] * code_f<2>(f.kr[k], gg * GS + i);
-                pr += z * Ug[gg] + s * dot;
+                const float dot = dlu[gg] * digit_dot<DW, 4>(nib, du, gg * DW);
+                pr += fp8(krm[k], 2 * gg) * Ug[gg] + fp8(krm[k], 2 * gg + 1) * dot;
             }
             part_r += coef * pr;
-            coef *= valid ? bf16_to_f32(f.kc[k]) : 0.f;
+            coef *= bf16_to_f32(kc[k]);
         }
-        float score = chunk_sum<LPT>(coef * part_a + part_r) * sm_scale;
+        float score = group_sum_dpp<LPT>(coef * part_a + part_r) * sm_scale;
         score = valid ? score : -INFINITY;
-        const float pmax = slot_max<LPT>(score);
-        if (pmax > m_run) {                         // uniform across the wave
-            const float fs = __expf(m_run - pmax);
+        if (wave_any(score > m_run + kRescaleSlack)) {      // rare: raise the reference
+            const float m_new = wave_max_uniform(score);
+            const float fs = __expf(m_run - m_new);
 #pragma unroll
             for (int i = 0; i < 32; ++i) accA[i] *= fs;
 #pragma unroll
             for (int i = 0; i < (NRES ? 32 : 1); ++i) accR[i] *= fs;
 #pragma unroll
-            for (int gg = 0; gg < GPL; ++gg) { offA[gg] *= fs; offR[gg] *= fs; }
+            for (int gg = 0; gg < GPL; ++gg) {
+                wA[gg] *= fs;
+                wR[gg] *= fs;
+                zA[gg] *= fs;
+                zR[gg] *= fs;
+            }
             l_lane *= fs;
-            m_run = pmax;
+            m_run = m_new;
         }
         const float pw = valid ? __expf(score - m_run) : 0.f;
         l_lane += pw;
@@ -240,72 +481,46 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
         for (int k = 0; k < NRES; ++k) {
 #pragma unroll
             for (int gg = 0; gg < GPL; ++gg) {
-                const float z = e4m3_to_f32((f.vrm[k] >> (16 * gg)) & 0xFF);
-                const float s = e4m3_to_f32((f.vrm[k] >> (16 * gg + 8)) & 0xFF);
-                offR[gg] += wv * z;
-                const float ws = wv * s;
-#pragma unroll
-                for (int i = 0; i < GS; ++i) accR[gg * GS + i] += ws * code_f<2>(f.vr[k], gg * GS + i);
+                const float ws = wv * fp8(vrm[k], 2 * gg + 1);
+                zR[gg] += wv * fp8(vrm[k], 2 * gg);
+                wR[gg] += ws;
+                v_acc<2>(accR, vr[k], ws, gg * 2 / GPL, 2 / GPL, magic);
             }
-            wv *= valid ? bf16_to_f32(f.vc[k]) : 0.f;
+            wv *= bf16_to_f32(vc[k]);
         }
 #pragma unroll
         for (int gg = 0; gg < GPL; ++gg) {
-            const float z = e4m3_to_f32((f.vam >> (16 * gg)) & 0xFF);
-            const float s = e4m3_to_f32((f.vam >> (16 * gg + 8)) & 0xFF);
-            offA[gg] += wv * z;
-            const float ws = wv * s;
-#pragma unroll
-            for (int i = 0; i < GS; ++i) accA[gg * GS + i] += ws * code_f<BA>(f.va, gg * GS + i);
+            const float ws = wv * fp8(vam, 2 * gg + 1);
+            zA[gg] += wv * fp8(vam, 2 * gg);
+            wA[gg] += ws;
+            v_acc<BA>(accA, va, ws, gg * AW / GPL, AW / GPL, magic);
         }
     };
 
-    // ---- main loop, two frames in flight
-    for (int it = 0; it < n_it; it += 2) {
-        if (it + 1 < n_it) load(fb, it + 1);
-        compute(fa, it);
-        if (it + 1 < n_it) {
-            if (it + 2 < n_it) load(fa, it + 2);
-            compute(fb, it + 1);
-        }
+    // ---- main loop: NB-1 passes in flight while one is computed from LDS
+    for (int it = 0; it < n_it; ++it) {
+        if (it + NB - 1 < n_it) issue(it + NB - 1);
+        wait_pass(min(NB - 1, n_it - 1 - it));
+        compute(it);
     }
 
-    // ---- fold group offsets, merge the waves, apply R_V^T to the residual part
+    // ---- undo the FP16 magic offsets, merge the waves, apply R_V^T to the residual part
     float v[NV];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = accA[i] + offA[i / GS];
+    for (int i = 0; i < 32; ++i)
+        v[i] = (accA[i] - 1024.f * wA[i / GS]) * inv_mult<BA>(i) + zA[i / GS];
     if constexpr (NRES > 0) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) v[32 + i] = accR[i] + offR[i / GS];
+        for (int i = 0; i < 32; ++i)
+            v[32 + i] = (accR[i] - 1024.f * wR[i / GS]) * inv_mult<2>(i) + zR[i / GS];
     }
     const float2 ml = splitk_merge_waves<D, NV>(v, m_run, l_lane, sm);
+    // record: acc_a[D], acc_r[D] (R_V^T is applied once per head in the merge kernel), m, l
     float* rec = a.partials + ((int64_t)bh * kMaxSplits + split) * partial_stride(D);
-    if constexpr (NRES > 0) {
-        // o_i = A_i + sum_k R_V[k][i] * Rr_k ; TPR threads per output, k split in parts
-        const float* RV = a.rot + (int64_t)(h * 2 + 1) * D * D;
-        constexpr int PARTS = kThreads / D;
-        constexpr int KP = D / PARTS;
-        const int i = threadIdx.x % D, part = threadIdx.x / D;
-        float t0 = 0.f, t1 = 0.f;
-#pragma unroll 8
-        for (int k = part * KP; k < (part + 1) * KP; k += 2) {
-            t0 += RV[(int64_t)k * D + i] * sm.sum[D + k];
-            t1 += RV[(int64_t)(k + 1) * D + i] * sm.sum[D + k + 1];
-        }
-        sm.acc[part][i] = t0 + t1;                 // wave scratch is free again
-        __syncthreads();
-        if (threadIdx.x < D) {
-            float o = sm.sum[i];
-#pragma unroll
-            for (int p = 0; p < PARTS; ++p) o += sm.acc[p][i];
-            rec[i] = o;
-        }
-    } else {
-        if (threadIdx.x < D) rec[threadIdx.x] = sm.sum[threadIdx.x];
-    }
+    for (int t = threadIdx.x; t < (NRES ? 2 * D : D); t += kThreads) rec[t] = sm.sum[t];
     if (threadIdx.x == 0) {
-        rec[D] = ml.x;
-        rec[D + 1] = ml.y;
+        rec[2 * D] = ml.x;
+        rec[2 * D + 1] = ml.y;
     }
 }
 
@@ -328,7 +543,7 @@ static hipError_t launch_q(const DecodeArgs& a, int nres, bool qbf16, dim3 grid,
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int nres, bool qbf16, hipStream_t st) {
-    if (!a.cache || !a.q || !a.ctx_len || !a.rot || !a.partials || a.batch < 1 || a.n_splits < 1 ||
+    if (!a.cache || !a.q || !a.rot || !a.ctx_len || !a.partials || a.batch < 1 || a.n_splits < 1 ||
         a.n_splits > kMaxSplits)
         return hipErrorInvalidValue;
     const dim3 grid(a.batch * a.geo.hq * a.n_splits);

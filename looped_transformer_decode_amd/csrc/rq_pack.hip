@@ -93,18 +93,29 @@ __device__ inline QOut quantize_lane(double x, int bits, int g) {
     return o;
 }
 
-template <int D>
-__device__ inline double block_sum(double v, double* red) {
-    for (int off = 32; off >= 1; off >>= 1) v += shfl_xor_d(v, off);
+// Sums over the D threads of the workgroup of N values per thread (float64).
+template <int D, int N>
+__device__ inline void block_sum_vec(double (&v)[N], double (*red)[N]) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+#pragma unroll
+        for (int k = 0; k < N; ++k) v[k] += shfl_xor_d(v[k], off);
     constexpr int W = D / 64;
-    if (W == 1) return v;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    __syncthreads();
-    if (lane == 0) red[w] = v;
-    __syncthreads();
-    double s = 0.0;
-    for (int i = 0; i < W; ++i) s += red[i];
-    return s;
+    if constexpr (W > 1) {
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+        __syncthreads();
+        if (lane == 0)
+#pragma unroll
+            for (int k = 0; k < N; ++k) red[w][k] = v[k];
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            double s = 0.0;
+#pragma unroll
+            for (int i = 0; i < W; ++i) s += red[i][k];
+            v[k] = s;
+        }
+    }
 }
 
 // Pack `bits`-wide codes of consecutive lanes into 32-bit words and store them.
@@ -121,6 +132,15 @@ __device__ inline void store_meta(uint8_t* row, const QOut& q, int g) {
     if (i % g == 0) reinterpret_cast<uint16_t*>(row)[i / g] = (uint16_t)(q.zb | (q.sb << 8));
 }
 
+__device__ inline void store_c(uint8_t* cblk, int jj, double c) {
+    if (threadIdx.x == 0) {
+        const uint32_t cb = __float_as_uint((float)c) >> 16;    // c is a BF16 value
+        reinterpret_cast<uint16_t*>(cblk)[jj] = (uint16_t)cb;
+    }
+}
+
+// One workgroup per (token range, batch row, KV head, K|V); thread i owns channel i and
+// keeps row i of R in registers for all tokens of the range.
 template <int D>
 __global__ __launch_bounds__(D) void rq_pack_kernel(PackArgs a) {
     const Geom& G = a.geo;
@@ -131,76 +151,114 @@ __global__ __launch_bounds__(D) void rq_pack_kernel(PackArgs a) {
     const int h = wg % G.hkv;
     wg /= G.hkv;
     const int b = wg % a.batch;
-    const int t = wg / a.batch;
-    const int slot = a.pos[b] + t;
-    if (slot < 0 || slot >= G.max_ctx) return;       // same for the whole workgroup
-    const int tile = slot / kTile, jj = slot % kTile;
+    const int t0 = (wg / a.batch) * a.tokens_per_wg;
+    const int t1 = min(t0 + a.tokens_per_wg, a.n_tokens);
     const int L = G.L;
-
-    __shared__ double sh_v[D];
-    __shared__ double red[D / 64];
-
-    double xv[kMaxLoops];
-    const uint16_t* src = a.pending + t * a.st[0] + b * a.st[1] + x * a.st[3] + h * a.st[4] + i;
-#pragma unroll
-    for (int l = 0; l < kMaxLoops; ++l)
-        if (l < L) xv[l] = (double)bf16_to_f32(src[l * a.st[2]]);
-
-    // anchor: the group's last loop
     const int loop0 = a.group_idx * L;
-    const QOut qa = quantize_lane(xv[L - 1], G.ba, G.g);
-    {
-        uint8_t* p = a.cache + G.plane_offset(b, h, x, loop0 + L - 1) + tile * G.a_tile;
-        store_codes(p + jj * G.a_row, qa.code, G.ba);
-        store_meta(p + kTile * G.a_row + jj * G.m_row, qa, G.g);
-    }
-    double ref = qa.z + qa.code * qa.s;                 // dequantized anchor (exact)
     const float* R = a.rot + (int64_t)(h * 2 + x) * D * D;
 
-    for (int l = L - 2; l >= 0; --l) {
-        const double num = block_sum<D>(xv[l] * ref, red);
-        const double den = block_sum<D>(ref * ref, red);
-        const double c = bf16_round(den > 0.0 ? num / den : 0.0);
-        const double y = xv[l] - c * ref;
-        __syncthreads();
-        sh_v[i] = y;
-        __syncthreads();
-        // r = R y : lane i takes row i of R
-        double r = 0.0;
-        const float4* Rrow = reinterpret_cast<const float4*>(R + (int64_t)i * D);
-#pragma unroll 8
+    __shared__ double sh_y[kMaxLoops][D];
+    __shared__ double red[D / 64][kMaxLoops];
+
+    float rrow[D];                                     // row i of R: r_i = sum_k R[i][k] y_k
+    {
+        const float4* rp = reinterpret_cast<const float4*>(R + (int64_t)i * D);
+#pragma unroll
         for (int k4 = 0; k4 < D / 4; ++k4) {
-            const float4 rv = Rrow[k4];
-            r += (double)rv.x * sh_v[4 * k4 + 0];
-            r += (double)rv.y * sh_v[4 * k4 + 1];
-            r += (double)rv.z * sh_v[4 * k4 + 2];
-            r += (double)rv.w * sh_v[4 * k4 + 3];
+            const float4 v = rp[k4];
+            rrow[4 * k4] = v.x;
+            rrow[4 * k4 + 1] = v.y;
+            rrow[4 * k4 + 2] = v.z;
+            rrow[4 * k4 + 3] = v.w;
         }
-        const QOut qr = quantize_lane(r, G.br, G.g);
-        uint8_t* p = a.cache + G.plane_offset(b, h, x, loop0 + l) + tile * G.r_tile;
-        store_codes(p + jj * G.r_row, qr.code, G.br);
-        store_meta(p + kTile * G.r_row + jj * G.m_row, qr, G.g);
-        if (i == 0) {
-            const uint32_t cb = __float_as_uint((float)c) >> 16;    // c is a BF16 value
-            reinterpret_cast<uint16_t*>(p + kTile * (G.r_row + G.m_row))[jj] = (uint16_t)cb;
+    }
+    uint8_t* a_plane = a.cache + G.plane_offset(b, h, x, loop0 + L - 1);
+
+    for (int t = t0; t < t1; ++t) {
+        const int slot = a.pos[b] + t;
+        if (slot < 0 || slot >= G.max_ctx) continue;   // same for the whole workgroup
+        const int tile = slot / kTile, jj = slot % kTile;
+
+        double xv[kMaxLoops];
+        const uint16_t* src = a.pending + t * a.st[0] + b * a.st[1] + x * a.st[3] + h * a.st[4] + i;
+#pragma unroll
+        for (int l = 0; l < kMaxLoops; ++l)
+            if (l < L) xv[l] = (double)bf16_to_f32(src[l * a.st[2]]);
+
+        // anchor: the group's last loop
+        const QOut qa = quantize_lane(xv[L - 1], G.ba, G.g);
+        {
+            uint8_t* p = a_plane + tile * G.a_tile;
+            store_codes(p + jj * G.a_row, qa.code, G.ba);
+            store_meta(p + kTile * G.a_row + jj * G.m_row, qa, G.g);
         }
-        if (G.chained) {
-            // rebuilt loop l = c * ref + R^T r_hat becomes the reference of loop l-1
-            const double rhat = qr.z + qr.code * qr.s;
+        const double a_hat = qa.z + qa.code * qa.s;      // dequantized anchor (exact)
+
+        if (!G.chained) {
+            // all loops reference a_hat: one reduction for every <x_l, a> and <a, a>
+            double sums[kMaxLoops];
+#pragma unroll
+            for (int l = 0; l < kMaxLoops; ++l) sums[l] = (l < L - 1) ? xv[l] * a_hat : 0.0;
+            sums[kMaxLoops - 1] = a_hat * a_hat;
+            block_sum_vec<D, kMaxLoops>(sums, red);
+            const double den = sums[kMaxLoops - 1];
+            double cs[kMaxLoops];
+#pragma unroll
+            for (int l = 0; l < kMaxLoops - 1; ++l) {
+                if (l < L - 1) {
+                    cs[l] = bf16_round(den > 0.0 ? sums[l] / den : 0.0);
+                    sh_y[l][i] = xv[l] - cs[l] * a_hat;
+                }
+            }
             __syncthreads();
-            sh_v[i] = rhat;
-            __syncthreads();
-            double tcol = 0.0;
-#pragma unroll 8
-            for (int k = 0; k < D; ++k) tcol += (double)R[(int64_t)k * D + i] * sh_v[k];
-            ref = c * ref + tcol;
+#pragma unroll
+            for (int l = 0; l < kMaxLoops - 1; ++l) {
+                if (l < L - 1) {
+                    double r = 0.0;
+#pragma unroll
+                    for (int k = 0; k < D; ++k) r += (double)rrow[k] * sh_y[l][k];
+                    const QOut qr = quantize_lane(r, G.br, G.g);
+                    uint8_t* p = a.cache + G.plane_offset(b, h, x, loop0 + l) + tile * G.r_tile;
+                    store_codes(p + jj * G.r_row, qr.code, G.br);
+                    store_meta(p + kTile * G.r_row + jj * G.m_row, qr, G.g);
+                    store_c(p + kTile * (G.r_row + G.m_row), jj, cs[l]);
+                }
+            }
+            __syncthreads();                              // sh_y is reused by the next token
+        } else {
+            // loop l references the rebuilt loop l+1 (the anchor closes the chain)
+            double ref = a_hat;
+            for (int l = L - 2; l >= 0; --l) {
+                double s2[2] = {xv[l] * ref, ref * ref};
+                block_sum_vec<D, 2>(s2, reinterpret_cast<double(*)[2]>(&red[0][0]));
+                const double c = bf16_round(s2[1] > 0.0 ? s2[0] / s2[1] : 0.0);
+                sh_y[0][i] = xv[l] - c * ref;
+                __syncthreads();
+                double r = 0.0;
+#pragma unroll
+                for (int k = 0; k < D; ++k) r += (double)rrow[k] * sh_y[0][k];
+                const QOut qr = quantize_lane(r, G.br, G.g);
+                uint8_t* p = a.cache + G.plane_offset(b, h, x, loop0 + l) + tile * G.r_tile;
+                store_codes(p + jj * G.r_row, qr.code, G.br);
+                store_meta(p + kTile * G.r_row + jj * G.m_row, qr, G.g);
+                store_c(p + kTile * (G.r_row + G.m_row), jj, c);
+                // R^T r_hat: thread i takes column i of R (coalesced across threads)
+                sh_y[1][i] = qr.z + qr.code * qr.s;
+                __syncthreads();
+                double tcol = 0.0;
+#pragma unroll 16
+                for (int k = 0; k < D; ++k) tcol += (double)R[(int64_t)k * D + i] * sh_y[1][k];
+                ref = c * ref + tcol;
+                __syncthreads();
+            }
         }
     }
 }
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t stream) {
-    if (!a.cache || !a.pending || !a.pos || !a.rot || a.batch < 1 || a.n_tokens < 1) return hipErrorInvalidValue;
-    const int nwg = a.n_tokens * a.batch * a.geo.hkv * 2;
+    if (!a.cache || !a.pending || !a.pos || !a.rot || a.batch < 1 || a.n_tokens < 1 || a.tokens_per_wg < 1)
+        return hipErrorInvalidValue;
+    const int nwg = (a.n_tokens + a.tokens_per_wg - 1) / a.tokens_per_wg * a.batch * a.geo.hkv * 2;
     if (a.geo.d == 128)
         hipLaunchKernelGGL(rq_pack_kernel<128>, dim3(nwg), dim3(128), 0, stream, a);
     else

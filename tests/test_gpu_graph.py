@@ -1,0 +1,56 @@
+"""A decode step captured in a HIP graph (torch.cuda.CUDAGraph) replays to the same
+outputs as eager launches: every replay, with eager work and synchronisations in
+between, is compared with the eager result.  The library enqueues no allocation,
+memset or synchronisation, so it can be captured."""
+import pytest
+import torch
+
+from looped_transformer_decode_amd import synth
+
+from _support import gpu_pack, say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_graph_replay_matches_eager():
+    from looped_transformer_decode_amd import binding as B
+    wl = synth.WORKLOADS["ouro_b4_t8192"].with_(batch=2, ctx=700, n_kv_heads=4, n_q_heads=4)
+    dev = torch.device("cuda:0")
+    inp = synth.generate(wl, seed=21, device=dev)
+    cfg = B.config_for(wl)
+    T, L, d = wl.ctx, wl.loops_per_group, wl.head_dim
+    cache = gpu_pack(B, cfg, inp.kv, inp.rot, T)
+    ws = torch.zeros(B.rq_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    pending = torch.zeros(wl.batch, L, 2, wl.n_kv_heads, d, dtype=torch.bfloat16, device=dev)
+    ctx_len = torch.tensor([T, 333], dtype=torch.int32, device=dev)
+    outs = [torch.empty(wl.batch, wl.n_q_heads, d, device=dev) for _ in range(L)]
+    q = [inp.q[l].contiguous() for l in range(L)]
+    kc = [inp.kv[0, l, 0, :, :, T].contiguous() for l in range(L)]
+    vc = [inp.kv[0, l, 1, :, :, T].contiguous() for l in range(L)]
+
+    def step():
+        for l in range(L):
+            B.rq_decode_attention(cfg, cache, l, q[l], kc[l], vc[l], pending, ctx_len, T, inp.rot, 0.088, outs[l],
+                                  ws, wl.batch, n_splits=3)
+        B.rq_quantize_token(cfg, cache, pending, 0, ctx_len, inp.rot, wl.batch, 1)
+
+    say("[graph] eager")
+    step()
+    torch.cuda.synchronize()
+    want = [o.clone() for o in outs]
+    cache_want = cache.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        say(f"[graph] replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        for o, w in zip(outs, want):
+            assert torch.equal(o, w)
+        assert torch.equal(cache, cache_want)
+        step()                                   # eager work between replays
+        torch.cuda.synchronize()
