@@ -44,6 +44,49 @@ __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// Prologue loads go through inline asm as well: the compiler counts outstanding loads
+// for its own waits and cannot see the stream DMAs issued after these, so its waits
+// would also stall on the DMAs.  pin() orders every use of a loaded register after the
+// explicit wait that follows the DMA issue.
+__device__ __forceinline__ f32x4 gload16(const uint8_t* sbase, uint32_t voff) {
+    f32x4 r;
+    asm volatile("global_load_dwordx4 %0, %1, %2" : "=v"(r) : "v"(voff), "s"(sbase));
+    return r;
+}
+__device__ __forceinline__ u32x2 gload8(const uint8_t* sbase, uint32_t voff) {
+    u32x2 r;
+    asm volatile("global_load_dwordx2 %0, %1, %2" : "=v"(r) : "v"(voff), "s"(sbase));
+    return r;
+}
+template <class T>
+__device__ __forceinline__ void pin(T& x) {
+    asm volatile("" : "+v"(x));
+}
+
+// Sum each of N values over aligned groups of 2M consecutive lanes.  Reduce-scatter
+// while values remain (lanes with bit M set keep the upper half), then plain
+// butterflies; on return v[0] is the group sum of value `off`.
+template <int CUR, int M, int N>
+__device__ __forceinline__ void group_reduce_scatter(float (&v)[N], int lane, int& off) {
+    if constexpr (M >= 1) {
+        if constexpr (CUR > 1) {
+            constexpr int half = CUR / 2;
+            const bool upper = (lane & M) != 0;
+#pragma unroll
+            for (int i = 0; i < half; ++i) {
+                const float send = upper ? v[i] : v[i + half];
+                const float keep = upper ? v[i + half] : v[i];
+                v[i] = keep + shfl_xor_f(send, M);
+            }
+            if (upper) off += half;
+            group_reduce_scatter<half, M / 2, N>(v, lane, off);
+        } else {
+            v[0] += shfl_xor_f(v[0], M);
+            group_reduce_scatter<1, M / 2, N>(v, lane, off);
+        }
+    }
+}
+
 // ---- keys: exact integer dot products on the packed codes
 //
 // q is written per quantization group as 24-bit fixed point Q_i = rint(q_i / delta),
@@ -185,8 +228,9 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
     constexpr int RC = SLOTS * D * 2 / 8;          // residual codes
     constexpr int CC = SLOTS * 2;                  // BF16 coefficients
     constexpr int PASS = 2 * (AC + AM + NRES * (RC + AM + CC));
-    constexpr int NB = kStageDepth;                // ring slots per wave
     constexpr int NDMA = 2 * (2 + 3 * NRES);       // DMA instructions per pass
+    // ring slots per wave: the loads of NB - 1 passes in flight must fit the 6-bit vmcnt
+    constexpr int NB = (kStageDepth - 1) * NDMA <= 63 ? kStageDepth : 1 + 63 / NDMA;
 
     const Geom& G = a.geo;
     const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -263,54 +307,66 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
         }
     };
     // wait until pass `it` has landed while `ahead` later passes stay in flight
+    static_assert((NB - 1) * NDMA <= 63, "vmcnt holds at most 63 outstanding loads");
     auto wait_pass = [&](int ahead) {
+        if constexpr (NB >= 5) {
+            if (ahead >= 4) { wait_vm<4 * NDMA>(); return; }
+        }
+        if constexpr (NB >= 4) {
+            if (ahead >= 3) { wait_vm<3 * NDMA>(); return; }
+        }
         if constexpr (NB >= 3) {
             if (ahead >= 2) { wait_vm<2 * NDMA>(); return; }
         }
         if (ahead >= 1) wait_vm<NDMA>();
         else wait_vm<0>();
     };
-    // ---- prologue, one load round: every thread loads the R_K row segment and the q
-    // segment its part of u = R_K q needs (plus q_t itself) before the stream DMAs are
-    // issued, so all of it is in flight together.
-    constexpr int TPR = kThreads / D;                  // threads per row of R_K
-    constexpr int COLS = D / TPR;
-    const int prow = threadIdx.x / TPR, ppart = threadIdx.x % TPR;
-    float4 rseg[NRES ? COLS / 4 : 1];
-    float qseg[NRES ? COLS : 1];
-    float qown = 0.f;
+    // ---- prologue.  R_K and q are loaded first, coalesced: load k of thread t holds row
+    // k * RPL + t / C4, columns [4 * (t % C4), 4 * (t % C4) + 4) of R_K, and the thread's
+    // q segment covers the same columns.  The stream DMAs of the first passes are issued
+    // behind them; vector loads return in order, so waiting until only those DMAs are
+    // outstanding leaves them in flight while u = R_K q and the digits are computed.
+    constexpr int C4 = D / 4;                          // 16-byte columns per row
+    constexpr int RPL = kThreads / C4;                 // rows covered by one load
+    constexpr int RL = NRES ? D / RPL : 1;             // R_K loads per thread
+    const int c4 = threadIdx.x % C4;
+    f32x4 rq4[RL];
+    f32x4 q4f;
+    u32x2 q4b;
     {
-        const int64_t qo = (int64_t)bh * D;
-        if (threadIdx.x < D) {
-            qown = QBF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qo + threadIdx.x])
-                         : reinterpret_cast<const float*>(a.q)[qo + threadIdx.x];
-        }
+        const uint8_t* qb = static_cast<const uint8_t*>(a.q) + (int64_t)bh * D * (QBF16 ? 2 : 4);
+        if constexpr (QBF16) q4b = gload8(qb, (uint32_t)c4 * 8u);
+        else q4f = gload16(qb, (uint32_t)c4 * 16u);
         if constexpr (NRES > 0) {
-            const float4* rr = reinterpret_cast<const float4*>(a.rot + (int64_t)(h * 2) * D * D +
-                                                               (int64_t)prow * D + ppart * COLS);
+            const uint8_t* rb = reinterpret_cast<const uint8_t*>(a.rot + (int64_t)(h * 2) * D * D);
 #pragma unroll
-            for (int k4 = 0; k4 < COLS / 4; ++k4) rseg[k4] = rr[k4];
-#pragma unroll
-            for (int k = 0; k < COLS; ++k) {
-                const int c = ppart * COLS + k;
-                qseg[k] = QBF16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qo + c])
-                                : reinterpret_cast<const float*>(a.q)[qo + c];
-            }
+            for (int k = 0; k < RL; ++k) rq4[k] = gload16(rb, (uint32_t)(k * kThreads + threadIdx.x) * 16u);
         }
     }
-    for (int k = 0; k < NB - 1 && k < n_it; ++k) issue(k);
+    const int n_pre = min(NB - 1, n_it);
+    for (int k = 0; k < n_pre; ++k) issue(k);
+    wait_pass(n_pre);
+    if constexpr (QBF16) {
+        pin(q4b);
+        q4f = f32x4{bf16lo(q4b.x), bf16hi(q4b.x), bf16lo(q4b.y), bf16hi(q4b.y)};
+    } else {
+        pin(q4f);
+    }
     for (int i = threadIdx.x; i < 10 * (D / 8); i += kThreads) s_dig[i] = 0u;
-    if (threadIdx.x < D) sv[0][threadIdx.x] = qown;
+    if (threadIdx.x < C4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sv[0][4 * c4 + e] = q4f[e];
+    }
     if constexpr (NRES > 0) {
-        float acc = 0.f;
+        float pr[RL];
 #pragma unroll
-        for (int k4 = 0; k4 < COLS / 4; ++k4) {
-            acc += rseg[k4].x * qseg[4 * k4] + rseg[k4].y * qseg[4 * k4 + 1] +
-                   rseg[k4].z * qseg[4 * k4 + 2] + rseg[k4].w * qseg[4 * k4 + 3];
+        for (int k = 0; k < RL; ++k) {
+            pin(rq4[k]);
+            pr[k] = rq4[k].x * q4f.x + rq4[k].y * q4f.y + rq4[k].z * q4f.z + rq4[k].w * q4f.w;
         }
-#pragma unroll
-        for (int m = 1; m < TPR; m <<= 1) acc += shfl_xor_f(acc, m);
-        if (ppart == 0) sv[1][prow] = acc;
+        int off = 0;
+        group_reduce_scatter<RL, C4 / 2, RL>(pr, lane, off);
+        sv[1][off * RPL + threadIdx.x / C4] = pr[0];
     }
     __syncthreads();
     // fixed-point digits (see the comment above digit_dot): q in the anchor-code layout,
