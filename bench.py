@@ -16,6 +16,7 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -28,6 +29,33 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "ouro_b4_t8192"
+CSRC = os.path.join(ROOT, "looped_transformer_decode_amd", "csrc")
+# sources of the two kernels of one decode loop-step (split kernel + merge kernel)
+DECODE_SOURCES = ("rq_api.hip", "rq_decode.hip", "rq_combine.hip", "rq_args.hpp", "rq_common.hpp",
+                  "rq_splitk.hpp")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "rq_decode_residual_ouro_b4_t8192_hbm_traffic.txt")
+
+
+def decode_source_digest() -> str:
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per residual loop-step from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, or None when it was taken on other kernel sources or another workload."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("source_digest") != decode_source_digest() or kv.get("workload") != workload:
+        return None
+    return int(float(kv["traffic_bytes_per_loop_step"]))
 
 
 def algorithmic_bytes(wl, loop_local: int, chained: bool) -> int:
@@ -96,6 +124,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--replicas", type=int, default=0)
+    ap.add_argument("--eager-only", action="store_true",
+                    help="time whole steps from eager launches instead of HIP graph replay "
+                         "(for profilers that cannot follow graph launches)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode hot path has no cross-GPU step here "
@@ -166,24 +197,33 @@ def main():
         step(args.warmup + s, True)
     torch.cuda.synchronize()
 
-    # whole-step time: each step replayed from a HIP graph (one graph per replica pattern)
-    n_pat = n_rep // math.gcd(n_rep, n_loops)
-    graphs = []
-    for p_ in range(n_pat):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(p_, False)
-        graphs.append(g)
-    torch.cuda.synchronize()
-    for s in range(args.warmup):
-        graphs[s % n_pat].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        graphs[s % n_pat].replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    if args.eager_only:
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            step(args.warmup + args.steps + s, False)
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        launch = "eager"
+    else:
+        # whole-step time: each step replayed from a HIP graph (one graph per replica pattern)
+        n_pat = n_rep // math.gcd(n_rep, n_loops)
+        graphs = []
+        for p_ in range(n_pat):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(p_, False)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for s in range(args.warmup):
+            graphs[s % n_pat].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            graphs[s % n_pat].replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_step = (t1 - t0) * 1e3 / args.steps
+        launch = "hip graph replay"
     stream = torch.cuda.current_stream()
 
     def avg_ms(key):
@@ -234,6 +274,7 @@ def main():
     bf16_gbps = bf16_bytes(wl) / (bf16_ms * 1e-3) / 1e9
 
     value = step_bytes / (ms_step * 1e-3) / 1e9
+    traffic = measured_traffic(wl.name) if not wl.chained and args.splits == 0 else None
     result = {
         "metric": "RQ decode-attn HBM GB/s (% of peak) & KV-tokens/s read, vs BF16 decode",
         "value": round(value, 2),
@@ -254,7 +295,7 @@ def main():
                    "resid_bits": wl.resid_bits, "chained": wl.chained, "cache_replicas": n_rep},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "kv_tokens_per_s": round(Bt * T / (res_ms * 1e-3), 1),
-        "step": {"bytes": step_bytes, "ms_wall": round(ms_step, 4), "launch": "hip graph replay",
+        "step": {"bytes": step_bytes, "ms_wall": round(ms_step, 4), "launch": launch,
                  "ms_per_loop_step": {str(l): round(v, 4) for l, v in per_loop.items()},
                  "ms_pack": round(pack_ms, 4)},
         "residual_loop_step": {"bytes": res_bytes, "ms": round(res_ms, 4), "gbps": round(res_gbps, 1),
@@ -265,8 +306,9 @@ def main():
                  "speedup_rq_residual_vs_bf16": round(bf16_ms / res_ms, 3),
                  "speedup_rq_step_vs_bf16_step": round(bf16_ms * n_loops / ms_step, 3)},
         "roofline": {"bound": "hbm", "achieved": round(res_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(res_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "rq_decode_kernel (residual loop-step)"},
+                     "frac": round(res_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "residual loop-step of rq_decode_attention: rq_decode_kernel + rq_combine_kernel",
+                     "algorithmic_bytes": res_bytes, "source_digest": decode_source_digest()},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)

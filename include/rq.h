@@ -128,8 +128,11 @@ rq_status rq_quantize_token(const rq_config* cfg, void* cache, const uint16_t* p
  * anchor a loop reads two planes (anchor + its residual), chained loop l reads the
  * anchor and the residual planes l..L-2.  The kernel never rebuilds K/V explicitly:
  * score_j = C_j (q . a_j) + sum_k gamma_jk (R_K q) . r_jk and the output accumulates
- * sum p_j C_j a_j and sum p_j gamma_jk r_jk separately, applying R_V^T once per split.  The
- * current token (not yet quantized) is the last attention entry, in BF16.
+ * sum p_j C_j a_j and sum p_j gamma_jk r_jk separately, applying R_V^T once per
+ * (batch row, query head) when the split-K partial results are merged.  The current
+ * token (not yet quantized) is the last attention entry, in BF16.
+ * Two kernels are enqueued: the split kernel (one workgroup per row, query head and
+ * split) and the merge kernel.
  * For each batch row b and query head hq (KV head h = hq / (Hq/Hkv)):
  *   out[b][hq] = softmax over j in [0, ctx_len[b]) and the current token of
  *                sm_scale * q . k_j, applied to the rebuilt values v_j.

@@ -25,7 +25,7 @@ Quantization for Looped Transformers with 2-Bit Residuals"):
   (not of the KV), INT4/INT2 mixed precision; Huginn-3.5B runs its 32 loops as
   8 groups of 4.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings adopted where the pages are silent:
 asymmetric min/max quantizer ``x_hat = z + q * s`` with FP8-E4M3 offset ``z``
 rounded down and scale ``s`` the smallest E4M3 value >= 2^-9 that covers the
 group maximum; codes rounded half-to-even; ``c`` rounded to BF16 once from the

@@ -127,9 +127,9 @@ def test_quantize_token_rejects_bad_arguments(B):
     assert call(pending=A + 1) == 3
     bad = (ctypes.c_int64 * 5)(1, 1, -1, 1, 1)
     assert call(st=bad) == 1
-    cfg2 = B.config_for(wl)
-    cfg2.head_dim = 96
-    assert f(ctypes.byref(cfg2), A, A, None, 0, A, A, 1, 1, None) == 2
+    bad = B.config_for(wl)
+    bad.head_dim = 96
+    assert f(ctypes.byref(bad), A, A, None, 0, A, A, 1, 1, None) == 2
 
 
 def test_bf16_decode_rejects_bad_arguments(B):

@@ -147,3 +147,29 @@ def test_empty_context_returns_current_value():
     o = RQ.decode_attention(cache, RQ.Layout(cfg), 1, inp.q.double().numpy()[1],
                             kv[0, 1, 0, :, :, 0], vc, [0], rot, 0.125)
     assert np.array_equal(o, vc)
+
+
+@pytest.mark.parametrize("chained", [False, True])
+def test_token_permutation_invariance(chained):
+    """Softmax attention does not depend on the order of the context tokens.  Packing the
+    same tokens in another order must give the same output at every loop (this catches a
+    key scored against another token's value, coefficient or metadata)."""
+    wl = synth.WORKLOADS["tiny_d64_t256"]
+    inp = synth.generate(wl, seed=36)
+    cfg = _cfg(wl, chained)
+    kv = inp.kv.double().numpy()
+    rot = inp.rot.double().numpy()
+    T = 150
+    perm = np.random.default_rng(37).permutation(T)
+    kvp = kv.copy()
+    kvp[..., :T, :] = kv[..., perm, :]
+    lay = RQ.Layout(cfg)
+    c0 = RQ.pack_context(kv, rot, cfg, T)
+    c1 = RQ.pack_context(kvp, rot, cfg, T)
+    assert not np.array_equal(c0, c1)
+    q = inp.q.double().numpy()
+    for loop in range(4):
+        kc, vc = kv[0, loop, 0, :, :, T], kv[0, loop, 1, :, :, T]
+        o0 = RQ.decode_attention(c0, lay, loop, q[loop], kc, vc, [T], rot, 0.125)
+        o1 = RQ.decode_attention(c1, lay, loop, q[loop], kc, vc, [T], rot, 0.125)
+        assert np.allclose(o0, o1, rtol=1e-12, atol=1e-13)
