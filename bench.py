@@ -30,8 +30,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "ouro_b4_t8192"
 CSRC = os.path.join(ROOT, "looped_transformer_decode_amd", "csrc")
-# sources of the two kernels of one decode loop-step (split kernel + merge kernel)
-DECODE_SOURCES = ("rq_api.hip", "rq_decode.hip", "rq_combine.hip", "rq_args.hpp", "rq_common.hpp",
+# sources of the decode kernel (split-K with the merge in its last workgroup)
+DECODE_SOURCES = ("rq_api.hip", "rq_decode.hip", "rq_args.hpp", "rq_common.hpp",
                   "rq_splitk.hpp")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "rq_decode_residual_ouro_b4_t8192_hbm_traffic.txt")
 

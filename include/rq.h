@@ -73,9 +73,12 @@ typedef struct rq_config {
  * KV head per K|V.  Returns 0 for an invalid or unsupported configuration. */
 size_t rq_cache_bytes(const rq_config* cfg);
 
-/* Bytes of scratch that rq_decode_attention needs for `cfg`: one split-K partial record
- * (unnormalised output, running max, denominator) per (batch row, query head, split).
- * The caller allocates it; its contents need no initialisation and are not kept. */
+/* Bytes of workspace that rq_decode_attention needs for `cfg`: one split-K partial record
+ * (unnormalised output, running max, denominator) per (batch row, query head, split), then
+ * one arrival counter per (batch row, query head).  The caller allocates it and fills it
+ * with zeros once before its first use; every call leaves the counters at zero again, so
+ * the same workspace serves any number of later calls (and HIP graph replays) as long as
+ * they do not overlap in time and nothing else writes to it. */
 size_t rq_workspace_bytes(const rq_config* cfg);
 
 /* Shape of one loop's uncompressed BF16 cache for the baseline decode kernel. */
@@ -131,8 +134,8 @@ rq_status rq_quantize_token(const rq_config* cfg, void* cache, const uint16_t* p
  * sum p_j C_j a_j and sum p_j gamma_jk r_jk separately, applying R_V^T once per
  * (batch row, query head) when the split-K partial results are merged.  The current
  * token (not yet quantized) is the last attention entry, in BF16.
- * Two kernels are enqueued: the split kernel (one workgroup per row, query head and
- * split) and the merge kernel.
+ * One kernel is enqueued: one workgroup per (row, query head, split); the last
+ * workgroup of a (row, query head) to finish merges the splits.
  * For each batch row b and query head hq (KV head h = hq / (Hq/Hkv)):
  *   out[b][hq] = softmax over j in [0, ctx_len[b]) and the current token of
  *                sm_scale * q . k_j, applied to the rebuilt values v_j.
@@ -147,7 +150,7 @@ rq_status rq_quantize_token(const rq_config* cfg, void* cache, const uint16_t* p
  *   ctx_bound : host upper bound of every ctx_len[b], 0..max_ctx; sizes the launch.
  *   rot       : device float32 [n_kv_heads][2][head_dim][head_dim].
  *   out       : device float32 [batch][n_q_heads][head_dim].
- *   workspace : device, >= rq_workspace_bytes(cfg) bytes of scratch.
+ *   workspace : device, >= rq_workspace_bytes(cfg) bytes, zero-filled before first use.
  *   n_splits  : split-K factor 1..64, or 0 to let the library choose.
  * Alignment: cache, q, k_cur, v_cur, pending, out, rot and workspace 16-byte aligned. */
 rq_status rq_decode_attention(const rq_config* cfg, const void* cache, int32_t loop,
@@ -164,7 +167,7 @@ rq_status rq_decode_attention(const rq_config* cfg, const void* cache, int32_t l
  *   k_cache, v_cache : device BF16 [max_batch][n_kv_heads][t_cap][head_dim] of one loop.
  *   append    : if nonzero, k_cur/v_cur are also stored at slot ctx_len[b] (when < t_cap).
  *   ctx_bound : host upper bound of every ctx_len[b], 0..t_cap.
- *   workspace : >= rq_bf16_workspace_bytes(cfg) bytes of scratch.
+ *   workspace : >= rq_bf16_workspace_bytes(cfg) bytes, zero-filled before first use.
  * Other arguments as for rq_decode_attention. */
 rq_status rq_bf16_decode_attention(const rq_bf16_config* cfg, uint16_t* k_cache, uint16_t* v_cache,
                                    const void* q, int32_t q_is_bf16,

@@ -175,27 +175,24 @@ rq_status rq_decode_attention(const rq_config* cfg, const void* cache, int32_t l
     a.ctx_len = ctx_len;
     a.ctx_bound = ctx_bound;
     a.sm_scale = sm_scale;
-    a.partials = static_cast<float*>(workspace);
     a.batch = batch;
     a.n_splits = S;
     a.tiles_per_split = n_tiles > 0 ? (n_tiles + S - 1) / S : 0;
-    if (launch_decode(a, nres, q_is_bf16 != 0, stream) != hipSuccess) return RQ_ERR_HIP;
-    CombineArgs c;
-    memset(&c, 0, sizeof(c));
-    c.partials = a.partials;
-    c.n_splits = S;
-    c.q = q;
-    c.k_cur = k_cur;
-    c.v_cur = v_cur;
-    c.hkv = g.hkv;
-    c.hq = g.hq;
-    c.sm_scale = sm_scale;
-    c.out = out;
-    c.pending = pending;
-    c.L = g.L;
-    c.lloc = lloc;
-    c.rot_v = nres > 0 ? rot + (size_t)g.d * g.d : nullptr;      // R of (KV head 0, V)
-    return launch_combine(c, g.d, q_is_bf16 != 0, batch, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
+    MergeArgs& m = a.mg;
+    m.partials = static_cast<float*>(workspace);
+    m.arrivals = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + records_bytes(g.max_batch, g.hq, g.d));
+    m.n_splits = S;
+    m.hkv = g.hkv;
+    m.hq = g.hq;
+    m.sm_scale = sm_scale;
+    m.k_cur = k_cur;
+    m.v_cur = v_cur;
+    m.out = out;
+    m.pending = pending;
+    m.L = g.L;
+    m.lloc = lloc;
+    m.rot = rot;
+    return launch_decode(a, nres, q_is_bf16 != 0, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 
 rq_status rq_bf16_decode_attention(const rq_bf16_config* cfg, uint16_t* k_cache, uint16_t* v_cache,
@@ -232,30 +229,28 @@ rq_status rq_bf16_decode_attention(const rq_bf16_config* cfg, uint16_t* k_cache,
     a.ctx_len = ctx_len;
     a.ctx_bound = ctx_bound;
     a.sm_scale = sm_scale;
-    a.partials = static_cast<float*>(workspace);
     a.batch = batch;
     a.n_splits = S;
     a.tiles_per_split = n_tiles > 0 ? (n_tiles + S - 1) / S : 0;
-    if (launch_bf16(a, head_dim, q_is_bf16 != 0, stream) != hipSuccess) return RQ_ERR_HIP;
-    CombineArgs c;
-    memset(&c, 0, sizeof(c));
-    c.partials = a.partials;
-    c.n_splits = S;
-    c.q = q;
-    c.k_cur = k_cur;
-    c.v_cur = v_cur;
-    c.hkv = cfg->n_kv_heads;
-    c.hq = n_q_heads;
-    c.sm_scale = sm_scale;
-    c.out = out;
+    MergeArgs& m = a.mg;
+    m.partials = static_cast<float*>(workspace);
+    m.arrivals = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) +
+                                             records_bytes(cfg->max_batch, n_q_heads, head_dim));
+    m.n_splits = S;
+    m.hkv = cfg->n_kv_heads;
+    m.hq = n_q_heads;
+    m.sm_scale = sm_scale;
+    m.k_cur = k_cur;
+    m.v_cur = v_cur;
+    m.out = out;
     if (append) {
-        c.k_app = k_cache;
-        c.v_app = v_cache;
-        c.t_cap = cfg->t_cap;
-        c.ctx_len = ctx_len;
-        c.ctx_bound = ctx_bound;
+        m.k_app = k_cache;
+        m.v_app = v_cache;
+        m.t_cap = cfg->t_cap;
+        m.ctx_len = ctx_len;
+        m.ctx_bound = ctx_bound;
     }
-    return launch_combine(c, head_dim, q_is_bf16 != 0, batch, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
+    return launch_bf16(a, head_dim, q_is_bf16 != 0, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 
 }  // extern "C"

@@ -18,6 +18,26 @@ struct PackArgs {
     int tokens_per_wg;          // tokens handled by one workgroup (it keeps its row of R)
 };
 
+// The split-K merge that the last workgroup of each (batch row, query head) performs.
+struct MergeArgs {
+    float* partials;            // [batch * hq][kMaxSplits] records of partial_stride(d) floats
+    uint32_t* arrivals;         // [batch * hq] arrival counters; zero between calls
+    int n_splits;
+    int hkv, hq;
+    float sm_scale;
+    const uint16_t* k_cur;      // [batch][hkv][d] BF16 current token of this loop
+    const uint16_t* v_cur;
+    float* out;                 // [batch][hq][d]
+    uint16_t* pending;          // ResidualQuant: [batch][L][2][hkv][d] or null
+    int L, lloc;
+    const float* rot;           // ResidualQuant residual loops: R of (KV head h, V) at rot + (2h+1)*d*d
+    uint16_t* k_app;            // BF16 baseline append target [batch][hkv][t_cap][d] or null
+    uint16_t* v_app;
+    int t_cap;
+    const int32_t* ctx_len;
+    int ctx_bound;
+};
+
 struct DecodeArgs {
     Geom geo;
     const uint8_t* cache;
@@ -27,10 +47,10 @@ struct DecodeArgs {
     const int32_t* ctx_len;
     int ctx_bound;
     float sm_scale;
-    float* partials;
     int batch;
     int n_splits;
     int tiles_per_split;
+    MergeArgs mg;
 };
 
 // BF16 baseline split kernel: K and V caches [batch][hkv][t_cap][d].
@@ -42,34 +62,13 @@ struct Bf16Args {
     const int32_t* ctx_len;
     int ctx_bound;
     float sm_scale;
-    float* partials;
     int batch;
     int n_splits;
     int tiles_per_split;
-};
-
-// Merge of the split-K partial records of one loop-step, plus the current token.
-struct CombineArgs {
-    const float* partials;      // [batch * hq][kMaxSplits][d + 4]
-    int n_splits;
-    const void* q;
-    const uint16_t* k_cur;      // [batch][hkv][d]
-    const uint16_t* v_cur;
-    int hkv, hq;
-    float sm_scale;
-    float* out;                 // [batch][hq][d]
-    uint16_t* pending;          // ResidualQuant: [batch][L][2][hkv][d] or null
-    int L, lloc;
-    const float* rot_v;         // ResidualQuant residual loops: R_V of KV head h at rot_v + h*2*d*d, else null
-    uint16_t* k_app;            // BF16 baseline append target [batch][hkv][t_cap][d] or null
-    uint16_t* v_app;
-    int t_cap;
-    const int32_t* ctx_len;
-    int ctx_bound;
+    MergeArgs mg;
 };
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t stream);
-hipError_t launch_combine(const CombineArgs& a, int d, bool qbf16, int batch, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int nres, bool qbf16, hipStream_t st);
 hipError_t launch_bf16(const Bf16Args& a, int d, bool qbf16, hipStream_t st);
 

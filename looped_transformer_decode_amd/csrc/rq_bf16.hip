@@ -108,6 +108,7 @@ __global__ __launch_bounds__(kThreads) void rq_bf16_decode_kernel(Bf16Args a) {
     };
 
     for (int it = 0; it < n_it; it += 2) {
+        if (it % PPT == 0) prio_by_progress(it, n_it);
         if (it + 1 < n_it) load(fb, it + 1);
         compute(fa, it);
         if (it + 1 < n_it) {
@@ -116,18 +117,15 @@ __global__ __launch_bounds__(kThreads) void rq_bf16_decode_kernel(Bf16Args a) {
         }
     }
 
+    __builtin_amdgcn_s_setprio(3);
     const float2 ml = splitk_merge_waves<D, 32>(acc, m_run, l_lane, sm);
-    float* rec = a.partials + ((int64_t)bh * kMaxSplits + split) * partial_stride(D);
-    if (threadIdx.x < D) rec[threadIdx.x] = sm.sum[threadIdx.x];
-    if (threadIdx.x == 0) {
-        rec[2 * D] = ml.x;
-        rec[2 * D + 1] = ml.y;
-    }
+    splitk_finish<D, false>(a.mg, bh, split, sm.sum, ml, sq, sm);
 }
 
 hipError_t launch_bf16(const Bf16Args& a, int d, bool qbf16, hipStream_t st) {
-    if (!a.k || !a.v || !a.q || !a.ctx_len || !a.partials || a.batch < 1 || a.n_splits < 1 ||
-        a.n_splits > kMaxSplits || a.t_cap < 1)
+    if (!a.k || !a.v || !a.q || !a.ctx_len || !a.mg.partials || !a.mg.arrivals || !a.mg.k_cur || !a.mg.v_cur ||
+        !a.mg.out || a.batch < 1 || a.n_splits < 1 || a.n_splits > kMaxSplits || a.mg.n_splits != a.n_splits ||
+        a.t_cap < 1)
         return hipErrorInvalidValue;
     const dim3 grid(a.batch * a.hq * a.n_splits);
     if (d == 128) {

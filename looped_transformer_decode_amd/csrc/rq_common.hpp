@@ -35,10 +35,14 @@ bool make_geom(const rq_config* cfg, Geom* g);
 
 // Workspace layout for split-K decode: per (batch row, query head, split) a record of
 // acc_a[d] (anchor part, or the whole output of the BF16 kernel), acc_r[d] (residual part,
-// before R_V^T), m (running max), l (denominator), 2 floats of padding.
+// before R_V^T), m (running max), l (denominator), 2 floats of padding; then one 32-bit
+// arrival counter per (batch row, query head), which every call leaves at zero.
 __host__ __device__ inline int partial_stride(int d) { return 2 * d + 4; }
-inline size_t workspace_bytes(int max_batch, int hq, int d) {
+inline size_t records_bytes(int max_batch, int hq, int d) {
     return (size_t)max_batch * hq * kMaxSplits * partial_stride(d) * sizeof(float);
+}
+inline size_t workspace_bytes(int max_batch, int hq, int d) {
+    return records_bytes(max_batch, hq, d) + (((size_t)max_batch * hq * sizeof(uint32_t) + 255) & ~(size_t)255);
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -108,6 +112,20 @@ __device__ __forceinline__ float group_sum_dpp(float v) {
 // only has to bound the scores well enough that p cannot overflow, so it is raised only
 // when a score exceeds it by more than this slack (natural-log units; p <= e^8).
 constexpr float kRescaleSlack = 8.0f;
+
+// Two workgroups share each CU and their waves pair up on the SIMDs, where the older wave
+// wins instruction issue.  With equal work the younger one would finish late and run
+// alone at the end; giving issue priority to the wave with less of its loop done keeps
+// the pair in step.  Called with wave-uniform arguments.
+__device__ __forceinline__ void prio_by_progress(int done, int total) {
+    const int quarter = total > 0 ? (4 * done) / total : 3;
+    switch (quarter) {
+        case 0: __builtin_amdgcn_s_setprio(3); break;
+        case 1: __builtin_amdgcn_s_setprio(2); break;
+        case 2: __builtin_amdgcn_s_setprio(1); break;
+        default: __builtin_amdgcn_s_setprio(0); break;
+    }
+}
 
 // True in every lane if any lane of the wave has pred set.
 __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }

@@ -12,8 +12,8 @@
 //   q . k_j = C_j (q . a_j) + sum_k gamma_jk (R_K q) . r_jk
 // and with a = z + s * code per group,  q . a = sum_groups (z * sum(q) + s * sum(q * code)).
 // Values: o = (sum_j p_j C_j a_j + R_V^T sum_j p_j sum_k gamma_jk r_jk + p_cur v_cur) / sum p,
-// so the kernel accumulates the anchor part and the residual part separately and
-// applies R_V^T once per output in the final merge.
+// so the kernel accumulates the anchor part and the residual part separately; the last
+// workgroup of each (batch row, query head) merges the splits and applies R_V^T once.
 #include "rq_args.hpp"
 #include "rq_splitk.hpp"
 
@@ -555,12 +555,13 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
 
     // ---- main loop: NB-1 passes in flight while one is computed from LDS
     for (int it = 0; it < n_it; ++it) {
+        if (it % PPT == 0) prio_by_progress(it, n_it);
         if (it + NB - 1 < n_it) issue(it + NB - 1);
         wait_pass(min(NB - 1, n_it - 1 - it));
         compute(it);
     }
 
-    // ---- undo the FP16 magic offsets, merge the waves, apply R_V^T to the residual part
+    // ---- undo the FP16 magic offsets, merge the waves; the last split applies R_V^T
     float v[NV];
 #pragma unroll
     for (int i = 0; i < 32; ++i)
@@ -570,14 +571,9 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
         for (int i = 0; i < 32; ++i)
             v[32 + i] = (accR[i] - 1024.f * wR[i / GS]) * inv_mult<2>(i) + zR[i / GS];
     }
+    __builtin_amdgcn_s_setprio(3);                // the merge is on the critical path
     const float2 ml = splitk_merge_waves<D, NV>(v, m_run, l_lane, sm);
-    // record: acc_a[D], acc_r[D] (R_V^T is applied once per head in the merge kernel), m, l
-    float* rec = a.partials + ((int64_t)bh * kMaxSplits + split) * partial_stride(D);
-    for (int t = threadIdx.x; t < (NRES ? 2 * D : D); t += kThreads) rec[t] = sm.sum[t];
-    if (threadIdx.x == 0) {
-        rec[2 * D] = ml.x;
-        rec[2 * D + 1] = ml.y;
-    }
+    splitk_finish<D, (NRES > 0)>(a.mg, bh, split, sm.sum, ml, sv[0], sm);
 }
 
 template <int D, int GS, int BA, bool QB>
@@ -599,8 +595,9 @@ static hipError_t launch_q(const DecodeArgs& a, int nres, bool qbf16, dim3 grid,
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int nres, bool qbf16, hipStream_t st) {
-    if (!a.cache || !a.q || !a.rot || !a.ctx_len || !a.partials || a.batch < 1 || a.n_splits < 1 ||
-        a.n_splits > kMaxSplits)
+    if (!a.cache || !a.q || !a.rot || !a.ctx_len || !a.mg.partials || !a.mg.arrivals || !a.mg.k_cur ||
+        !a.mg.v_cur || !a.mg.out || !a.mg.rot || a.batch < 1 || a.n_splits < 1 || a.n_splits > kMaxSplits ||
+        a.mg.n_splits != a.n_splits)
         return hipErrorInvalidValue;
     const dim3 grid(a.batch * a.geo.hq * a.n_splits);
     const int d = a.geo.d, g = a.geo.g, ba = a.geo.ba;

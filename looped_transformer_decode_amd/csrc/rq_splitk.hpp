@@ -4,14 +4,12 @@
 // consecutive channels (LPT = d/32 lanes per token) and slot selects one of 64/LPT tokens
 // processed per pass.  Each lane keeps partial output sums for its 32 channels; at the end
 // of a split they are reduced over slots (reduce-scatter) and merged across the waves of
-// the workgroup in LDS.  The split kernel writes one partial record per split
-// (unnormalised output o[d], running max m, denominator l); a second, small kernel merges
-// the records of each (batch row, query head) and adds the current token.  The kernel
-// boundary orders the two, so no device-scope fence is needed inside the split kernel
-// (on gfx950 such a fence writes back and invalidates the whole L2 of the XCD).
+// the workgroup in LDS.  Each workgroup then publishes one record per split (unnormalised
+// output o, running max m, denominator l) and counts its arrival; the last workgroup of a
+// (batch row, query head) merges the records, adds the current token and writes the output.
 #pragma once
 
-#include "rq_common.hpp"
+#include "rq_args.hpp"
 
 namespace rq {
 
@@ -112,6 +110,172 @@ __device__ __forceinline__ float2 splitk_merge_waves(float (&v)[NV], float m_w, 
     }
     __syncthreads();
     return make_float2(m_wg, l_wg);
+}
+
+// ---- publishing split records and the merge by the last workgroup
+//
+// Records and arrival counters are accessed with relaxed agent-scope atomic loads, stores
+// and adds, each of which is coherent across the XCDs by itself, so no L2 writeback or
+// invalidate is needed.  Every thread waits for its own record stores (vmcnt) before the
+// barrier that precedes the arrival count; the workgroup that brings the count to
+// n_splits reads the records only after that, and puts the counter back to zero.
+
+__device__ __forceinline__ void st_agent(float* p, float v) {
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+    return __uint_as_float(__hip_atomic_load(const_cast<uint32_t*>(reinterpret_cast<const uint32_t*>(p)),
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+template <int N>
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = N / 2; m >= 1; m >>= 1) v += shfl_xor_f(v, m);
+    return v;
+}
+
+// sum: LDS values of this split (acc_a[D], then acc_r[D] when RES); ml = (m, l) of the
+// split; qf: LDS float32 query.  The last workgroup of (batch row, query head) bh writes
+//   out = (sum_s w_s acc_a_s + R_V^T sum_s w_s acc_r_s + p_cur v_cur) / (sum_s w_s l_s + p_cur)
+// with w_s = exp(m_s - m), p_cur = exp(s_cur - m), m = max(max_s m_s, s_cur), and stores the
+// current token into the pending buffer (or the BF16 cache) for the first query head of
+// its KV head.
+template <int D, bool RES>
+__device__ __forceinline__ void splitk_finish(const MergeArgs& g, int bh, int split, const float* sum, float2 ml,
+                                              const float* qf, SplitSmem<D>& sm) {
+    constexpr int NVAL = RES ? 2 * D : D;
+    constexpr int PS = 2 * D + 4;
+    static_assert(kMaxSplits <= kWave, "one lane per split record");
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    float* recs = g.partials + (int64_t)bh * kMaxSplits * PS;
+    {
+        float* rec = recs + (int64_t)split * PS;
+        for (int t = tid; t < NVAL; t += kThreads) st_agent(rec + t, sum[t]);
+        if (tid == 0) {
+            st_agent(rec + 2 * D, ml.x);
+            st_agent(rec + 2 * D + 1, ml.y);
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __shared__ int s_last;
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(g.arrivals + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = old == (uint32_t)(g.n_splits - 1);
+        if (last) __hip_atomic_store(g.arrivals + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = last;
+    }
+    __syncthreads();
+    if (!s_last) return;
+
+    const int S = g.n_splits;
+    const int hq = bh % g.hq, b = bh / g.hq;
+    const int gqa = g.hq / g.hkv, h = hq / gqa;
+    float* scr = &sm.acc[0][0];
+    float* s_red = scr;                 // [kWaves]
+    float* s_w = scr + kWaves;          // [kMaxSplits]
+    float* s_sc = s_w + kMaxSplits;     // m, l_tot, p_cur
+    float* s_r = s_sc + 4;              // [D] merged residual part
+    float* s_p = s_r + D;               // [kThreads / D][D] partial R_V^T products
+    static_assert(kWaves + kMaxSplits + 4 + D + kThreads <= kWaves * 2 * D, "merge scratch fits SplitSmem::acc");
+    // every load that does not depend on the merge weights goes out first
+    const int64_t kvo = ((int64_t)b * g.hkv + h) * D;
+    uint32_t kc = 0, vc = 0;
+    if (tid < D) {
+        kc = g.k_cur[kvo + tid];
+        vc = g.v_cur[kvo + tid];
+    }
+    float ms = -INFINITY, ls = 0.f;
+    if (tid < S) {
+        ms = ld_agent(recs + (int64_t)tid * PS + 2 * D);
+        ls = ld_agent(recs + (int64_t)tid * PS + 2 * D + 1);
+    }
+    constexpr int CH = 8;
+    float pv[CH];
+    auto load_chunk = [&](int s0) {
+#pragma unroll
+        for (int k = 0; k < CH; ++k)
+            pv[k] = (tid < NVAL && s0 + k < S) ? ld_agent(recs + (int64_t)(s0 + k) * PS + tid) : 0.f;
+    };
+    load_chunk(0);
+    constexpr int RP = kThreads / D;           // parts of the R_V^T product
+    constexpr int RROWS = D / RP;
+    float rv[RES ? RROWS : 1];
+    if constexpr (RES) {
+        // column tid % D of R_V, rows of part tid / D: coalesced across the threads
+        const float* Rv = g.rot + (int64_t)(2 * h + 1) * D * D + (int64_t)(tid / D) * RROWS * D + tid % D;
+#pragma unroll
+        for (int k = 0; k < RROWS; ++k) rv[k] = Rv[(int64_t)k * D];
+    }
+    // score of the current token
+    float qk = tid < D ? qf[tid] * bf16_to_f32(kc) : 0.f;
+    qk = wave_sum<kWave>(qk);
+    if (lane == 0) s_red[w] = qk;
+    __syncthreads();
+    if (w == 0) {
+        float s_cur = 0.f;
+#pragma unroll
+        for (int i = 0; i < kWaves; ++i) s_cur += s_red[i];
+        s_cur *= g.sm_scale;
+        float mx = (ls > 0.f) ? ms : -INFINITY;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, m));
+        const float m_f = fmaxf(mx, s_cur);
+        const float ws = (ls > 0.f) ? __expf(ms - m_f) : 0.f;
+        if (lane < kMaxSplits) s_w[lane] = ws;
+        const float lt = wave_sum<kWave>(ws * ls);
+        if (lane == 0) {
+            s_sc[0] = m_f;
+            s_sc[1] = lt;
+            s_sc[2] = __expf(s_cur - m_f);
+        }
+    }
+    __syncthreads();
+    float acc = 0.f;
+    for (int s0 = 0; s0 < S; s0 += CH) {
+        if (s0 > 0) load_chunk(s0);
+#pragma unroll
+        for (int k = 0; k < CH; ++k)
+            if (s0 + k < S) acc += s_w[s0 + k] * pv[k];
+    }
+    float o = 0.f;
+    if constexpr (RES) {
+        if (tid >= D && tid < 2 * D) s_r[tid - D] = acc;
+        __syncthreads();
+        float pr = 0.f;
+        const int r0 = (tid / D) * RROWS;
+#pragma unroll
+        for (int k = 0; k < RROWS; ++k) pr += rv[k] * s_r[r0 + k];
+        s_p[tid] = pr;
+        __syncthreads();
+        if (tid < D) {
+#pragma unroll
+            for (int p = 0; p < RP; ++p) o += s_p[p * D + tid];
+        }
+    }
+    if (tid < D) {
+        const float p_cur = s_sc[2];
+        o = (acc + o + p_cur * bf16_to_f32(vc)) / (s_sc[1] + p_cur);
+        g.out[(int64_t)bh * D + tid] = o;
+        if (hq % gqa == 0) {
+            if (g.pending != nullptr) {
+                uint16_t* pd = g.pending + (((int64_t)b * g.L + g.lloc) * 2 * g.hkv + h) * D + tid;
+                pd[0] = (uint16_t)kc;
+                pd[(int64_t)g.hkv * D] = (uint16_t)vc;
+            }
+            if (g.k_app != nullptr) {
+                int n = g.ctx_len[b];
+                n = n < 0 ? 0 : (n > g.ctx_bound ? g.ctx_bound : n);
+                if (n < g.t_cap) {
+                    const int64_t off = (((int64_t)b * g.hkv + h) * g.t_cap + n) * D + tid;
+                    g.k_app[off] = (uint16_t)kc;
+                    g.v_app[off] = (uint16_t)vc;
+                }
+            }
+        }
+    }
 }
 
 }  // namespace rq

@@ -1,0 +1,100 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times
+(automatic split count, every row at the full context), on sampled (row, KV head) pairs
+that the float64 oracle can check one by one:
+
+* the bulk-packed cache bytes of each sampled pair against the oracle's encoding rules;
+* decode attention at residual and anchor loops of first, middle and last anchor groups,
+  for every query head of the sampled KV heads, against the oracle's decode of the GPU's
+  own bytes and of the oracle's own encoding.
+"""
+import numpy as np
+import pytest
+import torch
+
+from looped_transformer_decode_amd import synth
+from oracle import residualquant as RQ
+
+from _support import (assert_stats, check_pack_block, close, device_block, gpu_pack, new_stats, oracle_cfg,
+                      say, sub_cache)
+
+pytestmark = pytest.mark.gpu
+
+FULL = [
+    ("ouro_b4_t8192", False),
+    ("ouro_b16_t8192", False),
+    ("int2g16_b4_t16384", False),
+    ("int2g16_b4_t16384", True),
+    ("huginn_gqa4_b8_t8192", False),
+]
+
+
+def _pairs(wl, rng):
+    pairs = {(0, 0), (wl.batch - 1, wl.n_kv_heads - 1)}
+    pairs.add((int(rng.integers(wl.batch)), int(rng.integers(wl.n_kv_heads))))
+    return sorted(pairs)
+
+
+def _loops(wl):
+    L, G = wl.loops_per_group, wl.n_groups
+    groups = sorted({0, G // 2, G - 1})
+    return [k * L + l for k in groups for l in range(L)] if G <= 2 else \
+        [k * L + l for k in groups for l in (0, L - 2, L - 1)]
+
+
+@pytest.mark.parametrize("name,chained", FULL, ids=[f"{n}{'_chained' if c else ''}" for n, c in FULL])
+def test_full_size_parity(name, chained):
+    from looped_transformer_decode_amd import binding as B
+    wl = synth.WORKLOADS[name].with_(chained=chained)
+    T, L, d = wl.ctx, wl.loops_per_group, wl.head_dim
+    gqa = wl.n_q_heads // wl.n_kv_heads
+    say(f"[full] {name} chained={chained}: generating")
+    inp = synth.generate(wl, seed=4242, device="cuda")
+    cfg = B.config_for(wl)
+    ocfg = oracle_cfg(wl)
+    say(f"[full] {name} chained={chained}: bulk pack of {T} tokens")
+    cache = gpu_pack(B, cfg, inp.kv, inp.rot, T)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    pairs = _pairs(wl, rng)
+    rot = inp.rot.double().cpu().numpy()
+    sc = synth.sm_scale(d)
+
+    # current token of every loop, and the outputs of the sampled loops at the benchmark's split count
+    loops = _loops(wl)
+    ws = torch.zeros(B.rq_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+    ctx_len = torch.full((wl.batch,), T, dtype=torch.int32, device="cuda")
+    outs = {}
+    for loop in loops:
+        grp, l = divmod(loop, L)
+        out = torch.full((wl.batch, wl.n_q_heads, d), float("nan"), device="cuda")
+        say(f"[full] {name} chained={chained}: decode loop {loop}")
+        B.rq_decode_attention(cfg, cache, loop, inp.q[loop].contiguous(),
+                              inp.kv[grp, l, 0, :, :, T].contiguous(), inp.kv[grp, l, 1, :, :, T].contiguous(),
+                              None, ctx_len, T, inp.rot, sc, out, ws, wl.batch, n_splits=0)
+        torch.cuda.synchronize()
+        outs[loop] = out.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(outs[loop]))
+
+    stats = new_stats()
+    worst = 0.0
+    for b, h in pairs:
+        say(f"[full] {name} chained={chained}: oracle checks of row {b}, KV head {h}")
+        kv = inp.kv[:, :, :, b, h].double().cpu().numpy()          # [G][L][2][T+1][d]
+        block = device_block(cache, ocfg, b, h)
+        _, sub = sub_cache(np.zeros(0, np.uint8), ocfg, b, h)
+        xs = [[kv[k, :, x, :T] for x in range(2)] for k in range(wl.n_groups)]
+        check_pack_block(block, sub, xs, rot[h], T, stats)
+        own = RQ.pack_context(kv[:, :, :, None, None], rot[h:h + 1], sub, T)
+        lay = RQ.Layout(sub)
+        for loop in loops:
+            grp, l = divmod(loop, L)
+            qh = inp.q[loop][b:b + 1, h * gqa:(h + 1) * gqa].double().cpu().numpy()
+            kc, vc = kv[grp, l, 0, T][None, None], kv[grp, l, 1, T][None, None]
+            ref_gpu = RQ.decode_attention(block, lay, loop, qh, kc, vc, [T], rot[h:h + 1], sc)
+            ref_own = RQ.decode_attention(own, lay, loop, qh, kc, vc, [T], rot[h:h + 1], sc)
+            o = outs[loop][b:b + 1, h * gqa:(h + 1) * gqa]
+            e1, e2 = close(o, ref_gpu), close(o, ref_own)
+            worst = max(worst, e1, e2)
+            assert e1 <= 1.0 and e2 <= 1.0, (loop, b, h, e1, e2)
+    say(f"[full] {name} chained={chained}: pack stats {stats}, worst err/bound {worst:.3f}")
+    assert_stats(stats)
