@@ -307,7 +307,7 @@ def main():
                  "speedup_rq_step_vs_bf16_step": round(bf16_ms * n_loops / ms_step, 3)},
         "roofline": {"bound": "hbm", "achieved": round(res_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(res_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "residual loop-step of rq_decode_attention: rq_decode_kernel + rq_combine_kernel",
+                     "kernel": "rq_decode_kernel, residual loop-step (split-K with the merge in its last workgroup)",
                      "algorithmic_bytes": res_bytes, "source_digest": decode_source_digest()},
     }
     if not args.no_cpu_baseline:

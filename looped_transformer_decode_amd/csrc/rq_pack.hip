@@ -8,221 +8,303 @@
 // "Worked example" of the same page and the arXiv digest's Figure 1 caption (g = 32).
 //
 // All arithmetic is float64 so that the integer decisions (codes, FP8 metadata, BF16
-// rounding of c) are taken exactly like a float64 reference would take them.
+// rounding of c) are taken exactly like a float64 reference would take them.  A token
+// is a chain of short dependent steps, so the kernel is written for latency: group
+// reductions use DPP inside a 16-lane row, E4M3 rounding uses exponent arithmetic
+// instead of division, and the residual loops are rotated and quantized side by side.
 #include "rq_args.hpp"
 
 namespace rq {
 
 
-// ---- FP8 E4M3FN on the float64 grid (exact: every step is a power-of-two scaling,
-// floor/ceil or a comparison)
+// ---- FP8 E4M3FN bytes and values (exact: power-of-two scalings, floor/ceil, compares)
 
-// largest grid value <= a, for 0 <= a (values above 448 give 448)
-__device__ inline double e4m3_down_mag(double a) {
-    if (a >= 448.0) return 448.0;
-    if (a < 0x1p-6) return floor(a * 512.0) * 0x1p-9;        // subnormal spacing 2^-9
-    const int e = ilogb(a);                                    // 2^e <= a < 2^(e+1)
-    const double q = ldexp(1.0, e - 3);                        // 3 mantissa bits
-    return floor(a / q) * q;
-}
-
-// smallest grid value >= a, for 0 <= a <= 448
-__device__ inline double e4m3_up_mag(double a) {
-    if (a <= 0x1p-6) return ceil(a * 512.0) * 0x1p-9;
-    const int e = ilogb(a);
-    const double q = ldexp(1.0, e - 3);
-    return ceil(a / q) * q;
-}
-
-__device__ inline double e4m3_floor(double v) {
-    return v >= 0.0 ? e4m3_down_mag(v) : -e4m3_up_mag(fmin(-v, 448.0));
-}
-
-__device__ inline uint32_t e4m3_bits(double v) {          // v on the grid
-    const uint32_t sign = v < 0.0 ? 0x80u : 0u;
-    const double a = fabs(v);
-    if (a == 0.0) return 0u;
-    if (a < 0x1p-6) return sign | (uint32_t)(a * 512.0);
-    const int e = ilogb(a);
-    const uint32_t man = (uint32_t)(a * ldexp(1.0, 3 - e)) - 8u;
-    return sign | ((uint32_t)(e + 7) << 3) | man;
-}
-
-__device__ inline double e4m3_pos_value(uint32_t b) {     // 0 < b <= 0x7E
+// value of an E4M3 byte (finite patterns; bit 7 is the sign)
+__device__ __forceinline__ double e4m3_value(uint32_t b) {
     const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-    return e == 0 ? m * 0x1p-9 : ldexp(1.0 + m * 0.125, (int)e - 7);
+    const double mag = e == 0 ? (double)m * 0x1p-9 : ldexp((double)(8u + m), (int)e - 10);
+    return (b & 0x80u) ? -mag : mag;
+}
+
+// byte of the largest grid value <= a, for 0 <= a (values above 448 give 448)
+__device__ __forceinline__ uint32_t e4m3_down_byte(double a) {
+    if (a >= 448.0) return 0x7Eu;
+    if (a < 0x1p-6) return (uint32_t)floor(a * 512.0);          // subnormals: m * 2^-9
+    const int e = ilogb(a);                                      // 2^e <= a < 2^(e+1)
+    return ((uint32_t)(e + 7) << 3) | ((uint32_t)floor(ldexp(a, 3 - e)) - 8u);
+}
+
+// byte of the smallest grid value >= a, for 0 <= a <= 448
+__device__ __forceinline__ uint32_t e4m3_up_byte(double a) {
+    if (a <= 0x1p-6) return (uint32_t)ceil(a * 512.0);           // 8 is the byte of 2^-6
+    const int e = ilogb(a);
+    return ((uint32_t)(e + 7) << 3) + ((uint32_t)ceil(ldexp(a, 3 - e)) - 8u);   // 8 carries
+}
+
+// byte of the largest grid value <= v, for -448 <= v
+__device__ __forceinline__ uint32_t e4m3_floor_byte(double v) {
+    return v >= 0.0 ? e4m3_down_byte(v) : (0x80u | e4m3_up_byte(-v));
 }
 
 // BF16 round-to-nearest-even of a float64 value, in one rounding step.
-__device__ inline double bf16_round(double v) {
+__device__ __forceinline__ double bf16_round(double v) {
     if (v == 0.0) return 0.0;
     int e = ilogb(v);
     if (e < -126) e = -126;
-    const double q = ldexp(1.0, e - 7);
-    return rint(v / q) * q;
+    return ldexp(rint(ldexp(v, 7 - e)), e - 7);
 }
 
+// ---- cross-lane steps on float64 values
+
+constexpr int kDppRowMirror = 0x140, kDppRowHalfMirror = 0x141;
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp((int)(uint32_t)u, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp((int)(uint32_t)(u >> 32), (int)(uint32_t)(u >> 32), CTRL, 0xF,
+                                               0xF, false);
+    return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+// min / max over aligned groups of NL = 16, 32 or 64 lanes, result in every lane
+template <int NL>
+__device__ __forceinline__ double group_min(double v) {
+    v = fmin(v, dpp_d<kDppQuadXor1>(v));
+    v = fmin(v, dpp_d<kDppQuadXor2>(v));
+    v = fmin(v, dpp_d<kDppRowHalfMirror>(v));
+    v = fmin(v, dpp_d<kDppRowMirror>(v));
+    if constexpr (NL >= 32) v = fmin(v, shfl_xor_d(v, 16));
+    if constexpr (NL >= 64) v = fmin(v, shfl_xor_d(v, 32));
+    return v;
+}
+template <int NL>
+__device__ __forceinline__ double group_max(double v) {
+    v = fmax(v, dpp_d<kDppQuadXor1>(v));
+    v = fmax(v, dpp_d<kDppQuadXor2>(v));
+    v = fmax(v, dpp_d<kDppRowHalfMirror>(v));
+    v = fmax(v, dpp_d<kDppRowMirror>(v));
+    if constexpr (NL >= 32) v = fmax(v, shfl_xor_d(v, 16));
+    if constexpr (NL >= 64) v = fmax(v, shfl_xor_d(v, 32));
+    return v;
+}
+__device__ __forceinline__ double row_sum(double v) {
+    v += dpp_d<kDppQuadXor1>(v);
+    v += dpp_d<kDppQuadXor2>(v);
+    v += dpp_d<kDppRowHalfMirror>(v);
+    v += dpp_d<kDppRowMirror>(v);
+    return v;
+}
+
+// the two threads of a channel hold halves of a sum: both get the whole (a + b == b + a)
+__device__ __forceinline__ double pair_sum(double v) { return v + dpp_d<kDppQuadXor1>(v); }
+
+// ---- the group quantizer (two lanes per channel, groups of G consecutive channels)
+//
+// offset z = largest E4M3 value <= group min; scale s = smallest E4M3 value >= 2^-9 with
+// z + n s >= group max (n = 2^bits - 1); code = round-half-even((x - z) / s) in [0, n].
+// n s has at most 8 significant bits and z + n s is a multiple of 2^-9 below 2^13, so the
+// covering test is exact; the candidate scale from an approximate quotient is off by at
+// most one grid step and is corrected by that test.  The code divides exactly as a
+// float64 reference does.
 struct QOut {
-    uint32_t code;
+    uint32_t code, zb, sb;
     double z, s;
-    uint32_t zb, sb;
 };
 
-// Group quantizer: every lane holds one channel; groups are `g` consecutive lanes.
-__device__ inline QOut quantize_lane(double x, int bits, int g) {
-    double lo = x, hi = x;
-    for (int off = g >> 1; off >= 1; off >>= 1) {
-        lo = fmin(lo, shfl_xor_d(lo, off));
-        hi = fmax(hi, shfl_xor_d(hi, off));
-    }
-    QOut o;
+template <int G>
+__device__ __forceinline__ QOut quantize_lane(double x, int bits) {
+    const double lo = group_min<2 * G>(x), hi = group_max<2 * G>(x);
     const double n = (double)((1 << bits) - 1);
-    o.z = e4m3_floor(lo);
-    // smallest scale s >= 2^-9 on the grid with z + n*s >= hi (the sum is exact)
-    double need = (hi - o.z) / n;
-    if (need < 0x1p-9) need = 0x1p-9;
-    uint32_t sb = e4m3_bits(e4m3_up_mag(fmin(need, 448.0)));
-    while (sb > 1u && o.z + n * e4m3_pos_value(sb - 1u) >= hi) --sb;
-    while (sb < 0x7Eu && o.z + n * e4m3_pos_value(sb) < hi) ++sb;
-    o.s = e4m3_pos_value(sb);
+    QOut o;
+    o.zb = e4m3_floor_byte(lo);
+    o.z = e4m3_value(o.zb);
+    const double need = fmin(fmax((hi - o.z) * (bits == 4 ? 1.0 / 15.0 : 1.0 / 3.0), 0x1p-9), 448.0);
+    uint32_t sb = e4m3_up_byte(need);
+    if (sb > 1u && o.z + n * e4m3_value(sb - 1u) >= hi) --sb;
+    if (sb < 0x7Eu && o.z + n * e4m3_value(sb) < hi) ++sb;
     o.sb = sb;
-    o.zb = e4m3_bits(o.z);
-    double t = rint((x - o.z) / o.s);
-    t = fmin(fmax(t, 0.0), n);
-    o.code = (uint32_t)t;
+    o.s = e4m3_value(sb);
+    const double t = rint((x - o.z) / o.s);
+    o.code = (uint32_t)fmin(fmax(t, 0.0), n);
     return o;
 }
 
-// Sums over the D threads of the workgroup of N values per thread (float64).
-template <int D, int N>
-__device__ inline void block_sum_vec(double (&v)[N], double (*red)[N]) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-#pragma unroll
-        for (int k = 0; k < N; ++k) v[k] += shfl_xor_d(v[k], off);
-    constexpr int W = D / 64;
-    if constexpr (W > 1) {
-        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-        __syncthreads();
-        if (lane == 0)
-#pragma unroll
-            for (int k = 0; k < N; ++k) red[w][k] = v[k];
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < N; ++k) {
-            double s = 0.0;
-#pragma unroll
-            for (int i = 0; i < W; ++i) s += red[i][k];
-            v[k] = s;
-        }
-    }
+// ---- stores (two lanes per channel: thread t holds channel t / 2)
+
+// Pack `bits`-wide codes of consecutive channels into 32-bit words and store them.
+__device__ __forceinline__ void store_codes(uint8_t* row, uint32_t code, int bits) {
+    const int per = 32 / bits;                          // channels per word
+    const int t = threadIdx.x, ch = t >> 1;
+    uint32_t v = (t & 1) ? 0u : code << ((ch % per) * bits);
+    for (int off = 2; off < 2 * per; off <<= 1) v |= (uint32_t)__shfl_xor((int)v, off, kWave);
+    if ((t & (2 * per - 1)) == 0) reinterpret_cast<uint32_t*>(row)[ch / per] = v;
 }
 
-// Pack `bits`-wide codes of consecutive lanes into 32-bit words and store them.
-__device__ inline void store_codes(uint8_t* row, uint32_t code, int bits) {
-    const int per = 32 / bits;
-    const int i = threadIdx.x;
-    uint32_t v = code << ((i % per) * bits);
-    for (int off = 1; off < per; off <<= 1) v |= (uint32_t)__shfl_xor((int)v, off, kWave);
-    if (i % per == 0) reinterpret_cast<uint32_t*>(row)[i / per] = v;
+__device__ __forceinline__ void store_meta(uint8_t* row, const QOut& q, int g) {
+    const int t = threadIdx.x;
+    if ((t & 1) == 0 && (t >> 1) % g == 0) reinterpret_cast<uint16_t*>(row)[(t >> 1) / g] = (uint16_t)(q.zb | (q.sb << 8));
 }
 
-__device__ inline void store_meta(uint8_t* row, const QOut& q, int g) {
-    const int i = threadIdx.x;
-    if (i % g == 0) reinterpret_cast<uint16_t*>(row)[i / g] = (uint16_t)(q.zb | (q.sb << 8));
-}
-
-__device__ inline void store_c(uint8_t* cblk, int jj, double c) {
+__device__ __forceinline__ void store_c(uint8_t* cblk, int jj, double c) {
     if (threadIdx.x == 0) {
         const uint32_t cb = __float_as_uint((float)c) >> 16;    // c is a BF16 value
         reinterpret_cast<uint16_t*>(cblk)[jj] = (uint16_t)cb;
     }
 }
 
-// One workgroup per (token range, batch row, KV head, K|V); thread i owns channel i and
-// keeps row i of R in registers for all tokens of the range.
-template <int D>
-__global__ __launch_bounds__(D) void rq_pack_kernel(PackArgs a) {
-    const Geom& G = a.geo;
-    const int i = threadIdx.x;
+// Sum over the channels of N float64 values per channel (each given by both threads of
+// the channel): DPP inside each 16-lane row, then the row sums through LDS, added in a
+// fixed order.  Every thread gets the sums.
+template <int NT, int N>
+__device__ __forceinline__ void block_sum(double (&v)[N], double (*red)[NT / 16]) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) v[k] = row_sum((threadIdx.x & 1) ? 0.0 : v[k]);
+    __syncthreads();                                    // red is reused
+    if ((threadIdx.x & 15) == 0) {
+#pragma unroll
+        for (int k = 0; k < N; ++k) red[k][threadIdx.x >> 4] = v[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        double s = 0.0;
+#pragma unroll
+        for (int r = 0; r < NT / 16; ++r) s += red[k][r];
+        v[k] = s;
+    }
+}
+
+// The float64 copy of an R element is made where it is used: the empty asm keeps the
+// compiler from hoisting 2 * D registers of converted R out of the token loop.
+__device__ __forceinline__ double r_elem(float r) {
+    asm volatile("" : "+v"(r));
+    return (double)r;
+}
+
+// r_l = sum_k R[i][k] y_l[k] for LR vectors y_l in LDS: this thread holds half of row i
+// of R (columns [H p, H p + H), H = D / 2) and the pair of threads adds its halves.  Each
+// R element is converted once and used by every vector.
+template <int D, int LR>
+__device__ __forceinline__ void rotate_rows(const float (&rhalf)[D / 2], const double (*y)[D], int p,
+                                            double (&r)[LR]) {
+    constexpr int H = D / 2;
+    double r0[LR], r1[LR];
+#pragma unroll
+    for (int l = 0; l < LR; ++l) r0[l] = r1[l] = 0.0;
+#pragma unroll
+    for (int k = 0; k < H; k += 2) {
+        // the empty asm with a memory clobber bounds how far ahead the LDS reads of y are
+        // scheduled, which would otherwise keep most of y in registers
+        if (k % 8 == 0) asm volatile("" ::: "memory");
+        const double ra = r_elem(rhalf[k]), rb = r_elem(rhalf[k + 1]);
+#pragma unroll
+        for (int l = 0; l < LR; ++l) {
+            r0[l] = fma(ra, y[l][H * p + k], r0[l]);
+            r1[l] = fma(rb, y[l][H * p + k + 1], r1[l]);
+        }
+    }
+#pragma unroll
+    for (int l = 0; l < LR; ++l) r[l] = pair_sum(r0[l] + r1[l]);
+}
+
+// All LR residual loops, rotated three at a time (register pressure).
+template <int D, int LR, int L0 = 0>
+__device__ __forceinline__ void rotate_all(const float (&rhalf)[D / 2], const double (*y)[D], int p,
+                                           double (&r)[LR]) {
+    if constexpr (L0 < LR) {
+        constexpr int NB = (LR - L0) < 3 ? (LR - L0) : 3;
+        double rb[NB];
+        rotate_rows<D, NB>(rhalf, y + L0, p, rb);
+#pragma unroll
+        for (int l = 0; l < NB; ++l) r[L0 + l] = rb[l];
+        rotate_all<D, LR, L0 + NB>(rhalf, y, p, r);
+    }
+}
+
+// One workgroup of 2 D threads per (token range, batch row, KV head, K|V): threads 2i
+// and 2i+1 own channel i and keep the two halves of row i of R in registers for all
+// tokens of the range.  LR = L - 1 residual loops.
+template <int D, int G, int LR>
+__global__ __launch_bounds__(2 * D) void rq_pack_kernel(PackArgs a) {
+    constexpr int L = LR + 1;
+    constexpr int NT = 2 * D;
+    constexpr int H = D / 2;
+    const Geom& Gm = a.geo;
+    const int i = threadIdx.x >> 1, p = threadIdx.x & 1;
     int wg = blockIdx.x;
     const int x = wg & 1;
     wg >>= 1;
-    const int h = wg % G.hkv;
-    wg /= G.hkv;
+    const int h = wg % Gm.hkv;
+    wg /= Gm.hkv;
     const int b = wg % a.batch;
     const int t0 = (wg / a.batch) * a.tokens_per_wg;
     const int t1 = min(t0 + a.tokens_per_wg, a.n_tokens);
-    const int L = G.L;
     const int loop0 = a.group_idx * L;
     const float* R = a.rot + (int64_t)(h * 2 + x) * D * D;
 
-    __shared__ double sh_y[kMaxLoops][D];
-    __shared__ double red[D / 64][kMaxLoops];
+    __shared__ double sh_y[LR > 1 ? LR : 2][D];
+    __shared__ double red[L > 2 ? L : 2][NT / 16];
 
-    float rrow[D];                                     // row i of R: r_i = sum_k R[i][k] y_k
+    float rhalf[H];                                    // R[i][H p + k]
     {
-        const float4* rp = reinterpret_cast<const float4*>(R + (int64_t)i * D);
+        const float4* rp = reinterpret_cast<const float4*>(R + (int64_t)i * D + H * p);
 #pragma unroll
-        for (int k4 = 0; k4 < D / 4; ++k4) {
+        for (int k4 = 0; k4 < H / 4; ++k4) {
             const float4 v = rp[k4];
-            rrow[4 * k4] = v.x;
-            rrow[4 * k4 + 1] = v.y;
-            rrow[4 * k4 + 2] = v.z;
-            rrow[4 * k4 + 3] = v.w;
+            rhalf[4 * k4] = v.x;
+            rhalf[4 * k4 + 1] = v.y;
+            rhalf[4 * k4 + 2] = v.z;
+            rhalf[4 * k4 + 3] = v.w;
         }
     }
-    uint8_t* a_plane = a.cache + G.plane_offset(b, h, x, loop0 + L - 1);
+    uint8_t* a_plane = a.cache + Gm.plane_offset(b, h, x, loop0 + L - 1);
 
     for (int t = t0; t < t1; ++t) {
         const int slot = a.pos[b] + t;
-        if (slot < 0 || slot >= G.max_ctx) continue;   // same for the whole workgroup
+        if (slot < 0 || slot >= Gm.max_ctx) continue;  // same for the whole workgroup
         const int tile = slot / kTile, jj = slot % kTile;
 
-        double xv[kMaxLoops];
+        double xv[L];
         const uint16_t* src = a.pending + t * a.st[0] + b * a.st[1] + x * a.st[3] + h * a.st[4] + i;
 #pragma unroll
-        for (int l = 0; l < kMaxLoops; ++l)
-            if (l < L) xv[l] = (double)bf16_to_f32(src[l * a.st[2]]);
+        for (int l = 0; l < L; ++l) xv[l] = (double)bf16_to_f32(src[l * a.st[2]]);
 
         // anchor: the group's last loop
-        const QOut qa = quantize_lane(xv[L - 1], G.ba, G.g);
+        const QOut qa = quantize_lane<G>(xv[L - 1], Gm.ba);
         {
-            uint8_t* p = a_plane + tile * G.a_tile;
-            store_codes(p + jj * G.a_row, qa.code, G.ba);
-            store_meta(p + kTile * G.a_row + jj * G.m_row, qa, G.g);
+            uint8_t* pl = a_plane + tile * Gm.a_tile;
+            store_codes(pl + jj * Gm.a_row, qa.code, Gm.ba);
+            store_meta(pl + kTile * Gm.a_row + jj * Gm.m_row, qa, Gm.g);
         }
         const double a_hat = qa.z + qa.code * qa.s;      // dequantized anchor (exact)
 
-        if (!G.chained) {
-            // all loops reference a_hat: one reduction for every <x_l, a> and <a, a>
-            double sums[kMaxLoops];
+        if (!Gm.chained) {
+            // every loop l < L-1 references a_hat: one reduction gives all <x_l, a> and
+            // <a, a>; the loops are rotated together and then quantized side by side
+            double sums[L];
 #pragma unroll
-            for (int l = 0; l < kMaxLoops; ++l) sums[l] = (l < L - 1) ? xv[l] * a_hat : 0.0;
-            sums[kMaxLoops - 1] = a_hat * a_hat;
-            block_sum_vec<D, kMaxLoops>(sums, red);
-            const double den = sums[kMaxLoops - 1];
-            double cs[kMaxLoops];
+            for (int l = 0; l < LR; ++l) sums[l] = xv[l] * a_hat;
+            sums[LR] = a_hat * a_hat;
+            block_sum<NT, L>(sums, red);
+            double cs[LR];
 #pragma unroll
-            for (int l = 0; l < kMaxLoops - 1; ++l) {
-                if (l < L - 1) {
-                    cs[l] = bf16_round(den > 0.0 ? sums[l] / den : 0.0);
-                    sh_y[l][i] = xv[l] - cs[l] * a_hat;
-                }
+            for (int l = 0; l < LR; ++l) {
+                cs[l] = bf16_round(sums[LR] > 0.0 ? sums[l] / sums[LR] : 0.0);
+                if (p == 0) sh_y[l][i] = xv[l] - cs[l] * a_hat;
             }
             __syncthreads();
+            double rl[LR];
+            rotate_all<D, LR>(rhalf, sh_y, p, rl);
+            QOut qr[LR];
 #pragma unroll
-            for (int l = 0; l < kMaxLoops - 1; ++l) {
-                if (l < L - 1) {
-                    double r = 0.0;
+            for (int l = 0; l < LR; ++l) qr[l] = quantize_lane<G>(rl[l], Gm.br);
 #pragma unroll
-                    for (int k = 0; k < D; ++k) r += (double)rrow[k] * sh_y[l][k];
-                    const QOut qr = quantize_lane(r, G.br, G.g);
-                    uint8_t* p = a.cache + G.plane_offset(b, h, x, loop0 + l) + tile * G.r_tile;
-                    store_codes(p + jj * G.r_row, qr.code, G.br);
-                    store_meta(p + kTile * G.r_row + jj * G.m_row, qr, G.g);
-                    store_c(p + kTile * (G.r_row + G.m_row), jj, cs[l]);
-                }
+            for (int l = 0; l < LR; ++l) {
+                uint8_t* pl = a.cache + Gm.plane_offset(b, h, x, loop0 + l) + tile * Gm.r_tile;
+                store_codes(pl + jj * Gm.r_row, qr[l].code, Gm.br);
+                store_meta(pl + kTile * Gm.r_row + jj * Gm.m_row, qr[l], Gm.g);
+                store_c(pl + kTile * (Gm.r_row + Gm.m_row), jj, cs[l]);
             }
             __syncthreads();                              // sh_y is reused by the next token
         } else {
@@ -230,40 +312,61 @@ __global__ __launch_bounds__(D) void rq_pack_kernel(PackArgs a) {
             double ref = a_hat;
             for (int l = L - 2; l >= 0; --l) {
                 double s2[2] = {xv[l] * ref, ref * ref};
-                block_sum_vec<D, 2>(s2, reinterpret_cast<double(*)[2]>(&red[0][0]));
+                block_sum<NT, 2>(s2, red);
                 const double c = bf16_round(s2[1] > 0.0 ? s2[0] / s2[1] : 0.0);
-                sh_y[0][i] = xv[l] - c * ref;
+                if (p == 0) sh_y[0][i] = xv[l] - c * ref;
                 __syncthreads();
-                double r = 0.0;
-#pragma unroll
-                for (int k = 0; k < D; ++k) r += (double)rrow[k] * sh_y[0][k];
-                const QOut qr = quantize_lane(r, G.br, G.g);
-                uint8_t* p = a.cache + G.plane_offset(b, h, x, loop0 + l) + tile * G.r_tile;
-                store_codes(p + jj * G.r_row, qr.code, G.br);
-                store_meta(p + kTile * G.r_row + jj * G.m_row, qr, G.g);
-                store_c(p + kTile * (G.r_row + G.m_row), jj, c);
-                // R^T r_hat: thread i takes column i of R (coalesced across threads)
-                sh_y[1][i] = qr.z + qr.code * qr.s;
+                double rl[1];
+                rotate_rows<D, 1>(rhalf, sh_y, p, rl);
+                const QOut qr = quantize_lane<G>(rl[0], Gm.br);
+                uint8_t* pl = a.cache + Gm.plane_offset(b, h, x, loop0 + l) + tile * Gm.r_tile;
+                store_codes(pl + jj * Gm.r_row, qr.code, Gm.br);
+                store_meta(pl + kTile * Gm.r_row + jj * Gm.m_row, qr, Gm.g);
+                store_c(pl + kTile * (Gm.r_row + Gm.m_row), jj, c);
+                // R^T r_hat: the thread pair of channel i takes column i of R, rows
+                // [H p, H p + H) each (coalesced across the pairs)
+                if (p == 0) sh_y[1][i] = qr.z + qr.code * qr.s;
                 __syncthreads();
-                double tcol = 0.0;
+                double c0 = 0.0, c1 = 0.0;
 #pragma unroll 16
-                for (int k = 0; k < D; ++k) tcol += (double)R[(int64_t)k * D + i] * sh_y[1][k];
-                ref = c * ref + tcol;
+                for (int k = 0; k < H; k += 2) {
+                    const int row = H * p + k;
+                    c0 = fma(r_elem(R[(int64_t)row * D + i]), sh_y[1][row], c0);
+                    c1 = fma(r_elem(R[(int64_t)(row + 1) * D + i]), sh_y[1][row + 1], c1);
+                }
+                ref = c * ref + pair_sum(c0 + c1);
                 __syncthreads();
             }
         }
     }
 }
 
+template <int D, int G>
+static hipError_t launch_dg(const PackArgs& a, int nwg, hipStream_t stream) {
+    switch (a.geo.L - 1) {
+        case 1: hipLaunchKernelGGL((rq_pack_kernel<D, G, 1>), dim3(nwg), dim3(2 * D), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((rq_pack_kernel<D, G, 2>), dim3(nwg), dim3(2 * D), 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((rq_pack_kernel<D, G, 3>), dim3(nwg), dim3(2 * D), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((rq_pack_kernel<D, G, 4>), dim3(nwg), dim3(2 * D), 0, stream, a); break;
+        case 5: hipLaunchKernelGGL((rq_pack_kernel<D, G, 5>), dim3(nwg), dim3(2 * D), 0, stream, a); break;
+        case 6: hipLaunchKernelGGL((rq_pack_kernel<D, G, 6>), dim3(nwg), dim3(2 * D), 0, stream, a); break;
+        case 7: hipLaunchKernelGGL((rq_pack_kernel<D, G, 7>), dim3(nwg), dim3(2 * D), 0, stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_d(const PackArgs& a, int nwg, hipStream_t stream) {
+    return a.geo.g == 32 ? launch_dg<D, 32>(a, nwg, stream) : launch_dg<D, 16>(a, nwg, stream);
+}
+
 hipError_t launch_pack(const PackArgs& a, hipStream_t stream) {
-    if (!a.cache || !a.pending || !a.pos || !a.rot || a.batch < 1 || a.n_tokens < 1 || a.tokens_per_wg < 1)
+    if (!a.cache || !a.pending || !a.pos || !a.rot || a.batch < 1 || a.n_tokens < 1 || a.tokens_per_wg < 1 ||
+        (a.geo.g != 16 && a.geo.g != 32) || (a.geo.d != 64 && a.geo.d != 128))
         return hipErrorInvalidValue;
     const int nwg = (a.n_tokens + a.tokens_per_wg - 1) / a.tokens_per_wg * a.batch * a.geo.hkv * 2;
-    if (a.geo.d == 128)
-        hipLaunchKernelGGL(rq_pack_kernel<128>, dim3(nwg), dim3(128), 0, stream, a);
-    else
-        hipLaunchKernelGGL(rq_pack_kernel<64>, dim3(nwg), dim3(64), 0, stream, a);
-    return hipGetLastError();
+    return a.geo.d == 128 ? launch_d<128>(a, nwg, stream) : launch_d<64>(a, nwg, stream);
 }
 
 }  // namespace rq
