@@ -48,10 +48,10 @@ static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 // Split-K factor: about two workgroups per CU (4 waves each) in flight, and at least four
 // 64-token tiles per workgroup so that its prologue (queries, R_K q) and epilogue (wave
 // merge, R_V^T) stay small next to its stream.
-static int auto_splits(int batch, int hq, int n_tiles) {
+// rows = independent (batch row, head) units of the grid; target = workgroups wanted
+static int auto_splits(int rows, int n_tiles, int target = 512) {
     if (n_tiles <= 0) return 1;
-    constexpr int kTargetWorkgroups = 512;
-    int s = (kTargetWorkgroups + batch * hq - 1) / (batch * hq);
+    int s = (target + rows - 1) / rows;
     const int by_tiles = n_tiles / 4 > 0 ? n_tiles / 4 : 1;
     if (s > by_tiles) s = by_tiles;
     if (s > kMaxSplits) s = kMaxSplits;
@@ -162,7 +162,10 @@ rq_status rq_decode_attention(const rq_config* cfg, const void* cache, int32_t l
     const int lloc = loop % g.L;
     const int nres = (lloc == g.L - 1) ? 0 : (g.chained ? g.L - 1 - lloc : 1);
     const int n_tiles = (ctx_bound + kTile - 1) / kTile;
-    int S = n_splits ? n_splits : auto_splits(batch, g.hq, n_tiles);
+    // the grouped-query kernel runs one workgroup per KV head and split (one per CU)
+    const bool grouped = gqa_supported(g, nres);
+    int S = n_splits ? n_splits
+                     : (grouped ? auto_splits(batch * g.hkv, n_tiles, 256) : auto_splits(batch * g.hq, n_tiles));
     if (n_tiles > 0 && S > n_tiles) S = n_tiles;
     if (S < 1) S = 1;
     DecodeArgs a;
@@ -215,7 +218,7 @@ rq_status rq_bf16_decode_attention(const rq_bf16_config* cfg, uint16_t* k_cache,
     const size_t need = workspace_bytes(cfg->max_batch, n_q_heads, head_dim);
     if (!workspace || workspace_bytes_ < need) return RQ_ERR_WORKSPACE;
     const int n_tiles = (ctx_bound + kTile - 1) / kTile;
-    int S = n_splits ? n_splits : auto_splits(batch, n_q_heads, n_tiles);
+    int S = n_splits ? n_splits : auto_splits(batch * n_q_heads, n_tiles);
     if (n_tiles > 0 && S > n_tiles) S = n_tiles;
     if (S < 1) S = 1;
     Bf16Args a;

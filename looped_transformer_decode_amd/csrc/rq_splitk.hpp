@@ -136,50 +136,58 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// sum: LDS values of this split (acc_a[D], then acc_r[D] when RES); ml = (m, l) of the
-// split; qf: LDS float32 query.  The last workgroup of (batch row, query head) bh writes
+// Store this split's record (sum: LDS values acc_a[D], then acc_r[D] when RES; ml = (m, l)).
+template <int D, bool RES, int NT = kThreads>
+__device__ __forceinline__ void splitk_publish(const MergeArgs& g, int bh, int split, const float* sum, float2 ml) {
+    constexpr int NVAL = RES ? 2 * D : D;
+    constexpr int PS = 2 * D + 4;
+    float* rec = g.partials + ((int64_t)bh * kMaxSplits + split) * PS;
+    for (int t = threadIdx.x; t < NVAL; t += NT) st_agent(rec + t, sum[t]);
+    if (threadIdx.x == 0) {
+        st_agent(rec + 2 * D, ml.x);
+        st_agent(rec + 2 * D + 1, ml.y);
+    }
+}
+
+// After every thread's records are stored, count this workgroup's arrival on counter
+// `slot`.  Returns true (in every thread) for the workgroup that arrives last; it also puts
+// the counter back to zero.
+__device__ __forceinline__ bool splitk_arrive(const MergeArgs& g, int slot) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __shared__ int s_last;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(g.arrivals + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = old == (uint32_t)(g.n_splits - 1);
+        if (last) __hip_atomic_store(g.arrivals + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = last;
+    }
+    __syncthreads();
+    return s_last != 0;
+}
+
+// Merge of the records of (batch row, query head) bh by the last workgroup:
 //   out = (sum_s w_s acc_a_s + R_V^T sum_s w_s acc_r_s + p_cur v_cur) / (sum_s w_s l_s + p_cur)
-// with w_s = exp(m_s - m), p_cur = exp(s_cur - m), m = max(max_s m_s, s_cur), and stores the
-// current token into the pending buffer (or the BF16 cache) for the first query head of
-// its KV head.
-template <int D, bool RES>
-__device__ __forceinline__ void splitk_finish(const MergeArgs& g, int bh, int split, const float* sum, float2 ml,
-                                              const float* qf, SplitSmem<D>& sm) {
+// with w_s = exp(m_s - m), p_cur = exp(s_cur - m), m = max(max_s m_s, s_cur); the current
+// token goes into the pending buffer (or the BF16 cache) for the first query head of its
+// KV head.  qf: LDS float32 query; scr: LDS scratch of at least NT/64 + kMaxSplits + 4 + D +
+// NT floats (NT: threads of the workgroup).
+template <int D, bool RES, int NT = kThreads>
+__device__ __forceinline__ void splitk_merge_last(const MergeArgs& g, int bh, const float* qf, float* scr) {
+    constexpr int NW = NT / kWave;
     constexpr int NVAL = RES ? 2 * D : D;
     constexpr int PS = 2 * D + 4;
     static_assert(kMaxSplits <= kWave, "one lane per split record");
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    float* recs = g.partials + (int64_t)bh * kMaxSplits * PS;
-    {
-        float* rec = recs + (int64_t)split * PS;
-        for (int t = tid; t < NVAL; t += kThreads) st_agent(rec + t, sum[t]);
-        if (tid == 0) {
-            st_agent(rec + 2 * D, ml.x);
-            st_agent(rec + 2 * D + 1, ml.y);
-        }
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __shared__ int s_last;
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(g.arrivals + bh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int last = old == (uint32_t)(g.n_splits - 1);
-        if (last) __hip_atomic_store(g.arrivals + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = last;
-    }
-    __syncthreads();
-    if (!s_last) return;
-
+    const float* recs = g.partials + (int64_t)bh * kMaxSplits * PS;
     const int S = g.n_splits;
     const int hq = bh % g.hq, b = bh / g.hq;
     const int gqa = g.hq / g.hkv, h = hq / gqa;
-    float* scr = &sm.acc[0][0];
-    float* s_red = scr;                 // [kWaves]
-    float* s_w = scr + kWaves;          // [kMaxSplits]
+    float* s_red = scr;                 // [NW]
+    float* s_w = scr + NW;              // [kMaxSplits]
     float* s_sc = s_w + kMaxSplits;     // m, l_tot, p_cur
     float* s_r = s_sc + 4;              // [D] merged residual part
-    float* s_p = s_r + D;               // [kThreads / D][D] partial R_V^T products
-    static_assert(kWaves + kMaxSplits + 4 + D + kThreads <= kWaves * 2 * D, "merge scratch fits SplitSmem::acc");
+    float* s_p = s_r + D;               // [NT / D][D] partial R_V^T products
     // every load that does not depend on the merge weights goes out first
     const int64_t kvo = ((int64_t)b * g.hkv + h) * D;
     uint32_t kc = 0, vc = 0;
@@ -200,7 +208,7 @@ __device__ __forceinline__ void splitk_finish(const MergeArgs& g, int bh, int sp
             pv[k] = (tid < NVAL && s0 + k < S) ? ld_agent(recs + (int64_t)(s0 + k) * PS + tid) : 0.f;
     };
     load_chunk(0);
-    constexpr int RP = kThreads / D;           // parts of the R_V^T product
+    constexpr int RP = NT / D;                 // parts of the R_V^T product
     constexpr int RROWS = D / RP;
     float rv[RES ? RROWS : 1];
     if constexpr (RES) {
@@ -217,7 +225,7 @@ __device__ __forceinline__ void splitk_finish(const MergeArgs& g, int bh, int sp
     if (w == 0) {
         float s_cur = 0.f;
 #pragma unroll
-        for (int i = 0; i < kWaves; ++i) s_cur += s_red[i];
+        for (int i = 0; i < NW; ++i) s_cur += s_red[i];
         s_cur *= g.sm_scale;
         float mx = (ls > 0.f) ? ms : -INFINITY;
 #pragma unroll
@@ -276,6 +284,16 @@ __device__ __forceinline__ void splitk_finish(const MergeArgs& g, int bh, int sp
             }
         }
     }
+}
+
+// One query head per workgroup: publish, count, and merge if last.
+template <int D, bool RES>
+__device__ __forceinline__ void splitk_finish(const MergeArgs& g, int bh, int split, const float* sum, float2 ml,
+                                              const float* qf, SplitSmem<D>& sm) {
+    static_assert(kWaves + kMaxSplits + 4 + D + kThreads <= kWaves * 2 * D, "merge scratch fits SplitSmem::acc");
+    splitk_publish<D, RES>(g, bh, split, sum, ml);
+    if (!splitk_arrive(g, bh)) return;
+    splitk_merge_last<D, RES>(g, bh, qf, &sm.acc[0][0]);
 }
 
 }  // namespace rq

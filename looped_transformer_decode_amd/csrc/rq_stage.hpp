@@ -1,0 +1,75 @@
+// Global -> LDS staging and prologue-load helpers shared by the decode kernels.
+#pragma once
+
+#include "rq_common.hpp"
+
+namespace rq {
+
+// ---- staging: the cache stream goes global -> LDS by DMA (global_load_lds_dwordx4), one
+// 16-byte chunk per lane, without passing through registers.  The compiler does not
+// track these LDS writes, so each wave waits for its own DMAs explicitly (vmcnt) before
+// reading a staged pass; no other vector-memory instruction is issued inside the loop.
+__device__ __forceinline__ void dma16(uint32_t voff, const uint8_t* sbase, uint32_t lds_addr) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+}
+
+// copy BYTES (multiple of 16, at most 1024) from sbase + goff to LDS lds_addr
+template <int BYTES>
+__device__ __forceinline__ void stage(const uint8_t* sbase, uint32_t goff, uint32_t lds_addr, int lane) {
+    static_assert(BYTES % 16 == 0 && BYTES <= 1024, "one DMA instruction per block");
+    if (BYTES == 1024 || lane < BYTES / 16) dma16(goff + 16u * lane, sbase, lds_addr);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Prologue loads go through inline asm as well: the compiler counts outstanding loads
+// for its own waits and cannot see the stream DMAs issued after these, so its waits
+// would also stall on the DMAs.  pin() orders every use of a loaded register after the
+// explicit wait that follows the DMA issue.
+__device__ __forceinline__ f32x4 gload16(const uint8_t* sbase, uint32_t voff) {
+    f32x4 r;
+    asm volatile("global_load_dwordx4 %0, %1, %2" : "=v"(r) : "v"(voff), "s"(sbase));
+    return r;
+}
+__device__ __forceinline__ u32x2 gload8(const uint8_t* sbase, uint32_t voff) {
+    u32x2 r;
+    asm volatile("global_load_dwordx2 %0, %1, %2" : "=v"(r) : "v"(voff), "s"(sbase));
+    return r;
+}
+template <class T>
+__device__ __forceinline__ void pin(T& x) {
+    asm volatile("" : "+v"(x));
+}
+
+// Sum each of N values over aligned groups of 2M consecutive lanes.  Reduce-scatter
+// while values remain (lanes with bit M set keep the upper half), then plain
+// butterflies; on return v[0] is the group sum of value `off`.
+template <int CUR, int M, int N>
+__device__ __forceinline__ void group_reduce_scatter(float (&v)[N], int lane, int& off) {
+    if constexpr (M >= 1) {
+        if constexpr (CUR > 1) {
+            constexpr int half = CUR / 2;
+            const bool upper = (lane & M) != 0;
+#pragma unroll
+            for (int i = 0; i < half; ++i) {
+                const float send = upper ? v[i] : v[i + half];
+                const float keep = upper ? v[i + half] : v[i];
+                v[i] = keep + shfl_xor_f(send, M);
+            }
+            if (upper) off += half;
+            group_reduce_scatter<half, M / 2, N>(v, lane, off);
+        } else {
+            v[0] += shfl_xor_f(v[0], M);
+            group_reduce_scatter<1, M / 2, N>(v, lane, off);
+        }
+    }
+}
+
+}  // namespace rq
