@@ -73,6 +73,16 @@ __device__ __forceinline__ h8 b_from_crumbs(uint32_t w) {
                    unmagic(and_or(w, 0x00300030u)), unmagic(and_or(w, 0x00C000C0u)));
 }
 
+// key operands keep the magic offset: D = 1024 sum(A) + sum(q code); the constant is removed
+// per (query, group) in the score
+__device__ __forceinline__ h8 b_magic_nibbles(uint32_t w) {
+    const uint32_t w8 = w >> 8;
+    return pack_h8(and_or(w, 0x000F000Fu), and_or(w, 0x00F000F0u), and_or(w8, 0x000F000Fu), and_or(w8, 0x00F000F0u));
+}
+__device__ __forceinline__ h8 b_magic_crumbs(uint32_t w) {
+    return pack_h8(and_or(w, 0x00030003u), and_or(w, 0x000C000Cu), and_or(w, 0x00300030u), and_or(w, 0x00C000C0u));
+}
+
 __device__ __forceinline__ float fp8(uint32_t word, int byte) {
     switch (byte) {
         case 0: return __builtin_amdgcn_cvt_f32_fp8((int)word, 0);
@@ -110,18 +120,137 @@ struct Smem {
     static constexpr int PASS = 2 * (AC + AM + NRES * (RC + RM + CC));
     uint8_t ring[NW][NB][PASS];                          // also the epilogue's scratch
     _Float16 wbuf[NW][2][NG][G][BT];                     // value weights, in MFMA K order
-    h8 akey[4][NG][kWave];                               // key A operands: q hi/lo, u hi/lo
+    h8 akey[3][NG][kWave];                               // key A operands: q hi, q lo, u
     float sq[G][D];                                      // queries (float32)
     float su[G][D];                                      // u = R_K q
     float qsum[2][G][NG];                                // group sums of q and of u
+    float koff[2][G][NG];                                // 1024 * sum of the key A values
     float mw[NW][G], lw[NW][G];
-    float sum[2 * D];                                    // merged record of one query head
 };
 
 // token position in the value K order and its FP16 magic weight
 __device__ __forceinline__ int vpos(int t) {
     const int e = t & 7;
     return 8 * (t >> 3) + 2 * (e & 3) + (e >> 2);
+}
+
+// Merge of the split records of the G query heads bh0 .. bh0+G-1 (one KV head) by the last
+// workgroup, all heads at once: NT/G threads per head, thread i of a head owns channel i.
+// Same arithmetic as the one-head merge (splitk_merge_last); R_V is read once for the group.
+template <int G, bool RES>
+__device__ __forceinline__ void merge_group(const MergeArgs& g, int bh0, const float (*sq)[D], float* scr) {
+    constexpr int TPH = NT / G;                           // threads per head (128 or 256)
+    constexpr int PS = 2 * D + 4;
+    static_assert(TPH >= D && TPH % kWave == 0, "one thread per channel");
+    const int tid = threadIdx.x, q = tid / TPH, i = tid % TPH;
+    const int lane = tid & 63;
+    const int bh = bh0 + q;
+    const int hq = bh % g.hq, b = bh / g.hq, h = hq / G;
+    const int S = g.n_splits;
+    const float* recs = g.partials + (int64_t)bh * kMaxSplits * PS;
+    float* s_red = scr;                                   // [NT / 64]
+    float* s_w = s_red + NT / kWave;                      // [G][kMaxSplits]
+    float* s_sc = s_w + G * kMaxSplits;                   // [G][4]: m, l_tot, p_cur
+    float* s_r = s_sc + 4 * G;                            // [G][D] merged residual parts
+    float* s_p = s_r + G * D;                             // [4][G][D] partial R_V^T products
+    const bool ch = i < D;
+    const int64_t kvo = ((int64_t)b * g.hkv + h) * D;
+    uint32_t kc = 0, vc = 0;
+    if (ch) {
+        kc = g.k_cur[kvo + i];
+        vc = g.v_cur[kvo + i];
+    }
+    float ms = -INFINITY, ls = 0.f;
+    if (i < S) {
+        ms = ld_agent(recs + (int64_t)i * PS + 2 * D);
+        ls = ld_agent(recs + (int64_t)i * PS + 2 * D + 1);
+    }
+    constexpr int CH = 8;
+    float pa[CH], pr[CH];
+    auto load_chunk = [&](int s0) {
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+            const bool ok = ch && s0 + k < S;
+            pa[k] = ok ? ld_agent(recs + (int64_t)(s0 + k) * PS + i) : 0.f;
+            pr[k] = (ok && RES) ? ld_agent(recs + (int64_t)(s0 + k) * PS + D + i) : 0.f;
+        }
+    };
+    load_chunk(0);
+    // R_V^T: thread (q, i) takes rows [32 q', 32 q' + 32) of column i for every head, q' = q
+    // for G = 4 (rows [64 q', ...) for G = 2)
+    constexpr int RR = D / G;
+    float rv[RES ? RR : 1];
+    if constexpr (RES) {
+        if (ch) {
+            const float* Rv = g.rot + (int64_t)(2 * h + 1) * D * D + (int64_t)(q * RR) * D + i;
+#pragma unroll
+            for (int k = 0; k < RR; ++k) rv[k] = Rv[(int64_t)k * D];
+        }
+    }
+    float qk = ch ? sq[q][i] * bf16_to_f32(kc) : 0.f;
+    qk = wave_sum<kWave>(qk);
+    if (lane == 0) s_red[tid / kWave] = qk;
+    __syncthreads();
+    if (i < kWave) {                                      // first wave of each head
+        float s_cur = 0.f;
+#pragma unroll
+        for (int k = 0; k < TPH / kWave; ++k) s_cur += s_red[q * (TPH / kWave) + k];
+        s_cur *= g.sm_scale;
+        float mx = (ls > 0.f) ? ms : -INFINITY;
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, m));
+        const float m_f = fmaxf(mx, s_cur);
+        const float ws = (ls > 0.f) ? __expf(ms - m_f) : 0.f;
+        s_w[q * kMaxSplits + i] = ws;
+        const float lt = wave_sum<kWave>(ws * ls);
+        if (i == 0) {
+            s_sc[4 * q] = m_f;
+            s_sc[4 * q + 1] = lt;
+            s_sc[4 * q + 2] = __expf(s_cur - m_f);
+        }
+    }
+    __syncthreads();
+    float acc_a = 0.f, acc_r = 0.f;
+    for (int s0 = 0; s0 < S; s0 += CH) {
+        if (s0 > 0) load_chunk(s0);
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+            if (s0 + k < S) {
+                acc_a += s_w[q * kMaxSplits + s0 + k] * pa[k];
+                acc_r += s_w[q * kMaxSplits + s0 + k] * pr[k];
+            }
+        }
+    }
+    float o_r = 0.f;
+    if constexpr (RES) {
+        if (ch) s_r[q * D + i] = acc_r;
+        __syncthreads();
+        if (ch) {
+#pragma unroll
+            for (int qq = 0; qq < G; ++qq) {
+                float t = 0.f;
+#pragma unroll
+                for (int k = 0; k < RR; ++k) t += rv[k] * s_r[qq * D + q * RR + k];
+                s_p[(q * G + qq) * D + i] = t;
+            }
+        }
+        __syncthreads();
+        if (ch) {
+#pragma unroll
+            for (int p = 0; p < G; ++p) o_r += s_p[(p * G + q) * D + i];
+        }
+    }
+    if (ch) {
+        const float p_cur = s_sc[4 * q + 2];
+        g.out[(int64_t)bh * D + i] = (acc_a + o_r + p_cur * bf16_to_f32(vc)) / (s_sc[4 * q + 1] + p_cur);
+        if (q == 0) {
+            if (g.pending != nullptr) {
+                uint16_t* pd = g.pending + (((int64_t)b * g.L + g.lloc) * 2 * g.hkv + h) * D + i;
+                pd[0] = (uint16_t)kc;
+                pd[(int64_t)g.hkv * D] = (uint16_t)vc;
+            }
+        }
+    }
 }
 
 template <int G, int NRES, bool QBF16>
@@ -252,16 +381,24 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
     if (threadIdx.x < 2 * G * NG) {
         const int pl = threadIdx.x / (G * NG), g = (threadIdx.x / NG) % G, gi = threadIdx.x % NG;
         const float* src = pl ? sm.su[g] : sm.sq[g];
-        float s = 0.f;
+        float s = 0.f, off = 0.f;
         if (pl == 0 || NRES > 0) {
-            for (int c = 0; c < GS; ++c) s += src[GS * gi + c];
+            for (int c = 0; c < GS; ++c) {
+                const float v = src[GS * gi + c];
+                s += v;
+                // the key A value of channel c, as the MFMA sees it (FP16, hi + lo for q)
+                const float a = pl ? ldexpf(v, -2 * (c & 3)) : ((c & 1) ? v * 0.0625f : v);
+                const _Float16 hi = (_Float16)a;
+                off += (float)hi + (pl ? 0.f : (float)(_Float16)(a - (float)hi));
+            }
         }
         sm.qsum[pl][g][gi] = s;
+        sm.koff[pl][g][gi] = 1024.f * off;
     }
     // A operands of the key products, shared by the waves: lane (m = 4 qh + g', kg) holds
     // row m, K elements 8 kg .. 8 kg + 7 of channel group gi, nonzero only where g' == gi.
-    // Thread t < 4 * 64 builds kind t / 64 (q hi, q lo, u hi, u lo) for lane t % 64.
-    if (threadIdx.x < 4 * kWave) {
+    // Thread t < 3 * 64 builds kind t / 64 (q hi, q lo, u) for lane t % 64.
+    if (threadIdx.x < 3 * kWave) {
         const int kind = threadIdx.x / kWave, L = threadIdx.x % kWave;
         const int ll = L & 15, lk = L >> 4, qh_a = ll >> 2, ga = ll & 3;
         h8 frag;
@@ -289,11 +426,13 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
     // score-layout lane: token l16 of a 16-token round, query kg
     const int qs = kg;
     const bool q_ok = qs < G;
-    float Qs[NG], Us[NG];
+    float Qs[NG], Us[NG], Ca[NG], Cu[NG];
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
         Qs[gi] = q_ok ? sm.qsum[0][qs][gi] : 0.f;
         Us[gi] = q_ok ? sm.qsum[1][qs][gi] : 0.f;
+        Ca[gi] = q_ok ? sm.koff[0][qs][gi] : 0.f;
+        Cu[gi] = q_ok ? sm.koff[1][qs][gi] : 0.f;
     }
 
     // value accumulators: 8 anchor N-blocks (16 channels each) and 8 residual N-blocks
@@ -325,15 +464,14 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
                 const uint32_t wa = *reinterpret_cast<const uint32_t*>(sp + t * AROW + (4 * gi + kg) * 4);
-                const h8 bq = b_from_nibbles(wa);
+                const h8 bq = b_magic_nibbles(wa);
                 da = mfma(sm.akey[0][gi][lane], bq, da);
                 da = mfma(sm.akey[1][gi][lane], bq, da);
                 if constexpr (NRES > 0) {
                     uint32_t wr = *reinterpret_cast<const uint32_t*>(sp + RES_OFF + t * RROW + (2 * gi + (kg >> 1)) * 4);
                     wr = (kg & 1) ? (wr >> 8) : wr;
-                    const h8 bu = b_from_crumbs(wr);
+                    const h8 bu = b_magic_crumbs(wr);
                     dr = mfma(sm.akey[2][gi][lane], bu, dr);
-                    dr = mfma(sm.akey[3][gi][lane], bu, dr);
                 }
             }
             // score of (token t, query qs): this lane holds the 4 group products in da / dr
@@ -342,7 +480,7 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
                 const uint32_t mw = gi < 2 ? am.x : am.y;
-                part_a += fp8(mw, 2 * (gi & 1)) * Qs[gi] + fp8(mw, 2 * (gi & 1) + 1) * da[gi];
+                part_a += fp8(mw, 2 * (gi & 1)) * Qs[gi] + fp8(mw, 2 * (gi & 1) + 1) * (da[gi] - Ca[gi]);
             }
             float coef = 1.f, part_r = 0.f;
             uint2 rm = {0u, 0u};
@@ -351,7 +489,7 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi) {
                     const uint32_t mw = gi < 2 ? rm.x : rm.y;
-                    part_r += fp8(mw, 2 * (gi & 1)) * Us[gi] + fp8(mw, 2 * (gi & 1) + 1) * dr[gi];
+                    part_r += fp8(mw, 2 * (gi & 1)) * Us[gi] + fp8(mw, 2 * (gi & 1) + 1) * (dr[gi] - Cu[gi]);
                 }
                 coef = bf16_to_f32(*reinterpret_cast<const uint16_t*>(sp + RES_OFF + RC + RM + t * 2));
             }
@@ -518,25 +656,22 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
         }
     }
     __syncthreads();
-    // publish the G records (sum over the waves), count the arrival, merge if last
-    for (int q = 0; q < G; ++q) {
-        for (int c = threadIdx.x; c < 2 * D; c += NT) {
-            float s = 0.f;
+    // publish the G records (sums over the waves), then count the arrival
+    constexpr int NV = NRES ? 2 * D : D;
+    for (int idx = threadIdx.x; idx < G * NV; idx += NT) {
+        const int q = idx / NV, c = idx % NV;
+        float v = 0.f;
 #pragma unroll
-            for (int i = 0; i < NW; ++i) s += scr[((i * G) + q) * 2 * D + c];
-            sm.sum[c] = s;
-        }
-        __syncthreads();
-        splitk_publish<D, (NRES > 0), NT>(a.mg, bh0 + q, split, sm.sum, make_float2(m_wg[q], l_wg[q]));
-        __syncthreads();
+        for (int i = 0; i < NW; ++i) v += scr[((i * G) + q) * 2 * D + c];
+        st_agent(a.mg.partials + ((int64_t)(bh0 + q) * kMaxSplits + split) * (2 * D + 4) + c, v);
+    }
+    if (threadIdx.x < G) {
+        float* rec = a.mg.partials + ((int64_t)(bh0 + threadIdx.x) * kMaxSplits + split) * (2 * D + 4);
+        st_agent(rec + 2 * D, m_wg[threadIdx.x]);
+        st_agent(rec + 2 * D + 1, l_wg[threadIdx.x]);
     }
     if (!splitk_arrive(a.mg, bh0)) return;
-    for (int q = 0; q < G; ++q) {
-        // the merge uses SplitSmem-sized scratch; the ring serves again
-        splitk_merge_last<D, (NRES > 0), NT>(a.mg, bh0 + q, sm.sq[q],
-                                             reinterpret_cast<float*>(&sm.ring[0][0][0]));
-        __syncthreads();
-    }
+    merge_group<G, (NRES > 0)>(a.mg, bh0, sm.sq, reinterpret_cast<float*>(&sm.ring[0][0][0]));
 }
 
 template <int G, int NRES>
