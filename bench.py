@@ -32,7 +32,7 @@ DEFAULT_WORKLOAD = "ouro_b4_t8192"
 CSRC = os.path.join(ROOT, "looped_transformer_decode_amd", "csrc")
 # sources of the decode kernel (split-K with the merge in its last workgroup)
 DECODE_SOURCES = ("rq_api.hip", "rq_decode.hip", "rq_args.hpp", "rq_common.hpp",
-                  "rq_splitk.hpp")
+                  "rq_splitk.hpp", "rq_stage.hpp")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "rq_decode_residual_ouro_b4_t8192_hbm_traffic.txt")
 
 

@@ -99,6 +99,78 @@ __device__ __forceinline__ float dpp_f(float old, float v) {
                                                       BANKMASK, false));
 }
 
+constexpr int kDppRowHalfMirror = 0x141, kDppRowMirror = 0x140;
+
+// Lane exchanges on the VALU instead of the LDS crossbar.  xshfl<M> returns the value of
+// lane (lane ^ M): DPP quad permutes for M = 1, 2, row shifts for 4 and 8 (left for lanes
+// with the bit clear, right for those with it set, so the source stays in its 16-lane
+// row) and the gfx950 half swaps v_permlane16_swap / v_permlane32_swap for 16 and 32.
+template <int M>
+__device__ __forceinline__ int xshfl_i(int v) {
+    if constexpr (M == 1) {
+        return __builtin_amdgcn_update_dpp(v, v, kDppQuadXor1, 0xF, 0xF, false);
+    } else if constexpr (M == 2) {
+        return __builtin_amdgcn_update_dpp(v, v, kDppQuadXor2, 0xF, 0xF, false);
+    } else if constexpr (M == 4 || M == 8) {
+        const int up = __builtin_amdgcn_update_dpp(v, v, 0x100 + M, 0xF, 0xF, false);   // row_shl: lane + M
+        const int dn = __builtin_amdgcn_update_dpp(v, v, 0x110 + M, 0xF, 0xF, false);   // row_shr: lane - M
+        return (threadIdx.x & M) ? dn : up;
+    } else if constexpr (M == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (int)((threadIdx.x & 16) ? r[0] : r[1]);
+    } else {
+        static_assert(M == 32, "lane xor mask 1, 2, 4, 8, 16 or 32");
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (int)((threadIdx.x & 32) ? r[0] : r[1]);
+    }
+}
+template <int M>
+__device__ __forceinline__ float xshfl(float v) {
+    return __int_as_float(xshfl_i<M>(__float_as_int(v)));
+}
+
+// Partner exchange for butterflies: the value of lane (lane ^ P(M)), where P(M) = M except
+// P(4) = 7 and P(8) = 15, the DPP half-row and row mirrors (one instruction each).  P(M)
+// has bit M set and no bit above it, so a butterfly over bits taken from high to low
+// (a reduce-scatter that splits on bit M) pairs lanes that agree on every bit already
+// taken; and from low to high (an all-reduce) the extra low bits only move the source
+// inside a group whose values are already equal.
+template <int M>
+__device__ __forceinline__ float xpartner(float v) {
+    if constexpr (M == 4) return dpp_f<kDppRowHalfMirror>(v, v);
+    else if constexpr (M == 8) return dpp_f<kDppRowMirror>(v, v);
+    else return xshfl<M>(v);
+}
+
+// All-reduce over aligned groups of N lanes (N a power of two up to 64); every lane gets
+// the result.  At 16 and 32 the half swap hands each lane both halves' values at once.
+template <int N, int M = 1, class Op>
+__device__ __forceinline__ float group_reduce(float v, Op op) {
+    if constexpr (M >= N) {
+        return v;
+    } else if constexpr (M == 16 || M == 32) {
+        const int x = __float_as_int(v);
+        const auto r = (M == 16) ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
+                                 : __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return group_reduce<N, 2 * M>(op(__int_as_float((int)r[0]), __int_as_float((int)r[1])), op);
+    } else {
+        return group_reduce<N, 2 * M>(op(v, xpartner<M>(v)), op);
+    }
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    return group_reduce<N>(v, [](float a, float b) { return a + b; });
+}
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+    return group_reduce<N>(v, [](float a, float b) { return fmaxf(a, b); });
+}
+// Integer sums are exact in float up to 2^24, which bounds every digit sum here.
+template <int N>
+__device__ __forceinline__ int group_sum_i(int v) {
+    return (int)group_sum<N>((float)v);
+}
+
 // Sum over aligned groups of N = 1, 2 or 4 lanes; every lane of the group gets the sum.
 template <int N>
 __device__ __forceinline__ float group_sum_dpp(float v) {

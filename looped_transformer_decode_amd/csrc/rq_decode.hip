@@ -309,18 +309,12 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
         const int which = threadIdx.x / D, i = threadIdx.x % D;
         const float val = sv[which][i];
         const bool four = (which == 0) && (BA == 4);
-        float amax = fabsf(val), vsum = val;
-#pragma unroll
-        for (int m = 1; m < GS; m <<= 1) {
-            amax = fmaxf(amax, shfl_xor_f(amax, m));
-            vsum += shfl_xor_f(vsum, m);
-        }
+        const float amax = group_max<GS>(fabsf(val));
+        const float vsum = group_sum<GS>(val);
         const int e = amax > 0.f ? ilogbf(amax) : 0;
         const int fb = which ? 13 : 21;                    // |Q| <= 2^(fb + 1)
         int Q = (int)rintf(val * ldexpf(1.f, fb - e));     // exact power-of-two scaling
-        int qsum = Q;
-#pragma unroll
-        for (int m = 1; m < GS; m <<= 1) qsum += __shfl_xor(qsum, m, kWave);
+        const int qsum = group_sum_i<GS>(Q);
         const int shift = four ? 4 * (i % 8) : 4 * ((i % 16) / 2);
         const int widx = four ? i / 8 : (i / 16) * 2 + (i & 1);
         const int nd = which ? 4 : 6;

@@ -196,9 +196,7 @@ __device__ __forceinline__ void merge_group(const MergeArgs& g, int bh0, const f
 #pragma unroll
         for (int k = 0; k < TPH / kWave; ++k) s_cur += s_red[q * (TPH / kWave) + k];
         s_cur *= g.sm_scale;
-        float mx = (ls > 0.f) ? ms : -INFINITY;
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, m));
+        const float mx = group_max<kWave>((ls > 0.f) ? ms : -INFINITY);
         const float m_f = fmaxf(mx, s_cur);
         const float ws = (ls > 0.f) ? __expf(ms - m_f) : 0.f;
         s_w[q * kMaxSplits + i] = ws;

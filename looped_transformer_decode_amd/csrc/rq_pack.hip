@@ -56,8 +56,6 @@ __device__ __forceinline__ double bf16_round(double v) {
 
 // ---- cross-lane steps on float64 values
 
-constexpr int kDppRowMirror = 0x140, kDppRowHalfMirror = 0x141;
-
 template <int CTRL>
 __device__ __forceinline__ double dpp_d(double v) {
     const uint64_t u = (uint64_t)__double_as_longlong(v);

@@ -26,7 +26,7 @@ __device__ __forceinline__ void reduce_scatter_step(float (&v)[N], int lane, int
         for (int i = 0; i < half; ++i) {
             const float send = upper ? v[i] : v[i + half];
             const float keep = upper ? v[i + half] : v[i];
-            v[i] = keep + shfl_xor_f(send, M);
+            v[i] = keep + xshfl<M>(send);
         }
         if (upper) off += half;
         reduce_scatter_step<half, 2 * M, N>(v, lane, off);
@@ -42,25 +42,10 @@ __device__ __forceinline__ int slot_reduce_scatter(float (&v)[N], int lane) {
     return off;
 }
 
-template <int LPT>
+template <int LPT, int M = LPT>
 __device__ __forceinline__ float slot_sum(float v) {
-#pragma unroll
-    for (int m = LPT; m < kWave; m <<= 1) v += shfl_xor_f(v, m);
-    return v;
-}
-
-template <int LPT>
-__device__ __forceinline__ float slot_max(float v) {
-#pragma unroll
-    for (int m = LPT; m < kWave; m <<= 1) v = fmaxf(v, shfl_xor_f(v, m));
-    return v;
-}
-
-template <int LPT>
-__device__ __forceinline__ float chunk_sum(float v) {
-#pragma unroll
-    for (int m = 1; m < LPT; m <<= 1) v += shfl_xor_f(v, m);
-    return v;
+    if constexpr (M < kWave) return slot_sum<LPT, 2 * M>(v + xshfl<M>(v));
+    else return v;
 }
 
 // LDS of the split epilogue.
@@ -131,9 +116,7 @@ __device__ __forceinline__ float ld_agent(const float* p) {
 
 template <int N>
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = N / 2; m >= 1; m >>= 1) v += shfl_xor_f(v, m);
-    return v;
+    return group_sum<N>(v);
 }
 
 // Store this split's record (sum: LDS values acc_a[D], then acc_r[D] when RES; ml = (m, l)).
@@ -227,9 +210,7 @@ __device__ __forceinline__ void splitk_merge_last(const MergeArgs& g, int bh, co
 #pragma unroll
         for (int i = 0; i < NW; ++i) s_cur += s_red[i];
         s_cur *= g.sm_scale;
-        float mx = (ls > 0.f) ? ms : -INFINITY;
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, shfl_xor_f(mx, m));
+        const float mx = group_max<kWave>((ls > 0.f) ? ms : -INFINITY);
         const float m_f = fmaxf(mx, s_cur);
         const float ws = (ls > 0.f) ? __expf(ms - m_f) : 0.f;
         if (lane < kMaxSplits) s_w[lane] = ws;

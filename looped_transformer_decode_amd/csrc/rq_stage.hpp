@@ -61,12 +61,12 @@ __device__ __forceinline__ void group_reduce_scatter(float (&v)[N], int lane, in
             for (int i = 0; i < half; ++i) {
                 const float send = upper ? v[i] : v[i + half];
                 const float keep = upper ? v[i + half] : v[i];
-                v[i] = keep + shfl_xor_f(send, M);
+                v[i] = keep + xpartner<M>(send);
             }
             if (upper) off += half;
             group_reduce_scatter<half, M / 2, N>(v, lane, off);
         } else {
-            v[0] += shfl_xor_f(v[0], M);
+            v[0] += xpartner<M>(v[0]);
             group_reduce_scatter<1, M / 2, N>(v, lane, off);
         }
     }
