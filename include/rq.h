@@ -176,6 +176,25 @@ rq_status rq_bf16_decode_attention(const rq_bf16_config* cfg, uint16_t* k_cache,
                                    float* out, void* workspace, size_t workspace_bytes,
                                    int32_t batch, int32_t n_splits, hipStream_t stream);
 
+/* rq_unpack_debug - rebuild loop `loop` of every (batch row, KV head, K|V) for the token
+ * slots [t0, t1) in float32: the vectors decode attention attends to, which the decode
+ * kernel itself never materialises (a checking aid for the cache layout).  Explainer,
+ * paragraph on the master print (a loop's KV = c * anchor + residual, the residual
+ * stored in the rotated basis) and "Which print is the master" (chained loops):
+ *   anchor loop       : a_hat = z + code * s per channel group;
+ *   shared loop l     : c_l * a_hat + R^T r_hat_l;
+ *   chained loop l    : c_l * x_hat_{l+1} + R^T r_hat_l, with x_hat of the anchor loop = a_hat.
+ * Dequantized values are exact in float32; the R^T products are float32 sums.
+ *   cfg    : host pointer.   cache : device, as written by rq_quantize_token.
+ *   loop   : global loop index 0..L*n_groups-1.
+ *   rot    : device float32 [n_kv_heads][2][head_dim][head_dim].
+ *   t0, t1 : slot range, 0 <= t0 < t1 <= max_ctx (slots never written hold whatever the
+ *            cache held).
+ *   out    : device float32 [batch][n_kv_heads][2][t1 - t0][head_dim], written fully.
+ * Alignment: cache, rot and out 16-byte aligned. */
+rq_status rq_unpack_debug(const rq_config* cfg, const void* cache, int32_t loop, const float* rot,
+                          int32_t t0, int32_t t1, int32_t batch, float* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,7 @@ if not os.path.exists(_LIB_PATH):
 _lib = ctypes.CDLL(_LIB_PATH)
 
 EXPORTS = ("rq_cache_bytes", "rq_workspace_bytes", "rq_bf16_workspace_bytes", "rq_status_str",
-           "rq_quantize_token", "rq_decode_attention", "rq_bf16_decode_attention")
+           "rq_quantize_token", "rq_decode_attention", "rq_bf16_decode_attention", "rq_unpack_debug")
 
 
 class rq_config(ctypes.Structure):
@@ -61,6 +61,8 @@ _lib.rq_decode_attention.restype = _i32
 _lib.rq_bf16_decode_attention.argtypes = [_bcfgp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _f32,
                                           _vp, _vp, _sz, _i32, _i32, _vp]
 _lib.rq_bf16_decode_attention.restype = _i32
+_lib.rq_unpack_debug.argtypes = [_cfgp, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp]
+_lib.rq_unpack_debug.restype = _i32
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -134,6 +136,12 @@ def rq_bf16_decode_attention(cfg: rq_bf16_config, k_cache: torch.Tensor, v_cache
         ctypes.byref(cfg), _ptr(k_cache), _ptr(v_cache), _ptr(q), q_bf16, _ptr(k_cur), _ptr(v_cur),
         1 if append else 0, _ptr(ctx_len), ctx_bound, sm_scale, _ptr(out), _ptr(workspace),
         _nbytes(workspace), batch, n_splits, _stream(stream)))
+
+
+def rq_unpack_debug(cfg: rq_config, cache: torch.Tensor, loop: int, rot: torch.Tensor, t0: int, t1: int,
+                    batch: int, out: torch.Tensor, stream=None) -> None:
+    _check("rq_unpack_debug", _lib.rq_unpack_debug(
+        ctypes.byref(cfg), _ptr(cache), loop, _ptr(rot), t0, t1, batch, _ptr(out), _stream(stream)))
 
 
 def config_for(wl, chained: Optional[bool] = None, max_batch: Optional[int] = None,

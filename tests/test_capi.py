@@ -146,3 +146,21 @@ def test_bf16_decode_rejects_bad_arguments(B):
     assert call(q=A + 2) == 3
     assert call(ws_bytes=need - 1) == 4
     assert call(cfg=B.rq_bf16_config(128, 16, 24, 4, 8193)) == 2
+
+
+def test_unpack_debug_rejects_bad_arguments(B):
+    wl = synth.WORKLOADS["ouro_b4_t8192"]
+    cfg = B.config_for(wl)
+    f = B._lib.rq_unpack_debug
+
+    def call(cfg=cfg, cache=A, loop=0, rot=A, t0=0, t1=64, batch=4, out=A):
+        return f(ctypes.byref(cfg), cache, loop, rot, t0, t1, batch, out, None)
+
+    assert call(cfg=B.rq_config()) == 2
+    assert call(cache=None) == 1
+    assert call(loop=4) == 1
+    assert call(t0=-1) == 1
+    assert call(t0=64, t1=64) == 1
+    assert call(t1=wl.ctx + 2) == 1
+    assert call(batch=5) == 1
+    assert call(out=A + 4) == 3
