@@ -73,6 +73,17 @@ def bf16_bytes(wl) -> int:
     return 2 * 2 * wl.head_dim * wl.batch * wl.ctx * wl.n_kv_heads
 
 
+def bulk_in_bytes(wl) -> int:
+    """BF16 K/V of every loop of every anchor group, read once by the bulk context pack."""
+    return wl.batch * wl.ctx * wl.n_loops * 2 * wl.n_kv_heads * wl.head_dim * 2
+
+
+def rotation_fma(wl) -> int:
+    """Float64 FMAs of the residual rotations R y in a bulk pack of the whole context."""
+    n_res = wl.n_groups * (wl.loops_per_group - 1)
+    return wl.batch * wl.ctx * wl.n_kv_heads * 2 * n_res * wl.head_dim * wl.head_dim
+
+
 def cpu_baseline(wl, budget_s: float = 12.0):
     """Time the float64 oracle (as it is) on a bounded sample of the same workload:
     one residual loop-step of decode attention for single (row, KV head) pairs at the
@@ -154,6 +165,17 @@ def main():
         B.rq_quantize_token(cfg, cache, inp.kv[grp], grp, pos0, inp.rot, Bt, T,
                             pending_strides=(st[4], st[2], st[0], st[1], st[3]))
     torch.cuda.synchronize()
+    # bulk pack of the whole context (the step before decode), timed on a second run that
+    # rewrites the same bytes
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0.record()
+    for grp in range(wl.n_groups):
+        st = inp.kv[grp].stride()
+        B.rq_quantize_token(cfg, cache, inp.kv[grp], grp, pos0, inp.rot, Bt, T,
+                            pending_strides=(st[4], st[2], st[0], st[1], st[3]))
+    b1.record()
+    torch.cuda.synchronize()
+    bulk_ms = b0.elapsed_time(b1)
     n_rep = args.replicas or max(2, min(16, math.ceil(1.6e9 / cache_bytes)))
     caches = [cache] + [cache.clone() for _ in range(n_rep - 1)]
     print(f"[bench] packed context ({cache_bytes/1e6:.1f} MB), {n_rep} replicas", file=sys.stderr, flush=True)
@@ -273,6 +295,39 @@ def main():
     bf16_ms = sum(a.elapsed_time(b) for a, b in bev) / len(bev)
     bf16_gbps = bf16_bytes(wl) / (bf16_ms * 1e-3) / 1e9
 
+    # plain streaming read of the same replicas: the rate a simple load loop reaches here
+    sink = torch.empty(B.STREAM_SINK_WORDS, dtype=torch.int32, device=dev)
+    probe_bytes = res_bytes // 16 * 16
+
+    def stream_gbps(nbytes, reps):
+        for i in range(2):
+            B.rq_stream_read(caches[i % n_rep], nbytes, sink, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            B.rq_stream_read(caches[(i + 2) % n_rep], nbytes, sink, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+    stream_res = stream_gbps(min(probe_bytes, cache_bytes // 16 * 16), 4 * n_rep)
+    stream_full = stream_gbps(cache_bytes // 16 * 16, 2 * n_rep)
+
+    # roofline timing: back-to-back residual loop-steps over the cold replicas, one event
+    # pair around all of them (launches overlap the previous kernel, as in a decode step)
+    roof_calls = 6 * n_rep
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    for i in range(roof_calls):
+        loop = i % (L - 1)
+        B.rq_decode_attention(cfg, caches[i % n_rep], loop, q[loop], k_cur[loop], v_cur[loop], None, ctx_len, T,
+                              inp.rot, sc, out, ws, Bt, n_splits=args.splits, stream=stream)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    roof_ms = r0.elapsed_time(r1) / roof_calls
+    roof_bytes = sum(algorithmic_bytes(wl, i % (L - 1), wl.chained) for i in range(roof_calls)) / roof_calls
+    roof_gbps = roof_bytes / (roof_ms * 1e-3) / 1e9
+
     value = step_bytes / (ms_step * 1e-3) / 1e9
     traffic = measured_traffic(wl.name) if not wl.chained and args.splits == 0 else None
     result = {
@@ -305,10 +360,22 @@ def main():
         "bf16": {"bytes": bf16_bytes(wl), "ms_per_loop_step": round(bf16_ms, 4), "gbps": round(bf16_gbps, 1),
                  "speedup_rq_residual_vs_bf16": round(bf16_ms / res_ms, 3),
                  "speedup_rq_step_vs_bf16_step": round(bf16_ms * n_loops / ms_step, 3)},
-        "roofline": {"bound": "hbm", "achieved": round(res_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(res_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+        "bulk_pack": {"tokens": Bt * T, "ms": round(bulk_ms, 3),
+                      "tokens_per_s": round(Bt * T / (bulk_ms * 1e-3), 1),
+                      "bf16_in_bytes": bulk_in_bytes(wl), "gbps_in": round(bulk_in_bytes(wl) / (bulk_ms * 1e-3) / 1e9, 1),
+                      "rotation_fma": rotation_fma(wl),
+                      "f64_tflops": round(2 * rotation_fma(wl) / (bulk_ms * 1e-3) / 1e12, 2)},
+        "stream_read": {"kernel": "rq_stream_read (plain 16-byte load loop over the same cache replicas)",
+                        "gbps_at_residual_step_bytes": round(stream_res, 1),
+                        "gbps_at_full_replica": round(stream_full, 1),
+                        "residual_step_frac_of_stream": round(roof_gbps / stream_res, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(roof_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(roof_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "ms_per_launch": round(roof_ms, 4), "launches": roof_calls,
+                     "timing": "HIP events around back-to-back residual loop-steps (loops 0..L-2, cold replicas), "
+                               "on the library's stream, the last decode dispatches of the run",
                      "kernel": "rq_decode_kernel, residual loop-step (split-K with the merge in its last workgroup)",
-                     "algorithmic_bytes": res_bytes, "source_digest": decode_source_digest()},
+                     "algorithmic_bytes": round(roof_bytes), "source_digest": decode_source_digest()},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)

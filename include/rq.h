@@ -195,6 +195,15 @@ rq_status rq_bf16_decode_attention(const rq_bf16_config* cfg, uint16_t* k_cache,
 rq_status rq_unpack_debug(const rq_config* cfg, const void* cache, int32_t loop, const float* rot,
                           int32_t t0, int32_t t1, int32_t batch, float* out, hipStream_t stream);
 
+/* rq_stream_read - a measuring stick, not part of the method: read `bytes` of `buf`
+ * with plain 16-byte loads (one contiguous slab per workgroup, XOR-folded into one word
+ * per thread of `sink`).  Timed over the same buffers as the decode kernel it gives the
+ * read rate a simple load loop reaches on the device, next to the datasheet peak.
+ *   buf        : device, 16-byte aligned; bytes : a nonzero multiple of 16.
+ *   sink       : device uint32 scratch of sink_words >= 1048576 words (contents unspecified). */
+rq_status rq_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words,
+                         hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,8 @@ if not os.path.exists(_LIB_PATH):
 _lib = ctypes.CDLL(_LIB_PATH)
 
 EXPORTS = ("rq_cache_bytes", "rq_workspace_bytes", "rq_bf16_workspace_bytes", "rq_status_str",
-           "rq_quantize_token", "rq_decode_attention", "rq_bf16_decode_attention", "rq_unpack_debug")
+           "rq_quantize_token", "rq_decode_attention", "rq_bf16_decode_attention", "rq_unpack_debug",
+           "rq_stream_read")
 
 
 class rq_config(ctypes.Structure):
@@ -63,6 +64,8 @@ _lib.rq_bf16_decode_attention.argtypes = [_bcfgp, _vp, _vp, _vp, _i32, _vp, _vp,
 _lib.rq_bf16_decode_attention.restype = _i32
 _lib.rq_unpack_debug.argtypes = [_cfgp, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp]
 _lib.rq_unpack_debug.restype = _i32
+_lib.rq_stream_read.argtypes = [_vp, _sz, _vp, _sz, _vp]
+_lib.rq_stream_read.restype = _i32
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -142,6 +145,13 @@ def rq_unpack_debug(cfg: rq_config, cache: torch.Tensor, loop: int, rot: torch.T
                     batch: int, out: torch.Tensor, stream=None) -> None:
     _check("rq_unpack_debug", _lib.rq_unpack_debug(
         ctypes.byref(cfg), _ptr(cache), loop, _ptr(rot), t0, t1, batch, _ptr(out), _stream(stream)))
+
+
+STREAM_SINK_WORDS = 1 << 20
+
+
+def rq_stream_read(buf: torch.Tensor, nbytes: int, sink: torch.Tensor, stream=None) -> None:
+    _check("rq_stream_read", _lib.rq_stream_read(_ptr(buf), nbytes, _ptr(sink), sink.numel(), _stream(stream)))
 
 
 def config_for(wl, chained: Optional[bool] = None, max_batch: Optional[int] = None,

@@ -101,6 +101,14 @@ __device__ __forceinline__ float dpp_f(float old, float v) {
 
 constexpr int kDppRowHalfMirror = 0x141, kDppRowMirror = 0x140;
 
+// Full-mask DPP read with zero for lanes whose source is outside the row (bound_ctrl):
+// with no "old" operand the compiler can fold the move into the VALU op that uses it.
+template <int CTRL>
+__device__ __forceinline__ float dpp_z(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+
 // Lane exchanges on the VALU instead of the LDS crossbar.  xshfl<M> returns the value of
 // lane (lane ^ M): DPP quad permutes for M = 1, 2, row shifts for 4 and 8 (left for lanes
 // with the bit clear, right for those with it set, so the source stays in its 16-lane
@@ -108,12 +116,12 @@ constexpr int kDppRowHalfMirror = 0x141, kDppRowMirror = 0x140;
 template <int M>
 __device__ __forceinline__ int xshfl_i(int v) {
     if constexpr (M == 1) {
-        return __builtin_amdgcn_update_dpp(v, v, kDppQuadXor1, 0xF, 0xF, false);
+        return __builtin_amdgcn_mov_dpp(v, kDppQuadXor1, 0xF, 0xF, true);
     } else if constexpr (M == 2) {
-        return __builtin_amdgcn_update_dpp(v, v, kDppQuadXor2, 0xF, 0xF, false);
+        return __builtin_amdgcn_mov_dpp(v, kDppQuadXor2, 0xF, 0xF, true);
     } else if constexpr (M == 4 || M == 8) {
-        const int up = __builtin_amdgcn_update_dpp(v, v, 0x100 + M, 0xF, 0xF, false);   // row_shl: lane + M
-        const int dn = __builtin_amdgcn_update_dpp(v, v, 0x110 + M, 0xF, 0xF, false);   // row_shr: lane - M
+        const int up = __builtin_amdgcn_mov_dpp(v, 0x100 + M, 0xF, 0xF, true);   // row_shl: lane + M
+        const int dn = __builtin_amdgcn_mov_dpp(v, 0x110 + M, 0xF, 0xF, true);   // row_shr: lane - M
         return (threadIdx.x & M) ? dn : up;
     } else if constexpr (M == 16) {
         const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
@@ -129,6 +137,32 @@ __device__ __forceinline__ float xshfl(float v) {
     return __int_as_float(xshfl_i<M>(__float_as_int(v)));
 }
 
+// One pair of a reduce-scatter step over lane bit M: with a = element i and b = element
+// i + half of the lane's values, a lane with bit M clear returns a + (partner's a) and a
+// lane with bit M set returns b + (partner's b), the partner being lane ^ M.  DPP row
+// shifts (and quad permutes) read the partner for each half in one instruction; the
+// gfx950 half swaps exchange the two halves between partners in one instruction, so at
+// 16 and 32 every lane just adds the pair it receives.
+template <int M>
+__device__ __forceinline__ float rs_pair(float a, float b) {
+    if constexpr (M == 16 || M == 32) {
+        const int ia = __float_as_int(a), ib = __float_as_int(b);
+        const auto r = (M == 16) ? __builtin_amdgcn_permlane16_swap(ia, ib, false, false)
+                                 : __builtin_amdgcn_permlane32_swap(ia, ib, false, false);
+        return __int_as_float((int)r[0]) + __int_as_float((int)r[1]);
+    } else if constexpr (M == 4 || M == 8) {
+        const float lo = a + dpp_z<0x100 + M>(a);         // row_shl: lane + M
+        const float hi = b + dpp_z<0x110 + M>(b);         // row_shr: lane - M
+        return (threadIdx.x & M) ? hi : lo;
+    } else {
+        static_assert(M == 1 || M == 2, "lane bit 1, 2, 4, 8, 16 or 32");
+        constexpr int P = M == 1 ? kDppQuadXor1 : kDppQuadXor2;
+        const float lo = a + dpp_z<P>(a);
+        const float hi = b + dpp_z<P>(b);
+        return (threadIdx.x & M) ? hi : lo;
+    }
+}
+
 // Partner exchange for butterflies: the value of lane (lane ^ P(M)), where P(M) = M except
 // P(4) = 7 and P(8) = 15, the DPP half-row and row mirrors (one instruction each).  P(M)
 // has bit M set and no bit above it, so a butterfly over bits taken from high to low
@@ -137,8 +171,8 @@ __device__ __forceinline__ float xshfl(float v) {
 // inside a group whose values are already equal.
 template <int M>
 __device__ __forceinline__ float xpartner(float v) {
-    if constexpr (M == 4) return dpp_f<kDppRowHalfMirror>(v, v);
-    else if constexpr (M == 8) return dpp_f<kDppRowMirror>(v, v);
+    if constexpr (M == 4) return dpp_z<kDppRowHalfMirror>(v);
+    else if constexpr (M == 8) return dpp_z<kDppRowMirror>(v);
     else return xshfl<M>(v);
 }
 
@@ -174,8 +208,8 @@ __device__ __forceinline__ int group_sum_i(int v) {
 // Sum over aligned groups of N = 1, 2 or 4 lanes; every lane of the group gets the sum.
 template <int N>
 __device__ __forceinline__ float group_sum_dpp(float v) {
-    if constexpr (N >= 2) v += dpp_f<kDppQuadXor1>(v, v);
-    if constexpr (N >= 4) v += dpp_f<kDppQuadXor2>(v, v);
+    if constexpr (N >= 2) v += dpp_z<kDppQuadXor1>(v);
+    if constexpr (N >= 4) v += dpp_z<kDppQuadXor2>(v);
     static_assert(N <= 4, "group of at most 4 lanes");
     return v;
 }

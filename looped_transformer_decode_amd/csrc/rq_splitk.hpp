@@ -21,14 +21,9 @@ template <int CUR, int M, int N>
 __device__ __forceinline__ void reduce_scatter_step(float (&v)[N], int lane, int& off) {
     if constexpr (M < kWave) {
         constexpr int half = CUR / 2;
-        const bool upper = (lane & M) != 0;
 #pragma unroll
-        for (int i = 0; i < half; ++i) {
-            const float send = upper ? v[i] : v[i + half];
-            const float keep = upper ? v[i + half] : v[i];
-            v[i] = keep + xshfl<M>(send);
-        }
-        if (upper) off += half;
+        for (int i = 0; i < half; ++i) v[i] = rs_pair<M>(v[i], v[i + half]);
+        if (lane & M) off += half;
         reduce_scatter_step<half, 2 * M, N>(v, lane, off);
     }
 }

@@ -56,17 +56,19 @@ __device__ __forceinline__ void group_reduce_scatter(float (&v)[N], int lane, in
     if constexpr (M >= 1) {
         if constexpr (CUR > 1) {
             constexpr int half = CUR / 2;
-            const bool upper = (lane & M) != 0;
 #pragma unroll
-            for (int i = 0; i < half; ++i) {
-                const float send = upper ? v[i] : v[i + half];
-                const float keep = upper ? v[i + half] : v[i];
-                v[i] = keep + xpartner<M>(send);
-            }
-            if (upper) off += half;
+            for (int i = 0; i < half; ++i) v[i] = rs_pair<M>(v[i], v[i + half]);
+            if (lane & M) off += half;
             group_reduce_scatter<half, M / 2, N>(v, lane, off);
         } else {
-            v[0] += xpartner<M>(v[0]);
+            if constexpr (M == 16 || M == 32) {
+                const int x = __float_as_int(v[0]);
+                const auto r = (M == 16) ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
+                                         : __builtin_amdgcn_permlane32_swap(x, x, false, false);
+                v[0] = __int_as_float((int)r[0]) + __int_as_float((int)r[1]);
+            } else {
+                v[0] += xpartner<M>(v[0]);
+            }
             group_reduce_scatter<1, M / 2, N>(v, lane, off);
         }
     }

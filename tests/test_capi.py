@@ -164,3 +164,12 @@ def test_unpack_debug_rejects_bad_arguments(B):
     assert call(t1=wl.ctx + 2) == 1
     assert call(batch=5) == 1
     assert call(out=A + 4) == 3
+
+
+def test_stream_read_rejects_bad_arguments(B):
+    f = B._lib.rq_stream_read
+    assert f(None, 1 << 20, A, 1 << 20, None) == 1
+    assert f(A, 0, A, 1 << 20, None) == 1
+    assert f(A, 100, A, 1 << 20, None) == 1
+    assert f(A + 8, 1 << 20, A, 1 << 20, None) == 3
+    assert f(A, 1 << 20, A, (1 << 20) - 1, None) == 4
