@@ -233,6 +233,16 @@ __device__ __forceinline__ void prio_by_progress(int done, int total) {
     }
 }
 
+// Within one workgroup whose waves pair up on the SIMDs (wave w with wave w + NW/2), the
+// upper half of the wave ids are the younger waves, which lose every tie in issue.  The
+// younger wave gets the higher priority on every other step and the lower one in between,
+// so the two waves of a SIMD advance at about the same rate.  Wave-uniform arguments.
+__device__ __forceinline__ void prio_alternate(bool younger, int step) {
+    if (!younger) __builtin_amdgcn_s_setprio(1);
+    else if (step % 2 == 0) __builtin_amdgcn_s_setprio(2);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
 // True in every lane if any lane of the wave has pred set.
 __device__ __forceinline__ bool wave_any(bool pred) { return __builtin_amdgcn_ballot_w64(pred) != 0; }
 

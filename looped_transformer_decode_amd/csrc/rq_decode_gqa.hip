@@ -446,7 +446,7 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
     const float sm_scale = a.sm_scale;
 
     for (int it = 0; it < n_it; ++it) {
-        if (it % 2 == 0) prio_by_progress(it, n_it);
+        if (it % 2 == 0) prio_alternate(w >= NW / 2, it / 2);
         if (it + NB - 1 < n_it) issue(it + NB - 1);
         wait_pass(min(NB - 1, n_it - 1 - it));
         const uint8_t* sp = &sm.ring[w][it % NB][0];
@@ -617,30 +617,37 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
         }
     }
     __syncthreads();
-    float sc_w[G];                                        // this wave's scale per query
-    float m_wg[G], l_wg[G];
+    // workgroup maximum per query, and this wave's scale towards it (the denominators are
+    // only needed by the threads that publish them, below)
+    float sc_w[G], m_wg[G];
 #pragma unroll
     for (int q = 0; q < G; ++q) {
         m_wg[q] = -INFINITY;
 #pragma unroll
         for (int i = 0; i < NW; ++i) m_wg[q] = fmaxf(m_wg[q], sm.mw[i][q]);
-        l_wg[q] = 0.f;
-#pragma unroll
-        for (int i = 0; i < NW; ++i) {
-            const float f = sm.mw[i][q] == -INFINITY ? 0.f : __expf(sm.mw[i][q] - m_wg[q]);
-            l_wg[q] += f * sm.lw[i][q];
-            if (i == w) sc_w[q] = f;
-        }
+        const float mw = sm.mw[w][q];
+        sc_w[q] = mw == -INFINITY ? 0.f : __expf(mw - m_wg[q]);
     }
     // values of lanes 0..15 (rows = queries) -> scr[w][q][channel], plus the offsets
     if (kg == 0) {
+        // every offset first: the stores below go to the same array, and reads placed
+        // after them would each wait for the store before
+        float za[G][NG], zr[G][NG];
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                za[q][gi] = zsc[((w * 2 + 0) * G + q) * NG + gi];
+                zr[q][gi] = NRES > 0 ? zsc[((w * 2 + 1) * G + q) * NG + gi] : 0.f;
+            }
+        }
 #pragma unroll
         for (int q = 0; q < G; ++q) {
             float* dst = scr + ((w * G) + q) * 2 * D;
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) {
-                const int c = 16 * nb + l16;
-                dst[c] = (va[nb][q] + zsc[((w * 2 + 0) * G + q) * NG + c / GS]) * sc_w[q];
+                const int c = 16 * nb + l16;                  // channel group c / GS = 16 nb / GS
+                dst[c] = (va[nb][q] + za[q][16 * nb / GS]) * sc_w[q];
             }
             if constexpr (NRES > 0) {
 #pragma unroll
@@ -648,7 +655,7 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
                     const int chunk = nb >> 1, par = nb & 1;
                     const int c = GS * chunk + 2 * l16 + par;
                     const float v = par ? vr[nb][q] * 0.25f : vr[nb][q];
-                    dst[D + c] = (v + zsc[((w * 2 + 1) * G + q) * NG + chunk]) * sc_w[q];
+                    dst[D + c] = (v + zr[q][chunk]) * sc_w[q];
                 }
             }
         }
@@ -664,9 +671,16 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
         st_agent(a.mg.partials + ((int64_t)(bh0 + q) * kMaxSplits + split) * (2 * D + 4) + c, v);
     }
     if (threadIdx.x < G) {
-        float* rec = a.mg.partials + ((int64_t)(bh0 + threadIdx.x) * kMaxSplits + split) * (2 * D + 4);
-        st_agent(rec + 2 * D, m_wg[threadIdx.x]);
-        st_agent(rec + 2 * D + 1, l_wg[threadIdx.x]);
+        const int q = threadIdx.x;
+        float m_q = -INFINITY, l_q = 0.f;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) m_q = fmaxf(m_q, sm.mw[i][q]);
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+            if (sm.mw[i][q] != -INFINITY) l_q += __expf(sm.mw[i][q] - m_q) * sm.lw[i][q];
+        float* rec = a.mg.partials + ((int64_t)(bh0 + q) * kMaxSplits + split) * (2 * D + 4);
+        st_agent(rec + 2 * D, m_q);
+        st_agent(rec + 2 * D + 1, l_q);
     }
     if (!splitk_arrive(a.mg, bh0)) return;
     merge_group<G, (NRES > 0)>(a.mg, bh0, sm.sq, reinterpret_cast<float*>(&sm.ring[0][0][0]));
