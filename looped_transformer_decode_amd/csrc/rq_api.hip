@@ -1,6 +1,8 @@
 // C ABI of librq.so: argument validation on the host, then kernel launches.
 #include <string.h>
 
+#include <atomic>
+
 #include "rq_args.hpp"
 
 namespace rq {
@@ -45,11 +47,24 @@ bool make_geom(const rq_config* c, Geom* g) {
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Compute units of the current device (queried once per device; 256 on MI355X).
+static int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 // Split-K factor: about two workgroups per CU (4 waves each) in flight, and at least four
 // 64-token tiles per workgroup so that its prologue (queries, R_K q) and epilogue (wave
 // merge, R_V^T) stay small next to its stream.
 // rows = independent (batch row, head) units of the grid; target = workgroups wanted
-static int auto_splits(int rows, int n_tiles, int target = 512) {
+static int auto_splits(int rows, int n_tiles, int target) {
     if (n_tiles <= 0) return 1;
     int s = (target + rows - 1) / rows;
     const int by_tiles = n_tiles / 4 > 0 ? n_tiles / 4 : 1;
@@ -164,8 +179,10 @@ rq_status rq_decode_attention(const rq_config* cfg, const void* cache, int32_t l
     const int n_tiles = (ctx_bound + kTile - 1) / kTile;
     // the grouped-query kernel runs one workgroup per KV head and split (one per CU)
     const bool grouped = gqa_supported(g, nres);
+    const int n_cu = device_cu_count();
     int S = n_splits ? n_splits
-                     : (grouped ? auto_splits(batch * g.hkv, n_tiles, 256) : auto_splits(batch * g.hq, n_tiles));
+                     : (grouped ? auto_splits(batch * g.hkv, n_tiles, n_cu)
+                                : auto_splits(batch * g.hq, n_tiles, 2 * n_cu));
     if (n_tiles > 0 && S > n_tiles) S = n_tiles;
     if (S < 1) S = 1;
     DecodeArgs a;
@@ -181,6 +198,7 @@ rq_status rq_decode_attention(const rq_config* cfg, const void* cache, int32_t l
     a.batch = batch;
     a.n_splits = S;
     a.tiles_per_split = n_tiles > 0 ? (n_tiles + S - 1) / S : 0;
+    a.n_cu = n_cu;
     MergeArgs& m = a.mg;
     m.partials = static_cast<float*>(workspace);
     m.arrivals = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + records_bytes(g.max_batch, g.hq, g.d));
@@ -218,7 +236,8 @@ rq_status rq_bf16_decode_attention(const rq_bf16_config* cfg, uint16_t* k_cache,
     const size_t need = workspace_bytes(cfg->max_batch, n_q_heads, head_dim);
     if (!workspace || workspace_bytes_ < need) return RQ_ERR_WORKSPACE;
     const int n_tiles = (ctx_bound + kTile - 1) / kTile;
-    int S = n_splits ? n_splits : auto_splits(batch * n_q_heads, n_tiles);
+    const int n_cu = device_cu_count();
+    int S = n_splits ? n_splits : auto_splits(batch * n_q_heads, n_tiles, 2 * n_cu);
     if (n_tiles > 0 && S > n_tiles) S = n_tiles;
     if (S < 1) S = 1;
     Bf16Args a;
@@ -235,6 +254,7 @@ rq_status rq_bf16_decode_attention(const rq_bf16_config* cfg, uint16_t* k_cache,
     a.batch = batch;
     a.n_splits = S;
     a.tiles_per_split = n_tiles > 0 ? (n_tiles + S - 1) / S : 0;
+    a.n_cu = n_cu;
     MergeArgs& m = a.mg;
     m.partials = static_cast<float*>(workspace);
     m.arrivals = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) +

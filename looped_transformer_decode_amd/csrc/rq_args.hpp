@@ -50,6 +50,7 @@ struct DecodeArgs {
     int batch;
     int n_splits;
     int tiles_per_split;
+    int n_cu;                   // compute units of the device (workgroup pairing on a CU)
     MergeArgs mg;
 };
 
@@ -65,6 +66,7 @@ struct Bf16Args {
     int batch;
     int n_splits;
     int tiles_per_split;
+    int n_cu;
     MergeArgs mg;
 };
 

@@ -23,6 +23,9 @@ __global__ __launch_bounds__(kThreads) void rq_bf16_decode_kernel(Bf16Args a) {
     const int h = hq / (a.hq / a.hkv);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int chunk = lane % LPT, slot = lane / LPT;
+    const bool younger = younger_on_cu(a.n_cu);
+    if (younger) __builtin_amdgcn_s_setprio(2);
+    else __builtin_amdgcn_s_setprio(1);
 
     __shared__ float sq[D];
     __shared__ SplitSmem<D> sm;
@@ -108,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void rq_bf16_decode_kernel(Bf16Args a) {
     };
 
     for (int it = 0; it < n_it; it += 2) {
-        if (it % PPT == 0) prio_by_progress(it, n_it);
+        if (it % PPT == 0) prio_alternate(younger, it / PPT);
         if (it + 1 < n_it) load(fb, it + 1);
         compute(fa, it);
         if (it + 1 < n_it) {

@@ -219,28 +219,22 @@ __device__ __forceinline__ float group_sum_dpp(float v) {
 // when a score exceeds it by more than this slack (natural-log units; p <= e^8).
 constexpr float kRescaleSlack = 8.0f;
 
-// Two workgroups share each CU and their waves pair up on the SIMDs, where the older wave
-// wins instruction issue.  With equal work the younger one would finish late and run
-// alone at the end; giving issue priority to the wave with less of its loop done keeps
-// the pair in step.  Called with wave-uniform arguments.
-__device__ __forceinline__ void prio_by_progress(int done, int total) {
-    const int quarter = total > 0 ? (4 * done) / total : 3;
-    switch (quarter) {
-        case 0: __builtin_amdgcn_s_setprio(3); break;
-        case 1: __builtin_amdgcn_s_setprio(2); break;
-        case 2: __builtin_amdgcn_s_setprio(1); break;
-        default: __builtin_amdgcn_s_setprio(0); break;
-    }
-}
-
-// Within one workgroup whose waves pair up on the SIMDs (wave w with wave w + NW/2), the
-// upper half of the wave ids are the younger waves, which lose every tie in issue.  The
-// younger wave gets the higher priority on every other step and the lower one in between,
-// so the two waves of a SIMD advance at about the same rate.  Wave-uniform arguments.
+// Two waves that share a SIMD (wave w and w + NW/2 of one workgroup, or two workgroups
+// on one CU) advance at different rates because the older one wins every tie in issue.
+// The younger one gets the higher priority on every other step and the lower one in
+// between, so the pair advances at about the same rate.  Wave-uniform arguments.
 __device__ __forceinline__ void prio_alternate(bool younger, int step) {
     if (!younger) __builtin_amdgcn_s_setprio(1);
     else if (step % 2 == 0) __builtin_amdgcn_s_setprio(2);
     else __builtin_amdgcn_s_setprio(0);
+}
+
+// A grid of at most two workgroups per CU is dispatched one per CU first, so block b and
+// block b + n_cu share a CU and the second is the younger one (it loses ties in issue to
+// the first).  False when that pairing does not hold (one workgroup per CU, or more than
+// two rounds), where no side is favoured.
+__device__ __forceinline__ bool younger_on_cu(int n_cu) {
+    return n_cu > 0 && (int)gridDim.x > n_cu && (int)gridDim.x <= 2 * n_cu && (int)blockIdx.x >= n_cu;
 }
 
 // True in every lane if any lane of the wave has pred set.

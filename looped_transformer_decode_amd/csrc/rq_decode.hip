@@ -175,6 +175,9 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
     const int h = hq / (G.hq / G.hkv);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int chunk = lane % LPT, slot = lane / LPT;
+    const bool younger = younger_on_cu(a.n_cu);
+    if (younger) __builtin_amdgcn_s_setprio(2);        // it also fetches its prologue second
+    else __builtin_amdgcn_s_setprio(1);
 
     __shared__ SplitSmem<D> sm;
     __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][NB][PASS];
@@ -483,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
 
     // ---- main loop: NB-1 passes in flight while one is computed from LDS
     for (int it = 0; it < n_it; ++it) {
-        if (it % PPT == 0) prio_by_progress(it, n_it);
+        if (it % PPT == 0) prio_alternate(younger, it / PPT);
         if (it + NB - 1 < n_it) issue(it + NB - 1);
         wait_pass(min(NB - 1, n_it - 1 - it));
         compute(it);
