@@ -110,9 +110,8 @@ struct QOut {
     double z, s;
 };
 
-template <int G>
-__device__ __forceinline__ QOut quantize_lane(double x, int bits) {
-    const double lo = group_min<2 * G>(x), hi = group_max<2 * G>(x);
+// offset and scale of a group with minimum lo and maximum hi (code left unset)
+__device__ __forceinline__ QOut group_params(double lo, double hi, int bits) {
     const double n = (double)((1 << bits) - 1);
     QOut o;
     o.zb = e4m3_floor_byte(lo);
@@ -123,8 +122,19 @@ __device__ __forceinline__ QOut quantize_lane(double x, int bits) {
     if (sb < 0x7Eu && o.z + n * e4m3_value(sb) < hi) ++sb;
     o.sb = sb;
     o.s = e4m3_value(sb);
+    o.code = 0;
+    return o;
+}
+
+__device__ __forceinline__ uint32_t group_code(double x, const QOut& o, int bits) {
     const double t = rint((x - o.z) / o.s);
-    o.code = (uint32_t)fmin(fmax(t, 0.0), n);
+    return (uint32_t)fmin(fmax(t, 0.0), (double)((1 << bits) - 1));
+}
+
+template <int G>
+__device__ __forceinline__ QOut quantize_lane(double x, int bits) {
+    QOut o = group_params(group_min<2 * G>(x), group_max<2 * G>(x), bits);
+    o.code = group_code(x, o, bits);
     return o;
 }
 
@@ -339,6 +349,288 @@ __global__ __launch_bounds__(2 * D) void rq_pack_kernel(PackArgs a) {
     }
 }
 
+// ---- bulk pack: many tokens of one (row, KV head, K|V) per workgroup
+//
+// For a prefilled context the token-at-a-time chain above leaves the chip idle.  Here a
+// workgroup takes kBulkTokens tokens: the quantizers and the c dot products run one token
+// per wave (lane = D/64 consecutive channels), and the rotations of all residual loops of
+// all its tokens form one product R Y (D x D times D x (tokens x loops)) read from LDS
+// with register tiles.  Same float64 arithmetic and the same decisions as the kernel
+// above; only the order of the additions inside the dot products differs.
+constexpr int kBulkTokens = 16;
+// threads per workgroup: 8 waves (two per SIMD, to hide each other's latency) at D = 128
+template <int D>
+constexpr int bulk_threads() { return D == 128 ? 512 : 256; }
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// reduction over aligned groups of NL lanes (a power of two up to 64); every lane of the
+// group gets the same value (both lanes of a pair combine the same two operands)
+template <int NL, int M = 1, class Op>
+__device__ __forceinline__ double lanes_reduce(double v, Op op) {
+    if constexpr (M >= NL) {
+        return v;
+    } else if constexpr (M == 16 || M == 32) {
+        const uint64_t u = (uint64_t)__double_as_longlong(v);
+        const int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
+        const auto rl = (M == 16) ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                                  : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+        const auto rh = (M == 16) ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                                  : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+        const double p = __longlong_as_double((long long)(((uint64_t)(uint32_t)rh[0] << 32) | (uint32_t)rl[0]));
+        const double q = __longlong_as_double((long long)(((uint64_t)(uint32_t)rh[1] << 32) | (uint32_t)rl[1]));
+        return lanes_reduce<NL, 2 * M>(op(p, q), op);
+    } else {
+        constexpr int CTRL = M == 1 ? kDppQuadXor1 : M == 2 ? kDppQuadXor2 : M == 4 ? kDppRowHalfMirror : kDppRowMirror;
+        return lanes_reduce<NL, 2 * M>(op(v, dpp_d<CTRL>(v)), op);
+    }
+}
+
+// OR over aligned groups of NL <= 16 lanes
+template <int NL, int M = 1>
+__device__ __forceinline__ uint32_t lanes_or(uint32_t v) {
+    static_assert(NL <= 16, "within a DPP row");
+    if constexpr (M >= NL) {
+        return v;
+    } else {
+        constexpr int CTRL = M == 1 ? kDppQuadXor1 : M == 2 ? kDppQuadXor2 : M == 4 ? kDppRowHalfMirror : kDppRowMirror;
+        return lanes_or<NL, 2 * M>(v | dpp_u<CTRL>(v));
+    }
+}
+
+// Quantize the CPL channels of this lane (channels CPL*lane + c of one token, one wave per
+// token) with groups of G channels; store codes and metadata into token row jj of `tile`
+// when `store`; return the dequantized values.
+template <int G, int CPL, int BITS>
+__device__ __forceinline__ void quantize_row(const double (&x)[CPL], double (&xhat)[CPL], uint8_t* tile, int row_bytes,
+                                             int m_row, int jj, bool store, int lane) {
+    constexpr int GL = G / CPL;                       // lanes per group
+    double lo = x[0], hi = x[0];
+#pragma unroll
+    for (int c = 1; c < CPL; ++c) {
+        lo = fmin(lo, x[c]);
+        hi = fmax(hi, x[c]);
+    }
+    lo = lanes_reduce<GL>(lo, [](double p, double q) { return fmin(p, q); });
+    hi = lanes_reduce<GL>(hi, [](double p, double q) { return fmax(p, q); });
+    const QOut o = group_params(lo, hi, BITS);
+    constexpr int PER = 32 / BITS;                    // channels per code word
+    uint32_t word = 0;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+        const uint32_t code = group_code(x[c], o, BITS);
+        xhat[c] = o.z + (double)code * o.s;
+        word |= code << (((CPL * lane + c) % PER) * BITS);
+    }
+    word = lanes_or<PER / CPL>(word);
+    if (store) {
+        if ((CPL * lane) % PER == 0)
+            reinterpret_cast<uint32_t*>(tile + (int64_t)jj * row_bytes)[(CPL * lane) / PER] = word;
+        if ((CPL * lane) % G == 0)
+            reinterpret_cast<uint16_t*>(tile + (int64_t)kTile * row_bytes + (int64_t)jj * m_row)[(CPL * lane) / G] =
+                (uint16_t)(o.zb | (o.sb << 8));
+    }
+}
+
+template <int D, int G, int LR>
+__global__ __launch_bounds__(bulk_threads<D>()) void rq_pack_bulk_kernel(PackArgs a) {
+    constexpr int kBulkThreads = bulk_threads<D>();
+    constexpr int TK = kBulkTokens, NW = kBulkThreads / kWave;
+    constexpr int CPL = D / kWave;                    // channels per lane
+    constexpr int LB = LR < 3 ? LR : 3;               // residual loops per product
+    constexpr int NCOL = TK * LB;                     // columns of Y: (token, loop)
+    constexpr int RB = D / 4, CB = kBulkThreads / RB, CPT = NCOL / CB;
+    static_assert(NCOL % CB == 0 && CPT >= 1 && TK % NW == 0, "register tile, tokens per wave");
+    constexpr int RS = D + 4;                         // padded LDS row of R (floats)
+    constexpr int L = LR + 1;
+    const Geom& Gm = a.geo;
+    int wg = blockIdx.x;
+    const int x = wg & 1;
+    wg >>= 1;
+    const int h = wg % Gm.hkv;
+    wg /= Gm.hkv;
+    const int b = wg % a.batch;
+    const int t0 = (wg / a.batch) * TK;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int loop0 = a.group_idx * L;
+
+    __shared__ __attribute__((aligned(16))) float rs[D * RS];      // R, row-major
+    __shared__ __attribute__((aligned(16))) double yt[D][NCOL];    // Y, then R Y: [channel][column]
+    __shared__ double ah[TK][D];                                   // dequantized anchors
+    __shared__ double aa[TK];                                      // <a_hat, a_hat>
+    __shared__ uint16_t xs[LB][TK][D];                             // BF16 inputs of the loops at hand
+
+    const float* R = a.rot + (int64_t)(h * 2 + x) * D * D;
+    for (int idx = threadIdx.x; idx < D * D / 4; idx += kBulkThreads) {
+        const int i = idx / (D / 4), k4 = idx % (D / 4);
+        *reinterpret_cast<float4*>(&rs[i * RS + 4 * k4]) = reinterpret_cast<const float4*>(R)[idx];
+    }
+
+    const int p0 = a.pos[b] + t0;
+    auto valid = [&](int tok) {
+        const int slot = p0 + tok;
+        return t0 + tok < a.n_tokens && slot >= 0 && slot < Gm.max_ctx;
+    };
+    // Stage the BF16 inputs of loops [l0, l0 + nl) of every token in xs (all loads in flight
+    // together); tokens that are not packed read as zero.
+    constexpr int PE = TK * D / kBulkThreads;         // elements per thread and loop
+    auto stage_x = [&](int l0, int nl) {
+        uint16_t v[LB][PE];
+#pragma unroll
+        for (int li = 0; li < LB; ++li) {
+#pragma unroll
+            for (int e = 0; e < PE; ++e) {
+                const int idx = e * kBulkThreads + threadIdx.x, i = idx % D, tok = idx / D;
+                v[li][e] = (li < nl && valid(tok))
+                               ? a.pending[(int64_t)(t0 + tok) * a.st[0] + (int64_t)b * a.st[1] +
+                                           (int64_t)(l0 + li) * a.st[2] + (int64_t)x * a.st[3] +
+                                           (int64_t)h * a.st[4] + i]
+                               : (uint16_t)0;
+            }
+        }
+#pragma unroll
+        for (int li = 0; li < LB; ++li)
+#pragma unroll
+            for (int e = 0; e < PE; ++e) {
+                const int idx = e * kBulkThreads + threadIdx.x;
+                xs[li][idx / D][idx % D] = v[li][e];
+            }
+    };
+    auto load_x = [&](int li, int tok, double (&v)[CPL]) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) v[c] = (double)bf16_to_f32(xs[li][tok][CPL * lane + c]);
+    };
+    const auto add = [](double p, double q) { return p + q; };
+
+    // ---- anchors: one token per wave
+    stage_x(L - 1, 1);
+    __syncthreads();
+    for (int s = 0; s < TK / NW; ++s) {
+        const int tok = s * NW + w;
+        const bool ok = valid(tok);                   // wave-uniform
+        const int slot = ok ? p0 + tok : 0, tile = slot / kTile, jj = slot % kTile;
+        double xa[CPL], xh[CPL];
+        load_x(0, tok, xa);
+        uint8_t* pl = a.cache + Gm.plane_offset(b, h, x, loop0 + L - 1) + tile * Gm.a_tile;
+        if (Gm.ba == 4) quantize_row<G, CPL, 4>(xa, xh, pl, Gm.a_row, Gm.m_row, jj, ok, lane);
+        else quantize_row<G, CPL, 2>(xa, xh, pl, Gm.a_row, Gm.m_row, jj, ok, lane);
+        double ss = 0.0;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            ss = fma(xh[c], xh[c], ss);
+            ah[tok][CPL * lane + c] = xh[c];
+        }
+        ss = lanes_reduce<kWave>(ss, add);
+        if (lane == 0) aa[tok] = ss;
+    }
+
+    for (int lb0 = 0; lb0 < LR; lb0 += LB) {
+        // ---- c and y = x - c a_hat of the loops [lb0, lb0 + LB), one token per wave
+        __syncthreads();                              // ah and aa written; xs and yt free
+        stage_x(lb0, LB < LR - lb0 ? LB : LR - lb0);
+        __syncthreads();
+        for (int s = 0; s < TK / NW; ++s) {
+            const int tok = s * NW + w;
+            const bool ok = valid(tok);
+            const int slot = ok ? p0 + tok : 0, tile = slot / kTile, jj = slot % kTile;
+            double xh[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) xh[c] = ah[tok][CPL * lane + c];
+            const double na = aa[tok];
+#pragma unroll
+            for (int li = 0; li < LB; ++li) {
+                const int l = lb0 + li;
+                const bool lok = ok && l < LR;
+                double xl[CPL];
+                load_x(li, tok, xl);
+                if (!lok) {
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) xl[c] = 0.0;
+                }
+                double dot = 0.0;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) dot = fma(xl[c], xh[c], dot);
+                dot = lanes_reduce<kWave>(dot, add);
+                const double cl = bf16_round(na > 0.0 ? dot / na : 0.0);
+                if (lok && lane == 0) {
+                    uint8_t* pl = a.cache + Gm.plane_offset(b, h, x, loop0 + l) + tile * Gm.r_tile;
+                    reinterpret_cast<uint16_t*>(pl + (int64_t)kTile * (Gm.r_row + Gm.m_row))[jj] =
+                        (uint16_t)(__float_as_uint((float)cl) >> 16);
+                }
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) yt[CPL * lane + c][tok * LB + li] = xl[c] - cl * xh[c];
+            }
+        }
+        __syncthreads();
+        // ---- r = R y for every column: thread tile of 4 rows x CPT columns
+        {
+            const int r0 = 4 * (threadIdx.x / CB), c0 = (threadIdx.x % CB) * CPT;
+            double acc[4][CPT];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int j = 0; j < CPT; ++j) acc[e][j] = 0.0;
+            for (int k4 = 0; k4 < D / 4; ++k4) {
+                float4 rr[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) rr[e] = *reinterpret_cast<const float4*>(&rs[(r0 + e) * RS + 4 * k4]);
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    double yv[CPT];
+#pragma unroll
+                    for (int j = 0; j < CPT; ++j) yv[j] = yt[4 * k4 + kk][c0 + j];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const double re = (double)(kk == 0 ? rr[e].x : kk == 1 ? rr[e].y : kk == 2 ? rr[e].z : rr[e].w);
+#pragma unroll
+                        for (int j = 0; j < CPT; ++j) acc[e][j] = fma(re, yv[j], acc[e][j]);
+                    }
+                }
+            }
+            __syncthreads();                          // every thread has read Y
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int j = 0; j < CPT; ++j) yt[r0 + e][c0 + j] = acc[e][j];
+        }
+        __syncthreads();
+        // ---- residual codes, one token per wave
+        for (int s = 0; s < TK / NW; ++s) {
+            const int tok = s * NW + w;
+            const bool ok = valid(tok);
+            const int slot = ok ? p0 + tok : 0, tile = slot / kTile, jj = slot % kTile;
+#pragma unroll
+            for (int li = 0; li < LB; ++li) {
+                const int l = lb0 + li;
+                double r[CPL], rh[CPL];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) r[c] = yt[CPL * lane + c][tok * LB + li];
+                uint8_t* pl = a.cache + Gm.plane_offset(b, h, x, loop0 + (l < LR ? l : 0)) + tile * Gm.r_tile;
+                quantize_row<G, CPL, 2>(r, rh, pl, Gm.r_row, Gm.m_row, jj, ok && l < LR, lane);
+            }
+        }
+    }
+}
+
+template <int D, int G>
+static hipError_t launch_bulk(const PackArgs& a, int nwg, hipStream_t stream) {
+    constexpr int kBulkThreads = bulk_threads<D>();
+    switch (a.geo.L - 1) {
+        case 1: hipLaunchKernelGGL((rq_pack_bulk_kernel<D, G, 1>), dim3(nwg), dim3(kBulkThreads), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((rq_pack_bulk_kernel<D, G, 2>), dim3(nwg), dim3(kBulkThreads), 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((rq_pack_bulk_kernel<D, G, 3>), dim3(nwg), dim3(kBulkThreads), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((rq_pack_bulk_kernel<D, G, 4>), dim3(nwg), dim3(kBulkThreads), 0, stream, a); break;
+        case 5: hipLaunchKernelGGL((rq_pack_bulk_kernel<D, G, 5>), dim3(nwg), dim3(kBulkThreads), 0, stream, a); break;
+        case 6: hipLaunchKernelGGL((rq_pack_bulk_kernel<D, G, 6>), dim3(nwg), dim3(kBulkThreads), 0, stream, a); break;
+        case 7: hipLaunchKernelGGL((rq_pack_bulk_kernel<D, G, 7>), dim3(nwg), dim3(kBulkThreads), 0, stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 template <int D, int G>
 static hipError_t launch_dg(const PackArgs& a, int nwg, hipStream_t stream) {
     switch (a.geo.L - 1) {
@@ -363,6 +655,11 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t stream) {
     if (!a.cache || !a.pending || !a.pos || !a.rot || a.batch < 1 || a.n_tokens < 1 || a.tokens_per_wg < 1 ||
         (a.geo.g != 16 && a.geo.g != 32) || (a.geo.d != 64 && a.geo.d != 128))
         return hipErrorInvalidValue;
+    if (!a.geo.chained && a.n_tokens >= kBulkTokens) {
+        const int nwg = (a.n_tokens + kBulkTokens - 1) / kBulkTokens * a.batch * a.geo.hkv * 2;
+        if (a.geo.d == 128) return a.geo.g == 32 ? launch_bulk<128, 32>(a, nwg, stream) : launch_bulk<128, 16>(a, nwg, stream);
+        return a.geo.g == 32 ? launch_bulk<64, 32>(a, nwg, stream) : launch_bulk<64, 16>(a, nwg, stream);
+    }
     const int nwg = (a.n_tokens + a.tokens_per_wg - 1) / a.tokens_per_wg * a.batch * a.geo.hkv * 2;
     return a.geo.d == 128 ? launch_d<128>(a, nwg, stream) : launch_d<64>(a, nwg, stream);
 }
