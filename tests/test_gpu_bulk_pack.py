@@ -1,0 +1,60 @@
+"""GPU parity of the many-token pack path (16 tokens per workgroup, used for 16 or more
+tokens with a shared anchor) on the cases the default workloads do not reach: 2, 6 and
+8 loops per anchor group (one, two and three residual batches of the rotation product,
+the last one partial), head_dim 64 and 128, INT4 and INT2 anchors, a token count that is
+not a multiple of 16, and a start slot so close to max_ctx that the last tokens have no
+slot (they must be skipped: nothing written, nothing else touched).  Every stored code,
+FP8 offset/scale and c is checked against the float64 oracle under the parity rules."""
+import numpy as np
+import pytest
+import torch
+
+from looped_transformer_decode_amd import synth
+from oracle import residualquant as RQ
+
+from _support import (assert_stats, check_encoding, device_block, gpu_pack, new_stats, oracle_cfg, say,
+                      slice_enc, sub_cache)
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+U = "uniform(0.8,1.0)"
+CASES = {
+    # name: (workload, batch, tokens, n_kv_heads, first slot, max_ctx or None)
+    "L2_d128g32": (W["ouro_b4_t8192"].with_(loops_per_group=2, loop_scale=U), 2, 100, 2, 0, None),
+    "L6_d128g16int2": (W["int2g16_b4_t16384"].with_(loops_per_group=6, loop_scale=U), 1, 70, 2, 0, None),
+    "L8_d64": (W["tiny_d64_t256"].with_(loops_per_group=8, loop_scale=U), 1, 40, 2, 0, None),
+    "past_max_ctx": (W["ouro_b4_t8192"], 2, 50, 1, 51, 96),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_bulk_pack_parity(name):
+    from looped_transformer_decode_amd import binding as B
+    wl, batch, T, hkv, pos0, max_ctx = CASES[name]
+    wl = wl.with_(batch=batch, ctx=T, n_kv_heads=hkv, n_q_heads=hkv)
+    max_ctx = max_ctx or pos0 + T
+    say(f"[bulk] case={name} tokens={T} first slot={pos0} max_ctx={max_ctx} L={wl.loops_per_group}")
+    inp = synth.generate(wl, seed=321, device="cuda")
+    cfg = B.config_for(wl, max_ctx=max_ctx)
+    ocfg = oracle_cfg(wl, max_ctx=max_ctx)
+    cache = gpu_pack(B, cfg, inp.kv, inp.rot, T, pos0=pos0)
+    torch.cuda.synchronize()
+    n = min(T, max_ctx - pos0)                      # tokens that have a slot
+    kv = inp.kv.double().cpu().numpy()
+    rot = inp.rot.double().cpu().numpy()
+    stats = new_stats()
+    for b in range(wl.batch):
+        for h in range(wl.n_kv_heads):
+            block = device_block(cache, ocfg, b, h)
+            _, sub = sub_cache(np.zeros(0, np.uint8), ocfg, b, h)
+            lay = RQ.Layout(sub)
+            for k in range(wl.n_groups):
+                for x in range(2):
+                    enc = RQ.read_tokens(block, lay, 0, 0, x, k, pos0 + n)
+                    check_encoding(slice_enc(enc, slice(pos0, pos0 + n)), kv[k, :, x, b, h, :n], rot[h, x], sub, stats)
+                    if pos0 > 0:                    # slots before the first one are untouched
+                        head = slice_enc(enc, slice(0, pos0))
+                        assert not np.any(head.anchor[0]) and not np.any(head.anchor[1])
+    say(f"[bulk] case={name} stats={stats}")
+    assert_stats(stats)
