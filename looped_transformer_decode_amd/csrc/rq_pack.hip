@@ -65,33 +65,36 @@ __device__ __forceinline__ double dpp_d(double v) {
     return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
 }
 
+// reduction over aligned groups of NL lanes (a power of two up to 64); every lane of the
+// group gets the same value (both lanes of a pair combine the same two operands)
+template <int NL, int M = 1, class Op>
+__device__ __forceinline__ double lanes_reduce(double v, Op op) {
+    if constexpr (M >= NL) {
+        return v;
+    } else if constexpr (M == 16 || M == 32) {
+        const uint64_t u = (uint64_t)__double_as_longlong(v);
+        const int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
+        const auto rl = (M == 16) ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                                  : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+        const auto rh = (M == 16) ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                                  : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+        const double p = __longlong_as_double((long long)(((uint64_t)(uint32_t)rh[0] << 32) | (uint32_t)rl[0]));
+        const double q = __longlong_as_double((long long)(((uint64_t)(uint32_t)rh[1] << 32) | (uint32_t)rl[1]));
+        return lanes_reduce<NL, 2 * M>(op(p, q), op);
+    } else {
+        constexpr int CTRL = M == 1 ? kDppQuadXor1 : M == 2 ? kDppQuadXor2 : M == 4 ? kDppRowHalfMirror : kDppRowMirror;
+        return lanes_reduce<NL, 2 * M>(op(v, dpp_d<CTRL>(v)), op);
+    }
+}
+
 // min / max over aligned groups of NL = 16, 32 or 64 lanes, result in every lane
 template <int NL>
 __device__ __forceinline__ double group_min(double v) {
-    v = fmin(v, dpp_d<kDppQuadXor1>(v));
-    v = fmin(v, dpp_d<kDppQuadXor2>(v));
-    v = fmin(v, dpp_d<kDppRowHalfMirror>(v));
-    v = fmin(v, dpp_d<kDppRowMirror>(v));
-    if constexpr (NL >= 32) v = fmin(v, shfl_xor_d(v, 16));
-    if constexpr (NL >= 64) v = fmin(v, shfl_xor_d(v, 32));
-    return v;
+    return lanes_reduce<NL>(v, [](double p, double q) { return fmin(p, q); });
 }
 template <int NL>
 __device__ __forceinline__ double group_max(double v) {
-    v = fmax(v, dpp_d<kDppQuadXor1>(v));
-    v = fmax(v, dpp_d<kDppQuadXor2>(v));
-    v = fmax(v, dpp_d<kDppRowHalfMirror>(v));
-    v = fmax(v, dpp_d<kDppRowMirror>(v));
-    if constexpr (NL >= 32) v = fmax(v, shfl_xor_d(v, 16));
-    if constexpr (NL >= 64) v = fmax(v, shfl_xor_d(v, 32));
-    return v;
-}
-__device__ __forceinline__ double row_sum(double v) {
-    v += dpp_d<kDppQuadXor1>(v);
-    v += dpp_d<kDppQuadXor2>(v);
-    v += dpp_d<kDppRowHalfMirror>(v);
-    v += dpp_d<kDppRowMirror>(v);
-    return v;
+    return lanes_reduce<NL>(v, [](double p, double q) { return fmax(p, q); });
 }
 
 // the two threads of a channel hold halves of a sum: both get the whole (a + b == b + a)
@@ -162,23 +165,24 @@ __device__ __forceinline__ void store_c(uint8_t* cblk, int jj, double c) {
 }
 
 // Sum over the channels of N float64 values per channel (each given by both threads of
-// the channel): DPP inside each 16-lane row, then the row sums through LDS, added in a
-// fixed order.  Every thread gets the sums.
+// the channel): DPP and half swaps inside each wave, then the wave sums through LDS,
+// added in a fixed order.  Every thread gets the sums.
 template <int NT, int N>
-__device__ __forceinline__ void block_sum(double (&v)[N], double (*red)[NT / 16]) {
+__device__ __forceinline__ void block_sum(double (&v)[N], double (*red)[NT / 64]) {
+    const auto add = [](double p, double q) { return p + q; };
 #pragma unroll
-    for (int k = 0; k < N; ++k) v[k] = row_sum((threadIdx.x & 1) ? 0.0 : v[k]);
+    for (int k = 0; k < N; ++k) v[k] = lanes_reduce<64>((threadIdx.x & 1) ? 0.0 : v[k], add);
     __syncthreads();                                    // red is reused
-    if ((threadIdx.x & 15) == 0) {
+    if ((threadIdx.x & 63) == 0) {
 #pragma unroll
-        for (int k = 0; k < N; ++k) red[k][threadIdx.x >> 4] = v[k];
+        for (int k = 0; k < N; ++k) red[k][threadIdx.x >> 6] = v[k];
     }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < N; ++k) {
         double s = 0.0;
 #pragma unroll
-        for (int r = 0; r < NT / 16; ++r) s += red[k][r];
+        for (int r = 0; r < NT / 64; ++r) s += red[k][r];
         v[k] = s;
     }
 }
@@ -233,14 +237,23 @@ __device__ __forceinline__ void rotate_all(const float (&rhalf)[D / 2], const do
 // One workgroup of 2 D threads per (token range, batch row, KV head, K|V): threads 2i
 // and 2i+1 own channel i and keep the two halves of row i of R in registers for all
 // tokens of the range.  LR = L - 1 residual loops.
-template <int D, int G, int LR>
+// SPLIT (shared anchor only): one residual loop per workgroup, selected by the block index;
+// every workgroup of a token quantizes the anchor, the one of loop 0 stores it.  This
+// shortens the chain of a single token (rotation and residual quantizer of one loop).
+template <int D, int G, int LR, bool SPLIT>
 __global__ __launch_bounds__(2 * D) void rq_pack_kernel(PackArgs a) {
     constexpr int L = LR + 1;
+    constexpr int NL = SPLIT ? 1 : LR;                 // residual loops of this workgroup
     constexpr int NT = 2 * D;
     constexpr int H = D / 2;
     const Geom& Gm = a.geo;
     const int i = threadIdx.x >> 1, p = threadIdx.x & 1;
     int wg = blockIdx.x;
+    int lsel = 0;
+    if constexpr (SPLIT) {
+        lsel = wg % LR;
+        wg /= LR;
+    }
     const int x = wg & 1;
     wg >>= 1;
     const int h = wg % Gm.hkv;
@@ -251,8 +264,8 @@ __global__ __launch_bounds__(2 * D) void rq_pack_kernel(PackArgs a) {
     const int loop0 = a.group_idx * L;
     const float* R = a.rot + (int64_t)(h * 2 + x) * D * D;
 
-    __shared__ double sh_y[LR > 1 ? LR : 2][D];
-    __shared__ double red[L > 2 ? L : 2][NT / 16];
+    __shared__ double sh_y[NL > 1 ? NL : 2][D];
+    __shared__ double red[NL + 1 > 2 ? NL + 1 : 2][NT / 64];
 
     float rhalf[H];                                    // R[i][H p + k]
     {
@@ -273,14 +286,15 @@ __global__ __launch_bounds__(2 * D) void rq_pack_kernel(PackArgs a) {
         if (slot < 0 || slot >= Gm.max_ctx) continue;  // same for the whole workgroup
         const int tile = slot / kTile, jj = slot % kTile;
 
-        double xv[L];
+        // xv[0..NL): the residual loops of this workgroup; xv[NL]: the anchor (the group's last loop)
+        double xv[NL + 1];
         const uint16_t* src = a.pending + t * a.st[0] + b * a.st[1] + x * a.st[3] + h * a.st[4] + i;
 #pragma unroll
-        for (int l = 0; l < L; ++l) xv[l] = (double)bf16_to_f32(src[l * a.st[2]]);
+        for (int l = 0; l < NL; ++l) xv[l] = (double)bf16_to_f32(src[(int64_t)(SPLIT ? lsel : l) * a.st[2]]);
+        xv[NL] = (double)bf16_to_f32(src[(int64_t)(L - 1) * a.st[2]]);
 
-        // anchor: the group's last loop
-        const QOut qa = quantize_lane<G>(xv[L - 1], Gm.ba);
-        {
+        const QOut qa = quantize_lane<G>(xv[NL], Gm.ba);
+        if (!SPLIT || lsel == 0) {
             uint8_t* pl = a_plane + tile * Gm.a_tile;
             store_codes(pl + jj * Gm.a_row, qa.code, Gm.ba);
             store_meta(pl + kTile * Gm.a_row + jj * Gm.m_row, qa, Gm.g);
@@ -290,32 +304,32 @@ __global__ __launch_bounds__(2 * D) void rq_pack_kernel(PackArgs a) {
         if (!Gm.chained) {
             // every loop l < L-1 references a_hat: one reduction gives all <x_l, a> and
             // <a, a>; the loops are rotated together and then quantized side by side
-            double sums[L];
+            double sums[NL + 1];
 #pragma unroll
-            for (int l = 0; l < LR; ++l) sums[l] = xv[l] * a_hat;
-            sums[LR] = a_hat * a_hat;
-            block_sum<NT, L>(sums, red);
-            double cs[LR];
+            for (int l = 0; l < NL; ++l) sums[l] = xv[l] * a_hat;
+            sums[NL] = a_hat * a_hat;
+            block_sum<NT, NL + 1>(sums, red);
+            double cs[NL];
 #pragma unroll
-            for (int l = 0; l < LR; ++l) {
-                cs[l] = bf16_round(sums[LR] > 0.0 ? sums[l] / sums[LR] : 0.0);
+            for (int l = 0; l < NL; ++l) {
+                cs[l] = bf16_round(sums[NL] > 0.0 ? sums[l] / sums[NL] : 0.0);
                 if (p == 0) sh_y[l][i] = xv[l] - cs[l] * a_hat;
             }
             __syncthreads();
-            double rl[LR];
-            rotate_all<D, LR>(rhalf, sh_y, p, rl);
-            QOut qr[LR];
+            double rl[NL];
+            rotate_all<D, NL>(rhalf, sh_y, p, rl);
+            QOut qr[NL];
 #pragma unroll
-            for (int l = 0; l < LR; ++l) qr[l] = quantize_lane<G>(rl[l], Gm.br);
+            for (int l = 0; l < NL; ++l) qr[l] = quantize_lane<G>(rl[l], Gm.br);
 #pragma unroll
-            for (int l = 0; l < LR; ++l) {
-                uint8_t* pl = a.cache + Gm.plane_offset(b, h, x, loop0 + l) + tile * Gm.r_tile;
+            for (int l = 0; l < NL; ++l) {
+                uint8_t* pl = a.cache + Gm.plane_offset(b, h, x, loop0 + (SPLIT ? lsel : l)) + tile * Gm.r_tile;
                 store_codes(pl + jj * Gm.r_row, qr[l].code, Gm.br);
                 store_meta(pl + kTile * Gm.r_row + jj * Gm.m_row, qr[l], Gm.g);
                 store_c(pl + kTile * (Gm.r_row + Gm.m_row), jj, cs[l]);
             }
             __syncthreads();                              // sh_y is reused by the next token
-        } else {
+        } else if constexpr (!SPLIT) {
             // loop l references the rebuilt loop l+1 (the anchor closes the chain)
             double ref = a_hat;
             for (int l = L - 2; l >= 0; --l) {
@@ -365,28 +379,6 @@ constexpr int bulk_threads() { return D == 128 ? 512 : 256; }
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
-}
-
-// reduction over aligned groups of NL lanes (a power of two up to 64); every lane of the
-// group gets the same value (both lanes of a pair combine the same two operands)
-template <int NL, int M = 1, class Op>
-__device__ __forceinline__ double lanes_reduce(double v, Op op) {
-    if constexpr (M >= NL) {
-        return v;
-    } else if constexpr (M == 16 || M == 32) {
-        const uint64_t u = (uint64_t)__double_as_longlong(v);
-        const int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
-        const auto rl = (M == 16) ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
-                                  : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-        const auto rh = (M == 16) ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
-                                  : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-        const double p = __longlong_as_double((long long)(((uint64_t)(uint32_t)rh[0] << 32) | (uint32_t)rl[0]));
-        const double q = __longlong_as_double((long long)(((uint64_t)(uint32_t)rh[1] << 32) | (uint32_t)rl[1]));
-        return lanes_reduce<NL, 2 * M>(op(p, q), op);
-    } else {
-        constexpr int CTRL = M == 1 ? kDppQuadXor1 : M == 2 ? kDppQuadXor2 : M == 4 ? kDppRowHalfMirror : kDppRowMirror;
-        return lanes_reduce<NL, 2 * M>(op(v, dpp_d<CTRL>(v)), op);
-    }
 }
 
 // OR over aligned groups of NL <= 16 lanes
@@ -631,19 +623,28 @@ static hipError_t launch_bulk(const PackArgs& a, int nwg, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int D, int G>
-static hipError_t launch_dg(const PackArgs& a, int nwg, hipStream_t stream) {
-    switch (a.geo.L - 1) {
-        case 1: hipLaunchKernelGGL((rq_pack_kernel<D, G, 1>), dim3(nwg), dim3(2 * D), 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((rq_pack_kernel<D, G, 2>), dim3(nwg), dim3(2 * D), 0, stream, a); break;
-        case 3: hipLaunchKernelGGL((rq_pack_kernel<D, G, 3>), dim3(nwg), dim3(2 * D), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((rq_pack_kernel<D, G, 4>), dim3(nwg), dim3(2 * D), 0, stream, a); break;
-        case 5: hipLaunchKernelGGL((rq_pack_kernel<D, G, 5>), dim3(nwg), dim3(2 * D), 0, stream, a); break;
-        case 6: hipLaunchKernelGGL((rq_pack_kernel<D, G, 6>), dim3(nwg), dim3(2 * D), 0, stream, a); break;
-        case 7: hipLaunchKernelGGL((rq_pack_kernel<D, G, 7>), dim3(nwg), dim3(2 * D), 0, stream, a); break;
+template <int D, int G, bool SPLIT>
+static hipError_t launch_dgs(const PackArgs& a, int nwg, hipStream_t stream) {
+    const int LR = a.geo.L - 1;
+    const dim3 grid(SPLIT ? nwg * LR : nwg);
+    switch (LR) {
+        case 1: hipLaunchKernelGGL((rq_pack_kernel<D, G, 1, SPLIT>), grid, dim3(2 * D), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((rq_pack_kernel<D, G, 2, SPLIT>), grid, dim3(2 * D), 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((rq_pack_kernel<D, G, 3, SPLIT>), grid, dim3(2 * D), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((rq_pack_kernel<D, G, 4, SPLIT>), grid, dim3(2 * D), 0, stream, a); break;
+        case 5: hipLaunchKernelGGL((rq_pack_kernel<D, G, 5, SPLIT>), grid, dim3(2 * D), 0, stream, a); break;
+        case 6: hipLaunchKernelGGL((rq_pack_kernel<D, G, 6, SPLIT>), grid, dim3(2 * D), 0, stream, a); break;
+        case 7: hipLaunchKernelGGL((rq_pack_kernel<D, G, 7, SPLIT>), grid, dim3(2 * D), 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+// one residual loop per workgroup for a few tokens with a shared anchor (the per-step drain)
+template <int D, int G>
+static hipError_t launch_dg(const PackArgs& a, int nwg, hipStream_t stream) {
+    if (!a.geo.chained && a.tokens_per_wg == 1) return launch_dgs<D, G, true>(a, nwg, stream);
+    return launch_dgs<D, G, false>(a, nwg, stream);
 }
 
 template <int D>
