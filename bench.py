@@ -295,6 +295,30 @@ def main():
     bf16_ms = sum(a.elapsed_time(b) for a, b in bev) / len(bev)
     bf16_gbps = bf16_bytes(wl) / (bf16_ms * 1e-3) / 1e9
 
+    # With grouped queries the BF16 kernel above reads every KV tile once per query head. The
+    # same kernel with one query per KV head reads the same bytes once: a floor for any BF16
+    # kernel that shares the tile across the group (it reads as much and computes more).
+    bf16_once = None
+    if wl.n_q_heads > wl.n_kv_heads:
+        G = wl.n_q_heads // wl.n_kv_heads
+        bcfg1 = B.rq_bf16_config(d, wl.n_kv_heads, wl.n_kv_heads, Bt, T + 1)
+        bws1 = torch.zeros(B.rq_bf16_workspace_bytes(bcfg1), dtype=torch.uint8, device=dev)
+        q1 = [q[l][:, ::G].contiguous() for l in range(L)]
+        out1 = torch.empty(Bt, wl.n_kv_heads, d, dtype=torch.float32, device=dev)
+        for l in range(L):
+            B.rq_bf16_decode_attention(bcfg1, Ks[l], Vs[l], q1[l], k_cur[l], v_cur[l], False, ctx_len, T, sc, out1,
+                                       bws1, Bt, n_splits=args.splits, stream=stream)
+        b0_, b1_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(3, args.steps // 2) * L
+        b0_.record(stream)
+        for i in range(reps):
+            l = i % L
+            B.rq_bf16_decode_attention(bcfg1, Ks[l], Vs[l], q1[l], k_cur[l], v_cur[l], False, ctx_len, T, sc, out1,
+                                       bws1, Bt, n_splits=args.splits, stream=stream)
+        b1_.record(stream)
+        torch.cuda.synchronize()
+        bf16_once = b0_.elapsed_time(b1_) / reps
+
     # plain streaming read of the same replicas: the rate a simple load loop reaches here
     sink = torch.empty(B.STREAM_SINK_WORDS, dtype=torch.int32, device=dev)
     probe_bytes = res_bytes // 16 * 16
@@ -359,7 +383,10 @@ def main():
                              "gbps": round(anchor_bytes / (per_loop[L - 1] * 1e-3) / 1e9, 1)},
         "bf16": {"bytes": bf16_bytes(wl), "ms_per_loop_step": round(bf16_ms, 4), "gbps": round(bf16_gbps, 1),
                  "speedup_rq_residual_vs_bf16": round(bf16_ms / res_ms, 3),
-                 "speedup_rq_step_vs_bf16_step": round(bf16_ms * n_loops / ms_step, 3)},
+                 "speedup_rq_step_vs_bf16_step": round(bf16_ms * n_loops / ms_step, 3),
+                 **({"one_query_per_kv_head_ms": round(bf16_once, 4),
+                     "speedup_rq_residual_vs_bf16_one_query_per_kv_head": round(bf16_once / res_ms, 3)}
+                    if bf16_once is not None else {})},
         "bulk_pack": {"tokens": Bt * T, "ms": round(bulk_ms, 3),
                       "tokens_per_s": round(Bt * T / (bulk_ms * 1e-3), 1),
                       "bf16_in_bytes": bulk_in_bytes(wl), "gbps_in": round(bulk_in_bytes(wl) / (bulk_ms * 1e-3) / 1e9, 1),
