@@ -522,28 +522,35 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
             l_lane += p;
             // value weights from the V plane's metadata and coefficient: anchor p c s_a,
             // residual p s_r (zero for masked tokens), and the offsets
-            const uint2 vam = *reinterpret_cast<const uint2*>(vp + AC + t * MROW);
+            // a masked token's metadata and coefficient read as zero (its bytes may be anything,
+            // NaN patterns included), so with p = 0 every product below is an exact zero
+            uint2 vam = *reinterpret_cast<const uint2*>(vp + AC + t * MROW);
             uint2 vrm = {0u, 0u};
             float vcoef = 1.f;
             if constexpr (NRES > 0) {
                 vrm = *reinterpret_cast<const uint2*>(vp + RES_OFF + RC + t * MROW);
                 vcoef = bf16_to_f32(*reinterpret_cast<const uint16_t*>(vp + RES_OFF + RC + RM + t * 2));
             }
+            if (!valid) {
+                vam = uint2{0u, 0u};
+                vrm = uint2{0u, 0u};
+                vcoef = 0.f;
+            }
             const int pos = vpos(t);
             const float mult = (t & 1) ? (1.f / 16.f) : 1.f;
-            const float pc = valid ? p * vcoef : 0.f;
+            const float pc = p * vcoef;
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
                 const uint32_t mw = gi < 2 ? vam.x : vam.y;
                 const float za = fp8(mw, 2 * (gi & 1)), sa = fp8(mw, 2 * (gi & 1) + 1);
-                zA[gi] += valid ? pc * za : 0.f;
-                const float wa = valid ? pc * sa * mult : 0.f;
+                zA[gi] += pc * za;
+                const float wa = pc * sa * mult;
                 if (q_ok) sm.wbuf[w][0][gi][qs][pos] = (_Float16)wa;
                 if constexpr (NRES > 0) {
                     const uint32_t rw = gi < 2 ? vrm.x : vrm.y;
                     const float zr = fp8(rw, 2 * (gi & 1)), sr = fp8(rw, 2 * (gi & 1) + 1);
-                    zR[gi] += valid ? p * zr : 0.f;
-                    const float wr = valid ? p * sr * mult : 0.f;
+                    zR[gi] += p * zr;
+                    const float wr = p * sr * mult;
                     if (q_ok) sm.wbuf[w][1][gi][qs][pos] = (_Float16)wr;
                 }
             }
