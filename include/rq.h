@@ -195,6 +195,40 @@ rq_status rq_bf16_decode_attention(const rq_bf16_config* cfg, uint16_t* k_cache,
 rq_status rq_unpack_debug(const rq_config* cfg, const void* cache, int32_t loop, const float* rot,
                           int32_t t0, int32_t t1, int32_t batch, float* out, hipStream_t stream);
 
+/* Paged cache (vLLM-style block tables).  The same 64-token tiles live in a pool of
+ * physical blocks shared by all sequences.  One block holds one tile of every
+ * (KV head, K|V, anchor group, loop plane), laid out as [KV head][K|V][anchor group]
+ * [residual planes of loops 0..L-2 (tile bytes each), then the anchor plane's tile].
+ * Row b's logical tile t (token slots 64t..64t+63) lives in block
+ * block_table[b * table_stride + t].  The table is device data, so the host cannot check
+ * it: an entry outside [0, n_blocks) is clamped into range (giving wrong values, never an
+ * out-of-bounds access).  Rows must not share a block they write.
+ * The arguments not listed below are as for the contiguous entry points.
+ *   pool         : device, n_blocks * rq_paged_block_bytes(cfg) bytes, 16-byte aligned.
+ *   n_blocks     : physical blocks in the pool, >= 1.
+ *   block_table  : device int32 [max_batch][table_stride], 4-byte aligned.
+ *   table_stride : entries per row, >= ceil(max_ctx / 64).
+ * Returns 0 bytes for an invalid or unsupported configuration. */
+size_t rq_paged_block_bytes(const rq_config* cfg);
+
+/* rq_quantize_token over a paged cache: same computation as rq_quantize_token; the tile
+ * of slot pos[b] + t is found through the block table. */
+rq_status rq_quantize_token_paged(const rq_config* cfg, void* pool, int32_t n_blocks,
+                                  const int32_t* block_table, int32_t table_stride,
+                                  const uint16_t* pending, const int64_t* pending_strides,
+                                  int32_t group_idx, const int32_t* pos, const float* rot,
+                                  int32_t batch, int32_t n_tokens, hipStream_t stream);
+
+/* rq_decode_attention over a paged cache: same computation and results as
+ * rq_decode_attention on a contiguous cache holding the same tiles. */
+rq_status rq_decode_attention_paged(const rq_config* cfg, const void* pool, int32_t n_blocks,
+                                    const int32_t* block_table, int32_t table_stride, int32_t loop,
+                                    const void* q, int32_t q_is_bf16,
+                                    const uint16_t* k_cur, const uint16_t* v_cur, uint16_t* pending,
+                                    const int32_t* ctx_len, int32_t ctx_bound, const float* rot,
+                                    float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                                    int32_t batch, int32_t n_splits, hipStream_t stream);
+
 /* rq_stream_read - a measuring stick, not part of the method: read `bytes` of `buf`
  * with plain 16-byte loads (one contiguous slab per workgroup, XOR-folded into one word
  * per thread of `sink`).  Timed over the same buffers as the decode kernel it gives the

@@ -22,7 +22,7 @@ _lib = ctypes.CDLL(_LIB_PATH)
 
 EXPORTS = ("rq_cache_bytes", "rq_workspace_bytes", "rq_bf16_workspace_bytes", "rq_status_str",
            "rq_quantize_token", "rq_decode_attention", "rq_bf16_decode_attention", "rq_unpack_debug",
-           "rq_stream_read")
+           "rq_stream_read", "rq_paged_block_bytes", "rq_quantize_token_paged", "rq_decode_attention_paged")
 
 
 class rq_config(ctypes.Structure):
@@ -66,6 +66,14 @@ _lib.rq_unpack_debug.argtypes = [_cfgp, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _
 _lib.rq_unpack_debug.restype = _i32
 _lib.rq_stream_read.argtypes = [_vp, _sz, _vp, _sz, _vp]
 _lib.rq_stream_read.restype = _i32
+_lib.rq_paged_block_bytes.argtypes = [_cfgp]
+_lib.rq_paged_block_bytes.restype = _sz
+_lib.rq_quantize_token_paged.argtypes = [_cfgp, _vp, _i32, _vp, _i32, _vp, ctypes.POINTER(ctypes.c_int64), _i32, _vp,
+                                         _vp, _i32, _i32, _vp]
+_lib.rq_quantize_token_paged.restype = _i32
+_lib.rq_decode_attention_paged.argtypes = [_cfgp, _vp, _i32, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _i32,
+                                           _vp, _f32, _vp, _vp, _sz, _i32, _i32, _vp]
+_lib.rq_decode_attention_paged.restype = _i32
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -145,6 +153,33 @@ def rq_unpack_debug(cfg: rq_config, cache: torch.Tensor, loop: int, rot: torch.T
                     batch: int, out: torch.Tensor, stream=None) -> None:
     _check("rq_unpack_debug", _lib.rq_unpack_debug(
         ctypes.byref(cfg), _ptr(cache), loop, _ptr(rot), t0, t1, batch, _ptr(out), _stream(stream)))
+
+
+def rq_paged_block_bytes(cfg: rq_config) -> int:
+    return int(_lib.rq_paged_block_bytes(ctypes.byref(cfg)))
+
+
+def rq_quantize_token_paged(cfg: rq_config, pool: torch.Tensor, n_blocks: int, block_table: torch.Tensor,
+                            pending: torch.Tensor, group_idx: int, pos: torch.Tensor, rot: torch.Tensor, batch: int,
+                            n_tokens: int = 1, pending_strides: Optional[Sequence[int]] = None, stream=None) -> None:
+    st = None
+    if pending_strides is not None:
+        st = (ctypes.c_int64 * 5)(*[int(s) for s in pending_strides])
+    _check("rq_quantize_token_paged", _lib.rq_quantize_token_paged(
+        ctypes.byref(cfg), _ptr(pool), n_blocks, _ptr(block_table), block_table.shape[1], _ptr(pending), st,
+        group_idx, _ptr(pos), _ptr(rot), batch, n_tokens, _stream(stream)))
+
+
+def rq_decode_attention_paged(cfg: rq_config, pool: torch.Tensor, n_blocks: int, block_table: torch.Tensor,
+                              loop: int, q: torch.Tensor, k_cur: torch.Tensor, v_cur: torch.Tensor,
+                              pending: Optional[torch.Tensor], ctx_len: torch.Tensor, ctx_bound: int,
+                              rot: torch.Tensor, sm_scale: float, out: torch.Tensor, workspace: torch.Tensor,
+                              batch: int, n_splits: int = 0, stream=None) -> None:
+    q_bf16 = 1 if q.dtype == torch.bfloat16 else 0
+    _check("rq_decode_attention_paged", _lib.rq_decode_attention_paged(
+        ctypes.byref(cfg), _ptr(pool), n_blocks, _ptr(block_table), block_table.shape[1], loop, _ptr(q), q_bf16,
+        _ptr(k_cur), _ptr(v_cur), _ptr(pending), _ptr(ctx_len), ctx_bound, _ptr(rot), sm_scale, _ptr(out),
+        _ptr(workspace), _nbytes(workspace), batch, n_splits, _stream(stream)))
 
 
 STREAM_SINK_WORDS = 1 << 20

@@ -42,6 +42,11 @@ bool make_geom(const rq_config* c, Geom* g) {
     g->group_bytes = (int64_t)g->n_tiles * (g->a_tile + (int64_t)(g->L - 1) * g->r_tile);
     g->block_bytes = (int64_t)g->n_groups * g->group_bytes;
     g->total = (int64_t)g->max_batch * g->hkv * 2 * g->block_bytes;
+    g->bt = nullptr;
+    g->bt_stride = 0;
+    g->n_blocks = 0;
+    g->g_tile = g->a_tile + (int64_t)(g->L - 1) * g->r_tile;
+    g->p_block = (int64_t)g->hkv * 2 * g->n_groups * g->g_tile;
     return true;
 }
 
@@ -114,12 +119,17 @@ const char* rq_status_str(rq_status s) {
     return "unknown status";
 }
 
-rq_status rq_quantize_token(const rq_config* cfg, void* cache, const uint16_t* pending,
-                            const int64_t* pending_strides, int32_t group_idx, const int32_t* pos,
-                            const float* rot, int32_t batch, int32_t n_tokens, hipStream_t stream) {
+// paging: bt == nullptr for the contiguous layout, else the block table (checked by the callers)
+static rq_status quantize_impl(const rq_config* cfg, void* cache, const int32_t* bt, int32_t bt_stride,
+                               int32_t n_blocks, const uint16_t* pending, const int64_t* pending_strides,
+                               int32_t group_idx, const int32_t* pos, const float* rot, int32_t batch,
+                               int32_t n_tokens, hipStream_t stream) {
     Geom g;
     if (cfg == nullptr) return RQ_ERR_INVALID_ARG;
     if (!make_geom(cfg, &g)) return RQ_ERR_UNSUPPORTED;
+    g.bt = bt;
+    g.bt_stride = bt_stride;
+    g.n_blocks = n_blocks;
     if (!cache || !pending || !pos || !rot) return RQ_ERR_INVALID_ARG;
     if (batch < 1 || batch > g.max_batch || n_tokens < 1) return RQ_ERR_INVALID_ARG;
     if (group_idx < 0 || group_idx >= g.n_groups) return RQ_ERR_INVALID_ARG;
@@ -152,15 +162,52 @@ rq_status rq_quantize_token(const rq_config* cfg, void* cache, const uint16_t* p
     return launch_pack(a, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 
-rq_status rq_decode_attention(const rq_config* cfg, const void* cache, int32_t loop, const void* q,
-                              int32_t q_is_bf16, const uint16_t* k_cur, const uint16_t* v_cur,
-                              uint16_t* pending, const int32_t* ctx_len, int32_t ctx_bound,
-                              const float* rot, float sm_scale, float* out, void* workspace,
-                              size_t workspace_bytes_, int32_t batch, int32_t n_splits,
-                              hipStream_t stream) {
+// table_stride >= tiles of max_ctx, n_blocks >= 1, table 4-byte aligned
+static rq_status paging_ok(const rq_config* cfg, int32_t n_blocks, const int32_t* table, int32_t table_stride) {
     Geom g;
     if (cfg == nullptr) return RQ_ERR_INVALID_ARG;
     if (!make_geom(cfg, &g)) return RQ_ERR_UNSUPPORTED;
+    if (!table || n_blocks < 1 || table_stride < g.n_tiles) return RQ_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(table) & 3u) return RQ_ERR_MISALIGNED;
+    if ((int64_t)g.max_batch * table_stride > 0x7FFFFFFFLL) return RQ_ERR_INVALID_ARG;
+    return RQ_OK;
+}
+
+rq_status rq_quantize_token(const rq_config* cfg, void* cache, const uint16_t* pending,
+                            const int64_t* pending_strides, int32_t group_idx, const int32_t* pos,
+                            const float* rot, int32_t batch, int32_t n_tokens, hipStream_t stream) {
+    return quantize_impl(cfg, cache, nullptr, 0, 0, pending, pending_strides, group_idx, pos, rot, batch, n_tokens,
+                         stream);
+}
+
+size_t rq_paged_block_bytes(const rq_config* cfg) {
+    Geom g;
+    if (!make_geom(cfg, &g)) return 0;
+    return (size_t)g.p_block;
+}
+
+rq_status rq_quantize_token_paged(const rq_config* cfg, void* pool, int32_t n_blocks, const int32_t* block_table,
+                                  int32_t table_stride, const uint16_t* pending, const int64_t* pending_strides,
+                                  int32_t group_idx, const int32_t* pos, const float* rot, int32_t batch,
+                                  int32_t n_tokens, hipStream_t stream) {
+    const rq_status st = paging_ok(cfg, n_blocks, block_table, table_stride);
+    if (st != RQ_OK) return st;
+    return quantize_impl(cfg, pool, block_table, table_stride, n_blocks, pending, pending_strides, group_idx, pos,
+                         rot, batch, n_tokens, stream);
+}
+
+static rq_status decode_impl(const rq_config* cfg, const void* cache, const int32_t* bt, int32_t bt_stride,
+                             int32_t n_blocks, int32_t loop, const void* q, int32_t q_is_bf16,
+                             const uint16_t* k_cur, const uint16_t* v_cur, uint16_t* pending,
+                             const int32_t* ctx_len, int32_t ctx_bound, const float* rot, float sm_scale,
+                             float* out, void* workspace, size_t workspace_bytes_, int32_t batch,
+                             int32_t n_splits, hipStream_t stream) {
+    Geom g;
+    if (cfg == nullptr) return RQ_ERR_INVALID_ARG;
+    if (!make_geom(cfg, &g)) return RQ_ERR_UNSUPPORTED;
+    g.bt = bt;
+    g.bt_stride = bt_stride;
+    g.n_blocks = n_blocks;
     if (!cache || !q || !k_cur || !v_cur || !ctx_len || !rot || !out) return RQ_ERR_INVALID_ARG;
     if (batch < 1 || batch > g.max_batch) return RQ_ERR_INVALID_ARG;
     if (loop < 0 || loop >= g.L * g.n_groups) return RQ_ERR_INVALID_ARG;
@@ -214,6 +261,29 @@ rq_status rq_decode_attention(const rq_config* cfg, const void* cache, int32_t l
     m.lloc = lloc;
     m.rot = rot;
     return launch_decode(a, nres, q_is_bf16 != 0, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
+}
+
+rq_status rq_decode_attention(const rq_config* cfg, const void* cache, int32_t loop, const void* q,
+                              int32_t q_is_bf16, const uint16_t* k_cur, const uint16_t* v_cur,
+                              uint16_t* pending, const int32_t* ctx_len, int32_t ctx_bound,
+                              const float* rot, float sm_scale, float* out, void* workspace,
+                              size_t workspace_bytes_, int32_t batch, int32_t n_splits,
+                              hipStream_t stream) {
+    return decode_impl(cfg, cache, nullptr, 0, 0, loop, q, q_is_bf16, k_cur, v_cur, pending, ctx_len, ctx_bound, rot,
+                       sm_scale, out, workspace, workspace_bytes_, batch, n_splits, stream);
+}
+
+rq_status rq_decode_attention_paged(const rq_config* cfg, const void* pool, int32_t n_blocks,
+                                    const int32_t* block_table, int32_t table_stride, int32_t loop, const void* q,
+                                    int32_t q_is_bf16, const uint16_t* k_cur, const uint16_t* v_cur,
+                                    uint16_t* pending, const int32_t* ctx_len, int32_t ctx_bound,
+                                    const float* rot, float sm_scale, float* out, void* workspace,
+                                    size_t workspace_bytes_, int32_t batch, int32_t n_splits,
+                                    hipStream_t stream) {
+    const rq_status st = paging_ok(cfg, n_blocks, block_table, table_stride);
+    if (st != RQ_OK) return st;
+    return decode_impl(cfg, pool, block_table, table_stride, n_blocks, loop, q, q_is_bf16, k_cur, v_cur, pending,
+                       ctx_len, ctx_bound, rot, sm_scale, out, workspace, workspace_bytes_, batch, n_splits, stream);
 }
 
 rq_status rq_bf16_decode_attention(const rq_bf16_config* cfg, uint16_t* k_cache, uint16_t* v_cache,

@@ -28,7 +28,42 @@ struct Geom {
         return ((int64_t)(b * hkv + h) * 2 + x) * block_bytes + (int64_t)k * group_bytes +
                (int64_t)l * n_tiles * r_tile;
     }
+
+    // Paged layout: a pool of physical blocks, each holding one 64-token tile of every (KV
+    // head, K|V, anchor group, loop plane) as [head][K|V][group][residual planes..., anchor]
+    // (g_tile bytes per (head, K|V, group)); bt[b * bt_stride + t] names the block of tile t
+    // of row b.  bt == nullptr selects the contiguous layout above.
+    const int32_t* bt;
+    int bt_stride, n_blocks;
+    int64_t g_tile, p_block;
+
+    // byte offset of the tile of (h, x, loop) inside physical block blk
+    __host__ __device__ int64_t paged_offset(int blk, int h, int x, int loop) const {
+        const int k = loop / L, l = loop % L;
+        return (int64_t)blk * p_block + ((int64_t)(h * 2 + x) * n_groups + k) * g_tile + (int64_t)l * r_tile;
+    }
+
+    // byte offset of tile `tile` of (b, h, x, loop) in either layout; a block id outside
+    // [0, n_blocks) is clamped (the table is device data the host cannot check)
+    __device__ int64_t tile_offset(int b, int h, int x, int loop, int tile) const {
+        if (bt == nullptr) return plane_offset(b, h, x, loop) + (int64_t)tile * (loop % L == L - 1 ? a_tile : r_tile);
+        return paged_offset(block_id(b, tile), h, x, loop);
+    }
+    __device__ int block_id(int b, int tile) const {
+        int blk = bt[(int64_t)b * bt_stride + tile];
+        return blk < 0 ? 0 : (blk >= n_blocks ? n_blocks - 1 : blk);
+    }
 };
+
+// Block id of a wave-uniform (row, tile) through the scalar cache: the decode kernels keep
+// exact counts of their outstanding vector loads, which this load must not join.
+__device__ __forceinline__ int block_id_scalar(const Geom& g, int b, int tile) {
+    const int idx = __builtin_amdgcn_readfirstlane(b * g.bt_stride + tile);
+    typedef const int32_t __attribute__((address_space(4)))* cptr;
+    int blk = ((cptr)(uintptr_t)g.bt)[idx];
+    blk = __builtin_amdgcn_readfirstlane(blk);
+    return blk < 0 ? 0 : (blk >= g.n_blocks ? g.n_blocks - 1 : blk);
+}
 
 // Returns false if the configuration is outside the supported tuples.
 bool make_geom(const rq_config* cfg, Geom* g);

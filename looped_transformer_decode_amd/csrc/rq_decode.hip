@@ -144,8 +144,9 @@ __device__ __forceinline__ float fp8(uint32_t word, int byte) {
     }
 }
 
-// D: head dim; GS: group size; BA: anchor bits; NRES: residual planes read (0 = anchor loop).
-template <int D, int GS, int BA, int NRES, bool QBF16>
+// D: head dim; GS: group size; BA: anchor bits; NRES: residual planes read (0 = anchor loop);
+// PAGED: tiles addressed through the block table (G.bt).
+template <int D, int GS, int BA, int NRES, bool QBF16, bool PAGED>
 __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
     constexpr int LPT = D / 32;            // lanes per token
     constexpr int SLOTS = kWave / LPT;     // tokens per pass
@@ -215,6 +216,12 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
     const int r_meta = kTile * G.r_row;
     const int r_cblk = kTile * (G.r_row + G.m_row);
 
+    // Paged layout: the block of each of this wave's tiles is read through the scalar cache
+    // one tile ahead (the first one here, at the top of the prologue).
+    constexpr bool paged = PAGED;
+    int blk_cur = 0, blk_nxt = 0;
+    if (paged && my_tiles > 0) blk_nxt = block_id_scalar(G, b, first);
+
     // Stage pass `it` (SLOTS consecutive tokens of one tile) of every plane into ring slot
     // it % NB of this wave.  LDS slot layout: K then V, each [anchor codes][anchor meta]
     // then per residual plane [codes][meta][c].
@@ -223,21 +230,26 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
         const uint32_t tile = first + kWaves * (it / PPT);
         const uint32_t p = it % PPT;
         uint32_t dst = ring_base + (uint32_t)(it % NB) * PASS;
-        const uint32_t ta = tile * (uint32_t)G.a_tile;
+        if (paged && p == 0) {
+            blk_cur = blk_nxt;
+            if (it / PPT + 1 < my_tiles) blk_nxt = block_id_scalar(G, b, (int)tile + kWaves);
+        }
+        const uint32_t ta = paged ? 0u : tile * (uint32_t)G.a_tile;
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-            const uint8_t* ap = x ? aV : aK;
-            stage<AC>(ap, ta + p * AC, dst, lane);
-            stage<AM>(ap, ta + a_meta + p * AM, dst + AC, lane);
+            const uint8_t* ap = paged ? uniform_ptr(a.cache + G.paged_offset(blk_cur, h, x, aloop)) : (x ? aV : aK);
+            stage<AC, PAGED>(ap, ta + p * AC, dst, lane);
+            stage<AM, PAGED>(ap, ta + a_meta + p * AM, dst + AC, lane);
             dst += AC + AM;
             if constexpr (NRES > 0) {
-                const uint32_t tr = tile * (uint32_t)G.r_tile;
+                const uint32_t tr = paged ? 0u : tile * (uint32_t)G.r_tile;
 #pragma unroll
                 for (int k = 0; k < NRES; ++k) {
-                    const uint8_t* rp = x ? rV[k] : rK[k];
-                    stage<RC>(rp, tr + p * RC, dst, lane);
-                    stage<AM>(rp, tr + r_meta + p * AM, dst + RC, lane);
-                    stage<CC>(rp, tr + r_cblk + p * CC, dst + RC + AM, lane);
+                    const uint8_t* rp =
+                        paged ? uniform_ptr(a.cache + G.paged_offset(blk_cur, h, x, a.loop + k)) : (x ? rV[k] : rK[k]);
+                    stage<RC, PAGED>(rp, tr + p * RC, dst, lane);
+                    stage<AM, PAGED>(rp, tr + r_meta + p * AM, dst + RC, lane);
+                    stage<CC, PAGED>(rp, tr + r_cblk + p * CC, dst + RC + AM, lane);
                     dst += RC + AM + CC;
                 }
             }
@@ -507,13 +519,13 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
     splitk_finish<D, (NRES > 0)>(a.mg, bh, split, sm.sum, ml, sv[0], sm);
 }
 
-template <int D, int GS, int BA, bool QB>
+template <int D, int GS, int BA, bool QB, bool PG>
 static hipError_t launch_nres(const DecodeArgs& a, int nres, dim3 grid, hipStream_t st) {
     switch (nres) {
-        case 0: hipLaunchKernelGGL((rq_decode_kernel<D, GS, BA, 0, QB>), grid, dim3(kThreads), 0, st, a); break;
-        case 1: hipLaunchKernelGGL((rq_decode_kernel<D, GS, BA, 1, QB>), grid, dim3(kThreads), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((rq_decode_kernel<D, GS, BA, 2, QB>), grid, dim3(kThreads), 0, st, a); break;
-        case 3: hipLaunchKernelGGL((rq_decode_kernel<D, GS, BA, 3, QB>), grid, dim3(kThreads), 0, st, a); break;
+        case 0: hipLaunchKernelGGL((rq_decode_kernel<D, GS, BA, 0, QB, PG>), grid, dim3(kThreads), 0, st, a); break;
+        case 1: hipLaunchKernelGGL((rq_decode_kernel<D, GS, BA, 1, QB, PG>), grid, dim3(kThreads), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((rq_decode_kernel<D, GS, BA, 2, QB, PG>), grid, dim3(kThreads), 0, st, a); break;
+        case 3: hipLaunchKernelGGL((rq_decode_kernel<D, GS, BA, 3, QB, PG>), grid, dim3(kThreads), 0, st, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -521,8 +533,11 @@ static hipError_t launch_nres(const DecodeArgs& a, int nres, dim3 grid, hipStrea
 
 template <int D, int GS, int BA>
 static hipError_t launch_q(const DecodeArgs& a, int nres, bool qbf16, dim3 grid, hipStream_t st) {
-    return qbf16 ? launch_nres<D, GS, BA, true>(a, nres, grid, st)
-                 : launch_nres<D, GS, BA, false>(a, nres, grid, st);
+    if (a.geo.bt != nullptr)
+        return qbf16 ? launch_nres<D, GS, BA, true, true>(a, nres, grid, st)
+                     : launch_nres<D, GS, BA, false, true>(a, nres, grid, st);
+    return qbf16 ? launch_nres<D, GS, BA, true, false>(a, nres, grid, st)
+                 : launch_nres<D, GS, BA, false, false>(a, nres, grid, st);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int nres, bool qbf16, hipStream_t st) {

@@ -251,7 +251,7 @@ __device__ __forceinline__ void merge_group(const MergeArgs& g, int bh0, const f
     }
 }
 
-template <int G, int NRES, bool QBF16>
+template <int G, int NRES, bool QBF16, bool PAGED>
 __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
     static_assert(G == 2 || G == 4, "2 or 4 query heads per KV head");
     constexpr int PASS = Smem<G, NRES>::PASS;
@@ -287,23 +287,34 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
     const uint8_t* rV = a.cache + Gm.plane_offset(b, h, 1, a.loop);
     const uint32_t a_meta = kTile * AROW, r_meta = kTile * RROW, r_cblk = kTile * (RROW + MROW);
 
+    // Paged layout: the physical block of each block's tile is read through the scalar cache
+    // one block ahead (the first one here, at the top of the prologue).
+    int pblk_cur = 0, pblk_nxt = 0;
+    if constexpr (PAGED) {
+        if (n_it > 0) pblk_nxt = block_id_scalar(Gm, b, first >> 1);
+    }
+
     const uint32_t ring_base = __builtin_amdgcn_readfirstlane(lds_addr_of(&sm.ring[w][0][0]));
     auto issue = [&](int it) {
         const uint32_t blk = first + NW * it;
         const uint32_t tile = blk >> 1, hb = blk & 1;
         uint32_t dst = ring_base + (uint32_t)(it % NB) * PASS;
-        const uint32_t ta = tile * (uint32_t)Gm.a_tile, tr = tile * (uint32_t)Gm.r_tile;
+        if constexpr (PAGED) {
+            pblk_cur = pblk_nxt;
+            if (it + 1 < n_it) pblk_nxt = block_id_scalar(Gm, b, (int)((blk + NW) >> 1));
+        }
+        const uint32_t ta = PAGED ? 0u : tile * (uint32_t)Gm.a_tile, tr = PAGED ? 0u : tile * (uint32_t)Gm.r_tile;
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-            const uint8_t* ap = x ? aV : aK;
-            stage<1024>(ap, ta + hb * AC, dst, lane);
-            stage<1024>(ap, ta + hb * AC + 1024, dst + 1024, lane);
-            stage<AM>(ap, ta + a_meta + hb * AM, dst + AC, lane);
+            const uint8_t* ap = PAGED ? uniform_ptr(a.cache + Gm.paged_offset(pblk_cur, h, x, aloop)) : (x ? aV : aK);
+            stage<1024, PAGED>(ap, ta + hb * AC, dst, lane);
+            stage<1024, PAGED>(ap, ta + hb * AC + 1024, dst + 1024, lane);
+            stage<AM, PAGED>(ap, ta + a_meta + hb * AM, dst + AC, lane);
             if constexpr (NRES > 0) {
-                const uint8_t* rp = x ? rV : rK;
-                stage<RC>(rp, tr + hb * RC, dst + RES_OFF, lane);
-                stage<RM>(rp, tr + r_meta + hb * RM, dst + RES_OFF + RC, lane);
-                stage<CC>(rp, tr + r_cblk + hb * CC, dst + RES_OFF + RC + RM, lane);
+                const uint8_t* rp = PAGED ? uniform_ptr(a.cache + Gm.paged_offset(pblk_cur, h, x, a.loop)) : (x ? rV : rK);
+                stage<RC, PAGED>(rp, tr + hb * RC, dst + RES_OFF, lane);
+                stage<RM, PAGED>(rp, tr + r_meta + hb * RM, dst + RES_OFF + RC, lane);
+                stage<CC, PAGED>(rp, tr + r_cblk + hb * CC, dst + RES_OFF + RC + RM, lane);
             }
             dst += PLANE;
         }
@@ -695,8 +706,13 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
 
 template <int G, int NRES>
 static hipError_t launch_q(const DecodeArgs& a, bool qbf16, dim3 grid, hipStream_t st) {
-    if (qbf16) hipLaunchKernelGGL((rq_decode_gqa_kernel<G, NRES, true>), grid, dim3(NT), 0, st, a);
-    else hipLaunchKernelGGL((rq_decode_gqa_kernel<G, NRES, false>), grid, dim3(NT), 0, st, a);
+    if (a.geo.bt != nullptr) {
+        if (qbf16) hipLaunchKernelGGL((rq_decode_gqa_kernel<G, NRES, true, true>), grid, dim3(NT), 0, st, a);
+        else hipLaunchKernelGGL((rq_decode_gqa_kernel<G, NRES, false, true>), grid, dim3(NT), 0, st, a);
+    } else {
+        if (qbf16) hipLaunchKernelGGL((rq_decode_gqa_kernel<G, NRES, true, false>), grid, dim3(NT), 0, st, a);
+        else hipLaunchKernelGGL((rq_decode_gqa_kernel<G, NRES, false, false>), grid, dim3(NT), 0, st, a);
+    }
     return hipGetLastError();
 }
 

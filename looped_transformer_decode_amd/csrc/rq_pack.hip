@@ -279,8 +279,6 @@ __global__ __launch_bounds__(2 * D) void rq_pack_kernel(PackArgs a) {
             rhalf[4 * k4 + 3] = v.w;
         }
     }
-    uint8_t* a_plane = a.cache + Gm.plane_offset(b, h, x, loop0 + L - 1);
-
     for (int t = t0; t < t1; ++t) {
         const int slot = a.pos[b] + t;
         if (slot < 0 || slot >= Gm.max_ctx) continue;  // same for the whole workgroup
@@ -295,7 +293,7 @@ __global__ __launch_bounds__(2 * D) void rq_pack_kernel(PackArgs a) {
 
         const QOut qa = quantize_lane<G>(xv[NL], Gm.ba);
         if (!SPLIT || lsel == 0) {
-            uint8_t* pl = a_plane + tile * Gm.a_tile;
+            uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + L - 1, tile);
             store_codes(pl + jj * Gm.a_row, qa.code, Gm.ba);
             store_meta(pl + kTile * Gm.a_row + jj * Gm.m_row, qa, Gm.g);
         }
@@ -323,7 +321,7 @@ __global__ __launch_bounds__(2 * D) void rq_pack_kernel(PackArgs a) {
             for (int l = 0; l < NL; ++l) qr[l] = quantize_lane<G>(rl[l], Gm.br);
 #pragma unroll
             for (int l = 0; l < NL; ++l) {
-                uint8_t* pl = a.cache + Gm.plane_offset(b, h, x, loop0 + (SPLIT ? lsel : l)) + tile * Gm.r_tile;
+                uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + (SPLIT ? lsel : l), tile);
                 store_codes(pl + jj * Gm.r_row, qr[l].code, Gm.br);
                 store_meta(pl + kTile * Gm.r_row + jj * Gm.m_row, qr[l], Gm.g);
                 store_c(pl + kTile * (Gm.r_row + Gm.m_row), jj, cs[l]);
@@ -341,7 +339,7 @@ __global__ __launch_bounds__(2 * D) void rq_pack_kernel(PackArgs a) {
                 double rl[1];
                 rotate_rows<D, 1>(rhalf, sh_y, p, rl);
                 const QOut qr = quantize_lane<G>(rl[0], Gm.br);
-                uint8_t* pl = a.cache + Gm.plane_offset(b, h, x, loop0 + l) + tile * Gm.r_tile;
+                uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + l, tile);
                 store_codes(pl + jj * Gm.r_row, qr.code, Gm.br);
                 store_meta(pl + kTile * Gm.r_row + jj * Gm.m_row, qr, Gm.g);
                 store_c(pl + kTile * (Gm.r_row + Gm.m_row), jj, c);
@@ -506,7 +504,7 @@ __global__ __launch_bounds__(bulk_threads<D>()) void rq_pack_bulk_kernel(PackArg
         const int slot = ok ? p0 + tok : 0, tile = slot / kTile, jj = slot % kTile;
         double xa[CPL], xh[CPL];
         load_x(0, tok, xa);
-        uint8_t* pl = a.cache + Gm.plane_offset(b, h, x, loop0 + L - 1) + tile * Gm.a_tile;
+        uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + L - 1, tile);
         if (Gm.ba == 4) quantize_row<G, CPL, 4>(xa, xh, pl, Gm.a_row, Gm.m_row, jj, ok, lane);
         else quantize_row<G, CPL, 2>(xa, xh, pl, Gm.a_row, Gm.m_row, jj, ok, lane);
         double ss = 0.0;
@@ -548,7 +546,7 @@ __global__ __launch_bounds__(bulk_threads<D>()) void rq_pack_bulk_kernel(PackArg
                 dot = lanes_reduce<kWave>(dot, add);
                 const double cl = bf16_round(na > 0.0 ? dot / na : 0.0);
                 if (lok && lane == 0) {
-                    uint8_t* pl = a.cache + Gm.plane_offset(b, h, x, loop0 + l) + tile * Gm.r_tile;
+                    uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + l, tile);
                     reinterpret_cast<uint16_t*>(pl + (int64_t)kTile * (Gm.r_row + Gm.m_row))[jj] =
                         (uint16_t)(__float_as_uint((float)cl) >> 16);
                 }
@@ -600,7 +598,7 @@ __global__ __launch_bounds__(bulk_threads<D>()) void rq_pack_bulk_kernel(PackArg
                 double r[CPL], rh[CPL];
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) r[c] = yt[CPL * lane + c][tok * LB + li];
-                uint8_t* pl = a.cache + Gm.plane_offset(b, h, x, loop0 + (l < LR ? l : 0)) + tile * Gm.r_tile;
+                uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + (l < LR ? l : 0), tile);
                 quantize_row<G, CPL, 2>(r, rh, pl, Gm.r_row, Gm.m_row, jj, ok && l < LR, lane);
             }
         }

@@ -9,15 +9,35 @@ namespace rq {
 // 16-byte chunk per lane, without passing through registers.  The compiler does not
 // track these LDS writes, so each wave waits for its own DMAs explicitly (vmcnt) before
 // reading a staged pass; no other vector-memory instruction is issued inside the loop.
+//
+// FRESH: the base was just moved into scalar registers by a vector instruction
+// (v_readfirstlane, see uniform_ptr).  A vector-memory instruction that reads an SGPR
+// written by a VALU instruction needs 5 wait states in between, which the compiler
+// inserts for its own instructions but not in front of inline assembly; without them the
+// DMA can take the registers' previous contents as its address.  FRESH puts the wait
+// states inside the statement.
+template <bool FRESH = false>
 __device__ __forceinline__ void dma16(uint32_t voff, const uint8_t* sbase, uint32_t lds_addr) {
-    asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+    if constexpr (FRESH)
+        asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+    else
+        asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
 }
 
 // copy BYTES (multiple of 16, at most 1024) from sbase + goff to LDS lds_addr
-template <int BYTES>
+template <int BYTES, bool FRESH = false>
 __device__ __forceinline__ void stage(const uint8_t* sbase, uint32_t goff, uint32_t lds_addr, int lane) {
     static_assert(BYTES % 16 == 0 && BYTES <= 1024, "one DMA instruction per block");
-    if (BYTES == 1024 || lane < BYTES / 16) dma16(goff + 16u * lane, sbase, lds_addr);
+    if (BYTES == 1024 || lane < BYTES / 16) dma16<FRESH>(goff + 16u * lane, sbase, lds_addr);
+}
+
+// A wave-uniform pointer moved into scalar registers (the DMA takes its base there); a DMA
+// that reads it must be issued with FRESH = true.
+__device__ __forceinline__ const uint8_t* uniform_ptr(const uint8_t* p) {
+    const uint64_t u = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
 template <int N>

@@ -47,7 +47,6 @@ __global__ __launch_bounds__(128) void rq_unpack_kernel(UnpackArgs a) {
     const int grp = a.loop / L, lloc = a.loop % L;
     const int aloop = grp * L + L - 1;
     const float* R = a.rot + (int64_t)(2 * h + x) * D * D;
-    const uint8_t* a_plane = a.cache + G.plane_offset(b, h, x, aloop);
     __shared__ float r_hat[128];
 
     const int nt = a.t1 - a.t0;
@@ -55,12 +54,12 @@ __global__ __launch_bounds__(128) void rq_unpack_kernel(UnpackArgs a) {
         const int t = chunk * kUnpackTokens + k;
         if (t >= nt) break;                            // same for the whole workgroup
         const int slot = a.t0 + t, tile = slot / kTile, jj = slot % kTile;
-        float v = dequant(a_plane + tile * G.a_tile, G.a_row, G.ba, G, jj, i);
+        float v = dequant(a.cache + G.tile_offset(b, h, x, aloop, tile), G.a_row, G.ba, G, jj, i);
         // residual loops from the one nearest the anchor down to `lloc` (shared: only `lloc`;
         // the anchor loop has none)
         const int first = lloc == L - 1 ? -1 : (G.chained ? L - 2 : lloc);
         for (int l = first; l >= lloc; --l) {
-            const uint8_t* rt = a.cache + G.plane_offset(b, h, x, grp * L + l) + tile * G.r_tile;
+            const uint8_t* rt = a.cache + G.tile_offset(b, h, x, grp * L + l, tile);
             const float rh = dequant(rt, G.r_row, G.br, G, jj, i);
             const uint16_t cb = *reinterpret_cast<const uint16_t*>(rt + (int64_t)kTile * (G.r_row + G.m_row) + 2 * jj);
             __syncthreads();                           // r_hat is reused

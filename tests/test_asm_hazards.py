@@ -1,0 +1,121 @@
+"""Static check of the decode kernels' machine code (CPU only: hipcc cross-compiles).
+
+The cache stream is staged by inline-assembly DMAs (global_load_lds_dwordx4) whose base
+address sits in scalar registers.  On this GPU family a vector-memory instruction that
+reads an SGPR written by a VALU instruction (v_readfirstlane, a compare, the carry-out
+of a 64-bit multiply-add, ...) needs 5 wait states in between.  The compiler inserts them
+for its own instructions but cannot see into inline assembly, so a base moved into SGPRs
+right before the statement could be read stale, that is as the registers' previous
+contents: an arbitrary address.  This test compiles the decode sources to assembly with
+the library's own flags and checks every inline-assembly vector-memory instruction
+against the VALU writes of its base registers that precede it, counting s_nop wait
+states."""
+import concurrent.futures
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+from looped_transformer_decode_amd import build as B
+
+SOURCES = ["rq_decode.hip", "rq_decode_gqa.hip", "rq_bf16.hip"]
+NEEDED = 5
+
+
+def _sgprs(tok):
+    m = re.match(r"s\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"s(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def _valu_sgpr_defs(line):
+    parts = line.split(None, 1)
+    if len(parts) < 2 or not parts[0].startswith("v_"):
+        return set()
+    op, ops = parts[0], [o.strip() for o in parts[1].split(",")]
+    out = set()
+    if op.startswith(("v_readfirstlane", "v_readlane", "v_cmp")):
+        out |= _sgprs(ops[0])
+    if re.match(r"v_(mad_u64_u32|mad_i64_i32|add_co|sub_co|subrev_co|addc_co|subb_co|div_scale)", op) and len(ops) > 1:
+        out |= _sgprs(ops[1])
+    return out
+
+
+def scan(asm_text):
+    """(kernel, wait states, VALU line, memory line) for every short gap, in straight-line order."""
+    bad, hist, kern, inasm = [], [], None, False
+    for raw in asm_text.splitlines():
+        line = raw.strip()
+        if re.match(r"^_Z\S+:", line):
+            kern, hist = line.split(":")[0], []
+            continue
+        if line.startswith(";;#ASMSTART"):
+            inasm = True
+            continue
+        if line.startswith(";;#ASMEND"):
+            inasm = False
+            continue
+        line = line.split(";")[0].strip()
+        if not line or line.startswith(".") or line.endswith(":"):
+            continue
+        nop = re.match(r"s_nop\s+(\d+)", line)
+        if inasm and not nop:
+            m = re.match(r"(global_load\S*|buffer_load\S*|global_store\S*)\s+.*?(s\[\d+:\d+\])", line)
+            if m:
+                base, ws = _sgprs(m.group(2)), 0
+                for kind, val, text in reversed(hist):
+                    if kind == "nop":
+                        ws += val
+                        continue
+                    if val & base:
+                        if ws < NEEDED:
+                            bad.append((kern, ws, text, line))
+                        break
+                    ws += 1
+                    if ws >= NEEDED:
+                        break
+        hist.append(("nop", int(nop.group(1)) + 1, line) if nop else ("i", _valu_sgpr_defs(line), line))
+        hist = hist[-16:]
+    return bad
+
+
+def test_scanner_flags_a_short_gap_and_counts_nops():
+    text = "\n".join([
+        "_Zk:",
+        "v_mad_u64_u32 v[0:1], s[10:11], s4, v2, v[4:5]",
+        "v_readfirstlane_b32 s11, v1",
+        "v_readfirstlane_b32 s10, v0",
+        ";;#ASMSTART",
+        "global_load_lds_dwordx4 v8, s[10:11]",
+        ";;#ASMEND",
+        "v_readfirstlane_b32 s12, v0",
+        ";;#ASMSTART",
+        "s_nop 4",
+        "global_load_lds_dwordx4 v8, s[12:13]",
+        ";;#ASMEND",
+    ])
+    bad = scan(text)
+    assert len(bad) == 1 and bad[0][1] == 0 and "s10" in bad[0][2]
+
+
+@pytest.mark.skipif(shutil.which(B.HIPCC) is None and not os.path.exists(B.HIPCC), reason="hipcc not installed")
+def test_decode_kernels_wait_before_dma_bases():
+    with tempfile.TemporaryDirectory() as tmp:
+        def compile_one(src):
+            out = os.path.join(tmp, src + ".s")
+            cmd = [B.HIPCC, *B.FLAGS, "--cuda-device-only", "-S", os.path.join(B.CSRC, src), "-o", out]
+            r = subprocess.run(cmd, capture_output=True, text=True)
+            assert r.returncode == 0, r.stderr[-2000:]
+            with open(out) as f:
+                return src, f.read()
+        with concurrent.futures.ThreadPoolExecutor(len(SOURCES)) as ex:
+            texts = list(ex.map(compile_one, SOURCES))
+    for src, text in texts:
+        assert "global_load_lds_dwordx4" in text or src == "rq_bf16.hip"
+        bad = scan(text)
+        assert not bad, f"{src}: {len(bad)} DMA(s) too close to the VALU write of their base, e.g. {bad[0]}"

@@ -173,3 +173,35 @@ def test_stream_read_rejects_bad_arguments(B):
     assert f(A, 100, A, 1 << 20, None) == 1
     assert f(A + 8, 1 << 20, A, 1 << 20, None) == 3
     assert f(A, 1 << 20, A, (1 << 20) - 1, None) == 4
+
+
+def test_paged_entry_points_reject_bad_arguments(B):
+    wl = synth.WORKLOADS["ouro_b4_t8192"]
+    cfg = B.config_for(wl)
+    tiles = (cfg.max_ctx + 63) // 64
+    blk = B.rq_paged_block_bytes(cfg)
+    # one block holds a tile of every (head, K|V, group, plane): 16 * 2 * (4608 + 3 * 2688) bytes
+    assert blk == 16 * 2 * (4608 + 3 * 2688)
+    bad = B.config_for(wl)
+    bad.head_dim = 96
+    assert B.rq_paged_block_bytes(bad) == 0
+    fq = B._lib.rq_quantize_token_paged
+
+    def q(n_blocks=8, table=A, stride=tiles, batch=4):
+        return fq(ctypes.byref(cfg), A, n_blocks, table, stride, A, None, 0, A, A, batch, 1, None)
+
+    assert q(n_blocks=0) == 1
+    assert q(table=None) == 1
+    assert q(stride=tiles - 1) == 1
+    assert q(table=A + 2) == 3
+    assert q(batch=5) == 1
+    fd = B._lib.rq_decode_attention_paged
+
+    def d(n_blocks=8, table=A, stride=tiles, loop=0):
+        return fd(ctypes.byref(cfg), A, n_blocks, table, stride, loop, A, 1, A, A, None, A, 64, A, 0.1, A, A,
+                  1 << 40, 1, 0, None)
+
+    assert d(n_blocks=0) == 1
+    assert d(stride=0) == 1
+    assert d(table=A + 1) == 3
+    assert d(loop=4) == 1
