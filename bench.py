@@ -337,6 +337,35 @@ def main():
     stream_res = stream_gbps(min(probe_bytes, cache_bytes // 16 * 16), 4 * n_rep)
     stream_full = stream_gbps(cache_bytes // 16 * 16, 2 * n_rep)
 
+    # the same residual loop-steps through block tables: every replica's tiles scattered
+    # over one pool of 64-token blocks in a random order (rows and replicas interleaved)
+    n_tiles = (cfg.max_ctx + 63) // 64
+    blk_bytes = B.rq_paged_block_bytes(cfg)
+    n_blocks = n_rep * Bt * n_tiles
+    perm = torch.randperm(n_blocks, generator=torch.Generator().manual_seed(7)).to(torch.int32)
+    tables = [perm[r * Bt * n_tiles:(r + 1) * Bt * n_tiles].reshape(Bt, n_tiles).contiguous().to(dev)
+              for r in range(n_rep)]
+    pool = torch.zeros(n_blocks * blk_bytes, dtype=torch.uint8, device=dev)
+    for r in range(n_rep):
+        for grp in range(wl.n_groups):
+            st = inp.kv[grp].stride()
+            B.rq_quantize_token_paged(cfg, pool, n_blocks, tables[r], inp.kv[grp], grp, pos0, inp.rot, Bt, T,
+                                      pending_strides=(st[4], st[2], st[0], st[1], st[3]), stream=stream)
+    for i in range(2 * (L - 1)):
+        loop = i % (L - 1)
+        B.rq_decode_attention_paged(cfg, pool, n_blocks, tables[i % n_rep], loop, q[loop], k_cur[loop], v_cur[loop],
+                                    None, ctx_len, T, inp.rot, sc, out, ws, Bt, n_splits=args.splits, stream=stream)
+    p0_, p1_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0_.record(stream)
+    for i in range(6 * n_rep):
+        loop = i % (L - 1)
+        B.rq_decode_attention_paged(cfg, pool, n_blocks, tables[i % n_rep], loop, q[loop], k_cur[loop], v_cur[loop],
+                                    None, ctx_len, T, inp.rot, sc, out, ws, Bt, n_splits=args.splits, stream=stream)
+    p1_.record(stream)
+    torch.cuda.synchronize()
+    paged_ms = p0_.elapsed_time(p1_) / (6 * n_rep)
+    del pool
+
     # roofline timing: back-to-back residual loop-steps over the cold replicas, one event
     # pair around all of them (launches overlap the previous kernel, as in a decode step)
     roof_calls = 6 * n_rep
@@ -396,6 +425,12 @@ def main():
                         "gbps_at_residual_step_bytes": round(stream_res, 1),
                         "gbps_at_full_replica": round(stream_full, 1),
                         "residual_step_frac_of_stream": round(roof_gbps / stream_res, 4)},
+        "paged": {"block_tokens": 64, "n_blocks": n_blocks, "block_bytes": blk_bytes,
+                  "residual_loop_step_ms": round(paged_ms, 4),
+                  "gbps": round(roof_bytes / (paged_ms * 1e-3) / 1e9, 1),
+                  "vs_contiguous": round(roof_ms / paged_ms, 4),
+                  "timing": "HIP events around back-to-back residual loop-steps through shuffled block tables "
+                            "(one per replica, blocks of all replicas interleaved in one pool)"},
         "roofline": {"bound": "hbm", "achieved": round(roof_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(roof_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "ms_per_launch": round(roof_ms, 4), "launches": roof_calls,
