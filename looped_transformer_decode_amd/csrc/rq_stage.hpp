@@ -10,18 +10,21 @@ namespace rq {
 // track these LDS writes, so each wave waits for its own DMAs explicitly (vmcnt) before
 // reading a staged pass; no other vector-memory instruction is issued inside the loop.
 //
-// FRESH: the base was just moved into scalar registers by a vector instruction
-// (v_readfirstlane, see uniform_ptr).  A vector-memory instruction that reads an SGPR
-// written by a VALU instruction needs 5 wait states in between, which the compiler
-// inserts for its own instructions but not in front of inline assembly; without them the
-// DMA can take the registers' previous contents as its address.  FRESH puts the wait
-// states inside the statement.
+// The compiler inserts the wait states that the hardware requires between dependent
+// instructions in front of its own instructions, not in front of inline assembly, so the
+// statement carries them itself:
+// * an LDS DMA that reads M0 right after a scalar write of M0 (the compiler's own move
+//   of lds_addr into M0) needs 1 wait state;
+// * FRESH: the base was just moved into scalar registers by a vector instruction
+//   (v_readfirstlane, see uniform_ptr).  A vector-memory instruction that reads an SGPR
+//   written by a VALU instruction needs 5 wait states; without them the DMA can take the
+//   registers' previous contents as its address.
 template <bool FRESH = false>
 __device__ __forceinline__ void dma16(uint32_t voff, const uint8_t* sbase, uint32_t lds_addr) {
     if constexpr (FRESH)
         asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
     else
-        asm volatile("global_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
 }
 
 // copy BYTES (multiple of 16, at most 1024) from sbase + goff to LDS lds_addr

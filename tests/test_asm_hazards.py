@@ -9,7 +9,8 @@ right before the statement could be read stale, that is as the registers' previo
 contents: an arbitrary address.  This test compiles the decode sources to assembly with
 the library's own flags and checks every inline-assembly vector-memory instruction
 against the VALU writes of its base registers that precede it, counting s_nop wait
-states."""
+states, and every inline-assembly LDS DMA against a scalar write of M0 (the DMA's LDS
+address) right before it, which needs 1 wait state."""
 import concurrent.futures
 import os
 import re
@@ -46,8 +47,15 @@ def _valu_sgpr_defs(line):
     return out
 
 
+def _writes_m0(line):
+    parts = line.split(None, 1)
+    return len(parts) == 2 and parts[0].startswith("s_") and parts[1].split(",")[0].strip() == "m0"
+
+
 def scan(asm_text):
-    """(kernel, wait states, VALU line, memory line) for every short gap, in straight-line order."""
+    """(kernel, wait states, writer line, memory line) for every short gap, in straight-line order:
+    a VALU write of an inline-assembly memory instruction's SGPR base fewer than 5 wait states
+    before it, or a scalar write of M0 directly before an inline-assembly LDS DMA."""
     bad, hist, kern, inasm = [], [], None, False
     for raw in asm_text.splitlines():
         line = raw.strip()
@@ -79,6 +87,19 @@ def scan(asm_text):
                     ws += 1
                     if ws >= NEEDED:
                         break
+            if "_lds_" in line:
+                ws = 0
+                for kind, val, text in reversed(hist):
+                    if kind == "nop":
+                        ws += val
+                        continue
+                    if _writes_m0(text):
+                        if ws < 1:
+                            bad.append((kern, ws, text, line))
+                        break
+                    ws += 1
+                    if ws >= 1:
+                        break
         hist.append(("nop", int(nop.group(1)) + 1, line) if nop else ("i", _valu_sgpr_defs(line), line))
         hist = hist[-16:]
     return bad
@@ -98,9 +119,20 @@ def test_scanner_flags_a_short_gap_and_counts_nops():
         "s_nop 4",
         "global_load_lds_dwordx4 v8, s[12:13]",
         ";;#ASMEND",
+        "s_add_i32 m0, s5, 0x400",
+        ";;#ASMSTART",
+        "global_load_lds_dwordx4 v8, s[12:13]",
+        ";;#ASMEND",
+        "s_mov_b32 m0, s6",
+        ";;#ASMSTART",
+        "s_nop 0",
+        "global_load_lds_dwordx4 v8, s[12:13]",
+        ";;#ASMEND",
     ])
     bad = scan(text)
-    assert len(bad) == 1 and bad[0][1] == 0 and "s10" in bad[0][2]
+    assert len(bad) == 2, bad
+    assert bad[0][1] == 0 and "s10" in bad[0][2]
+    assert bad[1][1] == 0 and "m0" in bad[1][2]
 
 
 @pytest.mark.skipif(shutil.which(B.HIPCC) is None and not os.path.exists(B.HIPCC), reason="hipcc not installed")
