@@ -46,8 +46,11 @@ typedef enum rq_status {
 } rq_status;
 
 /* Shape of one layer's compressed cache.  Supported tuples: head_dim 64 or 128;
- * group 16 or 32 (dividing head_dim); anchor_bits 4 or 2; resid_bits 2;
- * loops_per_group 2..8; n_groups >= 1; n_q_heads a multiple (1..8) of n_kv_heads. */
+ * group 16 or 32 (dividing head_dim); anchor_bits 4 or 2; resid_bits 2 or 4 (4 with a
+ * shared anchor only); loops_per_group 2..16 (2..4 chained); n_groups >= 1; n_q_heads a
+ * multiple (1..8) of n_kv_heads; scale_rule 0 or 1.  The digest's precision settings map
+ * to (anchor_bits, resid_bits) = (4, 4) uniform INT4, (2, 2) uniform INT2 and (4, 2) the
+ * mixed INT2/4; its appendix's larger loop groups to loops_per_group 8 or 16. */
 typedef struct rq_config {
     int32_t head_dim;         /* d */
     int32_t group;            /* g: channels per quantization group */
@@ -60,6 +63,9 @@ typedef struct rq_config {
     int32_t n_q_heads;        /* query head hq reads KV head hq / (n_q_heads / n_kv_heads) */
     int32_t max_batch;
     int32_t max_ctx;          /* token slots per sequence; storage is rounded up to 64-token tiles */
+    int32_t scale_rule;       /* coefficient c of a residual loop: 0 = least squares <x,ref>/<ref,ref>
+                                 (explainer and digest), 1 = norm ratio ||x||/||ref|| (the digest's
+                                 appendix alternative, read as the ratio of Euclidean norms) */
 } rq_config;
 
 /* Byte layout of the cache (one flat, 16-byte-aligned device buffer):
@@ -102,7 +108,8 @@ const char* rq_status_str(rq_status status);
  * `group_idx`:
  *   anchor  : x_{L-1} quantized per group of g channels at anchor_bits;
  *   loop l<L-1 (shared): c = BF16(<x_l,a>/<a,a>) with a the dequantized anchor
- *             (c = 0 if a = 0), r = R (x_l - c a), r quantized per group at resid_bits;
+ *             (c = 0 if a = 0; BF16(||x_l||/||a||) with scale_rule 1),
+ *             r = R (x_l - c a), r quantized per group at resid_bits;
  *   chained : same with a replaced by the rebuilt loop l+1 (c_{l+1} a' + R^T r_hat_{l+1}).
  * Quantizer: offset z = largest E4M3 value <= group min; scale s = smallest E4M3
  * value >= 2^-9 with z + (2^bits-1) s >= group max; code = round-half-even((x-z)/s)

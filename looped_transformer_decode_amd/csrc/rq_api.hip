@@ -14,11 +14,13 @@ bool make_geom(const rq_config* c, Geom* g) {
     if (d != 64 && d != 128) return false;
     if ((gs != 16 && gs != 32) || d % gs != 0) return false;
     if (c->anchor_bits != 4 && c->anchor_bits != 2) return false;
-    if (c->resid_bits != 2) return false;
+    if (c->resid_bits != 2 && c->resid_bits != 4) return false;
     if (c->loops_per_group < 2 || c->loops_per_group > kMaxLoops) return false;
     if (c->n_groups < 1 || c->n_groups > 64) return false;
     if (c->chained != 0 && c->chained != 1) return false;
     if (c->chained && c->loops_per_group > 4) return false;     // kernels read at most 3 residual planes
+    if (c->chained && c->resid_bits != 2) return false;
+    if (c->scale_rule != 0 && c->scale_rule != 1) return false;
     if (c->n_kv_heads < 1 || c->n_q_heads < c->n_kv_heads || c->n_q_heads % c->n_kv_heads != 0) return false;
     if (c->n_q_heads / c->n_kv_heads > 8) return false;
     if (c->max_batch < 1 || c->max_ctx < 1 || c->max_ctx > (1 << 24)) return false;
@@ -33,6 +35,7 @@ bool make_geom(const rq_config* c, Geom* g) {
     g->hq = c->n_q_heads;
     g->max_batch = c->max_batch;
     g->max_ctx = c->max_ctx;
+    g->scale_rule = c->scale_rule;
     g->n_tiles = (c->max_ctx + kTile - 1) / kTile;
     g->a_row = d * g->ba / 8;
     g->r_row = d * g->br / 8;
@@ -158,7 +161,9 @@ static rq_status quantize_impl(const rq_config* cfg, void* cache, const int32_t*
     a.group_idx = group_idx;
     a.batch = batch;
     a.n_tokens = n_tokens;
-    a.tokens_per_wg = n_tokens <= 8 ? 1 : 32;
+    // a few tokens: one per workgroup; groups longer than the per-loop-count instantiations
+    // (L > 8, shared anchor) always take the one-loop-per-workgroup kernel below the bulk size
+    a.tokens_per_wg = (n_tokens <= 8 || (!g.chained && g.L > 8)) ? 1 : 32;
     return launch_pack(a, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 

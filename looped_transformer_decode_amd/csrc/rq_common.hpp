@@ -10,7 +10,7 @@ namespace rq {
 
 constexpr int kTile = 64;          // tokens per cache tile
 constexpr int kMaxSplits = 64;     // split-K upper bound (sizes the workspace)
-constexpr int kMaxLoops = 8;       // loops per anchor group
+constexpr int kMaxLoops = 16;      // loops per anchor group
 constexpr int kWave = 64;
 constexpr int kStageDepth = 3;     // LDS ring slots per wave in the decode kernel (passes)
 
@@ -20,6 +20,7 @@ struct Geom {
     int d, g, ba, br, L, n_groups, chained, hkv, hq, max_batch, max_ctx;
     int n_tiles;
     int a_row, r_row, m_row;           // bytes per token row: anchor codes, residual codes, meta
+    int scale_rule;                    // 0: least-squares c, 1: norm-ratio c
     int64_t a_tile, r_tile;            // bytes per tile
     int64_t group_bytes, block_bytes, total;
 

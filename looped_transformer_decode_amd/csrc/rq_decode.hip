@@ -25,8 +25,9 @@ namespace rq {
 //
 // q is written per quantization group as 24-bit fixed point Q_i = rint(q_i / delta),
 // delta = 2^(e-21) with 2^e <= max|q_i|, split into six balanced base-16 digits d_k in
-// [-8, 7] (Q = sum_k 16^k d_k).  u = R_K q multiplies the 2-bit residual codes (0..3,
-// with small scales) and uses 16-bit fixed point, delta = 2^(e-13), four digits.  A digit word holds the
+// [-8, 7] (Q = sum_k 16^k d_k).  u = R_K q multiplies the residual codes (2-bit, or 4-bit
+// in the uniform INT4 setting) and uses 16-bit fixed point, delta = 2^(e-13), four digits
+// in the digit layout of its code width.  A digit word holds the
 // digits of the 8 channels whose codes share one 32-bit code word, at the same nibble
 // positions, so v_dot8_i32_i4 multiplies codes by digits without unpacking: 4-bit codes
 // are first offset to signed c - 8 (xor 0x8 per nibble; the offset is added back as
@@ -144,9 +145,9 @@ __device__ __forceinline__ float fp8(uint32_t word, int byte) {
     }
 }
 
-// D: head dim; GS: group size; BA: anchor bits; NRES: residual planes read (0 = anchor loop);
-// PAGED: tiles addressed through the block table (G.bt).
-template <int D, int GS, int BA, int NRES, bool QBF16, bool PAGED>
+// D: head dim; GS: group size; BA: anchor bits; BR: residual bits; NRES: residual planes
+// read (0 = anchor loop); PAGED: tiles addressed through the block table (G.bt).
+template <int D, int GS, int BA, int BR, int NRES, bool QBF16, bool PAGED>
 __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
     constexpr int LPT = D / 32;            // lanes per token
     constexpr int SLOTS = kWave / LPT;     // tokens per pass
@@ -154,13 +155,14 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
     constexpr int GPL = 32 / GS;           // quantization groups per lane
     constexpr int AB = 32 * BA / 8;        // anchor code bytes per lane
     constexpr int AW = AB / 4;             // anchor code words per lane
+    constexpr int RW = BR;                 // residual code words per lane (32 channels)
     constexpr int NR = NRES ? NRES : 1;
     constexpr int NV = NRES ? 64 : 32;
     constexpr int NG = D / GS;             // groups per head vector
     // bytes of one pass (SLOTS tokens) per block; each block is one DMA instruction
     constexpr int AC = SLOTS * D * BA / 8;         // anchor codes
     constexpr int AM = SLOTS * 2 * D / GS;         // FP8 offset/scale pairs
-    constexpr int RC = SLOTS * D * 2 / 8;          // residual codes
+    constexpr int RC = SLOTS * D * BR / 8;         // residual codes
     constexpr int CC = SLOTS * 2;                  // BF16 coefficients
     constexpr int PASS = 2 * (AC + AM + NRES * (RC + AM + CC));
     constexpr int NDMA = 2 * (2 + 3 * NRES);       // DMA instructions per pass
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][NB][PASS];
     __shared__ float sv[2][D];                         // q and u = R_K q
     __shared__ uint32_t s_dig[10 * (D / 8)];           // digit words: q [6][D/8], u [4][D/8]
-    __shared__ float s_f[5][NG];                       // delta_q, corr_q, sum_q, delta_u, sum_u
+    __shared__ float s_f[6][NG];                       // delta_q, corr_q, sum_q, delta_u, sum_u, corr_u
 
     int n = a.ctx_len[b];
     n = n < 0 ? 0 : (n > a.ctx_bound ? a.ctx_bound : n);
@@ -323,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
     if (threadIdx.x < (NRES ? 2 : 1) * D) {
         const int which = threadIdx.x / D, i = threadIdx.x % D;
         const float val = sv[which][i];
-        const bool four = (which == 0) && (BA == 4);
+        const bool four = which ? (BR == 4) : (BA == 4);
         const float amax = group_max<GS>(fabsf(val));
         const float vsum = group_sum<GS>(val);
         const int e = amax > 0.f ? ilogbf(amax) : 0;
@@ -351,12 +353,13 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
             } else {
                 s_f[3][gi] = ldexpf(1.f, e - fb);
                 s_f[4][gi] = vsum;
+                s_f[5][gi] = four ? 8.f * (float)qsum : 0.f;
             }
         }
     }
     __syncthreads();
     uint32_t dq[6][4], du[4][4];
-    float dlq[GPL], crq[GPL], Qg[GPL], dlu[GPL], Ug[GPL];
+    float dlq[GPL], crq[GPL], Qg[GPL], dlu[GPL], Ug[GPL], cru[GPL];
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
 #pragma unroll
@@ -372,6 +375,7 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
         Qg[gg] = s_f[2][gi];
         dlu[gg] = NRES ? s_f[3][gi] : 0.f;
         Ug[gg] = NRES ? s_f[4][gi] : 0.f;
+        cru[gg] = (NRES && BR == 4) ? s_f[5][gi] : 0.f;
     }
 
     float accA[32], accR[NRES ? 32 : 1], wA[GPL], wR[GPL], zA[GPL], zR[GPL];
@@ -393,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
         const int row = valid ? slot : 0;          // tail slots read the pass's first (valid) token
         const uint8_t* sp = &ring[w][it % NB][0];
         // lane's words: anchor codes, metadata (GPL pairs), per residual plane codes/meta/c
-        uint32_t ka[AW], va[AW], kr[NR][2], vr[NR][2], krm[NR], vrm[NR], kc[NR], vc[NR];
+        uint32_t ka[AW], va[AW], kr[NR][RW], vr[NR][RW], krm[NR], vrm[NR], kc[NR], vc[NR];
         uint32_t kam, vam;
         {
             const uint8_t* kp = sp;
@@ -413,10 +417,11 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int k = 0; k < NRES; ++k) {
                 const int o = AC + AM + k * (RC + AM + CC);
-                kr[k][0] = reinterpret_cast<const uint32_t*>(kp + o + row * (RC / SLOTS) + chunk * 8)[0];
-                kr[k][1] = reinterpret_cast<const uint32_t*>(kp + o + row * (RC / SLOTS) + chunk * 8)[1];
-                vr[k][0] = reinterpret_cast<const uint32_t*>(vp + o + row * (RC / SLOTS) + chunk * 8)[0];
-                vr[k][1] = reinterpret_cast<const uint32_t*>(vp + o + row * (RC / SLOTS) + chunk * 8)[1];
+#pragma unroll
+                for (int q4 = 0; q4 < RW; ++q4) {
+                    kr[k][q4] = reinterpret_cast<const uint32_t*>(kp + o + row * (RC / SLOTS) + chunk * 4 * RW)[q4];
+                    vr[k][q4] = reinterpret_cast<const uint32_t*>(vp + o + row * (RC / SLOTS) + chunk * 4 * RW)[q4];
+                }
                 if constexpr (GPL == 1) {
                     krm[k] = *reinterpret_cast<const uint16_t*>(kp + o + RC + row * (AM / SLOTS) + chunk * 2);
                     vrm[k] = *reinterpret_cast<const uint16_t*>(vp + o + RC + row * (AM / SLOTS) + chunk * 2);
@@ -443,11 +448,11 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int k = 0; k < NRES; ++k) {
             uint32_t nib[4];
-            code_nibbles<2>(nib, kr[k]);
+            code_nibbles<BR>(nib, kr[k]);
             float pr = 0.f;
 #pragma unroll
             for (int gg = 0; gg < GPL; ++gg) {
-                const float dot = dlu[gg] * digit_dot<DW, 4>(nib, du, gg * DW);
+                const float dot = dlu[gg] * (digit_dot<DW, 4>(nib, du, gg * DW) + cru[gg]);
                 pr += fp8(krm[k], 2 * gg) * Ug[gg] + fp8(krm[k], 2 * gg + 1) * dot;
             }
             part_r += coef * pr;
@@ -483,7 +488,7 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
                 const float ws = wv * fp8(vrm[k], 2 * gg + 1);
                 zR[gg] += wv * fp8(vrm[k], 2 * gg);
                 wR[gg] += ws;
-                v_acc<2>(accR, vr[k], ws, gg * 2 / GPL, 2 / GPL, magic);
+                v_acc<BR>(accR, vr[k], ws, gg * RW / GPL, RW / GPL, magic);
             }
             wv *= bf16_to_f32(vc[k]);
         }
@@ -512,7 +517,7 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
     if constexpr (NRES > 0) {
 #pragma unroll
         for (int i = 0; i < 32; ++i)
-            v[32 + i] = (accR[i] - 1024.f * wR[i / GS]) * inv_mult<2>(i) + zR[i / GS];
+            v[32 + i] = (accR[i] - 1024.f * wR[i / GS]) * inv_mult<BR>(i) + zR[i / GS];
     }
     __builtin_amdgcn_s_setprio(3);                // the merge is on the critical path
     const float2 ml = splitk_merge_waves<D, NV>(v, m_run, l_lane, sm);
@@ -521,11 +526,19 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
 
 template <int D, int GS, int BA, bool QB, bool PG>
 static hipError_t launch_nres(const DecodeArgs& a, int nres, dim3 grid, hipStream_t st) {
+    // the anchor loop (nres 0) reads no residual plane: one instantiation for both widths
+    if (a.geo.br == 4) {
+        if (nres == 1) {
+            hipLaunchKernelGGL((rq_decode_kernel<D, GS, BA, 4, 1, QB, PG>), grid, dim3(kThreads), 0, st, a);
+            return hipGetLastError();
+        }
+        if (nres != 0) return hipErrorInvalidValue;  // 4-bit residuals: shared anchor only
+    }
     switch (nres) {
-        case 0: hipLaunchKernelGGL((rq_decode_kernel<D, GS, BA, 0, QB, PG>), grid, dim3(kThreads), 0, st, a); break;
-        case 1: hipLaunchKernelGGL((rq_decode_kernel<D, GS, BA, 1, QB, PG>), grid, dim3(kThreads), 0, st, a); break;
-        case 2: hipLaunchKernelGGL((rq_decode_kernel<D, GS, BA, 2, QB, PG>), grid, dim3(kThreads), 0, st, a); break;
-        case 3: hipLaunchKernelGGL((rq_decode_kernel<D, GS, BA, 3, QB, PG>), grid, dim3(kThreads), 0, st, a); break;
+        case 0: hipLaunchKernelGGL((rq_decode_kernel<D, GS, BA, 2, 0, QB, PG>), grid, dim3(kThreads), 0, st, a); break;
+        case 1: hipLaunchKernelGGL((rq_decode_kernel<D, GS, BA, 2, 1, QB, PG>), grid, dim3(kThreads), 0, st, a); break;
+        case 2: hipLaunchKernelGGL((rq_decode_kernel<D, GS, BA, 2, 2, QB, PG>), grid, dim3(kThreads), 0, st, a); break;
+        case 3: hipLaunchKernelGGL((rq_decode_kernel<D, GS, BA, 2, 3, QB, PG>), grid, dim3(kThreads), 0, st, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -377,8 +377,9 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
         }
         int off = 0;
         group_reduce_scatter<RL * G, C4 / 2, RL * G>(pr, lane, off);
-        // the lane now holds the 32-lane sums of values [off, off + RL*G/32)
-        constexpr int KEEP = RL * G / 32;
+        // the lane now holds the 32-lane sums of values [off, off + RL*G/32); with fewer values
+        // than lanes (G = 2) it holds one, which its butterfly partners hold as well
+        constexpr int KEEP = RL * G / 32 > 0 ? RL * G / 32 : 1;
 #pragma unroll
         for (int i = 0; i < KEEP; ++i) {
             const int v = off + i, k = v / G, g = v % G;
@@ -720,7 +721,7 @@ static hipError_t launch_q(const DecodeArgs& a, bool qbf16, dim3 grid, hipStream
 
 bool gqa_supported(const Geom& g, int nres) {
     const int gq = g.hq / g.hkv;
-    return g.d == gqa::D && g.g == gqa::GS && g.ba == 4 && nres <= 1 && (gq == 2 || gq == 4);
+    return g.d == gqa::D && g.g == gqa::GS && g.ba == 4 && (g.br == 2 || nres == 0) && nres <= 1 && (gq == 2 || gq == 4);
 }
 
 hipError_t launch_decode_gqa(const DecodeArgs& a, int nres, bool qbf16, hipStream_t st) {

@@ -239,10 +239,15 @@ __device__ __forceinline__ void rotate_all(const float (&rhalf)[D / 2], const do
 // tokens of the range.  LR = L - 1 residual loops.
 // SPLIT (shared anchor only): one residual loop per workgroup, selected by the block index;
 // every workgroup of a token quantizes the anchor, the one of loop 0 stores it.  This
-// shortens the chain of a single token (rotation and residual quantizer of one loop).
+// shortens the chain of a single token (rotation and residual quantizer of one loop).  A
+// SPLIT kernel takes the loop count from the configuration (LR is unused), so one
+// instantiation serves every group length.
+// The coefficient follows the configuration's rule: least squares <x, ref>/<ref, ref> or
+// the norm ratio sqrt(<x, x>/<ref, ref>), both rounded to BF16.
 template <int D, int G, int LR, bool SPLIT>
 __global__ __launch_bounds__(2 * D) void rq_pack_kernel(PackArgs a) {
-    constexpr int L = LR + 1;
+    const int LRr = SPLIT ? a.geo.L - 1 : LR;         // residual loops of the group
+    const int L = LRr + 1;
     constexpr int NL = SPLIT ? 1 : LR;                 // residual loops of this workgroup
     constexpr int NT = 2 * D;
     constexpr int H = D / 2;
@@ -251,8 +256,8 @@ __global__ __launch_bounds__(2 * D) void rq_pack_kernel(PackArgs a) {
     int wg = blockIdx.x;
     int lsel = 0;
     if constexpr (SPLIT) {
-        lsel = wg % LR;
-        wg /= LR;
+        lsel = wg % LRr;
+        wg /= LRr;
     }
     const int x = wg & 1;
     wg >>= 1;
@@ -263,6 +268,7 @@ __global__ __launch_bounds__(2 * D) void rq_pack_kernel(PackArgs a) {
     const int t1 = min(t0 + a.tokens_per_wg, a.n_tokens);
     const int loop0 = a.group_idx * L;
     const float* R = a.rot + (int64_t)(h * 2 + x) * D * D;
+    const bool norm_ratio = Gm.scale_rule == 1;
 
     __shared__ double sh_y[NL > 1 ? NL : 2][D];
     __shared__ double red[NL + 1 > 2 ? NL + 1 : 2][NT / 64];
@@ -304,13 +310,14 @@ __global__ __launch_bounds__(2 * D) void rq_pack_kernel(PackArgs a) {
             // <a, a>; the loops are rotated together and then quantized side by side
             double sums[NL + 1];
 #pragma unroll
-            for (int l = 0; l < NL; ++l) sums[l] = xv[l] * a_hat;
+            for (int l = 0; l < NL; ++l) sums[l] = xv[l] * (norm_ratio ? xv[l] : a_hat);
             sums[NL] = a_hat * a_hat;
             block_sum<NT, NL + 1>(sums, red);
             double cs[NL];
 #pragma unroll
             for (int l = 0; l < NL; ++l) {
-                cs[l] = bf16_round(sums[NL] > 0.0 ? sums[l] / sums[NL] : 0.0);
+                const double q = sums[l] / sums[NL];
+                cs[l] = bf16_round(sums[NL] > 0.0 ? (norm_ratio ? sqrt(q) : q) : 0.0);
                 if (p == 0) sh_y[l][i] = xv[l] - cs[l] * a_hat;
             }
             __syncthreads();
@@ -331,9 +338,10 @@ __global__ __launch_bounds__(2 * D) void rq_pack_kernel(PackArgs a) {
             // loop l references the rebuilt loop l+1 (the anchor closes the chain)
             double ref = a_hat;
             for (int l = L - 2; l >= 0; --l) {
-                double s2[2] = {xv[l] * ref, ref * ref};
+                double s2[2] = {xv[l] * (norm_ratio ? xv[l] : ref), ref * ref};
                 block_sum<NT, 2>(s2, red);
-                const double c = bf16_round(s2[1] > 0.0 ? s2[0] / s2[1] : 0.0);
+                const double q = s2[0] / s2[1];
+                const double c = bf16_round(s2[1] > 0.0 ? (norm_ratio ? sqrt(q) : q) : 0.0);
                 if (p == 0) sh_y[0][i] = xv[l] - c * ref;
                 __syncthreads();
                 double rl[1];
@@ -425,18 +433,20 @@ __device__ __forceinline__ void quantize_row(const double (&x)[CPL], double (&xh
     }
 }
 
-template <int D, int G, int LR>
+// LB = min(L - 1, 3) residual loops per product; the loop count itself comes from the
+// configuration, so one instantiation serves every group length of at least LB + 1.
+template <int D, int G, int LB>
 __global__ __launch_bounds__(bulk_threads<D>()) void rq_pack_bulk_kernel(PackArgs a) {
     constexpr int kBulkThreads = bulk_threads<D>();
     constexpr int TK = kBulkTokens, NW = kBulkThreads / kWave;
     constexpr int CPL = D / kWave;                    // channels per lane
-    constexpr int LB = LR < 3 ? LR : 3;               // residual loops per product
     constexpr int NCOL = TK * LB;                     // columns of Y: (token, loop)
     constexpr int RB = D / 4, CB = kBulkThreads / RB, CPT = NCOL / CB;
     static_assert(NCOL % CB == 0 && CPT >= 1 && TK % NW == 0, "register tile, tokens per wave");
     constexpr int RS = D + 4;                         // padded LDS row of R (floats)
-    constexpr int L = LR + 1;
     const Geom& Gm = a.geo;
+    const int LR = Gm.L - 1, L = Gm.L;
+    const bool norm_ratio = Gm.scale_rule == 1;
     int wg = blockIdx.x;
     const int x = wg & 1;
     wg >>= 1;
@@ -542,9 +552,10 @@ __global__ __launch_bounds__(bulk_threads<D>()) void rq_pack_bulk_kernel(PackArg
                 }
                 double dot = 0.0;
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) dot = fma(xl[c], xh[c], dot);
+                for (int c = 0; c < CPL; ++c) dot = fma(xl[c], norm_ratio ? xl[c] : xh[c], dot);
                 dot = lanes_reduce<kWave>(dot, add);
-                const double cl = bf16_round(na > 0.0 ? dot / na : 0.0);
+                const double qn = dot / na;
+                const double cl = bf16_round(na > 0.0 ? (norm_ratio ? sqrt(qn) : qn) : 0.0);
                 if (lok && lane == 0) {
                     uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + l, tile);
                     reinterpret_cast<uint16_t*>(pl + (int64_t)kTile * (Gm.r_row + Gm.m_row))[jj] =
@@ -599,7 +610,8 @@ __global__ __launch_bounds__(bulk_threads<D>()) void rq_pack_bulk_kernel(PackArg
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) r[c] = yt[CPL * lane + c][tok * LB + li];
                 uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + (l < LR ? l : 0), tile);
-                quantize_row<G, CPL, 2>(r, rh, pl, Gm.r_row, Gm.m_row, jj, ok && l < LR, lane);
+                if (Gm.br == 4) quantize_row<G, CPL, 4>(r, rh, pl, Gm.r_row, Gm.m_row, jj, ok && l < LR, lane);
+                else quantize_row<G, CPL, 2>(r, rh, pl, Gm.r_row, Gm.m_row, jj, ok && l < LR, lane);
             }
         }
     }
@@ -608,32 +620,35 @@ __global__ __launch_bounds__(bulk_threads<D>()) void rq_pack_bulk_kernel(PackArg
 template <int D, int G>
 static hipError_t launch_bulk(const PackArgs& a, int nwg, hipStream_t stream) {
     constexpr int kBulkThreads = bulk_threads<D>();
-    switch (a.geo.L - 1) {
+    const int LR = a.geo.L - 1;
+    if (LR < 1 || LR > kMaxLoops - 1) return hipErrorInvalidValue;
+    switch (LR < 3 ? LR : 3) {
         case 1: hipLaunchKernelGGL((rq_pack_bulk_kernel<D, G, 1>), dim3(nwg), dim3(kBulkThreads), 0, stream, a); break;
         case 2: hipLaunchKernelGGL((rq_pack_bulk_kernel<D, G, 2>), dim3(nwg), dim3(kBulkThreads), 0, stream, a); break;
-        case 3: hipLaunchKernelGGL((rq_pack_bulk_kernel<D, G, 3>), dim3(nwg), dim3(kBulkThreads), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((rq_pack_bulk_kernel<D, G, 4>), dim3(nwg), dim3(kBulkThreads), 0, stream, a); break;
-        case 5: hipLaunchKernelGGL((rq_pack_bulk_kernel<D, G, 5>), dim3(nwg), dim3(kBulkThreads), 0, stream, a); break;
-        case 6: hipLaunchKernelGGL((rq_pack_bulk_kernel<D, G, 6>), dim3(nwg), dim3(kBulkThreads), 0, stream, a); break;
-        case 7: hipLaunchKernelGGL((rq_pack_bulk_kernel<D, G, 7>), dim3(nwg), dim3(kBulkThreads), 0, stream, a); break;
-        default: return hipErrorInvalidValue;
+        default: hipLaunchKernelGGL((rq_pack_bulk_kernel<D, G, 3>), dim3(nwg), dim3(kBulkThreads), 0, stream, a); break;
     }
     return hipGetLastError();
 }
 
+// SPLIT: one instantiation (the loop count is read at run time); otherwise one per loop count
 template <int D, int G, bool SPLIT>
 static hipError_t launch_dgs(const PackArgs& a, int nwg, hipStream_t stream) {
     const int LR = a.geo.L - 1;
-    const dim3 grid(SPLIT ? nwg * LR : nwg);
+    if (LR < 1 || LR > kMaxLoops - 1) return hipErrorInvalidValue;
+    if constexpr (SPLIT) {
+        hipLaunchKernelGGL((rq_pack_kernel<D, G, 1, true>), dim3(nwg * LR), dim3(2 * D), 0, stream, a);
+        return hipGetLastError();
+    }
+    const dim3 grid(nwg);
     switch (LR) {
-        case 1: hipLaunchKernelGGL((rq_pack_kernel<D, G, 1, SPLIT>), grid, dim3(2 * D), 0, stream, a); break;
-        case 2: hipLaunchKernelGGL((rq_pack_kernel<D, G, 2, SPLIT>), grid, dim3(2 * D), 0, stream, a); break;
-        case 3: hipLaunchKernelGGL((rq_pack_kernel<D, G, 3, SPLIT>), grid, dim3(2 * D), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((rq_pack_kernel<D, G, 4, SPLIT>), grid, dim3(2 * D), 0, stream, a); break;
-        case 5: hipLaunchKernelGGL((rq_pack_kernel<D, G, 5, SPLIT>), grid, dim3(2 * D), 0, stream, a); break;
-        case 6: hipLaunchKernelGGL((rq_pack_kernel<D, G, 6, SPLIT>), grid, dim3(2 * D), 0, stream, a); break;
-        case 7: hipLaunchKernelGGL((rq_pack_kernel<D, G, 7, SPLIT>), grid, dim3(2 * D), 0, stream, a); break;
-        default: return hipErrorInvalidValue;
+        case 1: hipLaunchKernelGGL((rq_pack_kernel<D, G, 1, false>), grid, dim3(2 * D), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((rq_pack_kernel<D, G, 2, false>), grid, dim3(2 * D), 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((rq_pack_kernel<D, G, 3, false>), grid, dim3(2 * D), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((rq_pack_kernel<D, G, 4, false>), grid, dim3(2 * D), 0, stream, a); break;
+        case 5: hipLaunchKernelGGL((rq_pack_kernel<D, G, 5, false>), grid, dim3(2 * D), 0, stream, a); break;
+        case 6: hipLaunchKernelGGL((rq_pack_kernel<D, G, 6, false>), grid, dim3(2 * D), 0, stream, a); break;
+        case 7: hipLaunchKernelGGL((rq_pack_kernel<D, G, 7, false>), grid, dim3(2 * D), 0, stream, a); break;
+        default: return hipErrorInvalidValue;           // longer groups take the SPLIT kernel
     }
     return hipGetLastError();
 }

@@ -49,6 +49,7 @@ class Workload:
     loop_scale: Union[Tuple[float, ...], str]   # a_l for loops 0..L-2, or "uniform(0.8,1.0)"
     q_dtype: str             # "fp32" | "bf16"
     chained: bool = False
+    scale_rule: int = 0      # 0: least-squares c; 1: norm-ratio c
 
     @property
     def n_loops(self) -> int:

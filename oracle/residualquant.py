@@ -61,6 +61,7 @@ class Config:
     n_q_heads: int
     max_batch: int
     max_ctx: int
+    scale_rule: int = 0     # 0: least-squares c; 1: norm-ratio c (the digest's appendix alternative)
 
     @property
     def n_loops(self) -> int:
@@ -118,6 +119,24 @@ def ls_coefficient(x: np.ndarray, ref: np.ndarray) -> Tuple[np.ndarray, np.ndarr
     return bf16_round(exact), exact
 
 
+def norm_ratio_coefficient(x: np.ndarray, ref: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """c* = ||x|| / ||ref|| (0 when ref is all zero) and c = BF16(c*).
+
+    The digest names norm-ratio scaling (ablation section, appendix table) as the
+    alternative to least squares without printing it; the plain reading is the ratio of
+    the Euclidean norms, which matches the magnitude of c * ref to that of x and ignores
+    the direction."""
+    xx = np.sum(x * x, axis=-1)
+    rr = np.sum(ref * ref, axis=-1)
+    exact = np.where(rr > 0, np.sqrt(xx / np.where(rr > 0, rr, 1.0)), 0.0)
+    return bf16_round(exact), exact
+
+
+def coefficient(x: np.ndarray, ref: np.ndarray, cfg: "Config") -> Tuple[np.ndarray, np.ndarray]:
+    """The scaling rule the configuration selects."""
+    return norm_ratio_coefficient(x, ref) if cfg.scale_rule == 1 else ls_coefficient(x, ref)
+
+
 # ---------------------------------------------------------------------------
 # encoding one anchor group of loops for one (KV head, K|V)
 # ---------------------------------------------------------------------------
@@ -143,8 +162,8 @@ def encode(xs: np.ndarray, rot: np.ndarray, cfg: Config) -> Encoded:
     reads"): every loop l < L-1 is referenced to the dequantized anchor a_hat.
     Chained (same paragraph, the alternative design): loop l is referenced to the
     reconstruction of loop l+1, and the anchor closes the chain.
-    For each non-anchor loop: c = BF16(<x, ref>/<ref, ref>); y = x - c * ref;
-    r = R y; r is group-quantized at the residual width.
+    For each non-anchor loop: c = BF16(<x, ref>/<ref, ref>) (or the norm ratio, see
+    ``coefficient``); y = x - c * ref; r = R y; r is group-quantized at the residual width.
     """
     L = xs.shape[0]
     g = cfg.group
@@ -154,7 +173,7 @@ def encode(xs: np.ndarray, rot: np.ndarray, cfg: Config) -> Encoded:
     resid: List = [None] * (L - 1)
     ref = a_hat
     for l in range(L - 2, -1, -1):
-        c, _ = ls_coefficient(xs[l], ref)
+        c, _ = coefficient(xs[l], ref, cfg)
         y = xs[l] - c[..., None] * ref
         r = y @ R.T                                  # r = R y, tokens as rows
         qr, zr, sr = quantize(r, cfg.resid_bits, g)

@@ -36,7 +36,7 @@ def oracle_cfg(wl, chained=None, max_batch=None, max_ctx=None, n_kv_heads=None, 
     return RQ.Config(wl.head_dim, wl.group, wl.anchor_bits, wl.resid_bits, wl.loops_per_group,
                      wl.n_groups, bool(wl.chained if chained is None else chained),
                      n_kv_heads or wl.n_kv_heads, n_q_heads or wl.n_q_heads,
-                     max_batch or wl.batch, max_ctx or wl.ctx + 1)
+                     max_batch or wl.batch, max_ctx or wl.ctx + 1, wl.scale_rule)
 
 
 def pending_strides(kv: torch.Tensor):
@@ -64,7 +64,7 @@ def sub_cache(cache_np: np.ndarray, cfg: RQ.Config, b: int, h: int):
     lay = RQ.Layout(cfg)
     start = (b * cfg.n_kv_heads + h) * 2 * lay.block_bytes
     sub = RQ.Config(cfg.head_dim, cfg.group, cfg.anchor_bits, cfg.resid_bits, cfg.loops_per_group,
-                    cfg.n_groups, cfg.chained, 1, cfg.n_q_heads // cfg.n_kv_heads, 1, cfg.max_ctx)
+                    cfg.n_groups, cfg.chained, 1, cfg.n_q_heads // cfg.n_kv_heads, 1, cfg.max_ctx, cfg.scale_rule)
     return np.ascontiguousarray(cache_np[start: start + 2 * lay.block_bytes]), sub
 
 
@@ -103,7 +103,7 @@ def check_encoding(enc: RQ.Encoded, xs: np.ndarray, R: np.ndarray, sub: RQ.Confi
     a_hat = RQ.dequantize(qa, za, sa, g)
     for l in range(L - 2, -1, -1):
         ref = RQ.reconstruct(enc, l + 1, R, sub) if sub.chained else a_hat
-        c_exp, _ = RQ.ls_coefficient(xs[l], ref)
+        c_exp, _ = RQ.coefficient(xs[l], ref, sub)
         qg, zg, sg, cg = enc.resid[l]
         dc = np.abs(cg - c_exp)
         assert np.all(dc <= _ulp_bf16(c_exp)), f"c off by more than 1 ulp: {dc.max()}"
@@ -155,3 +155,93 @@ def close(o_gpu: np.ndarray, o_ref: np.ndarray) -> float:
     """Return max|diff| / bound; <= 1 passes."""
     bound = ATOL_REL * np.abs(o_ref).max() + ATOL_ABS
     return float(np.abs(o_gpu - o_ref).max() / bound)
+
+
+def setup_case(B, wl, chained, batch, ctx, hkv=None, hq=None, seed=1234):
+    """Workload of a small parity case: batch rows with context lengths ctx (the largest is
+    the packed context T), seeded inputs on the GPU, the library and oracle configurations."""
+    T = max(ctx)
+    wl = wl.with_(batch=batch, ctx=T, chained=chained,
+                  n_kv_heads=hkv or wl.n_kv_heads, n_q_heads=hq or wl.n_q_heads)
+    inp = synth.generate(wl, seed=seed, device="cuda")
+    return wl, inp, B.config_for(wl), oracle_cfg(wl), ctx, T
+
+
+def run_pack_parity(B, name, wl, inp, cfg, ocfg, T):
+    """Pack the whole context of every group on the GPU and check every stored code,
+    FP8 offset/scale and c against the oracle's rules."""
+    say(f"[pack] case={name} T={T} batch={wl.batch}")
+    cache = gpu_pack(B, cfg, inp.kv, inp.rot, T)
+    torch.cuda.synchronize()
+    kv = inp.kv.double().cpu().numpy()
+    rot = inp.rot.double().cpu().numpy()
+    stats = new_stats()
+    for b in range(wl.batch):
+        for h in range(wl.n_kv_heads):
+            block = device_block(cache, ocfg, b, h)
+            _, sub = sub_cache(np.zeros(0, np.uint8), ocfg, 0, 0)
+            xs = [[kv[k, :, x, b, h, :T] for x in range(2)] for k in range(wl.n_groups)]
+            check_pack_block(block, sub, xs, rot[h], T, stats)
+    say(f"[pack] case={name} stats={stats}")
+    assert_stats(stats)
+
+
+def run_decode_step_parity(B, name, wl, inp, cfg, ocfg, ctx, T, loops=None):
+    """One decode step through every loop (or the listed ones, then only the drains of
+    groups whose loops all ran): attention at each loop with the current token written to
+    the pending buffer, compared with the oracle on the GPU's bytes and on the oracle's own
+    pack, at several split counts; after a group's last loop, the finished token packed from
+    that buffer and checked."""
+    say(f"[decode] case={name} T={T} ctx={ctx}")
+    dev = inp.kv.device
+    L, d, Hq, Hkv = wl.loops_per_group, wl.head_dim, wl.n_q_heads, wl.n_kv_heads
+    cache = gpu_pack(B, cfg, inp.kv, inp.rot, T)
+    ctx_len = torch.tensor(ctx, dtype=torch.int32, device=dev)
+    ws = torch.zeros(B.rq_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    pending = torch.zeros(wl.batch, L, 2, Hkv, d, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    cache_np = cache.cpu().numpy()
+    kv = inp.kv.double().cpu().numpy()
+    rot = inp.rot.double().cpu().numpy()
+    own = RQ.pack_context(kv, rot, ocfg, T)
+    lay = RQ.Layout(ocfg)
+    sc = synth.sm_scale(d)
+    n_tiles = -(-T // 64)
+    run = list(range(wl.n_loops)) if loops is None else list(loops)
+    for loop in run:
+        grp, l = divmod(loop, L)
+        k_cur = inp.kv[grp, l, 0, :, :, T].contiguous()
+        v_cur = inp.kv[grp, l, 1, :, :, T].contiguous()
+        q = inp.q[loop].contiguous()
+        ref_gpu = RQ.decode_attention(cache_np, lay, loop, q.double().cpu().numpy(), kv[grp, l, 0, :, :, T],
+                                      kv[grp, l, 1, :, :, T], ctx, rot, sc)
+        ref_own = RQ.decode_attention(own, lay, loop, q.double().cpu().numpy(), kv[grp, l, 0, :, :, T],
+                                      kv[grp, l, 1, :, :, T], ctx, rot, sc)
+        for ns in sorted({0, 1, min(3, n_tiles), n_tiles}):
+            out = torch.full((wl.batch, Hq, d), float("nan"), dtype=torch.float32, device=dev)
+            say(f"[decode] case={name} loop={loop} n_splits={ns}")
+            B.rq_decode_attention(cfg, cache, loop, q, k_cur, v_cur, pending, ctx_len, T, inp.rot, sc, out,
+                                  ws, wl.batch, n_splits=ns)
+            torch.cuda.synchronize()
+            o = out.double().cpu().numpy()
+            assert np.all(np.isfinite(o))
+            e1, e2 = close(o, ref_gpu), close(o, ref_own)
+            say(f"    err/bound vs oracle(gpu cache)={e1:.3f} vs oracle(own cache)={e2:.3f}")
+            assert e1 <= 1.0 and e2 <= 1.0
+        if l == L - 1 and all(grp * L + m in run for m in range(L)):
+            # pending now holds the current token of every loop of this group
+            want = inp.kv[grp, :, :, :, :, T].permute(2, 0, 1, 3, 4)
+            assert torch.equal(pending, want)
+            say(f"[decode] case={name} pack finished token of group {grp}")
+            B.rq_quantize_token(cfg, cache, pending, grp, ctx_len, inp.rot, wl.batch, 1)
+            torch.cuda.synchronize()
+            cache_np = cache.cpu().numpy()
+            stats = new_stats()
+            for b in range(wl.batch):
+                for h in range(Hkv):
+                    block, sub = sub_cache(cache_np, ocfg, b, h)
+                    for x in range(2):
+                        enc = RQ.read_tokens(block, RQ.Layout(sub), 0, 0, x, grp, ctx[b] + 1)
+                        check_encoding(slice_enc(enc, slice(ctx[b], ctx[b] + 1)),
+                                       kv[grp, :, x, b, h, T:T + 1], rot[h, x], sub, stats)
+            assert_stats(stats)

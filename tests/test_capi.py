@@ -55,15 +55,31 @@ def test_cache_bytes_match_oracle_layout(B, name, chained):
 
 def test_invalid_configs_have_no_size(B):
     wl = synth.WORKLOADS["ouro_b4_t8192"]
-    for field, bad in (("head_dim", 96), ("group", 24), ("anchor_bits", 3), ("resid_bits", 4),
-                       ("loops_per_group", 1), ("n_q_heads", 17), ("max_batch", 0), ("max_ctx", 0)):
+    for field, bad in (("head_dim", 96), ("group", 24), ("anchor_bits", 3), ("resid_bits", 3),
+                       ("resid_bits", 8), ("loops_per_group", 1), ("loops_per_group", 17), ("n_q_heads", 17),
+                       ("max_batch", 0), ("max_ctx", 0), ("scale_rule", 2), ("scale_rule", -1)):
         cfg = B.config_for(wl)
         setattr(cfg, field, bad)
         assert B.rq_cache_bytes(cfg) == 0, field
         assert B.rq_workspace_bytes(cfg) == 0, field
     cfg = B.config_for(wl.with_(loops_per_group=8), chained=True)
     assert B.rq_cache_bytes(cfg) == 0                    # chained reads at most 3 residual planes
+    cfg = B.config_for(wl.with_(resid_bits=4), chained=True)
+    assert B.rq_cache_bytes(cfg) == 0                    # 4-bit residuals: shared anchor only
     assert B.rq_bf16_workspace_bytes(B.rq_bf16_config(96, 1, 1, 1, 64)) == 0
+
+
+@pytest.mark.parametrize("variant", [dict(resid_bits=4), dict(loops_per_group=16, loop_scale="uniform(0.8,1.0)"),
+                                     dict(loops_per_group=8, loop_scale="uniform(0.8,1.0)"), dict(scale_rule=1),
+                                     dict(group=16, anchor_bits=4, resid_bits=2)])
+def test_variant_configs_match_oracle_layout(B, variant):
+    """The precision, group-length and scale-rule settings are supported tuples whose cache
+    size is the oracle layout's."""
+    wl = synth.WORKLOADS["ouro_b4_t8192"].with_(**variant)
+    cfg = B.config_for(wl)
+    ocfg = RQ.Config(wl.head_dim, wl.group, wl.anchor_bits, wl.resid_bits, wl.loops_per_group, wl.n_groups,
+                     False, wl.n_kv_heads, wl.n_q_heads, wl.batch, wl.ctx + 1, wl.scale_rule)
+    assert B.rq_cache_bytes(cfg) == RQ.Layout(ocfg).total_bytes > 0
 
 
 def test_status_strings(B):

@@ -8,8 +8,7 @@ import torch
 from looped_transformer_decode_amd import synth
 from oracle import residualquant as RQ
 
-from _support import (assert_stats, check_encoding, check_pack_block, close, device_block, gpu_pack,
-                      new_stats, oracle_cfg, say, slice_enc, sub_cache)
+from _support import (close, gpu_pack, run_decode_step_parity, run_pack_parity, say, setup_case)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,32 +34,13 @@ CASES = {
 
 def _setup(B, name, seed=1234):
     wl, chained, batch, ctx, hkv, hq = CASES[name]
-    T = max(ctx)
-    wl = wl.with_(batch=batch, ctx=T, chained=chained,
-                  n_kv_heads=hkv or wl.n_kv_heads, n_q_heads=hq or wl.n_q_heads)
-    inp = synth.generate(wl, seed=seed, device="cuda")
-    cfg = B.config_for(wl)
-    ocfg = oracle_cfg(wl)
-    return wl, inp, cfg, ocfg, ctx, T
+    return setup_case(B, wl, chained, batch, ctx, hkv, hq, seed)
 
 
 @pytest.mark.parametrize("name", sorted(CASES))
 def test_pack_context_parity(B, name):
     wl, inp, cfg, ocfg, ctx, T = _setup(B, name)
-    say(f"[pack] case={name} T={T} batch={wl.batch}")
-    cache = gpu_pack(B, cfg, inp.kv, inp.rot, T)
-    torch.cuda.synchronize()
-    kv = inp.kv.double().cpu().numpy()
-    rot = inp.rot.double().cpu().numpy()
-    stats = new_stats()
-    for b in range(wl.batch):
-        for h in range(wl.n_kv_heads):
-            block = device_block(cache, ocfg, b, h)
-            _, sub = sub_cache(np.zeros(0, np.uint8), ocfg, 0, 0)
-            xs = [[kv[k, :, x, b, h, :T] for x in range(2)] for k in range(wl.n_groups)]
-            check_pack_block(block, sub, xs, rot[h], T, stats)
-    say(f"[pack] case={name} stats={stats}")
-    assert_stats(stats)
+    run_pack_parity(B, name, wl, inp, cfg, ocfg, T)
 
 
 @pytest.mark.parametrize("name", sorted(CASES))
@@ -68,58 +48,7 @@ def test_decode_step_parity(B, name):
     """One decode step through every loop: attention at each loop (with the current token
     written to the pending buffer), then the finished token packed from that buffer."""
     wl, inp, cfg, ocfg, ctx, T = _setup(B, name, seed=99)
-    say(f"[decode] case={name} T={T} ctx={ctx}")
-    dev = inp.kv.device
-    L, d, Hq, Hkv = wl.loops_per_group, wl.head_dim, wl.n_q_heads, wl.n_kv_heads
-    cache = gpu_pack(B, cfg, inp.kv, inp.rot, T)
-    ctx_len = torch.tensor(ctx, dtype=torch.int32, device=dev)
-    ws = torch.zeros(B.rq_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
-    pending = torch.zeros(wl.batch, L, 2, Hkv, d, dtype=torch.bfloat16, device=dev)
-    torch.cuda.synchronize()
-    cache_np = cache.cpu().numpy()
-    kv = inp.kv.double().cpu().numpy()
-    rot = inp.rot.double().cpu().numpy()
-    own = RQ.pack_context(kv, rot, ocfg, T)
-    lay = RQ.Layout(ocfg)
-    sc = synth.sm_scale(d)
-    n_tiles = -(-T // 64)
-    for loop in range(wl.n_loops):
-        grp, l = divmod(loop, L)
-        k_cur = inp.kv[grp, l, 0, :, :, T].contiguous()
-        v_cur = inp.kv[grp, l, 1, :, :, T].contiguous()
-        q = inp.q[loop].contiguous()
-        ref_gpu = RQ.decode_attention(cache_np, lay, loop, q.double().cpu().numpy(), kv[grp, l, 0, :, :, T],
-                                      kv[grp, l, 1, :, :, T], ctx, rot, sc)
-        ref_own = RQ.decode_attention(own, lay, loop, q.double().cpu().numpy(), kv[grp, l, 0, :, :, T],
-                                      kv[grp, l, 1, :, :, T], ctx, rot, sc)
-        for ns in sorted({0, 1, min(3, n_tiles), n_tiles}):
-            out = torch.full((wl.batch, Hq, d), float("nan"), dtype=torch.float32, device=dev)
-            say(f"[decode] case={name} loop={loop} n_splits={ns}")
-            B.rq_decode_attention(cfg, cache, loop, q, k_cur, v_cur, pending, ctx_len, T, inp.rot, sc, out,
-                                  ws, wl.batch, n_splits=ns)
-            torch.cuda.synchronize()
-            o = out.double().cpu().numpy()
-            assert np.all(np.isfinite(o))
-            e1, e2 = close(o, ref_gpu), close(o, ref_own)
-            say(f"    err/bound vs oracle(gpu cache)={e1:.3f} vs oracle(own cache)={e2:.3f}")
-            assert e1 <= 1.0 and e2 <= 1.0
-        if l == L - 1:
-            # pending now holds the current token of every loop of this group
-            want = inp.kv[grp, :, :, :, :, T].permute(2, 0, 1, 3, 4)
-            assert torch.equal(pending, want)
-            say(f"[decode] case={name} pack finished token of group {grp}")
-            B.rq_quantize_token(cfg, cache, pending, grp, ctx_len, inp.rot, wl.batch, 1)
-            torch.cuda.synchronize()
-            cache_np = cache.cpu().numpy()
-            stats = new_stats()
-            for b in range(wl.batch):
-                for h in range(Hkv):
-                    block, sub = sub_cache(cache_np, ocfg, b, h)
-                    for x in range(2):
-                        enc = RQ.read_tokens(block, RQ.Layout(sub), 0, 0, x, grp, ctx[b] + 1)
-                        check_encoding(slice_enc(enc, slice(ctx[b], ctx[b] + 1)),
-                                       kv[grp, :, x, b, h, T:T + 1], rot[h, x], sub, stats)
-            assert_stats(stats)
+    run_decode_step_parity(B, name, wl, inp, cfg, ocfg, ctx, T)
 
 
 @pytest.mark.parametrize("name", ["tiny", "d128g32_ragged", "gqa4_two_groups"])

@@ -1,5 +1,6 @@
 """Pins of the oracle's encoding: least-squares coefficient, rotation, reconstruction
 bounds, chained-variant special cases, byte layout and the pages' storage arithmetic."""
+import dataclasses
 import json
 import os
 
@@ -46,6 +47,63 @@ def test_ls_coefficient_normal_equation_and_rounding():
 def test_ls_coefficient_zero_reference():
     c, exact = RQ.ls_coefficient(np.ones((1, 8)), np.zeros((1, 8)))
     assert c[0] == 0 and exact[0] == 0
+
+
+def test_norm_ratio_coefficient_matches_norms():
+    """Norm ratio: |c*| * ||ref|| = ||x|| for every vector (the defining property), c* >= 0,
+    c = BF16(c*) within half an ulp."""
+    xs = _loops(21, 400, 128)
+    q, z, s = RQ.quantize(xs[3], 4, 32)
+    a_hat = RQ.dequantize(q, z, s, 32)
+    for l in range(3):
+        c, exact = RQ.norm_ratio_coefficient(xs[l], a_hat)
+        lhs = exact * np.linalg.norm(a_hat, axis=-1)
+        assert np.all(np.abs(lhs - np.linalg.norm(xs[l], axis=-1)) <= 1e-13 * lhs)
+        assert np.all(exact >= 0)
+        ulp = 2.0 ** (np.floor(np.log2(exact)) - 7)
+        assert np.all(np.abs(c - exact) <= ulp / 2)
+
+
+def test_norm_ratio_special_cases():
+    """x = k * ref with k > 0: both rules give k; x = -ref: least squares gives -1, the norm
+    ratio 1; x orthogonal to ref: least squares gives 0, the norm ratio ||x||/||ref||;
+    ref = 0: both give 0."""
+    rng = np.random.default_rng(3)
+    ref = rng.normal(size=(5, 64))
+    for k in (0.5, 1.0, 3.0):
+        for fn in (RQ.ls_coefficient, RQ.norm_ratio_coefficient):
+            _, exact = fn(k * ref, ref)
+            assert np.allclose(exact, k, rtol=1e-14, atol=0)
+    assert np.allclose(RQ.ls_coefficient(-ref, ref)[1], -1.0, rtol=1e-14)
+    assert np.allclose(RQ.norm_ratio_coefficient(-ref, ref)[1], 1.0, rtol=1e-14)
+    e1 = np.zeros((1, 8)); e1[0, 0] = 2.0
+    e2 = np.zeros((1, 8)); e2[0, 1] = 0.5
+    assert RQ.ls_coefficient(e1, e2)[1][0] == 0.0
+    assert RQ.norm_ratio_coefficient(e1, e2)[1][0] == 4.0
+    c, exact = RQ.norm_ratio_coefficient(np.ones((1, 8)), np.zeros((1, 8)))
+    assert c[0] == 0 and exact[0] == 0
+
+
+def test_encode_uses_the_configured_rule():
+    """A configuration with the norm-ratio rule stores ||x||/||a_hat|| (rounded to BF16) as c
+    and quantizes x - c * a_hat; the default stores the least-squares c."""
+    wl = synth.WORKLOADS["tiny_d64_t256"]
+    xs = _loops(22, 50, 64)
+    rot = synth.haar_rotations(1, 64, 9).double().numpy()[0, 0]
+    for rule, fn in ((0, RQ.ls_coefficient), (1, RQ.norm_ratio_coefficient)):
+        cfg = dataclasses.replace(_cfg(wl), scale_rule=rule)
+        enc = RQ.encode(xs, rot, cfg)
+        a_hat = RQ.dequantize(*enc.anchor, wl.group)
+        for l in range(3):
+            c_exp, _ = fn(xs[l], a_hat)
+            assert np.array_equal(enc.resid[l][3], c_exp)
+            r = (xs[l] - c_exp[:, None] * a_hat) @ rot.T
+            qr, zr, sr = RQ.quantize(r, wl.resid_bits, wl.group)
+            assert np.array_equal(enc.resid[l][0], qr)
+    # the two rules give different c on these inputs
+    c0 = RQ.encode(xs, rot, _cfg(wl)).resid[0][3]
+    c1 = RQ.encode(xs, rot, dataclasses.replace(_cfg(wl), scale_rule=1)).resid[0][3]
+    assert not np.array_equal(c0, c1)
 
 
 def test_synthetic_rotations_are_orthogonal():
