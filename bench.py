@@ -132,6 +132,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--chained", action="store_true")
+    ap.add_argument("--resid-bits", type=int, default=0, help="4: uniform INT4 (with 4-bit anchors)")
+    ap.add_argument("--loops-per-group", type=int, default=0, help="loop group length (8 or 16: the larger groups)")
+    ap.add_argument("--scale-rule", type=int, default=0, help="1: norm-ratio coefficient")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--replicas", type=int, default=0)
@@ -153,6 +156,17 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     if args.chained:
         wl = wl.with_(chained=True)
+    if args.resid_bits:
+        wl = wl.with_(resid_bits=args.resid_bits)
+    if args.loops_per_group:
+        wl = wl.with_(loops_per_group=args.loops_per_group, loop_scale="uniform(0.8,1.0)",
+                      n_groups=max(1, wl.n_loops // args.loops_per_group))
+    if args.scale_rule:
+        wl = wl.with_(scale_rule=args.scale_rule)
+    variant = "".join(t for t, on in (("+int4", args.resid_bits == 4), (f"+L{args.loops_per_group}", args.loops_per_group),
+                                      ("+norm_ratio", args.scale_rule == 1)) if on)
+    if variant:
+        wl = wl.with_(name=wl.name + variant)
     L, d, T, Bt = wl.loops_per_group, wl.head_dim, wl.ctx, wl.batch
     print(f"[bench] workload={wl.name} chained={wl.chained}: generating inputs", file=sys.stderr, flush=True)
     inp = synth.generate(wl, seed=20261202, device=dev)
@@ -400,7 +414,8 @@ def main():
         "config": {"workload": wl.name, "batch": Bt, "ctx": T, "n_q_heads": wl.n_q_heads,
                    "n_kv_heads": wl.n_kv_heads, "head_dim": d, "loops": wl.n_loops,
                    "loops_per_group": L, "group": wl.group, "anchor_bits": wl.anchor_bits,
-                   "resid_bits": wl.resid_bits, "chained": wl.chained, "cache_replicas": n_rep},
+                   "resid_bits": wl.resid_bits, "chained": wl.chained, "scale_rule": wl.scale_rule,
+                   "cache_replicas": n_rep},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "kv_tokens_per_s": round(Bt * T / (res_ms * 1e-3), 1),
         "step": {"bytes": step_bytes, "ms_wall": round(ms_step, 4), "launch": launch,
