@@ -395,6 +395,35 @@ def main():
     roof_bytes = sum(algorithmic_bytes(wl, i % (L - 1), wl.chained) for i in range(roof_calls)) / roof_calls
     roof_gbps = roof_bytes / (roof_ms * 1e-3) / 1e9
 
+    # K/V projection of the current token (the step before the pending buffer): back-to-back
+    # calls over cold copies of the layer's weights (a model's other layers evict them between
+    # two loops of this one), and warm on one copy (a looped layer re-reads its own weights)
+    pin_ = synth.projection_inputs(wl, seed=20261203, device=dev)
+    H = pin_.x.shape[-1]
+    w_bytes = pin_.w.numel() * 2
+    n_wrep = max(2, math.ceil(6.4e8 / w_bytes))
+    wreps = [pin_.w] + [pin_.w.clone() for _ in range(n_wrep - 1)]
+    pk = torch.empty(Bt, wl.n_kv_heads, d, dtype=torch.bfloat16, device=dev)
+    pv = torch.empty_like(pk)
+    ppend = torch.zeros_like(pending)
+
+    def proj_ms(reps, cold):
+        for i in range(2):
+            B.rq_kv_project(cfg, pin_.x[i % n_loops], wreps[i % n_wrep], i % n_loops, pk, pv, ppend, Bt, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            B.rq_kv_project(cfg, pin_.x[i % n_loops], wreps[(i + 2) % n_wrep if cold else 0], i % n_loops, pk, pv,
+                            ppend, Bt, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    proj_cold = proj_ms(4 * n_wrep, True)
+    proj_warm = proj_ms(4 * n_wrep, False)
+    proj_bytes = w_bytes + Bt * H * 2 + 2 * (Bt * 2 * wl.n_kv_heads * d * 2)
+    del wreps
+
     value = step_bytes / (ms_step * 1e-3) / 1e9
     traffic = measured_traffic(wl.name) if not wl.chained and args.splits == 0 else None
     result = {
@@ -446,6 +475,14 @@ def main():
                   "vs_contiguous": round(roof_ms / paged_ms, 4),
                   "timing": "HIP events around back-to-back residual loop-steps through shuffled block tables "
                             "(one per replica, blocks of all replicas interleaved in one pool)"},
+        "kv_project": {"hidden": H, "outputs": 2 * wl.n_kv_heads * d, "weight_bytes": w_bytes,
+                       "bytes": proj_bytes, "ms": round(proj_cold, 4),
+                       "gbps": round(proj_bytes / (proj_cold * 1e-3) / 1e9, 1),
+                       "frac_of_hbm_peak": round(proj_bytes / (proj_cold * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                       "warm_ms": round(proj_warm, 4), "weight_replicas": n_wrep,
+                       "timing": "HIP events around back-to-back rq_kv_project calls (BF16 K/V of the current "
+                                 "token into k_cur/v_cur and the pending slot), cold weight copies; warm_ms "
+                                 "on one copy"},
         "roofline": {"bound": "hbm", "achieved": round(roof_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(roof_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "ms_per_launch": round(roof_ms, 4), "launches": roof_calls,

@@ -236,6 +236,32 @@ rq_status rq_decode_attention_paged(const rq_config* cfg, const void* pool, int3
                                     float sm_scale, float* out, void* workspace, size_t workspace_bytes,
                                     int32_t batch, int32_t n_splits, hipStream_t stream);
 
+/* rq_kv_project - K and V of the current token at one loop, stored where the decode step
+ * reads them.  Explainer, paragraph "Which print is the master": each loop's K/V of the
+ * token being decoded stay BF16 in a temporary buffer until the anchor group's last loop
+ * has run.  A looped Transformer runs the same layer every loop, so loop `loop`'s K/V are
+ * the layer's projections of that loop's hidden state:
+ *   k[b][h][i] = BF16(sum_c W_K[h][i][c] x[b][c]),  v likewise with W_V,
+ * rounded once to BF16 (half to even) from float32 sums of the exact products (the
+ * matrix cores accumulate in float32; no bias, no positional rotation).
+ *   cfg       : host pointer; n_kv_heads, head_dim, loops_per_group, n_groups, max_batch.
+ *   x         : device BF16 [batch][x_stride], the first `hidden` of each row used.
+ *   x_stride  : elements between rows, >= hidden, a multiple of 8.
+ *   hidden    : model width, a multiple of 32 in [32, 65536].
+ *   w_kv      : device BF16 [2][n_kv_heads][head_dim][hidden]: the K weight rows, then the V
+ *               rows, each output channel's weights contiguous over `hidden`.
+ *   loop      : global loop index 0..L*n_groups-1; the pending slot is loop % L.
+ *   k_cur, v_cur : device BF16 [batch][n_kv_heads][head_dim] or NULL: the decode step's
+ *               current-token inputs for this loop.
+ *   pending   : device BF16 [batch][L][2][n_kv_heads][head_dim] or NULL: the slot of loop
+ *               `loop % L` is written, the other slots are left alone.
+ *               At least one of k_cur, v_cur, pending is set.
+ *   batch     : rows 1..min(max_batch, 64) (more rows return RQ_ERR_UNSUPPORTED).
+ * Alignment: x, w_kv and the outputs 16-byte aligned.  One kernel is enqueued. */
+rq_status rq_kv_project(const rq_config* cfg, const uint16_t* x, int64_t x_stride, int32_t hidden,
+                        const uint16_t* w_kv, int32_t loop, uint16_t* k_cur, uint16_t* v_cur,
+                        uint16_t* pending, int32_t batch, hipStream_t stream);
+
 /* rq_stream_read - a measuring stick, not part of the method: read `bytes` of `buf`
  * with plain 16-byte loads (one contiguous slab per workgroup, XOR-folded into one word
  * per thread of `sink`).  Timed over the same buffers as the decode kernel it gives the

@@ -22,7 +22,8 @@ _lib = ctypes.CDLL(_LIB_PATH)
 
 EXPORTS = ("rq_cache_bytes", "rq_workspace_bytes", "rq_bf16_workspace_bytes", "rq_status_str",
            "rq_quantize_token", "rq_decode_attention", "rq_bf16_decode_attention", "rq_unpack_debug",
-           "rq_stream_read", "rq_paged_block_bytes", "rq_quantize_token_paged", "rq_decode_attention_paged")
+           "rq_stream_read", "rq_paged_block_bytes", "rq_quantize_token_paged", "rq_decode_attention_paged",
+           "rq_kv_project")
 
 
 class rq_config(ctypes.Structure):
@@ -74,6 +75,8 @@ _lib.rq_quantize_token_paged.restype = _i32
 _lib.rq_decode_attention_paged.argtypes = [_cfgp, _vp, _i32, _vp, _i32, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _i32,
                                            _vp, _f32, _vp, _vp, _sz, _i32, _i32, _vp]
 _lib.rq_decode_attention_paged.restype = _i32
+_lib.rq_kv_project.argtypes = [_cfgp, _vp, ctypes.c_int64, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _vp]
+_lib.rq_kv_project.restype = _i32
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -180,6 +183,20 @@ def rq_decode_attention_paged(cfg: rq_config, pool: torch.Tensor, n_blocks: int,
         ctypes.byref(cfg), _ptr(pool), n_blocks, _ptr(block_table), block_table.shape[1], loop, _ptr(q), q_bf16,
         _ptr(k_cur), _ptr(v_cur), _ptr(pending), _ptr(ctx_len), ctx_bound, _ptr(rot), sm_scale, _ptr(out),
         _ptr(workspace), _nbytes(workspace), batch, n_splits, _stream(stream)))
+
+
+def rq_kv_project(cfg: rq_config, x: torch.Tensor, w_kv: torch.Tensor, loop: int,
+                  k_cur: Optional[torch.Tensor], v_cur: Optional[torch.Tensor], pending: Optional[torch.Tensor],
+                  batch: int, stream=None) -> None:
+    """x: [batch][hidden] BF16 (any row stride); w_kv: [2][Hkv][d][hidden] BF16."""
+    if x.dtype != torch.bfloat16 or w_kv.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("rq_kv_project: x must be a BF16 [batch][hidden] tensor with unit channel stride")
+    hidden = x.shape[1]
+    if not w_kv.is_contiguous() or w_kv.shape[-1] != hidden:
+        raise ValueError("rq_kv_project: w_kv must be a contiguous [2][Hkv][d][hidden] BF16 tensor")
+    _check("rq_kv_project", _lib.rq_kv_project(
+        ctypes.byref(cfg), _ptr(x), x.stride(0), hidden, _ptr(w_kv), loop, _ptr(k_cur), _ptr(v_cur), _ptr(pending),
+        batch, _stream(stream)))
 
 
 STREAM_SINK_WORDS = 1 << 20

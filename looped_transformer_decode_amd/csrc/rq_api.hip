@@ -351,4 +351,35 @@ rq_status rq_bf16_decode_attention(const rq_bf16_config* cfg, uint16_t* k_cache,
     return launch_bf16(a, head_dim, q_is_bf16 != 0, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 
+rq_status rq_kv_project(const rq_config* cfg, const uint16_t* x, int64_t x_stride, int32_t hidden,
+                        const uint16_t* w_kv, int32_t loop, uint16_t* k_cur, uint16_t* v_cur, uint16_t* pending,
+                        int32_t batch, hipStream_t stream) {
+    Geom g;
+    if (cfg == nullptr) return RQ_ERR_INVALID_ARG;
+    if (!make_geom(cfg, &g)) return RQ_ERR_UNSUPPORTED;
+    if (!x || !w_kv || (!k_cur && !v_cur && !pending)) return RQ_ERR_INVALID_ARG;
+    if (batch < 1 || batch > g.max_batch || loop < 0 || loop >= g.L * g.n_groups) return RQ_ERR_INVALID_ARG;
+    if (hidden < 32 || hidden > 65536 || hidden % 32 != 0 || x_stride < hidden || x_stride > (1LL << 30))
+        return RQ_ERR_INVALID_ARG;
+    if (batch > 64) return RQ_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(w_kv) || (x_stride % 8) != 0 || (k_cur && !aligned16(k_cur)) ||
+        (v_cur && !aligned16(v_cur)) || (pending && !aligned16(pending)))
+        return RQ_ERR_MISALIGNED;
+    KvProjArgs a;
+    memset(&a, 0, sizeof(a));
+    a.x = x;
+    a.x_stride = x_stride;
+    a.w = w_kv;
+    a.hidden = hidden;
+    a.batch = batch;
+    a.hkv = g.hkv;
+    a.d = g.d;
+    a.L = g.L;
+    a.lloc = loop % g.L;
+    a.k_out = k_cur;
+    a.v_out = v_cur;
+    a.pending = pending;
+    return launch_kv_project(a, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
+}
+
 }  // extern "C"

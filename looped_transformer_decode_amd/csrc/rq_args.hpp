@@ -70,7 +70,21 @@ struct Bf16Args {
     MergeArgs mg;
 };
 
+// K/V projection of the current token: x [batch][hidden] (row stride x_stride elements),
+// w [2][hkv][d][hidden]; outputs BF16 k_out/v_out [batch][hkv][d] and the pending slot
+// [batch][L][2][hkv][d] at loop lloc (each output may be null, not all three).
+struct KvProjArgs {
+    const uint16_t* x;
+    int64_t x_stride;
+    const uint16_t* w;
+    int hidden, batch, hkv, d, L, lloc;
+    uint16_t* k_out;
+    uint16_t* v_out;
+    uint16_t* pending;
+};
+
 hipError_t launch_pack(const PackArgs& a, hipStream_t stream);
+hipError_t launch_kv_project(const KvProjArgs& a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int nres, bool qbf16, hipStream_t st);
 // grouped-query kernel (several query heads per KV head read each tile once)
 bool gqa_supported(const Geom& g, int nres);

@@ -153,3 +153,28 @@ def generate(wl: Workload, seed: int = 20261202, device: Union[str, torch.device
 def sm_scale(head_dim: int) -> float:
     """Softmax temperature 1/sqrt(d) (the pages give none; standard scaled dot-product attention)."""
     return 1.0 / math.sqrt(head_dim)
+
+
+@dataclasses.dataclass
+class ProjectionInputs:
+    x: torch.Tensor         # [n_loops][B][hidden] bf16: the hidden state each loop projects
+    w: torch.Tensor         # [2][Hkv][d][hidden] bf16: the layer's K and V weight rows
+
+
+def model_width(wl: Workload) -> int:
+    """Hidden size of the stand-in model: n_q_heads * head_dim (2048 for the Ouro-1.4B-sized
+    layer, 4096 for the 32-query-head one)."""
+    return wl.n_q_heads * wl.head_dim
+
+
+def projection_inputs(wl: Workload, seed: int = 20261203, device: Union[str, torch.device] = "cpu",
+                      batch: Optional[int] = None, hidden: Optional[int] = None) -> ProjectionInputs:
+    """Hidden states ~ N(0, 1) (the output of a normalisation layer) and weights ~ N(0, 1/hidden),
+    so that K and V come out of unit scale like the cache generator's; all rounded to BF16."""
+    B = batch if batch is not None else wl.batch
+    H = hidden if hidden is not None else model_width(wl)
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    x = torch.randn(wl.n_loops, B, H, generator=gen, dtype=torch.float32)
+    w = torch.randn(2, wl.n_kv_heads, wl.head_dim, H, generator=gen, dtype=torch.float32) / math.sqrt(H)
+    return ProjectionInputs(x.to(torch.bfloat16).to(device), w.to(torch.bfloat16).to(device))

@@ -221,3 +221,30 @@ def test_paged_entry_points_reject_bad_arguments(B):
     assert d(stride=0) == 1
     assert d(table=A + 1) == 3
     assert d(loop=4) == 1
+
+
+def test_kv_project_rejects_bad_arguments(B):
+    wl = synth.WORKLOADS["ouro_b4_t8192"]
+    cfg = B.config_for(wl)
+    f = B._lib.rq_kv_project
+
+    def call(cfg=cfg, x=A, stride=2048, hidden=2048, w=A, loop=0, k=A, v=A, pending=A, batch=4):
+        return f(ctypes.byref(cfg), x, stride, hidden, w, loop, k, v, pending, batch, None)
+
+    assert call(cfg=B.rq_config()) == 2
+    assert call(x=None) == 1
+    assert call(w=None) == 1
+    assert call(k=None, v=None, pending=None) == 1
+    assert call(loop=4) == 1
+    assert call(loop=-1) == 1
+    assert call(batch=0) == 1
+    assert call(batch=5) == 1
+    assert call(hidden=2000) == 1                   # not a multiple of 32
+    assert call(hidden=16) == 1
+    assert call(stride=1024) == 1                   # rows overlap
+    assert call(stride=2052) == 3                   # rows not 16-byte aligned
+    assert call(x=A + 8) == 3
+    assert call(w=A + 2) == 3
+    assert call(pending=A + 4) == 3
+    big = B.config_for(wl, max_batch=80)
+    assert call(cfg=big, batch=65) == 2             # more than four 16-row tiles
