@@ -407,20 +407,34 @@ def main():
     pv = torch.empty_like(pk)
     ppend = torch.zeros_like(pending)
 
-    def proj_ms(reps, cold):
+    def graph_ms(call, reps):
+        """GPU time per call of `reps` calls captured in one HIP graph (no host launch cost)."""
         for i in range(2):
-            B.rq_kv_project(cfg, pin_.x[i % n_loops], wreps[i % n_wrep], i % n_loops, pk, pv, ppend, Bt, stream=stream)
+            call(i)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                call(i + 2)
+        g.replay()
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(reps):
-            B.rq_kv_project(cfg, pin_.x[i % n_loops], wreps[(i + 2) % n_wrep if cold else 0], i % n_loops, pk, pv,
-                            ppend, Bt, stream=stream)
-        e1.record(stream)
+        e0.record()
+        g.replay()
+        e1.record()
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    proj_cold = proj_ms(4 * n_wrep, True)
-    proj_warm = proj_ms(4 * n_wrep, False)
+    reps = 4 * n_wrep
+    proj_cold = graph_ms(lambda i: B.rq_kv_project(cfg, pin_.x[i % n_loops], wreps[i % n_wrep], i % n_loops, pk, pv,
+                                                   ppend, Bt), reps)
+    proj_warm = graph_ms(lambda i: B.rq_kv_project(cfg, pin_.x[i % n_loops], wreps[0], i % n_loops, pk, pv, ppend,
+                                                   Bt), reps)
+    # references: a plain load loop over the same weight bytes (cold copies), and the same
+    # launch with hidden = 32 (the grid, products and epilogue without the weight stream)
+    proj_stream = graph_ms(lambda i: B.rq_stream_read(wreps[i % n_wrep], w_bytes, sink), reps)
+    x32 = pin_.x[0][:, :32].contiguous()
+    w32 = pin_.w[..., :32].contiguous()
+    proj_floor = graph_ms(lambda i: B.rq_kv_project(cfg, x32, w32, 0, pk, pv, ppend, Bt), reps)
     proj_bytes = w_bytes + Bt * H * 2 + 2 * (Bt * 2 * wl.n_kv_heads * d * 2)
     del wreps
 
@@ -480,9 +494,11 @@ def main():
                        "gbps": round(proj_bytes / (proj_cold * 1e-3) / 1e9, 1),
                        "frac_of_hbm_peak": round(proj_bytes / (proj_cold * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                        "warm_ms": round(proj_warm, 4), "weight_replicas": n_wrep,
-                       "timing": "HIP events around back-to-back rq_kv_project calls (BF16 K/V of the current "
-                                 "token into k_cur/v_cur and the pending slot), cold weight copies; warm_ms "
-                                 "on one copy"},
+                       "stream_read_same_bytes_ms": round(proj_stream, 4),
+                       "launch_hidden32_ms": round(proj_floor, 4),
+                       "timing": "HIP graph of back-to-back rq_kv_project calls (BF16 K/V of the current "
+                                 "token into k_cur/v_cur and the pending slot) over cold weight copies, one "
+                                 "event pair around its replay; warm_ms on one copy"},
         "roofline": {"bound": "hbm", "achieved": round(roof_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(roof_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "ms_per_launch": round(roof_ms, 4), "launches": roof_calls,
