@@ -101,7 +101,9 @@ def cpu_baseline(wl, budget_s: float = 12.0):
                     small.loops_per_group, small.n_groups, small.chained, 1, small.n_q_heads, 1, T + 1)
     kv = inp.kv.double().numpy()
     rot = inp.rot.double().numpy()
+    tp = time.perf_counter()
     cache = RQ.pack_context(kv, rot, cfg, T)
+    pack_s = time.perf_counter() - tp
     lay = RQ.Layout(cfg)
     q = inp.q.double().numpy()
     sc = synth.sm_scale(small.head_dim)
@@ -122,6 +124,9 @@ def cpu_baseline(wl, budget_s: float = 12.0):
         "kind": "oracle",
         "sample": f"{reps} residual loop-steps of float64 oracle decode attention for one (row, KV head) "
                   f"at {T} context tokens ({el:.1f} s)",
+        "pack": {"tokens_per_s": round(T / pack_s, 1), "unit": "token-heads/s",
+                 "sample": f"float64 oracle pack of {T} tokens of one (row, KV head), K and V, all "
+                           f"{small.n_loops} loops ({pack_s:.1f} s)"},
     }
 
 
@@ -383,15 +388,18 @@ def main():
     # roofline timing: back-to-back residual loop-steps over the cold replicas, one event
     # pair around all of them (launches overlap the previous kernel, as in a decode step)
     roof_calls = 6 * n_rep
-    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    r0.record(stream)
-    for i in range(roof_calls):
-        loop = i % (L - 1)
-        B.rq_decode_attention(cfg, caches[i % n_rep], loop, q[loop], k_cur[loop], v_cur[loop], None, ctx_len, T,
-                              inp.rot, sc, out, ws, Bt, n_splits=args.splits, stream=stream)
-    r1.record(stream)
-    torch.cuda.synchronize()
-    roof_ms = r0.elapsed_time(r1) / roof_calls
+    roof_reps = []
+    for _ in range(3):
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r0.record(stream)
+        for i in range(roof_calls):
+            loop = i % (L - 1)
+            B.rq_decode_attention(cfg, caches[i % n_rep], loop, q[loop], k_cur[loop], v_cur[loop], None, ctx_len,
+                                  T, inp.rot, sc, out, ws, Bt, n_splits=args.splits, stream=stream)
+        r1.record(stream)
+        torch.cuda.synchronize()
+        roof_reps.append(r0.elapsed_time(r1) / roof_calls)
+    roof_ms = sum(roof_reps) / len(roof_reps)
     roof_bytes = sum(algorithmic_bytes(wl, i % (L - 1), wl.chained) for i in range(roof_calls)) / roof_calls
     roof_gbps = roof_bytes / (roof_ms * 1e-3) / 1e9
 
@@ -501,9 +509,12 @@ def main():
                                  "event pair around its replay; warm_ms on one copy"},
         "roofline": {"bound": "hbm", "achieved": round(roof_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(roof_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "ms_per_launch": round(roof_ms, 4), "launches": roof_calls,
+                     "ms_per_launch": round(roof_ms, 4), "launches": 3 * roof_calls,
+                     "repeats_ms_per_launch": [round(v, 4) for v in roof_reps],
+                     "min_frac": round(roof_bytes / (min(roof_reps) * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                      "timing": "HIP events around back-to-back residual loop-steps (loops 0..L-2, cold replicas), "
-                               "on the library's stream, the last decode dispatches of the run",
+                               "on the library's stream, the last decode dispatches of the run; mean of 3 "
+                               "repeats (min_frac: the fastest repeat)",
                      "kernel": "rq_decode_kernel, residual loop-step (split-K with the merge in its last workgroup)",
                      "algorithmic_bytes": round(roof_bytes), "source_digest": decode_source_digest()},
     }
