@@ -54,3 +54,54 @@ def test_graph_replay_matches_eager():
         assert torch.equal(cache, cache_want)
         step()                                   # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_graph_replay_with_projection_matches_eager():
+    """A decode step that starts every loop with rq_kv_project (current-token K/V into the
+    decode inputs and the pending slot) replays from a graph to the eager result."""
+    from looped_transformer_decode_amd import binding as B
+    wl = synth.WORKLOADS["ouro_b4_t8192"].with_(batch=3, ctx=500, n_kv_heads=4, n_q_heads=4)
+    dev = torch.device("cuda:0")
+    inp = synth.generate(wl, seed=22, device=dev)
+    pin = synth.projection_inputs(wl, seed=23, device=dev, hidden=512)
+    cfg = B.config_for(wl)
+    T, L, d = wl.ctx, wl.loops_per_group, wl.head_dim
+    cache = gpu_pack(B, cfg, inp.kv, inp.rot, T)
+    ws = torch.zeros(B.rq_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    pending = torch.zeros(wl.batch, L, 2, wl.n_kv_heads, d, dtype=torch.bfloat16, device=dev)
+    ctx_len = torch.tensor([T, 17, 400], dtype=torch.int32, device=dev)
+    outs = [torch.empty(wl.batch, wl.n_q_heads, d, device=dev) for _ in range(L)]
+    q = [inp.q[l].contiguous() for l in range(L)]
+    kc = torch.empty(wl.batch, wl.n_kv_heads, d, dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+
+    def step():
+        for l in range(L):
+            B.rq_kv_project(cfg, pin.x[l], pin.w, l, kc, vc, pending, wl.batch)
+            B.rq_decode_attention(cfg, cache, l, q[l], kc, vc, None, ctx_len, T, inp.rot, 0.088, outs[l], ws,
+                                  wl.batch)
+        B.rq_quantize_token(cfg, cache, pending, 0, ctx_len, inp.rot, wl.batch, 1)
+
+    say("[graph+projection] eager")
+    step()
+    torch.cuda.synchronize()
+    want = [o.clone() for o in outs]
+    cache_want = cache.clone()
+    pend_want = pending.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in outs:
+            o.fill_(float("nan"))
+        pending.zero_()
+        say(f"[graph+projection] replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        for o, w in zip(outs, want):
+            assert torch.equal(o, w)
+        assert torch.equal(cache, cache_want)
+        assert torch.equal(pending.view(torch.int16), pend_want.view(torch.int16))
+        step()
+        torch.cuda.synchronize()
