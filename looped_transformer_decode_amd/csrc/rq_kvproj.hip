@@ -46,16 +46,25 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 // one 16-byte load.
 // MT: tiles of 16 batch rows; KU: k-steps of 32 channels loaded per wave before its
 // products (the launch picks the smallest power of two covering a wave's share of `hidden`,
-// at most 16, so no load is spent on a k-step outside the share)
-template <int MT, int KU>
+// at most 16, so no load is spent on a k-step outside the share).  XC > 0 (one row tile):
+// the batch rows of x are staged once per workgroup in LDS, XC 16-byte chunks per thread,
+// instead of every wave loading its A operands from L2 (eight waves read the same rows).
+template <int MT, int KU, int XC>
 __global__ __launch_bounds__(kPW * 64) void rq_kv_project_kernel(KvProjArgs a) {
+    static_assert(XC == 0 || MT == 1, "x is staged for one row tile only");
     __shared__ float red[kPW][MT][4][64];
+    // staged rows, then one spare 16-byte slot that takes the stores of clamped chunks
+    constexpr int kSpare = XC * kPW * 64 * 16 + 16 * 16;
+    __shared__ __attribute__((aligned(16))) uint8_t xs[XC > 0 ? kSpare + 16 : 16];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int col = lane & 15, g = lane >> 4;
     const int n0 = blockIdx.x * 16;
     const int ns = a.hidden / 32;                       // k-steps
     const int s0 = wv * ns / kPW, s1 = (wv + 1) * ns / kPW;
     const uint8_t* wrow = reinterpret_cast<const uint8_t*>(a.w + (int64_t)(n0 + col) * a.hidden) + g * 16;
+    // staged row r starts at r * xrow bytes; the 16-byte pad moves each row four LDS banks on,
+    // so the 16 rows of an A-operand read hit distinct banks
+    const int xrow = 2 * a.hidden + 16;
     f32x4 acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -64,20 +73,52 @@ __global__ __launch_bounds__(kPW * 64) void rq_kv_project_kernel(KvProjArgs a) {
     // past `batch` reads row 0) and the operands of those are zeroed after they land; a
     // scheduling barrier keeps every load of a round ahead of the first product, so one
     // round costs one memory latency instead of one per k-step.
-    for (int s = s0; s < s1; s += KU) {
-        const int nk = min(KU, s1 - s);
-        u32x4 wb[KU], xb[MT][KU];
+    u32x4 xst[XC > 0 ? XC : 1];
+    if constexpr (XC > 0) {
+        const int per_row = a.hidden / 8, total = a.batch * per_row;
+#pragma unroll
+        for (int i = 0; i < XC; ++i) {
+            const int c = min((int)threadIdx.x + i * kPW * 64, total - 1);
+            const int r = c / per_row, k8 = c - r * per_row;
+            xst[i] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.x + (int64_t)r * a.x_stride) +
+                                                     k8 * 16);
+        }
+    }
+    u32x4 wb[KU];
+    auto load_w = [&](int s, int nk) {
 #pragma unroll
         for (int j = 0; j < KU; ++j)
-            wb[j] = *reinterpret_cast<const u32x4*>(wrow + (int64_t)(s + min(j, nk - 1)) * 64);
+            wb[j] = *reinterpret_cast<const u32x4*>(wrow + (int64_t)min(s + min(j, nk - 1), ns - 1) * 64);
+    };
+    // the first round's weights go out before the staging waits for x (a wave without a
+    // share loads and ignores its clamped last k-step)
+    load_w(s0, max(1, min(KU, s1 - s0)));
+    if constexpr (XC > 0) {
+        const int per_row = a.hidden / 8, total = a.batch * per_row;
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const int r = m * 16 + col;                  // batch row of this lane's A operand
-            const uint8_t* xrow =
-                reinterpret_cast<const uint8_t*>(a.x + (int64_t)(r < a.batch ? r : 0) * a.x_stride) + g * 16;
+        for (int i = 0; i < XC; ++i) {
+            // unconditional store (a branch would let the compiler sink the load into it,
+            // behind a wait for every weight load)
+            const int c = (int)threadIdx.x + i * kPW * 64;
+            const int r = c / per_row, k8 = c - r * per_row;
+            *reinterpret_cast<u32x4*>(&xs[c < total ? r * xrow + k8 * 16 : kSpare]) = xst[i];
+        }
+        __syncthreads();
+    }
+    for (int s = s0; s < s1; s += KU) {
+        const int nk = min(KU, s1 - s);
+        if (s != s0) load_w(s, nk);
+        u32x4 xb[MT][KU];
+        if constexpr (XC == 0) {
 #pragma unroll
-            for (int j = 0; j < KU; ++j)
-                xb[m][j] = *reinterpret_cast<const u32x4*>(xrow + (int64_t)(s + min(j, nk - 1)) * 64);
+            for (int m = 0; m < MT; ++m) {
+                const int r = m * 16 + col;              // batch row of this lane's A operand
+                const uint8_t* xr =
+                    reinterpret_cast<const uint8_t*>(a.x + (int64_t)(r < a.batch ? r : 0) * a.x_stride) + g * 16;
+#pragma unroll
+                for (int j = 0; j < KU; ++j)
+                    xb[m][j] = *reinterpret_cast<const u32x4*>(xr + (int64_t)(s + min(j, nk - 1)) * 64);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -85,7 +126,12 @@ __global__ __launch_bounds__(kPW * 64) void rq_kv_project_kernel(KvProjArgs a) {
             const bool live = m * 16 + col < a.batch;
 #pragma unroll
             for (int j = 0; j < KU; ++j) {
-                const u32x4 xa = (live && j < nk) ? xb[m][j] : u32x4{0u, 0u, 0u, 0u};
+                u32x4 xa;
+                if constexpr (XC > 0)
+                    xa = *reinterpret_cast<const u32x4*>(&xs[(live ? col : 0) * xrow + (s + min(j, nk - 1)) * 64 + g * 16]);
+                else
+                    xa = xb[m][j];
+                xa = (live && j < nk) ? xa : u32x4{0u, 0u, 0u, 0u};
                 acc[m] = mfma_bf16(xa, wb[j], acc[m]);
             }
         }
@@ -115,15 +161,15 @@ __global__ __launch_bounds__(kPW * 64) void rq_kv_project_kernel(KvProjArgs a) {
     }
 }
 
-template <int MT>
+template <int MT, int XC>
 hipError_t launch_ku(const KvProjArgs& a, int ku, dim3 grid, dim3 block, hipStream_t st) {
     switch (ku) {
-        case 1: hipLaunchKernelGGL((rq_kv_project_kernel<MT, 1>), grid, block, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((rq_kv_project_kernel<MT, 2>), grid, block, 0, st, a); break;
-        case 4: hipLaunchKernelGGL((rq_kv_project_kernel<MT, 4>), grid, block, 0, st, a); break;
-        case 8: hipLaunchKernelGGL((rq_kv_project_kernel<MT, 8>), grid, block, 0, st, a); break;
+        case 1: hipLaunchKernelGGL((rq_kv_project_kernel<MT, 1, XC>), grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((rq_kv_project_kernel<MT, 2, XC>), grid, block, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((rq_kv_project_kernel<MT, 4, XC>), grid, block, 0, st, a); break;
+        case 8: hipLaunchKernelGGL((rq_kv_project_kernel<MT, 8, XC>), grid, block, 0, st, a); break;
         default:
-            if constexpr (MT < 4) hipLaunchKernelGGL((rq_kv_project_kernel<MT, 16>), grid, block, 0, st, a);
+            if constexpr (MT < 4) hipLaunchKernelGGL((rq_kv_project_kernel<MT, 16, XC>), grid, block, 0, st, a);
             else return hipErrorInvalidValue;
             break;
     }
@@ -140,9 +186,16 @@ hipError_t launch_kv_project(const KvProjArgs& a, hipStream_t st) {
     const int share = (a.hidden / 32 + kPW - 1) / kPW;          // k-steps of the widest wave
     const int ku = share <= 1 ? 1 : share <= 2 ? 2 : share <= 4 ? 4 : share <= 8 ? 8 : 16;
     const int mt = (a.batch + 15) / 16;
-    if (mt == 1) return launch_ku<1>(a, ku, grid, block, st);
-    if (mt == 2) return launch_ku<2>(a, ku, grid, block, st);
-    return launch_ku<4>(a, ku < 16 ? ku : 8, grid, block, st);   // 4 row tiles: 8 k-steps per round at most
+    if (mt == 1) {
+        // x staged in LDS when its rows fit 16 chunks of 16 bytes per thread (<= 128 KB)
+        const int chunks = (a.batch * (a.hidden / 8) + kPW * 64 - 1) / (kPW * 64);
+        if (chunks <= 2) return launch_ku<1, 2>(a, ku, grid, block, st);
+        if (chunks <= 8) return launch_ku<1, 8>(a, ku, grid, block, st);
+        if (chunks <= 16) return launch_ku<1, 16>(a, ku, grid, block, st);
+        return launch_ku<1, 0>(a, ku, grid, block, st);
+    }
+    if (mt == 2) return launch_ku<2, 0>(a, ku, grid, block, st);
+    return launch_ku<4, 0>(a, ku < 16 ? ku : 8, grid, block, st);   // 4 row tiles: 8 k-steps per round at most
 }
 
 }  // namespace rq
