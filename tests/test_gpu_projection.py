@@ -44,6 +44,11 @@ CASES = {
     "rows20_two_tiles": (W["tiny_d64_t256"].with_(batch=24), 20, 1024, 1, None, 0),
     "rows40_four_tiles": (W["tiny_d64_t256"].with_(batch=64), 40, 512, 3, None, 8),
     "hidden8192_two_rounds": (W["ouro_b4_t8192"], 2, 8192, 2, 2, 0),
+    # x too large to stage in LDS (16 rows x 8192): A operands loaded per wave
+    "rows16_hidden8192_unstaged": (W["ouro_b16_t8192"], 16, 8192, 0, 2, 0),
+    # 64 rows (four full row tiles) and the largest hidden (16 k-steps per wave per round, two rounds)
+    "rows64_four_full_tiles": (W["tiny_d64_t256"].with_(batch=64), 64, 256, 1, None, 0),
+    "max_hidden65536": (W["tiny_d64_t256"], 1, 65536, 3, None, 0),
 }
 
 
