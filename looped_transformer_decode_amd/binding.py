@@ -188,12 +188,27 @@ def rq_decode_attention_paged(cfg: rq_config, pool: torch.Tensor, n_blocks: int,
 def rq_kv_project(cfg: rq_config, x: torch.Tensor, w_kv: torch.Tensor, loop: int,
                   k_cur: Optional[torch.Tensor], v_cur: Optional[torch.Tensor], pending: Optional[torch.Tensor],
                   batch: int, stream=None) -> None:
-    """x: [batch][hidden] BF16 (any row stride); w_kv: [2][Hkv][d][hidden] BF16."""
+    """x: [batch][hidden] BF16 (any row stride); w_kv: [2][Hkv][d][hidden] BF16; k_cur, v_cur:
+    [batch][Hkv][d] BF16; pending: [>= batch][L][2][Hkv][d] BF16 (the library writes through
+    these pointers, so their shapes are checked here)."""
     if x.dtype != torch.bfloat16 or w_kv.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("rq_kv_project: x must be a BF16 [batch][hidden] tensor with unit channel stride")
     hidden = x.shape[1]
-    if not w_kv.is_contiguous() or w_kv.shape[-1] != hidden:
+    hkv, d, L = cfg.n_kv_heads, cfg.head_dim, cfg.loops_per_group
+    if not w_kv.is_contiguous() or tuple(w_kv.shape) != (2, hkv, d, hidden):
         raise ValueError("rq_kv_project: w_kv must be a contiguous [2][Hkv][d][hidden] BF16 tensor")
+    if x.shape[0] < batch:
+        raise ValueError("rq_kv_project: x has fewer rows than batch")
+    for name, t, shape in (("k_cur", k_cur, (batch, hkv, d)), ("v_cur", v_cur, (batch, hkv, d))):
+        if t is not None and (t.dtype != torch.bfloat16 or not t.is_contiguous() or t.numel() < batch * hkv * d
+                              or tuple(t.shape[1:]) != shape[1:] or t.device != x.device):
+            raise ValueError(f"rq_kv_project: {name} must be a contiguous BF16 [batch][Hkv][d] tensor on x's device")
+    if pending is not None and (pending.dtype != torch.bfloat16 or not pending.is_contiguous()
+                                or tuple(pending.shape[1:]) != (L, 2, hkv, d) or pending.shape[0] < batch
+                                or pending.device != x.device):
+        raise ValueError("rq_kv_project: pending must be a contiguous BF16 [batch][L][2][Hkv][d] tensor on x's device")
+    if w_kv.device != x.device:
+        raise ValueError("rq_kv_project: x and w_kv must be on the same device")
     _check("rq_kv_project", _lib.rq_kv_project(
         ctypes.byref(cfg), _ptr(x), x.stride(0), hidden, _ptr(w_kv), loop, _ptr(k_cur), _ptr(v_cur), _ptr(pending),
         batch, _stream(stream)))

@@ -248,3 +248,28 @@ def test_kv_project_rejects_bad_arguments(B):
     assert call(pending=A + 4) == 3
     big = B.config_for(wl, max_batch=80)
     assert call(cfg=big, batch=65) == 2             # more than four 16-row tiles
+
+
+def test_kv_project_binding_rejects_wrong_shapes(B):
+    """The binding refuses output tensors whose shape would let the kernel write past them
+    (CPU tensors suffice: the checks run before any pointer reaches the library)."""
+    import torch
+    wl = synth.WORKLOADS["tiny_d64_t256"]
+    cfg = B.config_for(wl, max_batch=2)
+    bf = torch.bfloat16
+    x = torch.zeros(2, 128, dtype=bf)
+    w = torch.zeros(2, 2, 64, 128, dtype=bf)
+    k = torch.zeros(2, 2, 64, dtype=bf)
+    pend = torch.zeros(2, 4, 2, 2, 64, dtype=bf)
+    with pytest.raises(ValueError):
+        B.rq_kv_project(cfg, x, torch.zeros(2, 2, 64, 96, dtype=bf), 0, k, k, pend, 2)
+    with pytest.raises(ValueError):
+        B.rq_kv_project(cfg, x, w, 0, torch.zeros(1, 2, 64, dtype=bf), k, pend, 2)
+    with pytest.raises(ValueError):
+        B.rq_kv_project(cfg, x, w, 0, k, torch.zeros(2, 2, 32, dtype=bf), pend, 2)
+    with pytest.raises(ValueError):
+        B.rq_kv_project(cfg, x, w, 0, k, k, torch.zeros(2, 3, 2, 2, 64, dtype=bf), 2)
+    with pytest.raises(ValueError):
+        B.rq_kv_project(cfg, x, w, 0, k, k, pend, 3)
+    with pytest.raises(ValueError):
+        B.rq_kv_project(cfg, x.float(), w, 0, k, k, pend, 2)
