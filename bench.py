@@ -117,10 +117,18 @@ def cpu_baseline(wl, budget_s: float = 12.0):
             break
     per_head_bytes = algorithmic_bytes(small, 0, small.chained)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": round(per_head_bytes * reps / el / 1e9, 4),
         "unit": "GB/s",
         "cores": int(threads),
+        "host_cpus": os.cpu_count(),
+        "cpu_model": model,
         "kind": "oracle",
         "sample": f"{reps} residual loop-steps of float64 oracle decode attention for one (row, KV head) "
                   f"at {T} context tokens ({el:.1f} s)",
@@ -519,7 +527,7 @@ def main():
         "kv_tokens_per_s": round(Bt * T / (res_ms * 1e-3), 1),
         "step": {"bytes": step_bytes, "ms_wall": round(ms_step, 4), "launch": launch,
                  "ms_per_loop_step": {str(l): round(v, 4) for l, v in per_loop.items()},
-                 "ms_pack": round(pack_ms, 4)},
+                 "ms_pack": round(pack_ms, 4), "pack_tokens_per_s": round(Bt / (pack_ms * 1e-3), 1)},
         "residual_loop_step": {"bytes": res_bytes, "ms": round(res_ms, 4), "gbps": round(res_gbps, 1),
                                "warm_single_replica_ms": round(warm_ms, 4)},
         "anchor_loop_step": {"bytes": anchor_bytes, "ms": round(per_loop[L - 1], 4),
