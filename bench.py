@@ -393,24 +393,6 @@ def main():
     paged_ms = p0_.elapsed_time(p1_) / (6 * n_rep)
     del pool
 
-    # roofline timing: back-to-back residual loop-steps over the cold replicas, one event
-    # pair around all of them (launches overlap the previous kernel, as in a decode step)
-    roof_calls = 6 * n_rep
-    roof_reps = []
-    for _ in range(3):
-        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        r0.record(stream)
-        for i in range(roof_calls):
-            loop = i % (L - 1)
-            B.rq_decode_attention(cfg, caches[i % n_rep], loop, q[loop], k_cur[loop], v_cur[loop], None, ctx_len,
-                                  T, inp.rot, sc, out, ws, Bt, n_splits=args.splits, stream=stream)
-        r1.record(stream)
-        torch.cuda.synchronize()
-        roof_reps.append(r0.elapsed_time(r1) / roof_calls)
-    roof_ms = sum(roof_reps) / len(roof_reps)
-    roof_bytes = sum(algorithmic_bytes(wl, i % (L - 1), wl.chained) for i in range(roof_calls)) / roof_calls
-    roof_gbps = roof_bytes / (roof_ms * 1e-3) / 1e9
-
     # K/V projection of the current token (the step before the pending buffer): back-to-back
     # calls over cold copies of the layer's weights (a model's other layers evict them between
     # two loops of this one), and warm on one copy (a looped layer re-reads its own weights)
@@ -501,6 +483,25 @@ def main():
     proj_step_seq = step_graph_ms(False)
     proj_step_ovl = step_graph_ms(True)
     del wreps
+
+    # roofline timing: back-to-back residual loop-steps over the cold replicas, one event
+    # pair around all of them (launches overlap the previous kernel, as in a decode step)
+    roof_calls = 6 * n_rep
+    roof_reps = []
+    for _ in range(3):
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r0.record(stream)
+        for i in range(roof_calls):
+            loop = i % (L - 1)
+            B.rq_decode_attention(cfg, caches[i % n_rep], loop, q[loop], k_cur[loop], v_cur[loop], None, ctx_len,
+                                  T, inp.rot, sc, out, ws, Bt, n_splits=args.splits, stream=stream)
+        r1.record(stream)
+        torch.cuda.synchronize()
+        roof_reps.append(r0.elapsed_time(r1) / roof_calls)
+    roof_ms = sum(roof_reps) / len(roof_reps)
+    roof_bytes = sum(algorithmic_bytes(wl, i % (L - 1), wl.chained) for i in range(roof_calls)) / roof_calls
+    roof_gbps = roof_bytes / (roof_ms * 1e-3) / 1e9
+
 
     value = step_bytes / (ms_step * 1e-3) / 1e9
     traffic = measured_traffic(wl.name) if not wl.chained and args.splits == 0 else None
