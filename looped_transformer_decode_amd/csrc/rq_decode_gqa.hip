@@ -466,7 +466,10 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
         const int blk = first + NW * it;
         const int tok0 = blk * BT;
 
-        // ---- keys and softmax, two rounds of 16 tokens
+        // ---- keys: scores of both 16-token rounds first (independent work the compiler can
+        // interleave), then one rescale check for the 32 tokens, then the weights
+        float sc[2];
+        bool vl[2];
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int t = 16 * r + l16;                   // token of this lane's B column
@@ -493,9 +496,8 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
                 part_a += fp8(mw, 2 * (gi & 1)) * Qs[gi] + fp8(mw, 2 * (gi & 1) + 1) * (da[gi] - Ca[gi]);
             }
             float coef = 1.f, part_r = 0.f;
-            uint2 rm = {0u, 0u};
             if constexpr (NRES > 0) {
-                rm = *reinterpret_cast<const uint2*>(sp + RES_OFF + RC + t * MROW);
+                const uint2 rm = *reinterpret_cast<const uint2*>(sp + RES_OFF + RC + t * MROW);
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi) {
                     const uint32_t mw = gi < 2 ? rm.x : rm.y;
@@ -503,34 +505,41 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
                 }
                 coef = bf16_to_f32(*reinterpret_cast<const uint16_t*>(sp + RES_OFF + RC + RM + t * 2));
             }
-            const bool valid = q_ok && (tok0 + t < n);
-            float score = (coef * part_a + part_r) * sm_scale;
-            score = valid ? score : -INFINITY;
-            if (wave_any(score > m_run + kRescaleSlack)) {   // rare: raise the reference of each query
-                const float m_new = fmaxf(m_run, row_max16(score));
-                const float fs = m_run == -INFINITY ? 0.f : __expf(m_run - m_new);
-                float fq[4];
+            vl[r] = q_ok && (tok0 + t < n);
+            const float score = (coef * part_a + part_r) * sm_scale;
+            sc[r] = vl[r] ? score : -INFINITY;
+        }
+        const float smax = fmaxf(sc[0], sc[1]);
+        if (wave_any(smax > m_run + kRescaleSlack)) {     // rare: raise the reference of each query
+            const float m_new = fmaxf(m_run, row_max16(smax));
+            const float fs = m_run == -INFINITY ? 0.f : __expf(m_run - m_new);
+            float fq[4];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) fq[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fs), 16 * q));
+            for (int q = 0; q < 4; ++q) fq[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fs), 16 * q));
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) va[i][q] *= fq[q];
+            if constexpr (NRES > 0) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) va[i][q] *= fq[q];
-                if constexpr (NRES > 0) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) vr[i][q] *= fq[q];
-                }
-#pragma unroll
-                for (int gi = 0; gi < NG; ++gi) {
-                    zA[gi] *= fs;
-                    zR[gi] *= fs;
-                }
-                l_lane *= fs;
-                m_run = m_new;
+                    for (int q = 0; q < 4; ++q) vr[i][q] *= fq[q];
             }
-            const float p = valid ? __expf(score - m_run) : 0.f;
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                zA[gi] *= fs;
+                zR[gi] *= fs;
+            }
+            l_lane *= fs;
+            m_run = m_new;
+        }
+        // ---- softmax weights of both rounds
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int t = 16 * r + l16;
+            const bool valid = vl[r];
+            const float p = valid ? __expf(sc[r] - m_run) : 0.f;
             l_lane += p;
             // value weights from the V plane's metadata and coefficient: anchor p c s_a,
             // residual p s_r (zero for masked tokens), and the offsets
