@@ -19,12 +19,16 @@ namespace rq {
 //   (v_readfirstlane, see uniform_ptr).  A vector-memory instruction that reads an SGPR
 //   written by a VALU instruction needs 5 wait states; without them the DMA can take the
 //   registers' previous contents as its address.
+//
+// The stream is read once per loop-step, so its loads carry the non-temporal hint (nt):
+// the caches treat the lines as streaming, and the small data every loop-step reuses (the
+// rotations, queries, split records) is less likely to be evicted by them.
 template <bool FRESH = false>
 __device__ __forceinline__ void dma16(uint32_t voff, const uint8_t* sbase, uint32_t lds_addr) {
     if constexpr (FRESH)
-        asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+        asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 nt" :: "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
     else
-        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" :: "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
 }
 
 // copy BYTES (multiple of 16, at most 1024) from sbase + goff to LDS lds_addr
