@@ -2,10 +2,12 @@
 //
 // This is the baseline the arXiv digest's throughput paragraph (section 5.3) measures
 // ResidualQuant against: BF16 decode attention over each loop's own K/V.  It uses the
-// same lane mapping, online softmax, split-K merge and current-token handling as the
-// ResidualQuant kernel, so the two differ only in what they read per token.
+// same lane mapping, LDS DMA staging of the stream (non-temporal), online softmax, split-K
+// merge and current-token handling as the ResidualQuant kernel, so the two differ only in
+// what they read per token.
 #include "rq_args.hpp"
 #include "rq_splitk.hpp"
+#include "rq_stage.hpp"
 
 namespace rq {
 
@@ -37,26 +39,44 @@ __global__ __launch_bounds__(kThreads) void rq_bf16_decode_kernel(Bf16Args a) {
     const int t_end = min(n_tiles, t_begin + a.tiles_per_split);
     const int first = t_begin + w;
     const int my_tiles = first < t_end ? (t_end - first + kWaves - 1) / kWaves : 0;
-    const int n_it = my_tiles * PPT;
+    // passes: full tiles, except that only the globally last tile can be partial
+    int n_it = my_tiles * PPT;
+    if (my_tiles > 0 && first + kWaves * (my_tiles - 1) == n_tiles - 1) {
+        const int rem = n - (n_tiles - 1) * kTile;                 // 1..64 tokens in the last tile
+        n_it -= PPT - (rem + SLOTS - 1) / SLOTS;
+    }
 
     const int64_t base = ((int64_t)b * a.hkv + h) * a.t_cap * D;
-    const uint16_t* K = a.k + base;
-    const uint16_t* V = a.v + base;
+    const uint8_t* Kb = reinterpret_cast<const uint8_t*>(a.k + base);
+    const uint8_t* Vb = reinterpret_cast<const uint8_t*>(a.v + base);
 
-    struct F { u32x4 k[4], v[4]; };
-    auto load = [&](F& f, int it) {
-        const int j = (first + kWaves * (it / PPT)) * kTile + (it % PPT) * SLOTS + slot;
-        const int jl = j < n ? j : 0;             // tail slots of the last tile read token 0
-        const u32x4* kp = reinterpret_cast<const u32x4*>(K + (int64_t)jl * D + 32 * chunk);
-        const u32x4* vp = reinterpret_cast<const u32x4*>(V + (int64_t)jl * D + 32 * chunk);
+    // ---- streaming: a pass (SLOTS consecutive tokens, 4 KB of K and 4 KB of V) goes
+    // global -> LDS by 1 KB DMAs, each contiguous in memory and non-temporal, into a
+    // 2-slot ring per wave; the lanes then read their (token, 32-channel chunk) from LDS.
+    // A lane whose 16 bytes lie past t_cap reads the pass's first token instead (always
+    // below ctx_len), so every DMA stays inside the row's cache and every wave issues the
+    // same number of them (the explicit vmcnt counts depend on it).
+    constexpr int PB = SLOTS * D * 2;                  // bytes of one pass of K (or V)
+    constexpr int NC = PB / 1024;                      // 1 KB DMAs per pass of K (or V)
+    constexpr int NDMA = 2 * NC;
+    constexpr int NB = 2;
+    static_assert(PB % 1024 == 0 && (NB - 1) * NDMA <= 63, "pass layout");
+    __shared__ __attribute__((aligned(16))) uint8_t ring[kWaves][NB][2][PB];
+    const uint32_t ring_base = __builtin_amdgcn_readfirstlane(lds_addr_of(&ring[w][0][0][0]));
+    auto issue = [&](int it) {
+        const int j0 = (first + kWaves * (it / PPT)) * kTile + (it % PPT) * SLOTS;
+        const uint8_t* kp = uniform_ptr(Kb + (int64_t)j0 * (2 * D));
+        const uint8_t* vp = uniform_ptr(Vb + (int64_t)j0 * (2 * D));
+        const uint32_t dst = ring_base + (uint32_t)(it % NB) * 2 * PB;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            f.k[c] = kp[c];
-            f.v[c] = vp[c];
+        for (int m = 0; m < NC; ++m) {
+            const int tok = j0 + (m * 1024 + 16 * lane) / (2 * D);
+            const uint32_t voff = tok < a.t_cap ? (uint32_t)(m * 1024 + 16 * lane) : (uint32_t)((16 * lane) % (2 * D));
+            dma16<true>(voff, kp, dst + m * 1024);
+            dma16<true>(voff, vp, dst + PB + m * 1024);
         }
     };
-    F fa, fb;
-    if (n_it > 0) load(fa, 0);
+    if (n_it > 0) issue(0);
 
     for (int i = threadIdx.x; i < D; i += kThreads) {
         if constexpr (QBF16)
@@ -74,13 +94,22 @@ __global__ __launch_bounds__(kThreads) void rq_bf16_decode_kernel(Bf16Args a) {
     for (int i = 0; i < 32; ++i) acc[i] = 0.f;
     float m_run = -INFINITY, l_lane = 0.f;
 
-    auto compute = [&](const F& f, int it) {
+    auto compute = [&](int it) {
         const int j = (first + kWaves * (it / PPT)) * kTile + (it % PPT) * SLOTS + slot;
         const bool valid = j < n;
+        const int row = valid ? slot : 0;          // masked slots read the pass's first token
+        const uint8_t* kr = &ring[w][it % NB][0][0] + row * (2 * D) + chunk * 64;
+        const uint8_t* vr = &ring[w][it % NB][1][0] + row * (2 * D) + chunk * 64;
+        u32x4 fk[4], fv[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            fk[c] = reinterpret_cast<const u32x4*>(kr)[c];
+            fv[c] = reinterpret_cast<const u32x4*>(vr)[c];
+        }
         float part = 0.f;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const uint32_t ws[4] = {f.k[c].x, f.k[c].y, f.k[c].z, f.k[c].w};
+            const uint32_t ws[4] = {fk[c].x, fk[c].y, fk[c].z, fk[c].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 part += qr[8 * c + 2 * e] * bf16lo(ws[e]);
@@ -101,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void rq_bf16_decode_kernel(Bf16Args a) {
         l_lane += pw;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const uint32_t ws[4] = {f.v[c].x, f.v[c].y, f.v[c].z, f.v[c].w};
+            const uint32_t ws[4] = {fv[c].x, fv[c].y, fv[c].z, fv[c].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 acc[8 * c + 2 * e] += pw * bf16lo(ws[e]);
@@ -110,14 +139,15 @@ __global__ __launch_bounds__(kThreads) void rq_bf16_decode_kernel(Bf16Args a) {
         }
     };
 
-    for (int it = 0; it < n_it; it += 2) {
+    for (int it = 0; it < n_it; ++it) {
         if (it % PPT == 0) prio_alternate(younger, it / PPT);
-        if (it + 1 < n_it) load(fb, it + 1);
-        compute(fa, it);
         if (it + 1 < n_it) {
-            if (it + 2 < n_it) load(fa, it + 2);
-            compute(fb, it + 1);
+            issue(it + 1);
+            wait_vm<NDMA>();                       // pass `it` has landed, pass it + 1 in flight
+        } else {
+            wait_vm<0>();
         }
+        compute(it);
     }
 
     __builtin_amdgcn_s_setprio(3);

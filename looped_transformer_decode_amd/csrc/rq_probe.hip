@@ -1,7 +1,8 @@
 // rq_stream_read: a plain streaming read of a device buffer, as a measuring stick.
 //
-// Each workgroup reads one contiguous slab with 16-byte loads, eight in flight per
-// thread, and folds them with XOR into one word per thread (written to `sink` so the
+// Each workgroup reads one contiguous slab with 16-byte non-temporal loads (the hint that
+// reads a once-read stream fastest here), eight in flight per thread, and folds them with
+// XOR into one word per thread (written to `sink` so the
 // loads cannot be dropped).  It holds none of the method's arithmetic.  Timed over the
 // same buffers as the decode kernel, it shows the read rate that a simple load loop
 // reaches on the device, next to the datasheet peak.
@@ -23,7 +24,13 @@ __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const uint4*
 #pragma unroll
         for (int u = 0; u < kProbeUnroll; ++u) {
             const int64_t k = i + (int64_t)u * kProbeThreads;
-            v[u] = k < end ? p[k] : uint4{0u, 0u, 0u, 0u};
+            if (k < end) {
+                typedef uint32_t nt4 __attribute__((ext_vector_type(4)));
+                const nt4 t = __builtin_nontemporal_load(reinterpret_cast<const nt4*>(p + k));
+                v[u] = uint4{t.x, t.y, t.z, t.w};
+            } else {
+                v[u] = uint4{0u, 0u, 0u, 0u};
+            }
         }
 #pragma unroll
         for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
