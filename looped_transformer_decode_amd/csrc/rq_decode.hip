@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
                         paged ? uniform_ptr(a.cache + G.paged_offset(blk_cur, h, x, a.loop + k)) : (x ? rV[k] : rK[k]);
                     stage<RC, PAGED>(rp, tr + p * RC, dst, lane);
                     stage<AM, PAGED>(rp, tr + r_meta + p * AM, dst + RC, lane);
-                    stage<CC, PAGED>(rp, tr + r_cblk + p * CC, dst + RC + AM, lane);
+                    stage<CC, PAGED, false>(rp, tr + r_cblk + p * CC, dst + RC + AM, lane);   // line shared by the tile's passes
                     dst += RC + AM + CC;
                 }
             }

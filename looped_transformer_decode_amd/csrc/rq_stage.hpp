@@ -23,19 +23,24 @@ namespace rq {
 // The stream is read once per loop-step, so its loads carry the non-temporal hint (nt):
 // the caches treat the lines as streaming, and the small data every loop-step reuses (the
 // rotations, queries, split records) is less likely to be evicted by them.
-template <bool FRESH = false>
+// NT = false for a section that shares its cache lines with the next passes of its tile.
+template <bool FRESH = false, bool NT = true>
 __device__ __forceinline__ void dma16(uint32_t voff, const uint8_t* sbase, uint32_t lds_addr) {
-    if constexpr (FRESH)
+    if constexpr (FRESH && NT)
         asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 nt" :: "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
-    else
+    else if constexpr (NT)
         asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" :: "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+    else if constexpr (FRESH)
+        asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
+    else
+        asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" :: "v"(voff), "s"(sbase), "{m0}"(lds_addr) : "memory");
 }
 
 // copy BYTES (multiple of 16, at most 1024) from sbase + goff to LDS lds_addr
-template <int BYTES, bool FRESH = false>
+template <int BYTES, bool FRESH = false, bool NT = true>
 __device__ __forceinline__ void stage(const uint8_t* sbase, uint32_t goff, uint32_t lds_addr, int lane) {
     static_assert(BYTES % 16 == 0 && BYTES <= 1024, "one DMA instruction per block");
-    if (BYTES == 1024 || lane < BYTES / 16) dma16<FRESH>(goff + 16u * lane, sbase, lds_addr);
+    if (BYTES == 1024 || lane < BYTES / 16) dma16<FRESH, NT>(goff + 16u * lane, sbase, lds_addr);
 }
 
 // A wave-uniform pointer moved into scalar registers (the DMA takes its base there); a DMA
