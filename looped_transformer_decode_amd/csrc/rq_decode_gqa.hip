@@ -314,7 +314,7 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
                 const uint8_t* rp = PAGED ? uniform_ptr(a.cache + Gm.paged_offset(pblk_cur, h, x, a.loop)) : (x ? rV : rK);
                 stage<RC, PAGED>(rp, tr + hb * RC, dst + RES_OFF, lane);
                 stage<RM, PAGED>(rp, tr + r_meta + hb * RM, dst + RES_OFF + RC, lane);
-                stage<CC, PAGED>(rp, tr + r_cblk + hb * CC, dst + RES_OFF + RC + RM, lane);
+                stage<CC, PAGED, false>(rp, tr + r_cblk + hb * CC, dst + RES_OFF + RC + RM, lane);   // line shared by the tile's two blocks
             }
             dst += PLANE;
         }
