@@ -303,7 +303,6 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
     } else {
         pin(q4f);
     }
-    for (int i = threadIdx.x; i < 10 * (D / 8); i += kThreads) s_dig[i] = 0u;
     if (threadIdx.x < C4) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) sv[0][4 * c4 + e] = q4f[e];
@@ -336,12 +335,26 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
         const int widx = four ? i / 8 : (i / 16) * 2 + (i & 1);
         const int nd = which ? 4 : 6;
         const int base = which ? 6 * (D / 8) : 0;
+        // the 8 channels of a digit word sit in 8 lanes of this wave (consecutive ones for
+        // 4-bit codes, one parity of a 16-lane row for 2-bit codes) with disjoint nibbles:
+        // OR them over the lane exchanges, and the first lane of the group stores the word
+        const bool lead = four ? (i % 8) == 0 : (i % 16) < 2;
 #pragma unroll
         for (int k = 0; k < 6; ++k) {
             if (k < nd) {
                 const int d = ((Q + 8) & 15) - 8;
                 Q = (Q - d) >> 4;
-                atomicOr(&s_dig[base + k * (D / 8) + widx], (uint32_t)(d & 15) << shift);
+                int word = (d & 15) << shift;
+                if (four) {
+                    word |= xshfl_i<1>(word);
+                    word |= xshfl_i<2>(word);
+                    word |= xshfl_i<4>(word);
+                } else {
+                    word |= xshfl_i<2>(word);
+                    word |= xshfl_i<4>(word);
+                    word |= xshfl_i<8>(word);
+                }
+                if (lead) s_dig[base + k * (D / 8) + widx] = (uint32_t)word;
             }
         }
         if (i % GS == 0) {
