@@ -1,0 +1,44 @@
+"""The benchmark's byte accounting (the numerator of every GB/s it reports) against the
+oracle's cache layout and closed forms: a loop-step reads, for every
+context token and KV head, K and V of the anchor plane and of the residual planes it needs."""
+import pytest
+
+import bench
+from looped_transformer_decode_amd import synth
+from oracle import residualquant as RQ
+
+
+def _layout(wl):
+    return RQ.Layout(RQ.Config(wl.head_dim, wl.group, wl.anchor_bits, wl.resid_bits, wl.loops_per_group,
+                               wl.n_groups, wl.chained, wl.n_kv_heads, wl.n_q_heads, wl.batch, wl.ctx + 1))
+
+
+@pytest.mark.parametrize("name", sorted(synth.WORKLOADS))
+def test_loop_step_bytes_follow_the_layout(name):
+    wl = synth.WORKLOADS[name]
+    a, r = _layout(wl).bytes_per_token_head()
+    heads_tokens = wl.batch * wl.ctx * wl.n_kv_heads
+    L = wl.loops_per_group
+    for loop in range(L):
+        n_res = 0 if loop == L - 1 else 1
+        assert bench.algorithmic_bytes(wl, loop, False) == 2 * (a + n_res * r) * heads_tokens
+        n_chain = 0 if loop == L - 1 else L - 1 - loop        # chained: residual planes loop..L-2
+        assert bench.algorithmic_bytes(wl, loop, True) == 2 * (a + n_chain * r) * heads_tokens
+    assert bench.bf16_bytes(wl) == 2 * 2 * wl.head_dim * heads_tokens
+
+
+def test_ouro_b4_figures():
+    # 72 B anchor and 42 B residual per token, head and K|V at head_dim 128, g = 32, INT4/INT2
+    wl = synth.WORKLOADS["ouro_b4_t8192"]
+    assert _layout(wl).bytes_per_token_head() == (72, 42)
+    assert bench.algorithmic_bytes(wl, 0, False) == 119537664         # 2 * 114 * 4 * 8192 * 16
+    assert bench.algorithmic_bytes(wl, 3, False) == 75497472          # 2 * 72 * 4 * 8192 * 16
+    assert bench.bf16_bytes(wl) == 268435456                          # 4 * 128 * 4 * 8192 * 16
+
+
+def test_bulk_pack_and_rotation_counts():
+    wl = synth.WORKLOADS["ouro_b4_t8192"]
+    # every loop's BF16 K and V of every context token, read once
+    assert bench.bulk_in_bytes(wl) == wl.batch * wl.ctx * 4 * 2 * wl.n_kv_heads * wl.head_dim * 2
+    # one d x d product per residual vector
+    assert bench.rotation_fma(wl) == wl.batch * wl.ctx * wl.n_kv_heads * 2 * 3 * wl.head_dim ** 2
