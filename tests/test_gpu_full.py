@@ -5,7 +5,8 @@ that the float64 oracle can check one by one:
 * the bulk-packed cache bytes of each sampled pair against the oracle's encoding rules;
 * decode attention at residual and anchor loops of first, middle and last anchor groups,
   for every query head of the sampled KV heads, against the oracle's decode of the GPU's
-  own bytes and of the oracle's own encoding.
+  own bytes and of the oracle's own encoding;
+* the BF16 baseline against float64 softmax attention on sampled heads.
 """
 import numpy as np
 import pytest
@@ -98,3 +99,46 @@ def test_full_size_parity(name, chained):
             assert e1 <= 1.0 and e2 <= 1.0, (loop, b, h, e1, e2)
     say(f"[full] {name} chained={chained}: pack stats {stats}, worst err/bound {worst:.3f}")
     assert_stats(stats)
+
+
+@pytest.mark.parametrize("name", ["ouro_b4_t8192", "huginn_gqa4_b8_t8192"])
+def test_bf16_full_size_parity(name):
+    """The BF16 baseline at the full workload size, in the benchmark's launch configuration
+    (automatic split count), with row lengths that end on a full tile, one token past it,
+    mid-tile and at a single token, against float64 softmax attention on sampled heads."""
+    from looped_transformer_decode_amd import binding as B
+    wl = synth.WORKLOADS[name]
+    T, d = wl.ctx, wl.head_dim
+    gqa = wl.n_q_heads // wl.n_kv_heads
+    say(f"[bf16 full] {name}: generating")
+    g = torch.Generator().manual_seed(515)
+    K = torch.randn(wl.batch, wl.n_kv_heads, T + 1, d, generator=g).to(torch.bfloat16)
+    V = torch.randn(wl.batch, wl.n_kv_heads, T + 1, d, generator=g).to(torch.bfloat16)
+    q = torch.randn(wl.batch, wl.n_q_heads, d, generator=g)
+    lens = [T, T - 63, 4097, 1, T - 1, 65, 2048, 7][:wl.batch]
+    Kd, Vd, qd = K.cuda(), V.cuda(), q.cuda()
+    k_cur, v_cur = Kd[:, :, T].contiguous(), Vd[:, :, T].contiguous()
+    bcfg = B.bf16_config_for(wl)
+    ws = torch.zeros(B.rq_bf16_workspace_bytes(bcfg), dtype=torch.uint8, device="cuda")
+    ctx_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out = torch.full((wl.batch, wl.n_q_heads, d), float("nan"), device="cuda")
+    sc = synth.sm_scale(d)
+    say(f"[bf16 full] {name}: decode, rows {lens}")
+    B.rq_bf16_decode_attention(bcfg, Kd, Vd, qd, k_cur, v_cur, False, ctx_len, T, sc, out, ws, wl.batch,
+                               n_splits=0)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(o))
+    rng = np.random.default_rng(11)
+    worst = 0.0
+    for b in range(wl.batch):
+        h = int(rng.integers(wl.n_kv_heads)) if 0 < b < wl.batch - 1 else (0 if b == 0 else wl.n_kv_heads - 1)
+        n = lens[b]
+        keys = np.concatenate([K[b, h, :n].double().numpy(), K[b, h, T][None].double().numpy()])
+        vals = np.concatenate([V[b, h, :n].double().numpy(), V[b, h, T][None].double().numpy()])
+        for hq in range(h * gqa, (h + 1) * gqa):
+            ref = RQ.attention(q[b, hq].double().numpy(), keys, vals, sc)
+            e = close(o[b, hq][None], ref[None])
+            worst = max(worst, e)
+            assert e <= 1.0, (b, h, hq, n, e)
+    say(f"[bf16 full] {name}: worst err/bound {worst:.2e}")
