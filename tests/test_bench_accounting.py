@@ -1,6 +1,7 @@
 """The benchmark's byte accounting (the numerator of every GB/s it reports) against the
 oracle's cache layout and closed forms: a loop-step reads, for every
-context token and KV head, K and V of the anchor plane and of the residual planes it needs."""
+context token and KV head, K and V of the anchor plane and of the residual planes it needs.
+Also the benchmark's refusal of multi-GPU launches."""
 import pytest
 
 import bench
@@ -42,3 +43,17 @@ def test_bulk_pack_and_rotation_counts():
     assert bench.bulk_in_bytes(wl) == wl.batch * wl.ctx * 4 * 2 * wl.n_kv_heads * wl.head_dim * 2
     # one d x d product per residual vector
     assert bench.rotation_fma(wl) == wl.batch * wl.ctx * wl.n_kv_heads * 2 * 3 * wl.head_dim ** 2
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py measures one GPU: --gpus above 1 (or a multi-rank launch) exits with status 2
+    and says why, before touching a device."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for argv, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *argv], capture_output=True, text=True,
+                           env={**os.environ, **env}, timeout=60)
+        assert r.returncode == 2
+        assert "one GPU" in r.stderr and r.stdout == ""
