@@ -448,10 +448,3 @@ def pack_context(kv: np.ndarray, rot: np.ndarray, cfg: Config, n_tokens: int,
                     write_tokens(cache, lay, b, h, x, k, pos, enc)
     return cache
 
-
-def config_bits_per_element(cfg: Config) -> float:
-    """Average stored bits per cached element across one anchor group of loops."""
-    lay = Layout(cfg)
-    a, r = lay.bytes_per_token_head()
-    L = cfg.loops_per_group
-    return 8.0 * (a + (L - 1) * r) / (cfg.head_dim * L)
