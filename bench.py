@@ -20,6 +20,7 @@ import hashlib
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -28,12 +29,16 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-DEFAULT_WORKLOAD = "ouro_b4_t8192"
+DEFAULT_WORKLOAD = "ouro_b16_t8192"
 CSRC = os.path.join(ROOT, "looped_transformer_decode_amd", "csrc")
 # sources of the decode kernel (split-K with the merge in its last workgroup)
 DECODE_SOURCES = ("rq_api.hip", "rq_decode.hip", "rq_args.hpp", "rq_common.hpp",
                   "rq_splitk.hpp", "rq_stage.hpp")
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "rq_decode_residual_ouro_b4_t8192_hbm_traffic.txt")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def traffic_profile(workload: str) -> str:
+    return os.path.join(PROFILES, f"rq_decode_residual_{workload}_hbm_traffic.txt")
 
 
 def decode_source_digest() -> str:
@@ -48,7 +53,7 @@ def measured_traffic(workload: str):
     """HBM bytes per residual loop-step from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     summary, or None when it was taken on other kernel sources or another workload."""
     try:
-        with open(TRAFFIC_PROFILE) as f:
+        with open(traffic_profile(workload)) as f:
             kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
     except OSError:
         return None
@@ -84,39 +89,60 @@ def rotation_fma(wl) -> int:
     return wl.batch * wl.ctx * wl.n_kv_heads * 2 * n_res * wl.head_dim * wl.head_dim
 
 
-def cpu_baseline(wl, budget_s: float = 12.0):
-    """Time the float64 oracle (as it is) on a bounded sample of the same workload:
-    one residual loop-step of decode attention for single (row, KV head) pairs at the
-    full context, repeated until the time budget is used."""
+def _oracle_worker(args):
+    """One worker of the CPU baseline: the float64 oracle's residual loop-step of decode
+    attention for one (row, KV head) at the full context, repeated until the deadline."""
+    wl, seed, deadline = args
     import numpy as np
-    from threadpoolctl import threadpool_info
+    import torch
+    from threadpoolctl import threadpool_limits
 
     from looped_transformer_decode_amd import synth
     from oracle import residualquant as RQ
 
-    T = wl.ctx
-    small = wl.with_(batch=1, n_kv_heads=1, n_q_heads=wl.n_q_heads // wl.n_kv_heads)
-    inp = synth.generate(small, seed=11, device="cpu")
-    cfg = RQ.Config(small.head_dim, small.group, small.anchor_bits, small.resid_bits,
-                    small.loops_per_group, small.n_groups, small.chained, 1, small.n_q_heads, 1, T + 1)
-    kv = inp.kv.double().numpy()
-    rot = inp.rot.double().numpy()
-    tp = time.perf_counter()
-    cache = RQ.pack_context(kv, rot, cfg, T)
-    pack_s = time.perf_counter() - tp
-    lay = RQ.Layout(cfg)
-    q = inp.q.double().numpy()
-    sc = synth.sm_scale(small.head_dim)
-    reps = 0
+    torch.set_num_threads(1)
+    with threadpool_limits(limits=1):
+        T = wl.ctx
+        small = wl.with_(batch=1, n_kv_heads=1, n_q_heads=wl.n_q_heads // wl.n_kv_heads)
+        inp = synth.generate(small, seed=seed, device="cpu")
+        cfg = RQ.Config(small.head_dim, small.group, small.anchor_bits, small.resid_bits, small.loops_per_group,
+                        small.n_groups, small.chained, 1, small.n_q_heads, 1, T + 1)
+        kv = inp.kv.double().numpy()
+        rot = inp.rot.double().numpy()
+        tp = time.perf_counter()
+        cache = RQ.pack_context(kv, rot, cfg, T)
+        pack_s = time.perf_counter() - tp
+        lay = RQ.Layout(cfg)
+        q = inp.q.double().numpy()
+        sc = synth.sm_scale(small.head_dim)
+        reps = 0
+        t0 = time.perf_counter()
+        while True:
+            RQ.decode_attention(cache, lay, 0, q[0], kv[0, 0, 0, :, :, T], kv[0, 0, 1, :, :, T], [T], rot, sc)
+            reps += 1
+            if time.time() >= deadline:
+                break
+        return reps, time.perf_counter() - t0, pack_s
+
+
+def cpu_baseline(wl, budget_s: float = 15.0, workers: int = 0):
+    """Time the float64 oracle (as it is) on a bounded sample of the same workload: one
+    (row, KV head) per worker process, each running the residual loop-step of decode
+    attention at the full context until a common deadline.  All workers run at once, one
+    BLAS thread each, so the figure is the host's whole-socket oracle rate on this sample."""
+    import multiprocessing as mp
+
+    n = workers or min(16, os.cpu_count() or 1)
+    pairs = n
+    deadline = time.time() + budget_s
     t0 = time.perf_counter()
-    while True:
-        RQ.decode_attention(cache, lay, 0, q[0], kv[0, 0, 0, :, :, T], kv[0, 0, 1, :, :, T], [T], rot, sc)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    per_head_bytes = algorithmic_bytes(small, 0, small.chained)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    with mp.get_context("fork").Pool(n) as pool:
+        res = pool.map(_oracle_worker, [(wl, 1000 + i, deadline) for i in range(pairs)])
+    wall = time.perf_counter() - t0
+    reps = sum(r[0] for r in res)
+    per_head_bytes = algorithmic_bytes(wl.with_(batch=1, n_kv_heads=1), 0, wl.chained)
+    decode_s = max(r[1] for r in res)
+    pack_s = sum(r[2] for r in res) / len(res)
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -124,17 +150,19 @@ def cpu_baseline(wl, budget_s: float = 12.0):
     except OSError:
         pass
     return {
-        "value": round(per_head_bytes * reps / el / 1e9, 4),
+        "value": round(per_head_bytes * reps / decode_s / 1e9, 4),
         "unit": "GB/s",
-        "cores": int(threads),
+        "cores": n,
         "host_cpus": os.cpu_count(),
         "cpu_model": model,
         "kind": "oracle",
-        "sample": f"{reps} residual loop-steps of float64 oracle decode attention for one (row, KV head) "
-                  f"at {T} context tokens ({el:.1f} s)",
-        "pack": {"tokens_per_s": round(T / pack_s, 1), "unit": "token-heads/s",
-                 "sample": f"float64 oracle pack of {T} tokens of one (row, KV head), K and V, all "
-                           f"{small.n_loops} loops ({pack_s:.1f} s)"},
+        "sample": f"{reps} residual loop-steps of float64 oracle decode attention, one (row, KV head) at "
+                  f"{wl.ctx} context tokens per worker process, {n} processes at once with one BLAS thread "
+                  f"each, {decode_s:.1f} s ({wall:.1f} s with input generation and the pack)",
+        "kv_tokens_per_s": round(wl.ctx * reps / decode_s, 1),
+        "pack": {"token_heads_per_s": round(n * wl.ctx / pack_s, 1),
+                 "sample": f"float64 oracle pack of {wl.ctx} tokens of one (row, KV head), K and V, all "
+                           f"{wl.n_loops} loops, in each of the {n} processes ({pack_s:.1f} s each)"},
     }
 
 
@@ -150,6 +178,8 @@ def main():
     ap.add_argument("--scale-rule", type=int, default=0, help="1: norm-ratio coefficient")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-only", action="store_true",
+                    help="time the CPU oracle on the workload and print its JSON (no GPU use)")
     ap.add_argument("--replicas", type=int, default=0)
     ap.add_argument("--eager-only", action="store_true",
                     help="time whole steps from eager launches instead of HIP graph replay "
@@ -160,12 +190,8 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
-    import torch
-
-    from looped_transformer_decode_amd import binding as B
     from looped_transformer_decode_amd import synth
 
-    dev = torch.device("cuda:0")
     wl = synth.WORKLOADS[args.workload]
     if args.chained:
         wl = wl.with_(chained=True)
@@ -180,6 +206,27 @@ def main():
                                       ("+norm_ratio", args.scale_rule == 1)) if on)
     if variant:
         wl = wl.with_(name=wl.name + variant)
+    if args.cpu_baseline_only:
+        print(json.dumps(cpu_baseline(wl)))
+        return
+    cpu_base = None
+    if not args.no_cpu_baseline:
+        # The oracle runs in a child process started before this one touches the GPU; its
+        # worker processes never use the GPU.
+        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
+        child = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-only"] +
+                               [a for a in sys.argv[1:] if a != "--cpu-baseline-only"],
+                               stdout=subprocess.PIPE, text=True, timeout=300)
+        if child.returncode != 0:
+            print("[bench] CPU baseline failed", file=sys.stderr)
+            sys.exit(child.returncode or 1)
+        cpu_base = json.loads(child.stdout.strip().splitlines()[-1])
+
+    import torch
+
+    from looped_transformer_decode_amd import binding as B
+
+    dev = torch.device("cuda:0")
     L, d, T, Bt = wl.loops_per_group, wl.head_dim, wl.ctx, wl.batch
     print(f"[bench] workload={wl.name} chained={wl.chained}: generating inputs", file=sys.stderr, flush=True)
     inp = synth.generate(wl, seed=20261202, device=dev)
@@ -516,7 +563,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "u4/u2 codes; i32 key dots (v_dot8 on fixed-point q and R_K q digits); f32 softmax, value sums and output",
         "data": "synthetic (seeded stand-in for Ouro/Huginn K/V: anchor N(0,1) with x8 key outliers, "
                 "loops a_l*anchor + 0.15 N(0,1) + drift), random orthogonal rotations",
         "config": {"workload": wl.name, "batch": Bt, "ctx": T, "n_q_heads": wl.n_q_heads,
@@ -577,9 +624,8 @@ def main():
                      "kernel": "rq_decode_kernel, residual loop-step (split-K with the merge in its last workgroup)",
                      "algorithmic_bytes": round(roof_bytes), "source_digest": decode_source_digest()},
     }
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(wl)
+    if cpu_base is not None:
+        result["cpu_baseline"] = cpu_base
     print(json.dumps(result))
 
 

@@ -37,6 +37,16 @@ def test_ouro_b4_figures():
     assert bench.bf16_bytes(wl) == 268435456                          # 4 * 128 * 4 * 8192 * 16
 
 
+def test_ouro_b16_figures():
+    # the benchmark's default workload: batch 16 at 8k context
+    import bench as bn
+    assert bn.DEFAULT_WORKLOAD == "ouro_b16_t8192"
+    wl = synth.WORKLOADS["ouro_b16_t8192"]
+    assert bench.algorithmic_bytes(wl, 0, False) == 478150656         # 2 * 114 * 16 * 8192 * 16
+    assert bench.algorithmic_bytes(wl, 3, False) == 301989888         # 2 * 72 * 16 * 8192 * 16
+    assert bench.bf16_bytes(wl) == 1073741824                         # 4 * 128 * 16 * 8192 * 16
+
+
 def test_bulk_pack_and_rotation_counts():
     wl = synth.WORKLOADS["ouro_b4_t8192"]
     # every loop's BF16 K and V of every context token, read once
