@@ -125,8 +125,10 @@ const char* rq_status_str(rq_status status);
  *               outside [0, max_ctx) are skipped (nothing is written).
  *   rot       : device float32 [n_kv_heads][2][head_dim][head_dim], row-major R.
  *   batch     : rows 1..max_batch;  n_tokens : tokens per row, >= 1.
- * Inputs must be finite with |x| small enough that every group range fits E4M3
- * (offset >= -448, scale <= 448); other inputs give unspecified codes. */
+ * Inputs must be finite.  E4M3 metadata holds offsets >= -448 and scales <= 448: a
+ * group whose minimum lies below -448, or whose range needs a larger scale, gets the
+ * offset -448 or the scale 448 and codes clamped to [0, 2^bits-1], so the cache stays
+ * finite but those elements lose the scale/2 error bound. */
 rq_status rq_quantize_token(const rq_config* cfg, void* cache, const uint16_t* pending,
                             const int64_t* pending_strides, int32_t group_idx,
                             const int32_t* pos, const float* rot, int32_t batch,

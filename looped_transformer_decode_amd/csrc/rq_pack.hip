@@ -13,46 +13,10 @@
 // reductions use DPP inside a 16-lane row, E4M3 rounding uses exponent arithmetic
 // instead of division, and the residual loops are rotated and quantized side by side.
 #include "rq_args.hpp"
+#include "rq_fp8.hpp"
 
 namespace rq {
 
-
-// ---- FP8 E4M3FN bytes and values (exact: power-of-two scalings, floor/ceil, compares)
-
-// value of an E4M3 byte (finite patterns; bit 7 is the sign)
-__device__ __forceinline__ double e4m3_value(uint32_t b) {
-    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-    const double mag = e == 0 ? (double)m * 0x1p-9 : ldexp((double)(8u + m), (int)e - 10);
-    return (b & 0x80u) ? -mag : mag;
-}
-
-// byte of the largest grid value <= a, for 0 <= a (values above 448 give 448)
-__device__ __forceinline__ uint32_t e4m3_down_byte(double a) {
-    if (a >= 448.0) return 0x7Eu;
-    if (a < 0x1p-6) return (uint32_t)floor(a * 512.0);          // subnormals: m * 2^-9
-    const int e = ilogb(a);                                      // 2^e <= a < 2^(e+1)
-    return ((uint32_t)(e + 7) << 3) | ((uint32_t)floor(ldexp(a, 3 - e)) - 8u);
-}
-
-// byte of the smallest grid value >= a, for 0 <= a <= 448
-__device__ __forceinline__ uint32_t e4m3_up_byte(double a) {
-    if (a <= 0x1p-6) return (uint32_t)ceil(a * 512.0);           // 8 is the byte of 2^-6
-    const int e = ilogb(a);
-    return ((uint32_t)(e + 7) << 3) + ((uint32_t)ceil(ldexp(a, 3 - e)) - 8u);   // 8 carries
-}
-
-// byte of the largest grid value <= v, for -448 <= v
-__device__ __forceinline__ uint32_t e4m3_floor_byte(double v) {
-    return v >= 0.0 ? e4m3_down_byte(v) : (0x80u | e4m3_up_byte(-v));
-}
-
-// BF16 round-to-nearest-even of a float64 value, in one rounding step.
-__device__ __forceinline__ double bf16_round(double v) {
-    if (v == 0.0) return 0.0;
-    int e = ilogb(v);
-    if (e < -126) e = -126;
-    return ldexp(rint(ldexp(v, 7 - e)), e - 7);
-}
 
 // ---- cross-lane steps on float64 values
 

@@ -10,7 +10,15 @@ contents: an arbitrary address.  This test compiles the decode sources to assemb
 the library's own flags and checks every inline-assembly vector-memory instruction
 against the VALU writes of its base registers that precede it, counting s_nop wait
 states, and every inline-assembly LDS DMA against a scalar write of M0 (the DMA's LDS
-address) right before it, which needs 1 wait state."""
+address) right before it, which needs 1 wait state.
+
+The prologue loads of the decode kernels are inline assembly too (the compiler's own
+waits would also stall on the DMAs it cannot see), so the compiler takes their
+destination registers as written the moment the load issues.  A copy, spill or any other
+use of such a register before the explicit `s_waitcnt vmcnt` that the kernel places
+after it would read whatever the register held before the data arrived.  The scan also
+checks that no instruction touches an inline-assembly load's destination registers
+between the load and the next inline-assembly vmcnt wait."""
 import concurrent.futures
 import os
 import re
@@ -22,7 +30,7 @@ import pytest
 
 from looped_transformer_decode_amd import build as B
 
-SOURCES = ["rq_decode.hip", "rq_decode_gqa.hip", "rq_bf16.hip"]
+SOURCES = list(B.SOURCES)          # every source of the library
 NEEDED = 5
 
 
@@ -47,9 +55,56 @@ def _valu_sgpr_defs(line):
     return out
 
 
+def _vgprs(tok):
+    m = re.match(r"v\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def _vgprs_in(line):
+    out = set()
+    for tok in re.findall(r"v\[\d+:\d+\]|\bv\d+\b", line):
+        out |= _vgprs(tok)
+    return out
+
+
 def _writes_m0(line):
     parts = line.split(None, 1)
     return len(parts) == 2 and parts[0].startswith("s_") and parts[1].split(",")[0].strip() == "m0"
+
+
+def scan_load_uses(asm_text):
+    """(kernel, load line, offending line) for every instruction that reads or writes a
+    destination register of an inline-assembly load (a load into VGPRs, not an LDS DMA)
+    after the load and before the next inline-assembly vmcnt wait, in program order."""
+    bad, kern, inasm, pending = [], None, False, []
+    for raw in asm_text.splitlines():
+        line = raw.strip()
+        if re.match(r"^_Z\S+:", line):
+            kern, pending = line.split(":")[0], []
+            continue
+        if line.startswith(";;#ASMSTART"):
+            inasm = True
+            continue
+        if line.startswith(";;#ASMEND"):
+            inasm = False
+            continue
+        line = line.split(";")[0].strip()
+        if not line or line.startswith(".") or line.endswith(":"):
+            continue
+        if inasm and re.match(r"s_waitcnt\b.*vmcnt", line):
+            pending = []
+            continue
+        used = _vgprs_in(line)
+        for regs, load in pending:
+            if regs & used:
+                bad.append((kern, load, line))
+        m = re.match(r"(global_load_dword\S*|global_atomic\S*|buffer_load_dword\S*)\s+(v\[\d+:\d+\]|v\d+)", line)
+        if inasm and m and "_lds_" not in line:
+            pending.append((_vgprs(m.group(2)), line))
+    return bad
 
 
 def scan(asm_text):
@@ -135,6 +190,28 @@ def test_scanner_flags_a_short_gap_and_counts_nops():
     assert bad[1][1] == 0 and "m0" in bad[1][2]
 
 
+def test_load_use_scanner_flags_a_touch_before_the_wait():
+    text = "\n".join([
+        "_Zk:",
+        ";;#ASMSTART",
+        "global_load_dwordx4 v[20:23], v4, s[2:3]",
+        ";;#ASMEND",
+        "v_mov_b32 v30, v5",                       # other registers: fine
+        "v_accvgpr_write_b32 a0, v21",             # a copy of a register still in flight
+        ";;#ASMSTART",
+        "s_waitcnt vmcnt(8)",
+        ";;#ASMEND",
+        "v_add_f32 v31, v20, v22",                 # after the wait: fine
+        ";;#ASMSTART",
+        "global_load_dwordx2 v[40:41], v4, s[2:3]",
+        ";;#ASMEND",
+        "s_waitcnt lgkmcnt(0)",                    # the compiler's wait does not count
+        "v_mov_b32 v41, 0",
+    ])
+    bad = scan_load_uses(text)
+    assert [b[2] for b in bad] == ["v_accvgpr_write_b32 a0, v21", "v_mov_b32 v41, 0"], bad
+
+
 @pytest.mark.skipif(shutil.which(B.HIPCC) is None and not os.path.exists(B.HIPCC), reason="hipcc not installed")
 def test_decode_kernels_wait_before_dma_bases():
     with tempfile.TemporaryDirectory() as tmp:
@@ -148,6 +225,9 @@ def test_decode_kernels_wait_before_dma_bases():
         with concurrent.futures.ThreadPoolExecutor(len(SOURCES)) as ex:
             texts = list(ex.map(compile_one, SOURCES))
     for src, text in texts:
-        assert "global_load_lds_dwordx4" in text or src == "rq_bf16.hip"
+        if src in ("rq_decode.hip", "rq_decode_gqa.hip"):
+            assert "global_load_lds_dwordx4" in text
         bad = scan(text)
         assert not bad, f"{src}: {len(bad)} DMA(s) too close to the VALU write of their base, e.g. {bad[0]}"
+        bad = scan_load_uses(text)
+        assert not bad, f"{src}: {len(bad)} use(s) of an inline-assembly load's registers before its wait, e.g. {bad[0]}"
