@@ -169,6 +169,25 @@ rq_status rq_decode_attention(const rq_config* cfg, const void* cache, int32_t l
                               float sm_scale, float* out, void* workspace, size_t workspace_bytes,
                               int32_t batch, int32_t n_splits, hipStream_t stream);
 
+/* rq_decode_attention_noalloc - rq_decode_attention without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, same kernels and the same
+ * results as rq_decode_attention, except that the split records and arrival counters live
+ * in a static device array inside the library (about 4 MiB per GPU, held until the process
+ * ends): room for the arrival counters of batch * n_q_heads <= 4096 (row, query head) pairs
+ * and for 4 MiB of split records, i.e. batch * n_q_heads * splits * (2 * head_dim + 4) * 4
+ * bytes.  With n_splits = 0 the split count is capped to what fits; an explicit n_splits
+ * that does not fit, or more than 4096 pairs, returns RQ_ERR_WORKSPACE and launches nothing.
+ * It calls no allocation routine.  The first call on a device looks up the array's address
+ * (hipGetSymbolAddress) and enqueues a kernel on `stream` that zeroes the counters; every
+ * call leaves them at zero.  All calls on one GPU share the array: calls that overlap in
+ * time on one GPU (other streams, other threads) race and give wrong results. */
+rq_status rq_decode_attention_noalloc(const rq_config* cfg, const void* cache, int32_t loop, const void* q,
+                                      int32_t q_is_bf16, const uint16_t* k_cur, const uint16_t* v_cur,
+                                      uint16_t* pending, const int32_t* ctx_len, int32_t ctx_bound,
+                                      const float* rot, float sm_scale, float* out, int32_t batch,
+                                      int32_t n_splits, hipStream_t stream);
+
 /* rq_bf16_decode_attention - the same decode attention over an uncompressed BF16
  * cache (the baseline the arXiv digest's section 5.3 compares against: BF16
  * FlashAttention decode over each loop's own KV).

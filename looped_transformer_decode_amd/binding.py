@@ -23,7 +23,7 @@ _lib = ctypes.CDLL(_LIB_PATH)
 EXPORTS = ("rq_cache_bytes", "rq_workspace_bytes", "rq_bf16_workspace_bytes", "rq_status_str",
            "rq_quantize_token", "rq_decode_attention", "rq_bf16_decode_attention", "rq_unpack_debug",
            "rq_stream_read", "rq_paged_block_bytes", "rq_quantize_token_paged", "rq_decode_attention_paged",
-           "rq_kv_project")
+           "rq_kv_project", "rq_decode_attention_noalloc")
 
 
 class rq_config(ctypes.Structure):
@@ -60,6 +60,9 @@ _lib.rq_quantize_token.restype = _i32
 _lib.rq_decode_attention.argtypes = [_cfgp, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _f32,
                                      _vp, _vp, _sz, _i32, _i32, _vp]
 _lib.rq_decode_attention.restype = _i32
+_lib.rq_decode_attention_noalloc.argtypes = [_cfgp, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _f32, _vp,
+                                             _i32, _i32, _vp]
+_lib.rq_decode_attention_noalloc.restype = _i32
 _lib.rq_bf16_decode_attention.argtypes = [_bcfgp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _vp, _i32, _f32,
                                           _vp, _vp, _sz, _i32, _i32, _vp]
 _lib.rq_bf16_decode_attention.restype = _i32
@@ -139,6 +142,16 @@ def rq_decode_attention(cfg: rq_config, cache: torch.Tensor, loop: int, q: torch
         ctypes.byref(cfg), _ptr(cache), loop, _ptr(q), q_bf16, _ptr(k_cur), _ptr(v_cur), _ptr(pending),
         _ptr(ctx_len), ctx_bound, _ptr(rot), sm_scale, _ptr(out), _ptr(workspace), _nbytes(workspace),
         batch, n_splits, _stream(stream)))
+
+
+def rq_decode_attention_noalloc(cfg: rq_config, cache: torch.Tensor, loop: int, q: torch.Tensor,
+                                k_cur: torch.Tensor, v_cur: torch.Tensor, pending: Optional[torch.Tensor],
+                                ctx_len: torch.Tensor, ctx_bound: int, rot: torch.Tensor, sm_scale: float,
+                                out: torch.Tensor, batch: int, n_splits: int = 0, stream=None) -> None:
+    q_bf16 = 1 if q.dtype == torch.bfloat16 else 0
+    _check("rq_decode_attention_noalloc", _lib.rq_decode_attention_noalloc(
+        ctypes.byref(cfg), _ptr(cache), loop, _ptr(q), q_bf16, _ptr(k_cur), _ptr(v_cur), _ptr(pending),
+        _ptr(ctx_len), ctx_bound, _ptr(rot), sm_scale, _ptr(out), batch, n_splits, _stream(stream)))
 
 
 def rq_bf16_decode_attention(cfg: rq_bf16_config, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -2,6 +2,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "rq_args.hpp"
 
@@ -79,6 +80,42 @@ static int auto_splits(int rows, int n_tiles, int target) {
     if (s > by_tiles) s = by_tiles;
     if (s > kMaxSplits) s = kMaxSplits;
     return s < 1 ? 1 : s;
+}
+
+// ---- scratch of the entry point that allocates nothing (rq_decode_attention_noalloc):
+// one arrival counter per (batch row, query head) for up to kScratchPairs pairs, then the
+// split records.  Each GPU holds its own copy until the process ends; its address comes
+// from hipGetSymbolAddress once per device (the array's name is a host-side stand-in).
+constexpr int64_t kScratchPairs = 4096;
+constexpr int64_t kScratchCounterBytes = kScratchPairs * sizeof(uint32_t);
+constexpr int64_t kScratchRecordBytes = (int64_t)4 << 20;
+
+static __device__ __align__(256) uint8_t scratch[kScratchCounterBytes + kScratchRecordBytes];
+
+__global__ void scratch_zero_kernel(uint32_t* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// Device address of the current device's scratch; nullptr on a HIP error.  The first call
+// on a device looks the address up and enqueues a fill kernel on `stream` that zeroes the
+// counters (every decode call leaves them at zero again); a fill kernel rather than a memset,
+// so that a first call made under HIP graph capture records a kernel node.
+static uint8_t* scratch_base(hipStream_t stream) {
+    static std::mutex mu;
+    static uint8_t* addr[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+        const int n = (int)(kScratchCounterBytes / sizeof(uint32_t));
+        hipLaunchKernelGGL(scratch_zero_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, static_cast<uint32_t*>(p), n);
+        if (hipGetLastError() != hipSuccess) return nullptr;
+        addr[dev] = static_cast<uint8_t*>(p);
+    }
+    return addr[dev];
 }
 
 }  // namespace rq
@@ -201,31 +238,50 @@ rq_status rq_quantize_token_paged(const rq_config* cfg, void* pool, int32_t n_bl
                          rot, batch, n_tokens, stream);
 }
 
+// Split records and arrival counters of one decode call: `rec_splits` records per (batch row,
+// query head) at `partials`, one counter per pair at `arrivals` (zero between calls); the
+// automatic split count is capped at rec_splits.
+struct SplitStore {
+    float* partials;
+    uint32_t* arrivals;
+    int rec_splits;
+};
+
+// Host checks of every decode argument except the split store.
+static rq_status decode_check(const rq_config* cfg, Geom* g, const void* cache, int32_t loop, const void* q,
+                              int32_t q_is_bf16, const uint16_t* k_cur, const uint16_t* v_cur,
+                              const uint16_t* pending, const int32_t* ctx_len, int32_t ctx_bound,
+                              const float* rot, float sm_scale, const float* out, int32_t batch,
+                              int32_t n_splits) {
+    if (cfg == nullptr) return RQ_ERR_INVALID_ARG;
+    if (!make_geom(cfg, g)) return RQ_ERR_UNSUPPORTED;
+    if (!cache || !q || !k_cur || !v_cur || !ctx_len || !rot || !out) return RQ_ERR_INVALID_ARG;
+    if (batch < 1 || batch > g->max_batch) return RQ_ERR_INVALID_ARG;
+    if (loop < 0 || loop >= g->L * g->n_groups) return RQ_ERR_INVALID_ARG;
+    if (ctx_bound < 0 || ctx_bound > g->max_ctx) return RQ_ERR_INVALID_ARG;
+    if (n_splits < 0 || n_splits > kMaxSplits) return RQ_ERR_INVALID_ARG;
+    if (q_is_bf16 != 0 && q_is_bf16 != 1) return RQ_ERR_INVALID_ARG;
+    if (!(sm_scale > 0.f) || sm_scale != sm_scale) return RQ_ERR_INVALID_ARG;
+    if (!aligned16(cache) || !aligned16(q) || !aligned16(k_cur) || !aligned16(v_cur) || !aligned16(out) ||
+        !aligned16(rot) || (pending && !aligned16(pending)))
+        return RQ_ERR_MISALIGNED;
+    return RQ_OK;
+}
+
 static rq_status decode_impl(const rq_config* cfg, const void* cache, const int32_t* bt, int32_t bt_stride,
                              int32_t n_blocks, int32_t loop, const void* q, int32_t q_is_bf16,
                              const uint16_t* k_cur, const uint16_t* v_cur, uint16_t* pending,
                              const int32_t* ctx_len, int32_t ctx_bound, const float* rot, float sm_scale,
-                             float* out, void* workspace, size_t workspace_bytes_, int32_t batch,
-                             int32_t n_splits, hipStream_t stream) {
+                             float* out, const SplitStore& store, int32_t batch, int32_t n_splits,
+                             hipStream_t stream) {
     Geom g;
-    if (cfg == nullptr) return RQ_ERR_INVALID_ARG;
-    if (!make_geom(cfg, &g)) return RQ_ERR_UNSUPPORTED;
+    const rq_status chk = decode_check(cfg, &g, cache, loop, q, q_is_bf16, k_cur, v_cur, pending, ctx_len,
+                                       ctx_bound, rot, sm_scale, out, batch, n_splits);
+    if (chk != RQ_OK) return chk;
     g.bt = bt;
     g.bt_stride = bt_stride;
     g.n_blocks = n_blocks;
-    if (!cache || !q || !k_cur || !v_cur || !ctx_len || !rot || !out) return RQ_ERR_INVALID_ARG;
-    if (batch < 1 || batch > g.max_batch) return RQ_ERR_INVALID_ARG;
-    if (loop < 0 || loop >= g.L * g.n_groups) return RQ_ERR_INVALID_ARG;
-    if (ctx_bound < 0 || ctx_bound > g.max_ctx) return RQ_ERR_INVALID_ARG;
-    if (n_splits < 0 || n_splits > kMaxSplits) return RQ_ERR_INVALID_ARG;
-    if (q_is_bf16 != 0 && q_is_bf16 != 1) return RQ_ERR_INVALID_ARG;
-    if (!(sm_scale > 0.f) || sm_scale != sm_scale) return RQ_ERR_INVALID_ARG;
-    if (!aligned16(cache) || !aligned16(q) || !aligned16(k_cur) || !aligned16(v_cur) ||
-        !aligned16(out) || !aligned16(rot) || (pending && !aligned16(pending)) ||
-        (workspace && !aligned16(workspace)))
-        return RQ_ERR_MISALIGNED;
-    const size_t need = workspace_bytes(g.max_batch, g.hq, g.d);
-    if (!workspace || workspace_bytes_ < need) return RQ_ERR_WORKSPACE;
+    if (n_splits > store.rec_splits) return RQ_ERR_WORKSPACE;
     const int lloc = loop % g.L;
     const int nres = (lloc == g.L - 1) ? 0 : (g.chained ? g.L - 1 - lloc : 1);
     const int n_tiles = (ctx_bound + kTile - 1) / kTile;
@@ -236,6 +292,7 @@ static rq_status decode_impl(const rq_config* cfg, const void* cache, const int3
                      : (grouped ? auto_splits(batch * g.hkv, n_tiles, n_cu)
                                 : auto_splits(batch * g.hq, n_tiles, 2 * n_cu));
     if (n_tiles > 0 && S > n_tiles) S = n_tiles;
+    if (S > store.rec_splits) S = store.rec_splits;
     if (S < 1) S = 1;
     DecodeArgs a;
     memset(&a, 0, sizeof(a));
@@ -252,9 +309,10 @@ static rq_status decode_impl(const rq_config* cfg, const void* cache, const int3
     a.tiles_per_split = n_tiles > 0 ? (n_tiles + S - 1) / S : 0;
     a.n_cu = n_cu;
     MergeArgs& m = a.mg;
-    m.partials = static_cast<float*>(workspace);
-    m.arrivals = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + records_bytes(g.max_batch, g.hq, g.d));
+    m.partials = store.partials;
+    m.arrivals = store.arrivals;
     m.n_splits = S;
+    m.rec_splits = store.rec_splits;
     m.hkv = g.hkv;
     m.hq = g.hq;
     m.sm_scale = sm_scale;
@@ -268,14 +326,59 @@ static rq_status decode_impl(const rq_config* cfg, const void* cache, const int3
     return launch_decode(a, nres, q_is_bf16 != 0, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 
+// The caller's workspace: kMaxSplits records per (row, query head) of the configuration's
+// capacity, then the counters.
+static rq_status caller_store(const rq_config* cfg, void* workspace, size_t workspace_bytes_, SplitStore* st) {
+    Geom g;
+    if (cfg == nullptr) return RQ_ERR_INVALID_ARG;
+    if (!make_geom(cfg, &g)) return RQ_ERR_UNSUPPORTED;
+    if (workspace && !aligned16(workspace)) return RQ_ERR_MISALIGNED;
+    if (!workspace || workspace_bytes_ < workspace_bytes(g.max_batch, g.hq, g.d)) return RQ_ERR_WORKSPACE;
+    st->partials = static_cast<float*>(workspace);
+    st->arrivals = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + records_bytes(g.max_batch, g.hq, g.d));
+    st->rec_splits = kMaxSplits;
+    return RQ_OK;
+}
+
 rq_status rq_decode_attention(const rq_config* cfg, const void* cache, int32_t loop, const void* q,
                               int32_t q_is_bf16, const uint16_t* k_cur, const uint16_t* v_cur,
                               uint16_t* pending, const int32_t* ctx_len, int32_t ctx_bound,
                               const float* rot, float sm_scale, float* out, void* workspace,
                               size_t workspace_bytes_, int32_t batch, int32_t n_splits,
                               hipStream_t stream) {
+    Geom g;
+    const rq_status chk = decode_check(cfg, &g, cache, loop, q, q_is_bf16, k_cur, v_cur, pending, ctx_len,
+                                       ctx_bound, rot, sm_scale, out, batch, n_splits);
+    if (chk != RQ_OK) return chk;
+    SplitStore st;
+    const rq_status ws = caller_store(cfg, workspace, workspace_bytes_, &st);
+    if (ws != RQ_OK) return ws;
     return decode_impl(cfg, cache, nullptr, 0, 0, loop, q, q_is_bf16, k_cur, v_cur, pending, ctx_len, ctx_bound, rot,
-                       sm_scale, out, workspace, workspace_bytes_, batch, n_splits, stream);
+                       sm_scale, out, st, batch, n_splits, stream);
+}
+
+rq_status rq_decode_attention_noalloc(const rq_config* cfg, const void* cache, int32_t loop, const void* q,
+                                      int32_t q_is_bf16, const uint16_t* k_cur, const uint16_t* v_cur,
+                                      uint16_t* pending, const int32_t* ctx_len, int32_t ctx_bound,
+                                      const float* rot, float sm_scale, float* out, int32_t batch,
+                                      int32_t n_splits, hipStream_t stream) {
+    Geom g;
+    const rq_status chk = decode_check(cfg, &g, cache, loop, q, q_is_bf16, k_cur, v_cur, pending, ctx_len,
+                                       ctx_bound, rot, sm_scale, out, batch, n_splits);
+    if (chk != RQ_OK) return chk;
+    // records of batch * n_q_heads pairs in the static array: as many splits as fit
+    const int64_t pairs = (int64_t)batch * g.hq;
+    const int64_t rec = (int64_t)partial_stride(g.d) * sizeof(float);
+    const int64_t fit = pairs > kScratchPairs ? 0 : (int64_t)kScratchRecordBytes / (pairs * rec);
+    if (fit < 1 || (n_splits > 0 && n_splits > fit)) return RQ_ERR_WORKSPACE;
+    uint8_t* base = scratch_base(stream);
+    if (base == nullptr) return RQ_ERR_HIP;
+    SplitStore st;
+    st.arrivals = reinterpret_cast<uint32_t*>(base);
+    st.partials = reinterpret_cast<float*>(base + kScratchCounterBytes);
+    st.rec_splits = (int)(fit < kMaxSplits ? fit : kMaxSplits);
+    return decode_impl(cfg, cache, nullptr, 0, 0, loop, q, q_is_bf16, k_cur, v_cur, pending, ctx_len, ctx_bound, rot,
+                       sm_scale, out, st, batch, n_splits, stream);
 }
 
 rq_status rq_decode_attention_paged(const rq_config* cfg, const void* pool, int32_t n_blocks,
@@ -287,8 +390,15 @@ rq_status rq_decode_attention_paged(const rq_config* cfg, const void* pool, int3
                                     hipStream_t stream) {
     const rq_status st = paging_ok(cfg, n_blocks, block_table, table_stride);
     if (st != RQ_OK) return st;
+    Geom g;
+    const rq_status chk = decode_check(cfg, &g, pool, loop, q, q_is_bf16, k_cur, v_cur, pending, ctx_len,
+                                       ctx_bound, rot, sm_scale, out, batch, n_splits);
+    if (chk != RQ_OK) return chk;
+    SplitStore ss;
+    const rq_status ws = caller_store(cfg, workspace, workspace_bytes_, &ss);
+    if (ws != RQ_OK) return ws;
     return decode_impl(cfg, pool, block_table, table_stride, n_blocks, loop, q, q_is_bf16, k_cur, v_cur, pending,
-                       ctx_len, ctx_bound, rot, sm_scale, out, workspace, workspace_bytes_, batch, n_splits, stream);
+                       ctx_len, ctx_bound, rot, sm_scale, out, ss, batch, n_splits, stream);
 }
 
 rq_status rq_bf16_decode_attention(const rq_bf16_config* cfg, uint16_t* k_cache, uint16_t* v_cache,
@@ -335,6 +445,7 @@ rq_status rq_bf16_decode_attention(const rq_bf16_config* cfg, uint16_t* k_cache,
     m.arrivals = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) +
                                              records_bytes(cfg->max_batch, n_q_heads, head_dim));
     m.n_splits = S;
+    m.rec_splits = kMaxSplits;
     m.hkv = cfg->n_kv_heads;
     m.hq = n_q_heads;
     m.sm_scale = sm_scale;

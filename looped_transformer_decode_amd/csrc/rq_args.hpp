@@ -20,9 +20,10 @@ struct PackArgs {
 
 // The split-K merge that the last workgroup of each (batch row, query head) performs.
 struct MergeArgs {
-    float* partials;            // [batch * hq][kMaxSplits] records of partial_stride(d) floats
+    float* partials;            // [batch * hq][rec_splits] records of partial_stride(d) floats
     uint32_t* arrivals;         // [batch * hq] arrival counters; zero between calls
     int n_splits;
+    int rec_splits;             // records per (batch row, query head) in `partials` (>= n_splits)
     int hkv, hq;
     float sm_scale;
     const uint16_t* k_cur;      // [batch][hkv][d] BF16 current token of this loop

@@ -569,7 +569,7 @@ static hipError_t launch_q(const DecodeArgs& a, int nres, bool qbf16, dim3 grid,
 hipError_t launch_decode(const DecodeArgs& a, int nres, bool qbf16, hipStream_t st) {
     if (!a.cache || !a.q || !a.rot || !a.ctx_len || !a.mg.partials || !a.mg.arrivals || !a.mg.k_cur ||
         !a.mg.v_cur || !a.mg.out || !a.mg.rot || a.batch < 1 || a.n_splits < 1 || a.n_splits > kMaxSplits ||
-        a.mg.n_splits != a.n_splits)
+        a.mg.n_splits != a.n_splits || a.mg.rec_splits < a.n_splits)
         return hipErrorInvalidValue;
     if (gqa_supported(a.geo, nres)) return launch_decode_gqa(a, nres, qbf16, st);
     const dim3 grid(a.batch * a.geo.hq * a.n_splits);

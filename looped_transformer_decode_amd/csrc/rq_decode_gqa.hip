@@ -147,7 +147,7 @@ __device__ __forceinline__ void merge_group(const MergeArgs& g, int bh0, const f
     const int bh = bh0 + q;
     const int hq = bh % g.hq, b = bh / g.hq, h = hq / G;
     const int S = g.n_splits;
-    const float* recs = g.partials + (int64_t)bh * kMaxSplits * PS;
+    const float* recs = g.partials + (int64_t)bh * g.rec_splits * PS;
     float* s_red = scr;                                   // [NT / 64]
     float* s_w = s_red + NT / kWave;                      // [G][kMaxSplits]
     float* s_sc = s_w + G * kMaxSplits;                   // [G][4]: m, l_tot, p_cur
@@ -696,7 +696,7 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
         float v = 0.f;
 #pragma unroll
         for (int i = 0; i < NW; ++i) v += scr[((i * G) + q) * 2 * D + c];
-        st_agent(a.mg.partials + ((int64_t)(bh0 + q) * kMaxSplits + split) * (2 * D + 4) + c, v);
+        st_agent(a.mg.partials + ((int64_t)(bh0 + q) * a.mg.rec_splits + split) * (2 * D + 4) + c, v);
     }
     if (threadIdx.x < G) {
         const int q = threadIdx.x;
@@ -706,7 +706,7 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < NW; ++i)
             if (sm.mw[i][q] != -INFINITY) l_q += __expf(sm.mw[i][q] - m_q) * sm.lw[i][q];
-        float* rec = a.mg.partials + ((int64_t)(bh0 + q) * kMaxSplits + split) * (2 * D + 4);
+        float* rec = a.mg.partials + ((int64_t)(bh0 + q) * a.mg.rec_splits + split) * (2 * D + 4);
         st_agent(rec + 2 * D, m_q);
         st_agent(rec + 2 * D + 1, l_q);
     }
@@ -736,7 +736,7 @@ bool gqa_supported(const Geom& g, int nres) {
 hipError_t launch_decode_gqa(const DecodeArgs& a, int nres, bool qbf16, hipStream_t st) {
     if (!gqa_supported(a.geo, nres) || !a.cache || !a.q || !a.rot || !a.ctx_len || !a.mg.partials ||
         !a.mg.arrivals || !a.mg.k_cur || !a.mg.v_cur || !a.mg.out || a.batch < 1 || a.n_splits < 1 ||
-        a.n_splits > kMaxSplits || a.mg.n_splits != a.n_splits)
+        a.n_splits > kMaxSplits || a.mg.n_splits != a.n_splits || a.mg.rec_splits < a.n_splits)
         return hipErrorInvalidValue;
     const int gq = a.geo.hq / a.geo.hkv;
     const dim3 grid(a.batch * a.geo.hkv * a.n_splits);

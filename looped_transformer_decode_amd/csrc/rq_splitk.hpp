@@ -119,7 +119,7 @@ template <int D, bool RES, int NT = kThreads>
 __device__ __forceinline__ void splitk_publish(const MergeArgs& g, int bh, int split, const float* sum, float2 ml) {
     constexpr int NVAL = RES ? 2 * D : D;
     constexpr int PS = 2 * D + 4;
-    float* rec = g.partials + ((int64_t)bh * kMaxSplits + split) * PS;
+    float* rec = g.partials + ((int64_t)bh * g.rec_splits + split) * PS;
     for (int t = threadIdx.x; t < NVAL; t += NT) st_agent(rec + t, sum[t]);
     if (threadIdx.x == 0) {
         st_agent(rec + 2 * D, ml.x);
@@ -157,7 +157,7 @@ __device__ __forceinline__ void splitk_merge_last(const MergeArgs& g, int bh, co
     constexpr int PS = 2 * D + 4;
     static_assert(kMaxSplits <= kWave, "one lane per split record");
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const float* recs = g.partials + (int64_t)bh * kMaxSplits * PS;
+    const float* recs = g.partials + (int64_t)bh * g.rec_splits * PS;
     const int S = g.n_splits;
     const int hq = bh % g.hq, b = bh / g.hq;
     const int gqa = g.hq / g.hkv, h = hq / gqa;

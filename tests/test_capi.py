@@ -122,6 +122,28 @@ def test_decode_attention_rejects_bad_arguments(B):
     assert _decode(B, cfg, ws_bytes=need - 1) == 4
 
 
+def test_noalloc_decode_rejects_bad_arguments_and_oversize(B):
+    """The entry point without a workspace checks the same arguments, and rejects more than
+    4096 (row, query head) pairs or an explicit split count whose records do not fit its 4 MiB,
+    all on the host before looking up its device array."""
+    f = B._lib.rq_decode_attention_noalloc
+
+    def call(cfg, loop=0, q=A, batch=1, n_splits=0, ctx_bound=64):
+        return f(ctypes.byref(cfg), A, loop, q, 1, A, A, None, A, ctx_bound, A, 0.1, A, batch, n_splits, None)
+
+    wl = synth.WORKLOADS["ouro_b4_t8192"]
+    cfg = B.config_for(wl)
+    assert call(B.rq_config()) == 2
+    assert call(cfg, loop=4) == 1
+    assert call(cfg, batch=5) == 1
+    assert call(cfg, q=A + 8) == 3
+    assert call(cfg, n_splits=65) == 1
+    # 4 rows x 16 heads x 64 splits x (2 * 128 + 4) floats = 4.26 MB > 4 MiB
+    assert call(cfg, batch=4, n_splits=64) == 4
+    big = B.config_for(wl.with_(batch=257))              # 257 x 16 = 4112 pairs > 4096
+    assert call(big, batch=257) == 4
+
+
 def test_quantize_token_rejects_bad_arguments(B):
     wl = synth.WORKLOADS["ouro_b4_t8192"]
     cfg = B.config_for(wl)
