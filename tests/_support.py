@@ -27,6 +27,14 @@ ATOL_REL, ATOL_ABS = 1e-3, 1e-5
 NEAR = 1e-6
 
 
+#: (case, worst err/bound) of every parity check, printed at the end of the run
+MARGINS = []
+
+
+def record_margin(tag: str, worst: float) -> None:
+    MARGINS.append((tag, float(worst)))
+
+
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
@@ -147,8 +155,11 @@ def new_stats():
     return dict(codes=0, near_ties=0, near_meta=0, c_diff=0, c_total=0)
 
 
-def assert_stats(stats):
-    assert stats["near_ties"] <= 1e-5 * max(stats["codes"], 1), stats
+def assert_stats(stats, group: int = 32):
+    """Near-ties, plus every code of a group whose metadata the GPU took differently next to
+    a grid point, must stay below 1e-5 of all codes."""
+    charged = stats["near_ties"] + stats["near_meta"] * group
+    assert charged <= 1e-5 * max(stats["codes"], 1), stats
 
 
 def close(o_gpu: np.ndarray, o_ref: np.ndarray) -> float:
@@ -183,7 +194,7 @@ def run_pack_parity(B, name, wl, inp, cfg, ocfg, T):
             xs = [[kv[k, :, x, b, h, :T] for x in range(2)] for k in range(wl.n_groups)]
             check_pack_block(block, sub, xs, rot[h], T, stats)
     say(f"[pack] case={name} stats={stats}")
-    assert_stats(stats)
+    assert_stats(stats, wl.group)
 
 
 def run_decode_step_parity(B, name, wl, inp, cfg, ocfg, ctx, T, loops=None):
@@ -208,6 +219,7 @@ def run_decode_step_parity(B, name, wl, inp, cfg, ocfg, ctx, T, loops=None):
     sc = synth.sm_scale(d)
     n_tiles = -(-T // 64)
     run = list(range(wl.n_loops)) if loops is None else list(loops)
+    worst = 0.0
     for loop in run:
         grp, l = divmod(loop, L)
         k_cur = inp.kv[grp, l, 0, :, :, T].contiguous()
@@ -226,6 +238,7 @@ def run_decode_step_parity(B, name, wl, inp, cfg, ocfg, ctx, T, loops=None):
             o = out.double().cpu().numpy()
             assert np.all(np.isfinite(o))
             e1, e2 = close(o, ref_gpu), close(o, ref_own)
+            worst = max(worst, e1, e2)
             say(f"    err/bound vs oracle(gpu cache)={e1:.3f} vs oracle(own cache)={e2:.3f}")
             assert e1 <= 1.0 and e2 <= 1.0
         if l == L - 1 and all(grp * L + m in run for m in range(L)):
@@ -244,4 +257,5 @@ def run_decode_step_parity(B, name, wl, inp, cfg, ocfg, ctx, T, loops=None):
                         enc = RQ.read_tokens(block, RQ.Layout(sub), 0, 0, x, grp, ctx[b] + 1)
                         check_encoding(slice_enc(enc, slice(ctx[b], ctx[b] + 1)),
                                        kv[grp, :, x, b, h, T:T + 1], rot[h, x], sub, stats)
-            assert_stats(stats)
+            assert_stats(stats, wl.group)
+    record_margin(f"decode step {name}", worst)

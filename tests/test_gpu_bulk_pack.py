@@ -57,4 +57,4 @@ def test_bulk_pack_parity(name):
                         head = slice_enc(enc, slice(0, pos0))
                         assert not np.any(head.anchor[0]) and not np.any(head.anchor[1])
     say(f"[bulk] case={name} stats={stats}")
-    assert_stats(stats)
+    assert_stats(stats, wl.group)

@@ -3,9 +3,12 @@
 that the float64 oracle can check one by one:
 
 * the bulk-packed cache bytes of each sampled pair against the oracle's encoding rules;
-* decode attention at residual and anchor loops of first, middle and last anchor groups,
-  for every query head of the sampled KV heads, against the oracle's decode of the GPU's
-  own bytes and of the oracle's own encoding;
+* decode attention at every loop of the first, middle and last anchor groups, for every
+  query head of the sampled KV heads, against the oracle's decode of the GPU's own bytes
+  and of the oracle's own encoding;
+* the current token that each loop-step writes into the BF16 pending buffer, and, after a
+  group's anchor loop, the per-step pack of that finished token into the last slot of the
+  cache (slot T, in the last tile), against the oracle's encoding rules;
 * the BF16 baseline against float64 softmax attention on sampled heads.
 """
 import numpy as np
@@ -15,8 +18,8 @@ import torch
 from looped_transformer_decode_amd import synth
 from oracle import residualquant as RQ
 
-from _support import (assert_stats, check_pack_block, close, device_block, gpu_pack, new_stats, oracle_cfg,
-                      say, sub_cache)
+from _support import (assert_stats, check_encoding, check_pack_block, close, device_block, gpu_pack, new_stats,
+                      oracle_cfg, record_margin, say, slice_enc, sub_cache)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,8 +41,7 @@ def _pairs(wl, rng):
 def _loops(wl):
     L, G = wl.loops_per_group, wl.n_groups
     groups = sorted({0, G // 2, G - 1})
-    return [k * L + l for k in groups for l in range(L)] if G <= 2 else \
-        [k * L + l for k in groups for l in (0, L - 2, L - 1)]
+    return [k * L + l for k in groups for l in range(L)]
 
 
 @pytest.mark.parametrize("name,chained", FULL, ids=[f"{n}{'_chained' if c else ''}" for n, c in FULL])
@@ -64,6 +66,7 @@ def test_full_size_parity(name, chained):
     loops = _loops(wl)
     ws = torch.zeros(B.rq_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
     ctx_len = torch.full((wl.batch,), T, dtype=torch.int32, device="cuda")
+    pending = torch.zeros(wl.batch, L, 2, wl.n_kv_heads, d, dtype=torch.bfloat16, device="cuda")
     outs = {}
     for loop in loops:
         grp, l = divmod(loop, L)
@@ -71,10 +74,16 @@ def test_full_size_parity(name, chained):
         say(f"[full] {name} chained={chained}: decode loop {loop}")
         B.rq_decode_attention(cfg, cache, loop, inp.q[loop].contiguous(),
                               inp.kv[grp, l, 0, :, :, T].contiguous(), inp.kv[grp, l, 1, :, :, T].contiguous(),
-                              None, ctx_len, T, inp.rot, sc, out, ws, wl.batch, n_splits=0)
+                              pending, ctx_len, T, inp.rot, sc, out, ws, wl.batch, n_splits=0)
         torch.cuda.synchronize()
         outs[loop] = out.cpu().numpy().astype(np.float64)
         assert np.all(np.isfinite(outs[loop]))
+        if l == L - 1:
+            # the pending buffer holds this group's current token of every loop; drain it into slot T
+            assert torch.equal(pending, inp.kv[grp, :, :, :, :, T].permute(2, 0, 1, 3, 4))
+            say(f"[full] {name} chained={chained}: per-step pack of group {grp} into slot {T}")
+            B.rq_quantize_token(cfg, cache, pending, grp, ctx_len, inp.rot, wl.batch, 1)
+            torch.cuda.synchronize()
 
     stats = new_stats()
     worst = 0.0
@@ -85,6 +94,10 @@ def test_full_size_parity(name, chained):
         _, sub = sub_cache(np.zeros(0, np.uint8), ocfg, b, h)
         xs = [[kv[k, :, x, :T] for x in range(2)] for k in range(wl.n_groups)]
         check_pack_block(block, sub, xs, rot[h], T, stats)
+        for grp in sorted({lp // L for lp in loops}):
+            for x in range(2):
+                enc = RQ.read_tokens(block, RQ.Layout(sub), 0, 0, x, grp, T + 1)
+                check_encoding(slice_enc(enc, slice(T, T + 1)), kv[grp, :, x, T:T + 1], rot[h, x], sub, stats)
         own = RQ.pack_context(kv[:, :, :, None, None], rot[h:h + 1], sub, T)
         lay = RQ.Layout(sub)
         for loop in loops:
@@ -98,7 +111,8 @@ def test_full_size_parity(name, chained):
             worst = max(worst, e1, e2)
             assert e1 <= 1.0 and e2 <= 1.0, (loop, b, h, e1, e2)
     say(f"[full] {name} chained={chained}: pack stats {stats}, worst err/bound {worst:.3f}")
-    assert_stats(stats)
+    record_margin(f"full size {name}{' chained' if chained else ''}", worst)
+    assert_stats(stats, wl.group)
 
 
 @pytest.mark.parametrize("name", ["ouro_b4_t8192", "huginn_gqa4_b8_t8192"])
@@ -142,3 +156,4 @@ def test_bf16_full_size_parity(name):
             worst = max(worst, e)
             assert e <= 1.0, (b, h, hq, n, e)
     say(f"[bf16 full] {name}: worst err/bound {worst:.2e}")
+    record_margin(f"bf16 full size {name}", worst)

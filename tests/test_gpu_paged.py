@@ -93,7 +93,7 @@ def test_paged_pack_and_decode(name):
             xs = [[kv[k, :, x, b, h, :T] for x in range(2)] for k in range(wl.n_groups)]
             check_pack_block(block, sub, xs, rot[h], T, stats)
     say(f"[paged] case={name} pack stats {stats}")
-    assert_stats(stats)
+    assert_stats(stats, wl.group)
 
     # decode at every loop through the block table, then the drain of the current token
     L, d = wl.loops_per_group, wl.head_dim
@@ -138,4 +138,4 @@ def test_paged_pack_and_decode(name):
                     enc = RQ.read_tokens(block, slay, 0, 0, x, k, ctx[b] + 1)
                     check_encoding(slice_enc(enc, slice(ctx[b], ctx[b] + 1)), kv[k, :, x, b, h, ctx[b]: ctx[b] + 1],
                                    rot[h, x], sub, stats)
-    assert_stats(stats)
+    assert_stats(stats, wl.group)
