@@ -62,10 +62,18 @@ class Config:
     max_batch: int
     max_ctx: int
     scale_rule: int = 0     # 0: least-squares c; 1: norm-ratio c (the digest's appendix alternative)
+    # residual width of each local loop 0..L-2 (empty: resid_bits for all).  The commentary page
+    # ("它压的根本不是 KV" section) remarks that the loops near the anchor keep thinner residuals
+    # and the farther ones more bits; these widths express that allocation.
+    resid_bits_loop: Tuple[int, ...] = ()
 
     @property
     def n_loops(self) -> int:
         return self.loops_per_group * self.n_groups
+
+    def rbits(self, l: int) -> int:
+        """Residual width of local loop l (< L-1)."""
+        return self.resid_bits_loop[l] if self.resid_bits_loop else self.resid_bits
 
 
 # ---------------------------------------------------------------------------
@@ -176,7 +184,7 @@ def encode(xs: np.ndarray, rot: np.ndarray, cfg: Config) -> Encoded:
         c, _ = coefficient(xs[l], ref, cfg)
         y = xs[l] - c[..., None] * ref
         r = y @ R.T                                  # r = R y, tokens as rows
-        qr, zr, sr = quantize(r, cfg.resid_bits, g)
+        qr, zr, sr = quantize(r, cfg.rbits(l), g)
         resid[l] = (qr, zr, sr, c)
         if cfg.chained:
             ref = c[..., None] * ref + dequantize(qr, zr, sr, g) @ R   # c * ref + R^T r_hat
@@ -213,7 +221,7 @@ class Layout:
     in global loop order (the anchor plane is the last of its group); each plane is
     ceil(max_ctx/64) tiles of 64 tokens.  A tile is
       codes block : 64 rows of d*bits/8 bytes; channel i sits at bit i*bits of its row
-                    (little-endian within the row)
+                    (little-endian within the row); bits is the plane's own width
       meta block  : 64 rows of 2*(d/group) bytes; byte 2j = E4M3 offset, 2j+1 = E4M3 scale
                     of channel group j
       c block     : residual planes only, 64 little-endian BF16 values.
@@ -222,28 +230,43 @@ class Layout:
     def __init__(self, cfg: Config):
         self.cfg = cfg
         d, g = cfg.head_dim, cfg.group
+        L = cfg.loops_per_group
         self.n_tiles = -(-cfg.max_ctx // TILE)
         self.a_row = d * cfg.anchor_bits // 8
-        self.r_row = d * cfg.resid_bits // 8
         self.m_row = 2 * (d // g)
         self.a_tile = TILE * (self.a_row + self.m_row)
-        self.r_tile = TILE * (self.r_row + self.m_row + 2)
-        L = cfg.loops_per_group
-        self.group_bytes = self.n_tiles * (self.a_tile + (L - 1) * self.r_tile)
+        self.r_rows = [d * cfg.rbits(l) // 8 for l in range(L - 1)]
+        self.r_tiles = [TILE * (r + self.m_row + 2) for r in self.r_rows]
+        self.group_bytes = self.n_tiles * (self.a_tile + sum(self.r_tiles))
         self.block_bytes = cfg.n_groups * self.group_bytes
         self.total_bytes = cfg.max_batch * cfg.n_kv_heads * 2 * self.block_bytes
+
+    @property
+    def r_row(self) -> int:
+        """Residual code bytes per token row (uniform widths only)."""
+        assert len(set(self.r_rows)) <= 1
+        return self.r_rows[0]
+
+    @property
+    def r_tile(self) -> int:
+        assert len(set(self.r_tiles)) <= 1
+        return self.r_tiles[0]
 
     def plane_offset(self, b: int, h: int, x: int, loop: int) -> int:
         cfg = self.cfg
         L = cfg.loops_per_group
         k, l = divmod(loop, L)
         off = ((b * cfg.n_kv_heads + h) * 2 + x) * self.block_bytes + k * self.group_bytes
-        off += l * self.n_tiles * self.r_tile            # residual planes of loops < l
+        off += self.n_tiles * sum(self.r_tiles[:l])      # residual planes of loops < l
         return off
 
     def bytes_per_token_head(self) -> Tuple[int, int]:
-        """(anchor, residual) bytes per token per KV head per K|V."""
+        """(anchor, residual) bytes per token per KV head per K|V (uniform widths)."""
         return self.a_row + self.m_row, self.r_row + self.m_row + 2
+
+    def bytes_per_token_loop(self) -> List[int]:
+        """Bytes per token per KV head per K|V of each local loop's plane (anchor last)."""
+        return [r + self.m_row + 2 for r in self.r_rows] + [self.a_row + self.m_row]
 
 
 def _pack_bits(codes: np.ndarray, bits: int) -> np.ndarray:
@@ -269,11 +292,12 @@ def _meta_bytes(z: np.ndarray, s: np.ndarray) -> np.ndarray:
     return m.reshape(m.shape[:-2] + (m.shape[-2] * 2,))
 
 
-def _plane_views(cache: np.ndarray, lay: Layout, off: int, resid: bool):
-    """Views (codes, meta, c) of a plane as [n_tiles][64][row] arrays."""
+def _plane_views(cache: np.ndarray, lay: Layout, off: int, l: int):
+    """Views (codes, meta, c) of local loop l's plane as [n_tiles][64][row] arrays."""
     n = lay.n_tiles
-    row = lay.r_row if resid else lay.a_row
-    tile = lay.r_tile if resid else lay.a_tile
+    resid = l < lay.cfg.loops_per_group - 1
+    row = lay.r_rows[l] if resid else lay.a_row
+    tile = lay.r_tiles[l] if resid else lay.a_tile
     plane = cache[off: off + n * tile].reshape(n, tile)
     codes = plane[:, : TILE * row].reshape(n, TILE, row)
     meta = plane[:, TILE * row: TILE * (row + lay.m_row)].reshape(n, TILE, lay.m_row)
@@ -292,13 +316,13 @@ def write_tokens(cache: np.ndarray, lay: Layout, b: int, h: int, x: int, group_i
         off = lay.plane_offset(b, h, x, group_idx * L + l)
         if l == L - 1:
             qa, za, sa = enc.anchor
-            codes, meta, _ = _plane_views(cache, lay, off, False)
+            codes, meta, _ = _plane_views(cache, lay, off, l)
             codes[ti, tj] = _pack_bits(qa, cfg.anchor_bits)
             meta[ti, tj] = _meta_bytes(za, sa)
         else:
             qr, zr, sr, c = enc.resid[l]
-            codes, meta, cb = _plane_views(cache, lay, off, True)
-            codes[ti, tj] = _pack_bits(qr, cfg.resid_bits)
+            codes, meta, cb = _plane_views(cache, lay, off, l)
+            codes[ti, tj] = _pack_bits(qr, cfg.rbits(l))
             meta[ti, tj] = _meta_bytes(zr, sr)
             cb[ti, tj] = bf16_bits(c).view(np.uint8).reshape(c.shape + (2,))
 
@@ -316,11 +340,11 @@ def read_tokens(cache: np.ndarray, lay: Layout, b: int, h: int, x: int, group_id
     for l in range(L):
         off = lay.plane_offset(b, h, x, group_idx * L + l)
         is_res = l < L - 1
-        codes, meta, cb = _plane_views(cache, lay, off, is_res)
+        codes, meta, cb = _plane_views(cache, lay, off, l)
         m = meta[ti, tj].reshape(n_tokens, nd, 2)
         z, s = e4m3_decode(m[..., 0]), e4m3_decode(m[..., 1])
         if is_res:
-            q = _unpack_bits(codes[ti, tj], cfg.resid_bits)
+            q = _unpack_bits(codes[ti, tj], cfg.rbits(l))
             cbits = cb[ti, tj].copy().view(np.uint16).reshape(n_tokens)
             resid[l] = (q, z, s, bf16_from_bits(cbits))
         else:
