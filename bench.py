@@ -68,10 +68,11 @@ def algorithmic_bytes(wl, loop_local: int, chained: bool) -> int:
     plane the loop needs, for K and V, for all context tokens of all (row, KV head)."""
     d, g = wl.head_dim, wl.group
     A = d * wl.anchor_bits // 8 + 2 * d // g
-    R = d * wl.resid_bits // 8 + 2 * d // g + 2
     L = wl.loops_per_group
-    n_res = 0 if loop_local == L - 1 else (L - 1 - loop_local if chained else 1)
-    return 2 * (A + n_res * R) * wl.batch * wl.ctx * wl.n_kv_heads
+    widths = wl.resid_bits_loop or (wl.resid_bits,) * (L - 1)
+    planes = [] if loop_local == L - 1 else (list(range(loop_local, L - 1)) if chained else [loop_local])
+    R = sum(d * widths[l] // 8 + 2 * d // g + 2 for l in planes)
+    return 2 * (A + R) * wl.batch * wl.ctx * wl.n_kv_heads
 
 
 def bf16_bytes(wl) -> int:
@@ -106,7 +107,8 @@ def _oracle_worker(args):
         small = wl.with_(batch=1, n_kv_heads=1, n_q_heads=wl.n_q_heads // wl.n_kv_heads)
         inp = synth.generate(small, seed=seed, device="cpu")
         cfg = RQ.Config(small.head_dim, small.group, small.anchor_bits, small.resid_bits, small.loops_per_group,
-                        small.n_groups, small.chained, 1, small.n_q_heads, 1, T + 1)
+                        small.n_groups, small.chained, 1, small.n_q_heads, 1, T + 1, small.scale_rule,
+                        tuple(small.resid_bits_loop))
         kv = inp.kv.double().numpy()
         rot = inp.rot.double().numpy()
         tp = time.perf_counter()
@@ -176,6 +178,8 @@ def main():
     ap.add_argument("--resid-bits", type=int, default=0, help="4: uniform INT4 (with 4-bit anchors)")
     ap.add_argument("--loops-per-group", type=int, default=0, help="loop group length (8 or 16: the larger groups)")
     ap.add_argument("--scale-rule", type=int, default=0, help="1: norm-ratio coefficient")
+    ap.add_argument("--resid-widths", default="", help="residual width per loop of a group, e.g. 4,2,2 "
+                    "(more bits far from the anchor)")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-baseline-only", action="store_true",
@@ -202,8 +206,12 @@ def main():
                       n_groups=max(1, wl.n_loops // args.loops_per_group))
     if args.scale_rule:
         wl = wl.with_(scale_rule=args.scale_rule)
+    widths = tuple(int(v) for v in args.resid_widths.split(",")) if args.resid_widths else ()
+    if widths:
+        wl = wl.with_(resid_bits_loop=widths)
     variant = "".join(t for t, on in (("+int4", args.resid_bits == 4), (f"+L{args.loops_per_group}", args.loops_per_group),
-                                      ("+norm_ratio", args.scale_rule == 1)) if on)
+                                      ("+norm_ratio", args.scale_rule == 1),
+                                      ("+widths" + "".join(map(str, widths)), bool(widths))) if on)
     if variant:
         wl = wl.with_(name=wl.name + variant)
     if args.cpu_baseline_only:
@@ -331,7 +339,7 @@ def main():
     step_bytes = sum(algorithmic_bytes(wl, l % L, wl.chained) for l in range(n_loops))
     res_loops = [l for l in range(L - 1)]
     res_ms = sum(per_loop[l] for l in res_loops) / len(res_loops)
-    res_bytes = algorithmic_bytes(wl, 0, False)
+    res_bytes = sum(algorithmic_bytes(wl, l, False) for l in res_loops) // len(res_loops)
     anchor_bytes = algorithmic_bytes(wl, L - 1, False)
     res_gbps = res_bytes / (res_ms * 1e-3) / 1e9
 
@@ -570,6 +578,7 @@ def main():
                    "n_kv_heads": wl.n_kv_heads, "head_dim": d, "loops": wl.n_loops,
                    "loops_per_group": L, "group": wl.group, "anchor_bits": wl.anchor_bits,
                    "resid_bits": wl.resid_bits, "chained": wl.chained, "scale_rule": wl.scale_rule,
+                   "resid_bits_loop": list(wl.resid_bits_loop),
                    "cache_replicas": n_rep},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "kv_tokens_per_s": round(Bt * T / (res_ms * 1e-3), 1),

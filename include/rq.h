@@ -66,13 +66,19 @@ typedef struct rq_config {
     int32_t scale_rule;       /* coefficient c of a residual loop: 0 = least squares <x,ref>/<ref,ref>
                                  (explainer and digest), 1 = norm ratio ||x||/||ref|| (the digest's
                                  appendix alternative, read as the ratio of Euclidean norms) */
+    int32_t resid_bits_loop[16]; /* residual code width of local loop l (0..L-2): 2 or 4, or 0 for
+                                 resid_bits; entries from L-1 on must be 0.  Per-loop widths let
+                                 the loops far from the anchor keep more bits than the near ones
+                                 (commentary page, section "它压的根本不是 KV"); widths that differ
+                                 need the shared anchor (chained = 0).  All zero: uniform. */
 } rq_config;
 
 /* Byte layout of the cache (one flat, 16-byte-aligned device buffer):
  * [batch][KV head][K|V] blocks; each block holds the n_groups*L planes in global loop
  * order (the anchor plane is the last of its group); each plane is ceil(max_ctx/64)
  * tiles of 64 tokens; a tile holds
- *   codes: 64 rows of d*bits/8 bytes, channel i at bit i*bits of its row (little-endian);
+ *   codes: 64 rows of d*bits/8 bytes, channel i at bit i*bits of its row (little-endian),
+ *          bits being the plane's own width (anchor_bits, or the loop's residual width);
  *   meta : 64 rows of 2*(d/g) bytes: E4M3 offset then E4M3 scale of each channel group;
  *   c    : residual planes only, 64 BF16 coefficients.
  * At d=128, g=32, INT4/INT2 a token costs 72 B (anchor) + 42 B (each residual) per

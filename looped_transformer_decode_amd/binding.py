@@ -29,7 +29,8 @@ EXPORTS = ("rq_cache_bytes", "rq_workspace_bytes", "rq_bf16_workspace_bytes", "r
 class rq_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "head_dim", "group", "anchor_bits", "resid_bits", "loops_per_group", "n_groups", "chained",
-        "n_kv_heads", "n_q_heads", "max_batch", "max_ctx", "scale_rule")]
+        "n_kv_heads", "n_q_heads", "max_batch", "max_ctx", "scale_rule")] + [
+        ("resid_bits_loop", ctypes.c_int32 * 16)]
 
 
 class rq_bf16_config(ctypes.Structure):
@@ -237,9 +238,11 @@ def rq_stream_read(buf: torch.Tensor, nbytes: int, sink: torch.Tensor, stream=No
 def config_for(wl, chained: Optional[bool] = None, max_batch: Optional[int] = None,
                max_ctx: Optional[int] = None) -> rq_config:
     """rq_config for a synth.Workload (capacity: its batch, context + the current token)."""
+    widths = tuple(getattr(wl, "resid_bits_loop", ()) or ())
     return rq_config(wl.head_dim, wl.group, wl.anchor_bits, wl.resid_bits, wl.loops_per_group,
                      wl.n_groups, int(wl.chained if chained is None else chained), wl.n_kv_heads,
-                     wl.n_q_heads, max_batch or wl.batch, max_ctx or wl.ctx + 1, wl.scale_rule)
+                     wl.n_q_heads, max_batch or wl.batch, max_ctx or wl.ctx + 1, wl.scale_rule,
+                     (ctypes.c_int32 * 16)(*widths))
 
 
 def bf16_config_for(wl, max_batch: Optional[int] = None, t_cap: Optional[int] = None) -> rq_bf16_config:

@@ -17,6 +17,13 @@ bool make_geom(const rq_config* c, Geom* g) {
     if (c->anchor_bits != 4 && c->anchor_bits != 2) return false;
     if (c->resid_bits != 2 && c->resid_bits != 4) return false;
     if (c->loops_per_group < 2 || c->loops_per_group > kMaxLoops) return false;
+    bool mixed = false;
+    for (int l = 0; l < kMaxLoops; ++l) {
+        const int w = c->resid_bits_loop[l];
+        if (w != 0 && (l >= c->loops_per_group - 1 || (w != 2 && w != 4))) return false;
+        if (w != 0 && w != c->resid_bits) mixed = true;
+    }
+    if (mixed && c->chained) return false;                      // chained decode reads one width
     if (c->n_groups < 1 || c->n_groups > 64) return false;
     if (c->chained != 0 && c->chained != 1) return false;
     if (c->chained && c->loops_per_group > 4) return false;     // kernels read at most 3 residual planes
@@ -39,17 +46,21 @@ bool make_geom(const rq_config* c, Geom* g) {
     g->scale_rule = c->scale_rule;
     g->n_tiles = (c->max_ctx + kTile - 1) / kTile;
     g->a_row = d * g->ba / 8;
-    g->r_row = d * g->br / 8;
     g->m_row = 2 * (d / gs);
     g->a_tile = (int64_t)kTile * (g->a_row + g->m_row);
-    g->r_tile = (int64_t)kTile * (g->r_row + g->m_row + 2);
-    g->group_bytes = (int64_t)g->n_tiles * (g->a_tile + (int64_t)(g->L - 1) * g->r_tile);
+    int64_t pre = 0;
+    for (int l = 0; l < kMaxLoops; ++l) {
+        g->rb[l] = (l < g->L - 1) ? (c->resid_bits_loop[l] ? c->resid_bits_loop[l] : g->br) : 0;
+        g->r_pre[l] = pre;
+        if (l < g->L - 1) pre += g->rtile(l);
+    }
+    g->group_bytes = (int64_t)g->n_tiles * (g->a_tile + g->r_pre[g->L - 1]);
     g->block_bytes = (int64_t)g->n_groups * g->group_bytes;
     g->total = (int64_t)g->max_batch * g->hkv * 2 * g->block_bytes;
     g->bt = nullptr;
     g->bt_stride = 0;
     g->n_blocks = 0;
-    g->g_tile = g->a_tile + (int64_t)(g->L - 1) * g->r_tile;
+    g->g_tile = g->a_tile + g->r_pre[g->L - 1];
     g->p_block = (int64_t)g->hkv * 2 * g->n_groups * g->g_tile;
     return true;
 }
@@ -286,7 +297,7 @@ static rq_status decode_impl(const rq_config* cfg, const void* cache, const int3
     const int nres = (lloc == g.L - 1) ? 0 : (g.chained ? g.L - 1 - lloc : 1);
     const int n_tiles = (ctx_bound + kTile - 1) / kTile;
     // the grouped-query kernel runs one workgroup per KV head and split (one per CU)
-    const bool grouped = gqa_supported(g, nres);
+    const bool grouped = gqa_supported(g, loop, nres);
     const int n_cu = device_cu_count();
     int S = n_splits ? n_splits
                      : (grouped ? auto_splits(batch * g.hkv, n_tiles, n_cu)

@@ -88,7 +88,7 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t stream);
 hipError_t launch_kv_project(const KvProjArgs& a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, int nres, bool qbf16, hipStream_t st);
 // grouped-query kernel (several query heads per KV head read each tile once)
-bool gqa_supported(const Geom& g, int nres);
+bool gqa_supported(const Geom& g, int loop, int nres);
 hipError_t launch_decode_gqa(const DecodeArgs& a, int nres, bool qbf16, hipStream_t st);
 hipError_t launch_bf16(const Bf16Args& a, int d, bool qbf16, hipStream_t st);
 

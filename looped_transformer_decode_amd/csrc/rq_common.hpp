@@ -19,15 +19,21 @@ constexpr int kStageDepth = 3;     // LDS ring slots per wave in the decode kern
 struct Geom {
     int d, g, ba, br, L, n_groups, chained, hkv, hq, max_batch, max_ctx;
     int n_tiles;
-    int a_row, r_row, m_row;           // bytes per token row: anchor codes, residual codes, meta
+    int a_row, m_row;                  // bytes per token row: anchor codes, meta
     int scale_rule;                    // 0: least-squares c, 1: norm-ratio c
-    int64_t a_tile, r_tile;            // bytes per tile
+    int rb[kMaxLoops];                 // residual code width of each local loop 0..L-2
+    int64_t a_tile;                    // bytes per anchor tile
+    int64_t r_pre[kMaxLoops];          // bytes of the residual tiles of local loops < l (one tile each)
     int64_t group_bytes, block_bytes, total;
+
+    __host__ __device__ int rbits(int l) const { return rb[l]; }
+    __host__ __device__ int rrow(int l) const { return d * rb[l] / 8; }                 // code bytes per token
+    __host__ __device__ int64_t rtile(int l) const { return (int64_t)kTile * (rrow(l) + m_row + 2); }
 
     __host__ __device__ int64_t plane_offset(int b, int h, int x, int loop) const {
         const int k = loop / L, l = loop % L;
         return ((int64_t)(b * hkv + h) * 2 + x) * block_bytes + (int64_t)k * group_bytes +
-               (int64_t)l * n_tiles * r_tile;
+               (int64_t)n_tiles * r_pre[l];
     }
 
     // Paged layout: a pool of physical blocks, each holding one 64-token tile of every (KV
@@ -41,13 +47,14 @@ struct Geom {
     // byte offset of the tile of (h, x, loop) inside physical block blk
     __host__ __device__ int64_t paged_offset(int blk, int h, int x, int loop) const {
         const int k = loop / L, l = loop % L;
-        return (int64_t)blk * p_block + ((int64_t)(h * 2 + x) * n_groups + k) * g_tile + (int64_t)l * r_tile;
+        return (int64_t)blk * p_block + ((int64_t)(h * 2 + x) * n_groups + k) * g_tile + r_pre[l];
     }
 
     // byte offset of tile `tile` of (b, h, x, loop) in either layout; a block id outside
     // [0, n_blocks) is clamped (the table is device data the host cannot check)
     __device__ int64_t tile_offset(int b, int h, int x, int loop, int tile) const {
-        if (bt == nullptr) return plane_offset(b, h, x, loop) + (int64_t)tile * (loop % L == L - 1 ? a_tile : r_tile);
+        const int l = loop % L;
+        if (bt == nullptr) return plane_offset(b, h, x, loop) + (int64_t)tile * (l == L - 1 ? a_tile : rtile(l));
         return paged_offset(block_id(b, tile), h, x, loop);
     }
     __device__ int block_id(int b, int tile) const {

@@ -214,9 +214,11 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
         rK[k] = a.cache + G.plane_offset(b, h, 0, a.loop + k);
         rV[k] = a.cache + G.plane_offset(b, h, 1, a.loop + k);
     }
+    // the residual planes a loop-step reads all have BR-bit codes (the host picks the
+    // instantiation from the loop's width; chained layouts have one width)
     const int a_meta = kTile * G.a_row;
-    const int r_meta = kTile * G.r_row;
-    const int r_cblk = kTile * (G.r_row + G.m_row);
+    const int r_meta = kTile * (D * BR / 8);
+    const int r_cblk = kTile * (D * BR / 8 + G.m_row);
 
     // Paged layout: the block of each of this wave's tiles is read through the scalar cache
     // one tile ahead (the first one here, at the top of the prologue).
@@ -244,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
             stage<AM, PAGED>(ap, ta + a_meta + p * AM, dst + AC, lane);
             dst += AC + AM;
             if constexpr (NRES > 0) {
-                const uint32_t tr = paged ? 0u : tile * (uint32_t)G.r_tile;
+                const uint32_t tr = paged ? 0u : tile * (uint32_t)(kTile * (D * BR / 8 + G.m_row + 2));
 #pragma unroll
                 for (int k = 0; k < NRES; ++k) {
                     const uint8_t* rp =
@@ -540,7 +542,7 @@ __global__ __launch_bounds__(kThreads) void rq_decode_kernel(DecodeArgs a) {
 template <int D, int GS, int BA, bool QB, bool PG>
 static hipError_t launch_nres(const DecodeArgs& a, int nres, dim3 grid, hipStream_t st) {
     // the anchor loop (nres 0) reads no residual plane: one instantiation for both widths
-    if (a.geo.br == 4) {
+    if (nres >= 1 && a.geo.rbits(a.loop % a.geo.L) == 4) {
         if (nres == 1) {
             hipLaunchKernelGGL((rq_decode_kernel<D, GS, BA, 4, 1, QB, PG>), grid, dim3(kThreads), 0, st, a);
             return hipGetLastError();
@@ -571,7 +573,7 @@ hipError_t launch_decode(const DecodeArgs& a, int nres, bool qbf16, hipStream_t 
         !a.mg.v_cur || !a.mg.out || !a.mg.rot || a.batch < 1 || a.n_splits < 1 || a.n_splits > kMaxSplits ||
         a.mg.n_splits != a.n_splits || a.mg.rec_splits < a.n_splits)
         return hipErrorInvalidValue;
-    if (gqa_supported(a.geo, nres)) return launch_decode_gqa(a, nres, qbf16, st);
+    if (gqa_supported(a.geo, a.loop, nres)) return launch_decode_gqa(a, nres, qbf16, st);
     const dim3 grid(a.batch * a.geo.hq * a.n_splits);
     const int d = a.geo.d, g = a.geo.g, ba = a.geo.ba;
     if (d == 128 && g == 32 && ba == 4) return launch_q<128, 32, 4>(a, nres, qbf16, grid, st);

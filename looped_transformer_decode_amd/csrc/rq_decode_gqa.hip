@@ -303,7 +303,7 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
             pblk_cur = pblk_nxt;
             if (it + 1 < n_it) pblk_nxt = block_id_scalar(Gm, b, (int)((blk + NW) >> 1));
         }
-        const uint32_t ta = PAGED ? 0u : tile * (uint32_t)Gm.a_tile, tr = PAGED ? 0u : tile * (uint32_t)Gm.r_tile;
+        const uint32_t ta = PAGED ? 0u : tile * (uint32_t)Gm.a_tile, tr = PAGED ? 0u : tile * (uint32_t)Gm.rtile(a.loop % L);
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
             const uint8_t* ap = PAGED ? uniform_ptr(a.cache + Gm.paged_offset(pblk_cur, h, x, aloop)) : (x ? aV : aK);
@@ -728,13 +728,14 @@ static hipError_t launch_q(const DecodeArgs& a, bool qbf16, dim3 grid, hipStream
 
 }  // namespace gqa
 
-bool gqa_supported(const Geom& g, int nres) {
+bool gqa_supported(const Geom& g, int loop, int nres) {
     const int gq = g.hq / g.hkv;
-    return g.d == gqa::D && g.g == gqa::GS && g.ba == 4 && (g.br == 2 || nres == 0) && nres <= 1 && (gq == 2 || gq == 4);
+    return g.d == gqa::D && g.g == gqa::GS && g.ba == 4 && (nres == 0 || g.rbits(loop % g.L) == 2) && nres <= 1 &&
+           (gq == 2 || gq == 4);
 }
 
 hipError_t launch_decode_gqa(const DecodeArgs& a, int nres, bool qbf16, hipStream_t st) {
-    if (!gqa_supported(a.geo, nres) || !a.cache || !a.q || !a.rot || !a.ctx_len || !a.mg.partials ||
+    if (!gqa_supported(a.geo, a.loop, nres) || !a.cache || !a.q || !a.rot || !a.ctx_len || !a.mg.partials ||
         !a.mg.arrivals || !a.mg.k_cur || !a.mg.v_cur || !a.mg.out || a.batch < 1 || a.n_splits < 1 ||
         a.n_splits > kMaxSplits || a.mg.n_splits != a.n_splits || a.mg.rec_splits < a.n_splits)
         return hipErrorInvalidValue;

@@ -289,13 +289,14 @@ __global__ __launch_bounds__(2 * D) void rq_pack_kernel(PackArgs a) {
             rotate_all<D, NL>(rhalf, sh_y, p, rl);
             QOut qr[NL];
 #pragma unroll
-            for (int l = 0; l < NL; ++l) qr[l] = quantize_lane<G>(rl[l], Gm.br);
+            for (int l = 0; l < NL; ++l) qr[l] = quantize_lane<G>(rl[l], Gm.rbits(SPLIT ? lsel : l));
 #pragma unroll
             for (int l = 0; l < NL; ++l) {
-                uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + (SPLIT ? lsel : l), tile);
-                store_codes(pl + jj * Gm.r_row, qr[l].code, Gm.br);
-                store_meta(pl + kTile * Gm.r_row + jj * Gm.m_row, qr[l], Gm.g);
-                store_c(pl + kTile * (Gm.r_row + Gm.m_row), jj, cs[l]);
+                const int ll = SPLIT ? lsel : l;         // local loop of this residual
+                uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + ll, tile);
+                store_codes(pl + jj * Gm.rrow(ll), qr[l].code, Gm.rbits(ll));
+                store_meta(pl + kTile * Gm.rrow(ll) + jj * Gm.m_row, qr[l], Gm.g);
+                store_c(pl + kTile * (Gm.rrow(ll) + Gm.m_row), jj, cs[l]);
             }
             __syncthreads();                              // sh_y is reused by the next token
         } else if constexpr (!SPLIT) {
@@ -310,11 +311,11 @@ __global__ __launch_bounds__(2 * D) void rq_pack_kernel(PackArgs a) {
                 __syncthreads();
                 double rl[1];
                 rotate_rows<D, 1>(rhalf, sh_y, p, rl);
-                const QOut qr = quantize_lane<G>(rl[0], Gm.br);
+                const QOut qr = quantize_lane<G>(rl[0], Gm.rbits(l));
                 uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + l, tile);
-                store_codes(pl + jj * Gm.r_row, qr.code, Gm.br);
-                store_meta(pl + kTile * Gm.r_row + jj * Gm.m_row, qr, Gm.g);
-                store_c(pl + kTile * (Gm.r_row + Gm.m_row), jj, c);
+                store_codes(pl + jj * Gm.rrow(l), qr.code, Gm.rbits(l));
+                store_meta(pl + kTile * Gm.rrow(l) + jj * Gm.m_row, qr, Gm.g);
+                store_c(pl + kTile * (Gm.rrow(l) + Gm.m_row), jj, c);
                 // R^T r_hat: the thread pair of channel i takes column i of R, rows
                 // [H p, H p + H) each (coalesced across the pairs)
                 if (p == 0) sh_y[1][i] = qr.z + qr.code * qr.s;
@@ -522,7 +523,7 @@ __global__ __launch_bounds__(bulk_threads<D>()) void rq_pack_bulk_kernel(PackArg
                 const double cl = bf16_round(na > 0.0 ? (norm_ratio ? sqrt(qn) : qn) : 0.0);
                 if (lok && lane == 0) {
                     uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + l, tile);
-                    reinterpret_cast<uint16_t*>(pl + (int64_t)kTile * (Gm.r_row + Gm.m_row))[jj] =
+                    reinterpret_cast<uint16_t*>(pl + (int64_t)kTile * (Gm.rrow(l) + Gm.m_row))[jj] =
                         (uint16_t)(__float_as_uint((float)cl) >> 16);
                 }
 #pragma unroll
@@ -573,9 +574,10 @@ __global__ __launch_bounds__(bulk_threads<D>()) void rq_pack_bulk_kernel(PackArg
                 double r[CPL], rh[CPL];
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) r[c] = yt[CPL * lane + c][tok * LB + li];
-                uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + (l < LR ? l : 0), tile);
-                if (Gm.br == 4) quantize_row<G, CPL, 4>(r, rh, pl, Gm.r_row, Gm.m_row, jj, ok && l < LR, lane);
-                else quantize_row<G, CPL, 2>(r, rh, pl, Gm.r_row, Gm.m_row, jj, ok && l < LR, lane);
+                const int lq = l < LR ? l : 0;            // a loop past the group's last is not stored
+                uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + lq, tile);
+                if (Gm.rbits(lq) == 4) quantize_row<G, CPL, 4>(r, rh, pl, Gm.rrow(lq), Gm.m_row, jj, ok && l < LR, lane);
+                else quantize_row<G, CPL, 2>(r, rh, pl, Gm.rrow(lq), Gm.m_row, jj, ok && l < LR, lane);
             }
         }
     }

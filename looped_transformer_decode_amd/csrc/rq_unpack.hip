@@ -60,8 +60,8 @@ __global__ __launch_bounds__(128) void rq_unpack_kernel(UnpackArgs a) {
         const int first = lloc == L - 1 ? -1 : (G.chained ? L - 2 : lloc);
         for (int l = first; l >= lloc; --l) {
             const uint8_t* rt = a.cache + G.tile_offset(b, h, x, grp * L + l, tile);
-            const float rh = dequant(rt, G.r_row, G.br, G, jj, i);
-            const uint16_t cb = *reinterpret_cast<const uint16_t*>(rt + (int64_t)kTile * (G.r_row + G.m_row) + 2 * jj);
+            const float rh = dequant(rt, G.rrow(l), G.rbits(l), G, jj, i);
+            const uint16_t cb = *reinterpret_cast<const uint16_t*>(rt + (int64_t)kTile * (G.rrow(l) + G.m_row) + 2 * jj);
             __syncthreads();                           // r_hat is reused
             r_hat[i] = rh;
             __syncthreads();

@@ -50,6 +50,7 @@ class Workload:
     q_dtype: str             # "fp32" | "bf16"
     chained: bool = False
     scale_rule: int = 0      # 0: least-squares c; 1: norm-ratio c
+    resid_bits_loop: Tuple[int, ...] = ()   # residual width per local loop 0..L-2 (empty: resid_bits)
 
     @property
     def n_loops(self) -> int:

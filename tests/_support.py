@@ -44,7 +44,7 @@ def oracle_cfg(wl, chained=None, max_batch=None, max_ctx=None, n_kv_heads=None, 
     return RQ.Config(wl.head_dim, wl.group, wl.anchor_bits, wl.resid_bits, wl.loops_per_group,
                      wl.n_groups, bool(wl.chained if chained is None else chained),
                      n_kv_heads or wl.n_kv_heads, n_q_heads or wl.n_q_heads,
-                     max_batch or wl.batch, max_ctx or wl.ctx + 1, wl.scale_rule)
+                     max_batch or wl.batch, max_ctx or wl.ctx + 1, wl.scale_rule, tuple(wl.resid_bits_loop))
 
 
 def pending_strides(kv: torch.Tensor):
@@ -72,7 +72,8 @@ def sub_cache(cache_np: np.ndarray, cfg: RQ.Config, b: int, h: int):
     lay = RQ.Layout(cfg)
     start = (b * cfg.n_kv_heads + h) * 2 * lay.block_bytes
     sub = RQ.Config(cfg.head_dim, cfg.group, cfg.anchor_bits, cfg.resid_bits, cfg.loops_per_group,
-                    cfg.n_groups, cfg.chained, 1, cfg.n_q_heads // cfg.n_kv_heads, 1, cfg.max_ctx, cfg.scale_rule)
+                    cfg.n_groups, cfg.chained, 1, cfg.n_q_heads // cfg.n_kv_heads, 1, cfg.max_ctx, cfg.scale_rule,
+                    cfg.resid_bits_loop)
     return np.ascontiguousarray(cache_np[start: start + 2 * lay.block_bytes]), sub
 
 
@@ -119,19 +120,19 @@ def check_encoding(enc: RQ.Encoded, xs: np.ndarray, R: np.ndarray, sub: RQ.Confi
         stats["c_total"] += cg.size
         y = xs[l] - cg[:, None] * ref
         r = y @ R.T
-        qe, ze, se = RQ.quantize(r, sub.resid_bits, g)
+        qe, ze, se = RQ.quantize(r, sub.rbits(l), g)
         rg = r.reshape(r.shape[0], -1, g)
         bad_meta = (ze != zg) | (se != sg)
         if np.any(bad_meta):
             lo = rg.min(-1)
-            n = 2 ** sub.resid_bits - 1
+            n = 2 ** sub.rbits(l) - 1
             need = (rg.max(-1) - ze) / n
             ok = _near_grid(lo) | _near_grid(need)
             assert np.all(ok[bad_meta]), "residual metadata differs away from a grid point"
             stats["near_meta"] += int(np.count_nonzero(bad_meta))
         # codes, judged with the metadata the GPU stored
         t = (rg - zg[..., None]) / sg[..., None]
-        q_with_gpu_meta = np.clip(np.rint(t), 0, 2 ** sub.resid_bits - 1).reshape(qg.shape)
+        q_with_gpu_meta = np.clip(np.rint(t), 0, 2 ** sub.rbits(l) - 1).reshape(qg.shape)
         bad = q_with_gpu_meta != qg
         if np.any(bad):
             tt = t.reshape(qg.shape)[bad]

@@ -67,3 +67,16 @@ def test_more_than_one_gpu_is_refused():
                            env={**os.environ, **env}, timeout=60)
         assert r.returncode == 2
         assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_loop_step_bytes_with_per_loop_widths():
+    """Residual widths 4, 2, 2: loop 0 reads its 74-byte residual rows, loops 1 and 2 their
+    42-byte ones, beside the 72-byte anchor rows (per token, head and K|V)."""
+    wl = synth.WORKLOADS["ouro_b4_t8192"].with_(resid_bits_loop=(4, 2, 2))
+    ht = wl.batch * wl.ctx * wl.n_kv_heads
+    lay = RQ.Layout(RQ.Config(wl.head_dim, wl.group, wl.anchor_bits, wl.resid_bits, 4, 1, False, wl.n_kv_heads,
+                              wl.n_q_heads, wl.batch, wl.ctx + 1, 0, (4, 2, 2)))
+    per = lay.bytes_per_token_loop()
+    assert per == [74, 42, 42, 72]
+    assert [bench.algorithmic_bytes(wl, l, False) for l in range(4)] == \
+        [2 * (72 + 74) * ht, 2 * (72 + 42) * ht, 2 * (72 + 42) * ht, 2 * 72 * ht]

@@ -82,6 +82,26 @@ def test_variant_configs_match_oracle_layout(B, variant):
     assert B.rq_cache_bytes(cfg) == RQ.Layout(ocfg).total_bytes > 0
 
 
+@pytest.mark.parametrize("widths", [(4, 2, 2), (4, 4, 2), (2, 2, 2), (2, 4, 2)])
+def test_per_loop_widths_match_oracle_layout(B, widths):
+    wl = synth.WORKLOADS["ouro_b4_t8192"].with_(resid_bits_loop=widths)
+    cfg = B.config_for(wl)
+    ocfg = RQ.Config(wl.head_dim, wl.group, wl.anchor_bits, wl.resid_bits, wl.loops_per_group, wl.n_groups,
+                     False, wl.n_kv_heads, wl.n_q_heads, wl.batch, wl.ctx + 1, 0, widths)
+    assert B.rq_cache_bytes(cfg) == RQ.Layout(ocfg).total_bytes > 0
+    # the paged block holds one tile of every plane: the oracle's group bytes per tile
+    assert B.rq_paged_block_bytes(cfg) == 16 * 2 * RQ.Layout(ocfg).group_bytes // RQ.Layout(ocfg).n_tiles
+
+
+def test_invalid_per_loop_widths_are_rejected(B):
+    wl = synth.WORKLOADS["ouro_b4_t8192"]
+    for widths in ((3, 2, 2), (8, 2, 2), (2, 2, 2, 4), (-2, 2, 2)):
+        cfg = B.config_for(wl.with_(resid_bits_loop=widths))
+        assert B.rq_cache_bytes(cfg) == 0, widths
+    assert B.rq_cache_bytes(B.config_for(wl.with_(resid_bits_loop=(4, 2, 2)), chained=True)) == 0
+    assert B.rq_cache_bytes(B.config_for(wl.with_(resid_bits_loop=(2, 2, 2)), chained=True)) > 0
+
+
 def test_status_strings(B):
     assert B.rq_status_str(0) == "ok"
     assert "workspace" in B.rq_status_str(4)

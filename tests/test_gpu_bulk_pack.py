@@ -25,6 +25,8 @@ CASES = {
     "L6_d128g16int2": (W["int2g16_b4_t16384"].with_(loops_per_group=6, loop_scale=U), 1, 70, 2, 0, None),
     "L8_d64": (W["tiny_d64_t256"].with_(loops_per_group=8, loop_scale=U), 1, 40, 2, 0, None),
     "past_max_ctx": (W["ouro_b4_t8192"], 2, 50, 1, 51, 96),
+    "L6_widths_d128g32": (W["ouro_b4_t8192"].with_(loops_per_group=6, loop_scale=U, resid_bits_loop=(4, 4, 2, 2, 2)),
+                          2, 90, 2, 0, None),
 }
 
 

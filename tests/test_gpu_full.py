@@ -29,7 +29,15 @@ FULL = [
     ("int2g16_b4_t16384", False),
     ("int2g16_b4_t16384", True),
     ("huginn_gqa4_b8_t8192", False),
+    ("ouro_b4_t8192+widths422", False),     # residual widths 4, 2, 2 (more bits far from the anchor)
 ]
+VARIANTS = {"widths422": dict(resid_bits_loop=(4, 2, 2))}
+
+
+def _workload(name):
+    base, _, var = name.partition("+")
+    wl = synth.WORKLOADS[base]
+    return wl.with_(name=name, **VARIANTS[var]) if var else wl
 
 
 def _pairs(wl, rng):
@@ -47,7 +55,7 @@ def _loops(wl):
 @pytest.mark.parametrize("name,chained", FULL, ids=[f"{n}{'_chained' if c else ''}" for n, c in FULL])
 def test_full_size_parity(name, chained):
     from looped_transformer_decode_amd import binding as B
-    wl = synth.WORKLOADS[name].with_(chained=chained)
+    wl = _workload(name).with_(chained=chained)
     T, L, d = wl.ctx, wl.loops_per_group, wl.head_dim
     gqa = wl.n_q_heads // wl.n_kv_heads
     say(f"[full] {name} chained={chained}: generating")

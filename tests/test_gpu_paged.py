@@ -31,6 +31,7 @@ CASES = {
     "d128g16int2_chained": (W["int2g16_b4_t16384"], True, 2, [65, 200], 2, 2),
     "gqa4_two_groups": (W["huginn_gqa4_b8_t8192"].with_(n_groups=2), False, 2, [190, 77], 2, 8),
     "d64": (W["tiny_d64_t256"], False, 1, [150], 2, 2),
+    "widths_422_d128g32": (W["ouro_b4_t8192"].with_(resid_bits_loop=(4, 2, 2)), False, 2, [190, 64], 2, 2),
 }
 
 
@@ -38,7 +39,8 @@ def gather(pool: np.ndarray, table: np.ndarray, cfg: RQ.Config, block_bytes: int
     """The contiguous cache that holds the tiles the block table points at."""
     lay = RQ.Layout(cfg)
     L, G = cfg.loops_per_group, cfg.n_groups
-    g_tile = lay.a_tile + (L - 1) * lay.r_tile
+    g_tile = lay.a_tile + sum(lay.r_tiles)
+    pre = [sum(lay.r_tiles[:l]) for l in range(L)]          # tile bytes before plane l in a block
     cache = np.zeros(lay.total_bytes, np.uint8)
     for b in range(cfg.max_batch):
         for t in range(lay.n_tiles):
@@ -48,9 +50,9 @@ def gather(pool: np.ndarray, table: np.ndarray, cfg: RQ.Config, block_bytes: int
                     for k in range(G):
                         base = blk * block_bytes + ((h * 2 + x) * G + k) * g_tile
                         for l in range(L):
-                            size = lay.a_tile if l == L - 1 else lay.r_tile
+                            size = lay.a_tile if l == L - 1 else lay.r_tiles[l]
                             dst = lay.plane_offset(b, h, x, k * L + l) + t * size
-                            cache[dst: dst + size] = pool[base + l * lay.r_tile: base + l * lay.r_tile + size]
+                            cache[dst: dst + size] = pool[base + pre[l]: base + pre[l] + size]
     return cache
 
 

@@ -26,6 +26,7 @@ CASES = {
     "tiny_chained": (W["tiny_d64_t256"], True, 1, 256, None, None, (0, 256)),
     "d128g16int2_chained": (W["int2g16_b4_t16384"], True, 2, 190, 2, 2, (63, 190)),
     "gqa4_two_groups": (W["huginn_gqa4_b8_t8192"].with_(n_groups=2), False, 2, 130, 2, 8, (1, 129)),
+    "widths_422": (W["ouro_b4_t8192"].with_(resid_bits_loop=(4, 2, 2)), False, 2, 150, 2, 2, (3, 150)),
 }
 
 

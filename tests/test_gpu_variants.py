@@ -1,7 +1,9 @@
 """GPU parity of the precision, group-length and scale-rule settings on the same kernels:
 uniform INT4 (4-bit anchors and 4-bit residuals), the mixed INT2/4 at g = 16, loop groups
-of 8 and 16, the norm-ratio coefficient (shared and chained), and the grouped-query
-kernel with two query heads per KV head.  Each case packs a
+of 8 and 16, the norm-ratio coefficient (shared and chained), the grouped-query kernel
+with two query heads per KV head, and residual widths per loop (4 bits far from the
+anchor, 2 bits near it; with grouped queries the 2-bit loops run on the grouped kernel and
+the 4-bit ones on the one-query kernel).  Each case packs a
 ragged context (the many-token kernel), decodes every loop (or a spread of loops for the
 16-loop group) at several split counts against the oracle, and checks the drained token
 of every group whose loops all ran (the one-loop-per-workgroup kernel)."""
@@ -33,6 +35,14 @@ CASES = {
     "norm_ratio_chained_int2g16": (W["int2g16_b4_t16384"].with_(scale_rule=1), True, 2, [65, 130], 2, 2, None),
     "norm_ratio_int4_uniform_d64": (W["tiny_d64_t256"].with_(scale_rule=1, resid_bits=4), False, 1, [200], 2, 2,
                                     None),
+    "widths_422_d128g32": (W["ouro_b4_t8192"].with_(resid_bits_loop=(4, 2, 2)), False, 3, [0, 70, 200], 2, 2, None),
+    "widths_442_d64g16_bf16q": (W["tiny_d64_t256"].with_(group=16, resid_bits_loop=(4, 4, 2), q_dtype="bf16"), False,
+                                2, [129, 63], 2, 2, None),
+    "widths_loops8_gqa4": (W["huginn_gqa4_b8_t8192"].with_(loops_per_group=8, n_groups=2, loop_scale=U,
+                                                            resid_bits_loop=(4, 4, 4, 2, 2, 2, 2)), False, 2,
+                           [150, 90], 2, 8, None),
+    "widths_norm_ratio_d128g16": (W["int2g16_b4_t16384"].with_(anchor_bits=4, scale_rule=1, resid_bits_loop=(4, 2, 2)),
+                                  False, 2, [65, 130], 2, 2, None),
 }
 
 
