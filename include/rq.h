@@ -196,7 +196,9 @@ rq_status rq_decode_attention_noalloc(const rq_config* cfg, const void* cache, i
 
 /* rq_bf16_decode_attention - the same decode attention over an uncompressed BF16
  * cache (the baseline the arXiv digest's section 5.3 compares against: BF16
- * FlashAttention decode over each loop's own KV).
+ * FlashAttention decode over each loop's own KV).  With head_dim 128 and 2 or 4 query
+ * heads per KV head one workgroup serves the whole query group, so each K/V tile is read
+ * once per group; otherwise one workgroup per query head.
  *   cfg       : host pointer.
  *   k_cache, v_cache : device BF16 [max_batch][n_kv_heads][t_cap][head_dim] of one loop.
  *   append    : if nonzero, k_cur/v_cur are also stored at slot ctx_len[b] (when < t_cap).

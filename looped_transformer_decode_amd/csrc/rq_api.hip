@@ -433,7 +433,11 @@ rq_status rq_bf16_decode_attention(const rq_bf16_config* cfg, uint16_t* k_cache,
     if (!workspace || workspace_bytes_ < need) return RQ_ERR_WORKSPACE;
     const int n_tiles = (ctx_bound + kTile - 1) / kTile;
     const int n_cu = device_cu_count();
-    int S = n_splits ? n_splits : auto_splits(batch * n_q_heads, n_tiles, 2 * n_cu);
+    // grouped queries: one workgroup of 8 waves per (row, KV head, split), one per CU
+    const bool grouped = bf16_gqa_supported(head_dim, n_q_heads, cfg->n_kv_heads);
+    int S = n_splits ? n_splits
+                     : (grouped ? auto_splits(batch * cfg->n_kv_heads, n_tiles, n_cu)
+                                : auto_splits(batch * n_q_heads, n_tiles, 2 * n_cu));
     if (n_tiles > 0 && S > n_tiles) S = n_tiles;
     if (S < 1) S = 1;
     Bf16Args a;
@@ -470,6 +474,7 @@ rq_status rq_bf16_decode_attention(const rq_bf16_config* cfg, uint16_t* k_cache,
         m.ctx_len = ctx_len;
         m.ctx_bound = ctx_bound;
     }
+    if (grouped) return launch_bf16_gqa(a, q_is_bf16 != 0, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
     return launch_bf16(a, head_dim, q_is_bf16 != 0, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 

@@ -91,5 +91,8 @@ hipError_t launch_decode(const DecodeArgs& a, int nres, bool qbf16, hipStream_t 
 bool gqa_supported(const Geom& g, int loop, int nres);
 hipError_t launch_decode_gqa(const DecodeArgs& a, int nres, bool qbf16, hipStream_t st);
 hipError_t launch_bf16(const Bf16Args& a, int d, bool qbf16, hipStream_t st);
+// grouped-query BF16 kernel (the G query heads of a KV head read each tile once)
+bool bf16_gqa_supported(int d, int hq, int hkv);
+hipError_t launch_bf16_gqa(const Bf16Args& a, bool qbf16, hipStream_t st);
 
 }  // namespace rq

@@ -29,6 +29,7 @@ CASES = {
     "d128g16int2_chained": (W["int2g16_b4_t16384"], True, 3, [65, 200, 127], 2, 2),
     "gqa4_two_groups": (W["huginn_gqa4_b8_t8192"].with_(n_groups=2), False, 2, [190, 77], 2, 8),
     "d64_bf16q_ragged": (W["tiny_d64_t256"].with_(q_dtype="bf16"), False, 2, [129, 63], None, None),
+    "gqa2_ragged_fp32q": (W["huginn_gqa4_b8_t8192"].with_(n_groups=1, q_dtype="fp32"), False, 3, [100, 1, 300], 2, 4),
 }
 
 
@@ -51,8 +52,10 @@ def test_decode_step_parity(B, name):
     run_decode_step_parity(B, name, wl, inp, cfg, ocfg, ctx, T)
 
 
-@pytest.mark.parametrize("name", ["tiny", "d128g32_ragged", "gqa4_two_groups"])
+@pytest.mark.parametrize("name", ["tiny", "d128g32_ragged", "gqa4_two_groups", "gqa2_ragged_fp32q"])
 def test_bf16_decode_parity(B, name):
+    """The BF16 baseline against float64 softmax attention; with 2 or 4 query heads per KV
+    head at head_dim 128 it runs the kernel that serves the whole query group."""
     wl, inp, cfg, ocfg, ctx, T = _setup(B, name, seed=7)
     say(f"[bf16] case={name} ctx={ctx}")
     dev = inp.kv.device
@@ -78,7 +81,7 @@ def test_bf16_decode_parity(B, name):
                 keys = np.concatenate([kv[grp, l, 0, b, h, :ctx[b]], kv[grp, l, 0, b, h, T][None]])
                 vals = np.concatenate([kv[grp, l, 1, b, h, :ctx[b]], kv[grp, l, 1, b, h, T][None]])
                 ref[b, hq] = RQ.attention(qn[b, hq], keys, vals, sc)
-        for ns in (0, 1):
+        for ns in (0, 1, 3):
             out = torch.full((wl.batch, Hq, d), float("nan"), dtype=torch.float32, device=dev)
             say(f"[bf16] case={name} loop={loop} n_splits={ns}")
             B.rq_bf16_decode_attention(bcfg, K.contiguous(), V.contiguous(), q, k_cur, v_cur, False, ctx_len, T,
@@ -89,8 +92,9 @@ def test_bf16_decode_parity(B, name):
             assert e <= 1.0
 
 
-def test_bf16_append_writes_current_token(B):
-    wl, inp, cfg, ocfg, ctx, T = _setup(B, "d128g32_ragged", seed=8)
+@pytest.mark.parametrize("name", ["d128g32_ragged", "gqa4_two_groups"])
+def test_bf16_append_writes_current_token(B, name):
+    wl, inp, cfg, ocfg, ctx, T = _setup(B, name, seed=8)
     dev = inp.kv.device
     bcfg = B.bf16_config_for(wl)
     ws = torch.zeros(B.rq_bf16_workspace_bytes(bcfg), dtype=torch.uint8, device=dev)
@@ -100,7 +104,7 @@ def test_bf16_append_writes_current_token(B):
     k_cur = torch.randn(wl.batch, wl.n_kv_heads, wl.head_dim, device=dev).to(torch.bfloat16)
     v_cur = torch.randn(wl.batch, wl.n_kv_heads, wl.head_dim, device=dev).to(torch.bfloat16)
     out = torch.empty(wl.batch, wl.n_q_heads, wl.head_dim, device=dev)
-    say("[bf16-append]")
+    say(f"[bf16-append] case={name}")
     B.rq_bf16_decode_attention(bcfg, K, V, inp.q[0].contiguous(), k_cur, v_cur, True, ctx_len, T,
                                0.1, out, ws, wl.batch)
     torch.cuda.synchronize()
