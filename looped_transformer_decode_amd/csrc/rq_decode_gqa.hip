@@ -39,6 +39,15 @@ constexpr int AC = BT * AROW, AM = BT * MROW, RC = BT * RROW, RM = BT * MROW, CC
 constexpr int NB = 2;                            // ring slots (blocks) per wave
 constexpr int NW = 8, NT = NW * kWave;           // waves and threads per workgroup (one per CU)
 constexpr uint32_t kMagic2 = 0x64006400u;
+// The value weights p c s_a and p s_r (p = exp(score - reference)) are rounded to FP16 for
+// the matrix cores, whose largest finite value is 65504.  With the reference raised whenever
+// a score exceeds it by more than 4, p <= e^4 < 54.6.  s_r <= 448, and |c| s_a <= 0.16 |x|
+// (|c| <= |x| / |a_hat| by Cauchy-Schwarz; s_a <= 1.125 * (2 + 1/8) max|a_hat| / 15, the
+// offset lying at most an eighth below the group minimum), at most 810 for d = 128 inputs in
+// the E4M3 range: every weight stays below 44,300.  A larger slack would let p reach e^8 and
+// the anchor weights overflow once |c| s_a exceeds 22; a smaller one pushes more weights of
+// tokens that still matter into FP16's subnormal range.
+constexpr float kSlack = 4.0f;
 
 __device__ __forceinline__ uint32_t gload4(const uint8_t* sbase, uint32_t voff) {
     uint32_t r;
@@ -394,7 +403,7 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
             sc[r] = vl[r] ? score : -INFINITY;
         }
         const float smax = fmaxf(sc[0], sc[1]);
-        if (wave_any(smax > m_run + kRescaleSlack)) {     // rare: raise the reference of each query
+        if (wave_any(smax > m_run + kSlack)) {            // rare: raise the reference of each query
             const float m_new = fmaxf(m_run, row_max16(smax));
             const float fs = m_run == -INFINITY ? 0.f : __expf(m_run - m_new);
             float fq[4];
