@@ -16,8 +16,9 @@
 //    w = p c s_a (anchor) or p s_r (residual).  The token-major codes are turned into
 //    the channel-major B operand by the LDS transpose read ds_read_b64_tr_b4, which
 //    gives each lane one 4-bit column of 16 rows (rows = 8-byte chunks named by the
-//    16 lanes of its group).  The weights go through LDS as FP16 in the same K order;
-//    the group offsets z accumulate separately in float32.
+//    16 lanes of its group).  The weights go through LDS as FP16 in the same K order
+//    (the anchor weight as hi + lo terms, the residual weight as one term); the group
+//    offsets z accumulate separately in float32.
 // The split-K merge is the same as the one-query kernel's, run for each query head.
 #include "rq_args.hpp"
 #include "rq_merge_group.hpp"
@@ -129,8 +130,8 @@ template <int G, int NRES>
 struct Smem {
     static constexpr int PASS = 2 * (AC + AM + NRES * (RC + RM + CC));
     uint8_t ring[NW][NB][PASS];                          // also the epilogue's scratch
-    _Float16 wbuf[NW][2][NG][G][BT];                     // value weights, in MFMA K order
-    h8 akey[3][NG][kWave];                               // key A operands: q hi, q lo, u
+    _Float16 wbuf[NW][3][NG][G][BT];                     // value weights in MFMA K order: anchor hi, anchor lo, residual
+    h8 akey[4][NG][kWave];                               // key A operands: q hi, q lo, u hi, u lo
     float sq[G][D];                                      // queries (float32)
     float su[G][D];                                      // u = R_K q
     float qsum[2][G][NG];                                // group sums of q and of u
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
                 // the key A value of channel c, as the MFMA sees it (FP16, hi + lo for q)
                 const float a = pl ? ldexpf(v, -2 * (c & 3)) : ((c & 1) ? v * 0.0625f : v);
                 const _Float16 hi = (_Float16)a;
-                off += (float)hi + (pl ? 0.f : (float)(_Float16)(a - (float)hi));
+                off += (float)hi + (float)(_Float16)(a - (float)hi);
             }
         }
         sm.qsum[pl][g][gi] = s;
@@ -300,8 +301,8 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
     }
     // A operands of the key products, shared by the waves: lane (m = 4 qh + g', kg) holds
     // row m, K elements 8 kg .. 8 kg + 7 of channel group gi, nonzero only where g' == gi.
-    // Thread t < 3 * 64 builds kind t / 64 (q hi, q lo, u) for lane t % 64.
-    if (threadIdx.x < 3 * kWave) {
+    // Thread t < 4 * 64 builds kind t / 64 (q hi, q lo, u hi, u lo) for lane t % 64.
+    if (threadIdx.x < 4 * kWave) {
         const int kind = threadIdx.x / kWave, L = threadIdx.x % kWave;
         const int ll = L & 15, lk = L >> 4, qh_a = ll >> 2, ga = ll & 3;
         h8 frag;
@@ -377,7 +378,7 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
                     uint32_t wr = *reinterpret_cast<const uint32_t*>(sp + RES_OFF + t * RROW + (2 * gi + (kg >> 1)) * 4);
                     wr = (kg & 1) ? (wr >> 8) : wr;
                     const h8 bu = b_magic_crumbs(wr);
-                    dr = mfma(sm.akey[2][gi][lane], bu, dr);
+                    dr = mfma(sm.akey[3][gi][lane], bu, mfma(sm.akey[2][gi][lane], bu, dr));
                 }
             }
             // score of (token t, query qs): this lane holds the 4 group products in da / dr
@@ -459,25 +460,32 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
                 const float za = fp8(mw, 2 * (gi & 1)), sa = fp8(mw, 2 * (gi & 1) + 1);
                 zA[gi] += pc * za;
                 const float wa = pc * sa * mult;
-                if (q_ok) sm.wbuf[w][0][gi][qs][pos] = (_Float16)wa;
+                // the anchor weight as two FP16 terms (about 22 significant bits): the anchor part
+                // carries most of the output, so its weights get the second term
+                const _Float16 wa_hi = (_Float16)wa;
+                if (q_ok) {
+                    sm.wbuf[w][0][gi][qs][pos] = wa_hi;
+                    sm.wbuf[w][1][gi][qs][pos] = (_Float16)(wa - (float)wa_hi);
+                }
                 if constexpr (NRES > 0) {
                     const uint32_t rw = gi < 2 ? vrm.x : vrm.y;
                     const float zr = fp8(rw, 2 * (gi & 1)), sr = fp8(rw, 2 * (gi & 1) + 1);
                     zR[gi] += p * zr;
                     const float wr = p * sr * mult;
-                    if (q_ok) sm.wbuf[w][1][gi][qs][pos] = (_Float16)wr;
+                    if (q_ok) sm.wbuf[w][2][gi][qs][pos] = (_Float16)wr;
                 }
             }
         }
 
         // ---- values: K = the 32 tokens of the block, N = 16 channels per product
         // A: lane (m = query, kg) reads the 8 weights of tokens 8kg.. in K order
-        h8 wa8[NG], wr8[NG];
+        h8 wa8[NG], wl8[NG], wr8[NG];
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
             wa8[gi] = l16 < G ? *reinterpret_cast<const h8*>(&sm.wbuf[w][0][gi][l16][8 * kg]) : zero8;
+            wl8[gi] = l16 < G ? *reinterpret_cast<const h8*>(&sm.wbuf[w][1][gi][l16][8 * kg]) : zero8;
             if constexpr (NRES > 0)
-                wr8[gi] = l16 < G ? *reinterpret_cast<const h8*>(&sm.wbuf[w][1][gi][l16][8 * kg]) : zero8;
+                wr8[gi] = l16 < G ? *reinterpret_cast<const h8*>(&sm.wbuf[w][2][gi][l16][8 * kg]) : zero8;
         }
         // transpose reads: lane l16 of group kg names row (token 8kg + l16 % 8, chunk c0 + l16 / 8)
         typedef __attribute__((address_space(3))) v2i* lp;
@@ -486,8 +494,9 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
         for (int nb2 = 0; nb2 < NG; ++nb2) {              // anchor: 16-channel chunks 2nb2, 2nb2+1
             const uint32_t addr = vbase + (8 * kg + (l16 & 7)) * AROW + (2 * nb2 + (l16 >> 3)) * 8;
             const v2i tv = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lp)(uintptr_t)addr);
-            va[2 * nb2] = mfma(wa8[nb2], b_from_nibbles((uint32_t)tv.x), va[2 * nb2]);
-            va[2 * nb2 + 1] = mfma(wa8[nb2], b_from_nibbles((uint32_t)tv.y), va[2 * nb2 + 1]);
+            const h8 bx = b_from_nibbles((uint32_t)tv.x), by = b_from_nibbles((uint32_t)tv.y);
+            va[2 * nb2] = mfma(wl8[nb2], bx, mfma(wa8[nb2], bx, va[2 * nb2]));
+            va[2 * nb2 + 1] = mfma(wl8[nb2], by, mfma(wa8[nb2], by, va[2 * nb2 + 1]));
         }
         if constexpr (NRES > 0) {
 #pragma unroll
