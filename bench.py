@@ -31,9 +31,12 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_WORKLOAD = "ouro_b16_t8192"
 CSRC = os.path.join(ROOT, "looped_transformer_decode_amd", "csrc")
-# sources of the decode kernel (split-K with the merge in its last workgroup)
+# sources of the decode kernels (split-K with the merge in the last workgroup): the one-query
+# kernel, and the grouped-query kernel that serves the query heads of a KV head together
 DECODE_SOURCES = ("rq_api.hip", "rq_decode.hip", "rq_args.hpp", "rq_common.hpp",
                   "rq_splitk.hpp", "rq_stage.hpp")
+GQA_SOURCES = ("rq_api.hip", "rq_decode_gqa.hip", "rq_args.hpp", "rq_common.hpp",
+               "rq_merge_group.hpp", "rq_splitk.hpp", "rq_stage.hpp")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -41,9 +44,19 @@ def traffic_profile(workload: str) -> str:
     return os.path.join(PROFILES, f"rq_decode_residual_{workload}_hbm_traffic.txt")
 
 
-def decode_source_digest() -> str:
+def grouped_kernel(wl) -> bool:
+    """Whether the library runs this workload's residual loop-steps on the grouped-query kernel:
+    head_dim 128, g = 32, INT4 anchor, 2-bit residual planes read one at a time (not chained),
+    2 or 4 query heads per KV head (the routing rule of rq_decode_attention)."""
+    gq = wl.n_q_heads // wl.n_kv_heads
+    return (wl.head_dim == 128 and wl.group == 32 and wl.anchor_bits == 4 and not wl.chained
+            and all(b == 2 for b in (wl.resid_bits_loop or (wl.resid_bits,))) and gq in (2, 4))
+
+
+def decode_source_digest(wl=None) -> str:
+    """Digest of the sources of the kernel that runs the workload's residual loop-steps."""
     h = hashlib.sha256()
-    for name in DECODE_SOURCES:
+    for name in (GQA_SOURCES if wl is not None and grouped_kernel(wl) else DECODE_SOURCES):
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -58,7 +71,9 @@ def measured_traffic(workload: str):
     except OSError:
         return None
     kv = {k.strip(): v.strip() for k, v in kv.items()}
-    if kv.get("source_digest") != decode_source_digest() or kv.get("workload") != workload:
+    from looped_transformer_decode_amd import synth
+    wl = synth.WORKLOADS.get(workload)
+    if wl is None or kv.get("source_digest") != decode_source_digest(wl) or kv.get("workload") != workload:
         return None
     return int(float(kv["traffic_bytes_per_loop_step"]))
 
@@ -630,8 +645,9 @@ def main():
                      "timing": "HIP events around back-to-back residual loop-steps (loops 0..L-2, cold replicas), "
                                "on the library's stream, the last decode dispatches of the run; mean of 3 "
                                "repeats (min_frac: the fastest repeat)",
-                     "kernel": "rq_decode_kernel, residual loop-step (split-K with the merge in its last workgroup)",
-                     "algorithmic_bytes": round(roof_bytes), "source_digest": decode_source_digest()},
+                     "kernel": ("rq_decode_gqa_kernel" if grouped_kernel(wl) else "rq_decode_kernel")
+                     + ", residual loop-step (split-K with the merge in its last workgroup)",
+                     "algorithmic_bytes": round(roof_bytes), "source_digest": decode_source_digest(wl)},
     }
     if cpu_base is not None:
         result["cpu_baseline"] = cpu_base
