@@ -189,6 +189,12 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
     }
 
     const uint32_t ring_base = __builtin_amdgcn_readfirstlane(lds_addr_of(&sm.ring[w][0][0]));
+    // The residual code rows land swizzled: the 16-byte chunk j of token t at slot
+    // j ^ ((t >> 2) & 1) of its 32-byte row, so that a read of one chunk column over 16
+    // tokens (the key words, the transposed value reads) spreads over the LDS banks.  Each
+    // DMA lane fetches the chunk its slot holds.
+    const uint32_t r_swz = 16u * ((lane & ~1u) | ((lane & 1u) ^ ((lane >> 3) & 1u)));
+    const uint32_t hr = (l16 >> 2) & 1;                  // the swizzle of the lane's tokens
     auto issue = [&](int it) {
         const uint32_t blk = first + NW * it;
         const uint32_t tile = blk >> 1, hb = blk & 1;
@@ -206,7 +212,8 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
             stage<AM, PAGED>(ap, ta + a_meta + hb * AM, dst + AC, lane);
             if constexpr (NRES > 0) {
                 const uint8_t* rp = PAGED ? uniform_ptr(a.cache + Gm.paged_offset(pblk_cur, h, x, a.loop)) : (x ? rV : rK);
-                stage<RC, PAGED>(rp, tr + hb * RC, dst + RES_OFF, lane);
+                static_assert(RC == 1024, "one DMA per block of residual rows");
+                dma16<PAGED, true>(tr + hb * RC + r_swz, rp, dst + RES_OFF);
                 stage<RM, PAGED>(rp, tr + r_meta + hb * RM, dst + RES_OFF + RC, lane);
                 stage<CC, PAGED, false>(rp, tr + r_cblk + hb * CC, dst + RES_OFF + RC + RM, lane);   // line shared by the tile's two blocks
             }
@@ -290,7 +297,7 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
             for (int c = 0; c < GS; ++c) {
                 const float v = src[GS * gi + c];
                 s += v;
-                // the key A value of channel c, as the MFMA sees it (FP16, hi + lo for q)
+                // the key A value of channel c, as the MFMA sees it (FP16 hi + lo)
                 const float a = pl ? ldexpf(v, -2 * (c & 3)) : ((c & 1) ? v * 0.0625f : v);
                 const _Float16 hi = (_Float16)a;
                 off += (float)hi + (float)(_Float16)(a - (float)hi);
@@ -325,7 +332,6 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) sm.akey[kind][gi][L] = gi == ga ? frag : z8;
     }
-    const h8 zero8 = {};
     __syncthreads();
     // score-layout lane: token l16 of a 16-token round, query kg
     const int qs = kg;
@@ -375,7 +381,8 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
                 da = mfma(sm.akey[0][gi][lane], bq, da);
                 da = mfma(sm.akey[1][gi][lane], bq, da);
                 if constexpr (NRES > 0) {
-                    uint32_t wr = *reinterpret_cast<const uint32_t*>(sp + RES_OFF + t * RROW + (2 * gi + (kg >> 1)) * 4);
+                    uint32_t wr = *reinterpret_cast<const uint32_t*>(sp + RES_OFF + t * RROW + 16 * ((gi >> 1) ^ hr) +
+                                                                      4 * ((2 * gi + (kg >> 1)) & 3));
                     wr = (kg & 1) ? (wr >> 8) : wr;
                     const h8 bu = b_magic_crumbs(wr);
                     dr = mfma(sm.akey[3][gi][lane], bu, mfma(sm.akey[2][gi][lane], bu, dr));
@@ -478,14 +485,16 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
         }
 
         // ---- values: K = the 32 tokens of the block, N = 16 channels per product
-        // A: lane (m = query, kg) reads the 8 weights of tokens 8kg.. in K order
+        // A: lane (m = query, kg) reads the 8 weights of tokens 8kg.. in K order.  Rows m >= G
+        // hold a copy of row m mod G: their results are never read (the epilogue takes rows
+        // 0..G-1), and a real row costs no zero fill in the loop.
+        const int mrow = l16 & (G - 1);
         h8 wa8[NG], wl8[NG], wr8[NG];
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
-            wa8[gi] = l16 < G ? *reinterpret_cast<const h8*>(&sm.wbuf[w][0][gi][l16][8 * kg]) : zero8;
-            wl8[gi] = l16 < G ? *reinterpret_cast<const h8*>(&sm.wbuf[w][1][gi][l16][8 * kg]) : zero8;
-            if constexpr (NRES > 0)
-                wr8[gi] = l16 < G ? *reinterpret_cast<const h8*>(&sm.wbuf[w][2][gi][l16][8 * kg]) : zero8;
+            wa8[gi] = *reinterpret_cast<const h8*>(&sm.wbuf[w][0][gi][mrow][8 * kg]);
+            wl8[gi] = *reinterpret_cast<const h8*>(&sm.wbuf[w][1][gi][mrow][8 * kg]);
+            if constexpr (NRES > 0) wr8[gi] = *reinterpret_cast<const h8*>(&sm.wbuf[w][2][gi][mrow][8 * kg]);
         }
         // transpose reads: lane l16 of group kg names row (token 8kg + l16 % 8, chunk c0 + l16 / 8)
         typedef __attribute__((address_space(3))) v2i* lp;
@@ -501,7 +510,7 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
         if constexpr (NRES > 0) {
 #pragma unroll
             for (int cp = 0; cp < 2; ++cp) {               // residual: 32-channel chunks 2cp, 2cp+1
-                const uint32_t addr = vbase + RES_OFF + (8 * kg + (l16 & 7)) * RROW + (2 * cp + (l16 >> 3)) * 8;
+                const uint32_t addr = vbase + RES_OFF + (8 * kg + (l16 & 7)) * RROW + 16 * (cp ^ hr) + 8 * (l16 >> 3);
                 const v2i tv = __builtin_amdgcn_ds_read_tr4_b64_v2i32((lp)(uintptr_t)addr);
 #pragma unroll
                 for (int hw = 0; hw < 2; ++hw) {
