@@ -291,6 +291,72 @@ rq_status rq_kv_project(const rq_config* cfg, const uint16_t* x, int64_t x_strid
                         const uint16_t* w_kv, int32_t loop, uint16_t* k_cur, uint16_t* v_cur,
                         uint16_t* pending, int32_t batch, hipStream_t stream);
 
+/* ---- W4A4 linear layer with cross-loop residual activations --------------------------
+ * arXiv digest (ai4snews), scope paragraph after the results: the authors carry the same
+ * residual-reconstruction principle over to W4A4 activation quantization (the pages give
+ * no scheme).  A looped block runs the same linear layer y = W x at every loop.  Weights
+ * are 4-bit codes with the KV anchor's group quantizer (groups of 32 consecutive input
+ * channels of one output row, FP8-E4M3 offset rounded down, smallest covering E4M3 scale,
+ * codes rounded half to even).  In each group of loops the FIRST loop's activations are
+ * the 4-bit anchor a_hat (at decode time an earlier loop's layer runs before any later
+ * loop's activation exists) and its product y0 = W_hat a_hat is kept; every later loop
+ * takes a BF16 least-squares coefficient c = <x, a_hat> / <a_hat, a_hat> and the 4-bit
+ * quantized residual r = R (x - c a_hat) (one orthogonal 128 x 128 R applied to every block
+ * of 128 input channels), and its output is y = c y0 + W_R_hat r_hat, where W_R_hat is the
+ * 4-bit quantization of W R^T (the rotation folded into a second weight copy).
+ *
+ * Byte layouts.  Weights: rows in tiles of 16, input groups in quads of 4; per (row tile,
+ * quad) 1024 code bytes then 128 metadata bytes, blocks ordered by row tile then quad.
+ * The 16 code bytes at 16 (16 kg + i) hold for row i of the tile four little-endian words,
+ * word j for group j of the quad, channels 8 kg .. 8 kg + 7 (channel 8 kg + e in bits 4 e);
+ * metadata bytes 2 (4 i + j) and 2 (4 i + j) + 1 are that group's offset and scale.
+ * Activations: one row per token of K/2 code bytes (channel 2 i in the low nibble of byte
+ * i, 2 i + 1 in the high one) then K/16 metadata bytes (offset, scale per group). */
+typedef struct rq_w4a4_config {
+    int32_t in_features;      /* K: 1024, 2048, 3072 or 4096 */
+    int32_t out_features;     /* N: a positive multiple of 16 */
+    int32_t max_tokens;       /* tokens per call: 1..16 */
+} rq_w4a4_config;
+
+/* Bytes of one packed weight matrix (N K / 2 + N K / 16), of max_tokens activation rows
+ * (max_tokens (K/2 + K/16)), and of the workspace rq_w4a4_linear needs; 0 for an
+ * unsupported configuration. */
+size_t rq_w4_weight_bytes(const rq_w4a4_config* cfg);
+size_t rq_w4a4_act_bytes(const rq_w4a4_config* cfg);
+size_t rq_w4a4_workspace_bytes(const rq_w4a4_config* cfg);
+
+/* rq_w4_quantize_weights - offline: pack W (rot NULL) or W R^T (rot set) as 4-bit groups in
+ * the weight tile layout.  Float64 arithmetic: codes and metadata are those of a float64
+ * reference except at inexact ties of the code rounding.
+ *   w        : device BF16 [out_features][w_stride], the first in_features of each row used.
+ *   rot      : device float32 [128][128] (row-major R) or NULL.
+ *   out      : device, rq_w4_weight_bytes(cfg) bytes, 16-byte aligned.
+ * One kernel is enqueued. */
+rq_status rq_w4_quantize_weights(const rq_w4a4_config* cfg, const uint16_t* w, int64_t w_stride,
+                                 const float* rot, void* out, hipStream_t stream);
+
+/* rq_w4a4_linear - one loop of the layer for n_tokens tokens.
+ *   weights    : packed W_hat at loop_local 0, packed W_R_hat at loop_local > 0.
+ *   x          : device BF16 [n_tokens][x_stride] activations of this loop.
+ *   loop_local : position of the loop in its group; 0 is the anchor loop.
+ *   anchor     : device activation rows [max_tokens]: written at loop_local 0 (the 4-bit
+ *                anchor), read at loop_local > 0.  Keep it across the group's loops.
+ *   act        : device activation rows of this loop (a copy of the anchor rows at loop 0,
+ *                the residual rows otherwise) or NULL (then the workspace holds them).
+ *   rot        : device float32 [128][128] R; required at loop_local > 0.
+ *   c_out      : device float32 [n_tokens] coefficient used (1 at the anchor loop) or NULL.
+ *   y0         : device float32 [n_tokens][out_features]: the anchor product, written at
+ *                loop_local 0 and read at loop_local > 0 (y0 == y is allowed at loop 0).
+ *   y          : device float32 [n_tokens][out_features] output.
+ * Arithmetic: the quantizers in float64 (codes as a float64 reference except inexact
+ * near-ties; c within one BF16 step), the product on the matrix cores from exact FP16
+ * operands with float32 accumulation.  Alignment: weights, anchor, act, rot, workspace
+ * 16-byte aligned.  Two kernels are enqueued. */
+rq_status rq_w4a4_linear(const rq_w4a4_config* cfg, const void* weights, const uint16_t* x, int64_t x_stride,
+                         int32_t loop_local, void* anchor, void* act, const float* rot, float* c_out,
+                         float* y0, float* y, int32_t n_tokens, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
 /* rq_stream_read - a measuring stick, not part of the method: read `bytes` of `buf`
  * with plain 16-byte loads (one contiguous slab per workgroup, XOR-folded into one word
  * per thread of `sink`).  Timed over the same buffers as the decode kernel it gives the

@@ -23,7 +23,8 @@ _lib = ctypes.CDLL(_LIB_PATH)
 EXPORTS = ("rq_cache_bytes", "rq_workspace_bytes", "rq_bf16_workspace_bytes", "rq_status_str",
            "rq_quantize_token", "rq_decode_attention", "rq_bf16_decode_attention", "rq_unpack_debug",
            "rq_stream_read", "rq_paged_block_bytes", "rq_quantize_token_paged", "rq_decode_attention_paged",
-           "rq_kv_project", "rq_decode_attention_noalloc")
+           "rq_kv_project", "rq_decode_attention_noalloc", "rq_w4_weight_bytes", "rq_w4a4_act_bytes",
+           "rq_w4a4_workspace_bytes", "rq_w4_quantize_weights", "rq_w4a4_linear")
 
 
 class rq_config(ctypes.Structure):
@@ -35,6 +36,10 @@ class rq_config(ctypes.Structure):
 
 class rq_bf16_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("head_dim", "n_kv_heads", "n_q_heads", "max_batch", "t_cap")]
+
+
+class rq_w4a4_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("in_features", "out_features", "max_tokens")]
 
 
 class RQError(RuntimeError):
@@ -81,6 +86,15 @@ _lib.rq_decode_attention_paged.argtypes = [_cfgp, _vp, _i32, _vp, _i32, _i32, _v
 _lib.rq_decode_attention_paged.restype = _i32
 _lib.rq_kv_project.argtypes = [_cfgp, _vp, ctypes.c_int64, _i32, _vp, _i32, _vp, _vp, _vp, _i32, _vp]
 _lib.rq_kv_project.restype = _i32
+_wcfgp = ctypes.POINTER(rq_w4a4_config)
+for _fn in ("rq_w4_weight_bytes", "rq_w4a4_act_bytes", "rq_w4a4_workspace_bytes"):
+    getattr(_lib, _fn).argtypes = [_wcfgp]
+    getattr(_lib, _fn).restype = _sz
+_lib.rq_w4_quantize_weights.argtypes = [_wcfgp, _vp, ctypes.c_int64, _vp, _vp, _vp]
+_lib.rq_w4_quantize_weights.restype = _i32
+_lib.rq_w4a4_linear.argtypes = [_wcfgp, _vp, _vp, ctypes.c_int64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
+                                _sz, _vp]
+_lib.rq_w4a4_linear.restype = _i32
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -248,3 +262,64 @@ def config_for(wl, chained: Optional[bool] = None, max_batch: Optional[int] = No
 def bf16_config_for(wl, max_batch: Optional[int] = None, t_cap: Optional[int] = None) -> rq_bf16_config:
     return rq_bf16_config(wl.head_dim, wl.n_kv_heads, wl.n_q_heads, max_batch or wl.batch,
                           t_cap or wl.ctx + 1)
+
+
+# ---- W4A4 linear layer with cross-loop residual activations
+
+def w4a4_config(in_features: int, out_features: int, max_tokens: int) -> rq_w4a4_config:
+    return rq_w4a4_config(in_features, out_features, max_tokens)
+
+
+def rq_w4_weight_bytes(cfg: rq_w4a4_config) -> int:
+    return int(_lib.rq_w4_weight_bytes(ctypes.byref(cfg)))
+
+
+def rq_w4a4_act_bytes(cfg: rq_w4a4_config) -> int:
+    return int(_lib.rq_w4a4_act_bytes(ctypes.byref(cfg)))
+
+
+def rq_w4a4_workspace_bytes(cfg: rq_w4a4_config) -> int:
+    return int(_lib.rq_w4a4_workspace_bytes(ctypes.byref(cfg)))
+
+
+def _need(name: str, t: Optional[torch.Tensor], dtype, numel: int, dev) -> None:
+    if t is None:
+        return
+    if t.dtype != dtype or not t.is_contiguous() or t.numel() < numel or t.device != dev:
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of >= {numel} elements on {dev}")
+
+
+def rq_w4_quantize_weights(cfg: rq_w4a4_config, w: torch.Tensor, rot: Optional[torch.Tensor], out: torch.Tensor,
+                           stream=None) -> None:
+    """w: BF16 [out_features][>= in_features] (unit channel stride); rot: float32 [128][128] or None;
+    out: uint8 of rq_w4_weight_bytes(cfg) bytes."""
+    if w.dtype != torch.bfloat16 or w.dim() != 2 or w.stride(1) != 1 or w.shape[0] != cfg.out_features \
+            or w.shape[1] < cfg.in_features:
+        raise ValueError("rq_w4_quantize_weights: w must be a BF16 [out_features][in_features] tensor")
+    _need("rq_w4_quantize_weights: out", out, torch.uint8, rq_w4_weight_bytes(cfg), w.device)
+    _need("rq_w4_quantize_weights: rot", rot, torch.float32, 128 * 128, w.device)
+    _check("rq_w4_quantize_weights", _lib.rq_w4_quantize_weights(
+        ctypes.byref(cfg), _ptr(w), w.stride(0), _ptr(rot), _ptr(out), _stream(stream)))
+
+
+def rq_w4a4_linear(cfg: rq_w4a4_config, weights: torch.Tensor, x: torch.Tensor, loop_local: int,
+                   anchor: torch.Tensor, act: Optional[torch.Tensor], rot: Optional[torch.Tensor],
+                   c_out: Optional[torch.Tensor], y0: torch.Tensor, y: torch.Tensor, n_tokens: int,
+                   workspace: torch.Tensor, stream=None) -> None:
+    """x: BF16 [>= n_tokens][>= in_features] (unit channel stride); anchor, act: uint8 activation
+    rows; y0, y: float32 [n_tokens][out_features]; c_out: float32 [n_tokens] or None."""
+    dev = x.device
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1 or x.shape[0] < n_tokens \
+            or x.shape[1] < cfg.in_features:
+        raise ValueError("rq_w4a4_linear: x must be a BF16 [tokens][in_features] tensor")
+    _need("rq_w4a4_linear: weights", weights, torch.uint8, rq_w4_weight_bytes(cfg), dev)
+    _need("rq_w4a4_linear: anchor", anchor, torch.uint8, rq_w4a4_act_bytes(cfg), dev)
+    _need("rq_w4a4_linear: act", act, torch.uint8, rq_w4a4_act_bytes(cfg), dev)
+    _need("rq_w4a4_linear: rot", rot, torch.float32, 128 * 128, dev)
+    _need("rq_w4a4_linear: c_out", c_out, torch.float32, n_tokens, dev)
+    _need("rq_w4a4_linear: y0", y0, torch.float32, n_tokens * cfg.out_features, dev)
+    _need("rq_w4a4_linear: y", y, torch.float32, n_tokens * cfg.out_features, dev)
+    _need("rq_w4a4_linear: workspace", workspace, torch.uint8, 1, dev)
+    _check("rq_w4a4_linear", _lib.rq_w4a4_linear(
+        ctypes.byref(cfg), _ptr(weights), _ptr(x), x.stride(0), loop_local, _ptr(anchor), _ptr(act), _ptr(rot),
+        _ptr(c_out), _ptr(y0), _ptr(y), n_tokens, _ptr(workspace), _nbytes(workspace), _stream(stream)))

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librq.so")
 SOURCES = ["rq_api.hip", "rq_pack.hip", "rq_decode.hip", "rq_decode_gqa.hip", "rq_bf16.hip", "rq_unpack.hip", "rq_probe.hip",
-           "rq_kvproj.hip"]
+           "rq_kvproj.hip", "rq_w4a4.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -179,3 +179,53 @@ def projection_inputs(wl: Workload, seed: int = 20261203, device: Union[str, tor
     x = torch.randn(wl.n_loops, B, H, generator=gen, dtype=torch.float32)
     w = torch.randn(2, wl.n_kv_heads, wl.head_dim, H, generator=gen, dtype=torch.float32) / math.sqrt(H)
     return ProjectionInputs(x.to(torch.bfloat16).to(device), w.to(torch.bfloat16).to(device))
+
+
+# ---- W4A4 linear layer of a looped block (cross-loop residual activations)
+
+@dataclasses.dataclass(frozen=True)
+class W4A4Workload:
+    name: str
+    in_features: int         # K
+    out_features: int        # N
+    tokens: int              # decode batch
+    loops: int               # loops of one group (loop 0 is the anchor)
+
+
+#: Linear layers of an Ouro-1.4B-sized looped block (model width 2048) at decode.
+W4A4_WORKLOADS = {
+    # the MLP's up projection (4x width) for a decode batch of 16, one group of 4 loops
+    "ouro_up_b16": W4A4Workload("ouro_up_b16", 2048, 8192, 16, 4),
+    # a small case the float64 oracle checks in full
+    "tiny_w4a4": W4A4Workload("tiny_w4a4", 1024, 64, 3, 3),
+}
+
+
+@dataclasses.dataclass
+class W4A4Inputs:
+    w: torch.Tensor          # [N][K] bf16
+    rot: torch.Tensor        # [128][128] fp32, orthogonal
+    x: torch.Tensor          # [L][M][K] bf16 activations of loops 0..L-1
+
+
+def w4a4_inputs(wl: W4A4Workload, seed: int = 20261204, device: Union[str, torch.device] = "cpu",
+                tokens: Optional[int] = None) -> W4A4Inputs:
+    """Weights ~ N(0, 1/K); the anchor loop's activations ~ N(0, 1) with 8 outlier channels
+    per token (x8, shared by every token and loop, as in normalised hidden states of LLMs);
+    loop l >= 1: a_l * x0 + 0.15 N(0, 1) with a_l ~ U(0.8, 1.0) per token.  All BF16."""
+    M = tokens if tokens is not None else wl.tokens
+    K, N, L = wl.in_features, wl.out_features, wl.loops
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    w = torch.randn(N, K, generator=gen, dtype=torch.float64) / math.sqrt(K)
+    x0 = torch.randn(M, K, generator=gen, dtype=torch.float64)
+    out_ch = torch.randperm(K, generator=gen)[:8]
+    x0[:, out_ch] *= 8.0
+    xs = [x0]
+    for _ in range(1, L):
+        a = 0.8 + 0.2 * torch.rand(M, 1, generator=gen, dtype=torch.float64)
+        xs.append(a * x0 + 0.15 * torch.randn(M, K, generator=gen, dtype=torch.float64))
+    q, r = torch.linalg.qr(torch.randn(128, 128, generator=gen, dtype=torch.float64))
+    rot = (q * torch.sign(torch.diagonal(r))).to(torch.float32).contiguous()
+    return W4A4Inputs(w.to(torch.bfloat16).to(device), rot.to(device),
+                      torch.stack(xs).to(torch.bfloat16).to(device))

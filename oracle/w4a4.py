@@ -58,7 +58,7 @@ def rotate_blocks(v: np.ndarray, rot: np.ndarray) -> np.ndarray:
     k = v.shape[-1]
     assert k % ROT_BLOCK == 0 and rot.shape == (ROT_BLOCK, ROT_BLOCK)
     vb = v.reshape(v.shape[:-1] + (k // ROT_BLOCK, ROT_BLOCK))
-    return np.einsum("ji,...bi->...bj", np.asarray(rot, np.float64), vb).reshape(v.shape)
+    return (vb @ np.asarray(rot, np.float64).T).reshape(v.shape)     # [.., b, j] = sum_i v[.., b, i] R[j, i]
 
 
 def rotate_weights(w: np.ndarray, rot: np.ndarray) -> np.ndarray:
@@ -67,7 +67,7 @@ def rotate_weights(w: np.ndarray, rot: np.ndarray) -> np.ndarray:
     w = np.asarray(w, dtype=np.float64)
     n, k = w.shape
     wb = w.reshape(n, k // ROT_BLOCK, ROT_BLOCK)
-    return np.einsum("nbi,ji->nbj", wb, np.asarray(rot, np.float64)).reshape(n, k)
+    return (wb @ np.asarray(rot, np.float64).T).reshape(n, k)        # [n, b, j] = sum_i W[n, b, i] R[j, i]
 
 
 def quantize_weights(w: np.ndarray, rot: Optional[np.ndarray] = None) -> Quantized:
@@ -227,4 +227,18 @@ def read_act(buf: np.ndarray, m: int, k: int) -> Quantized:
         codes[t, 1::2] = b >> 4
         zb[t] = buf[base + k // 2: base + row: 2]
         sb[t] = buf[base + k // 2 + 1: base + row: 2]
+    return codes, e4m3_decode(zb), e4m3_decode(sb)
+
+
+def read_weights_fast(buf: np.ndarray, n: int, k: int) -> Quantized:
+    """read_weights by array reshapes (for full-size matrices); equal to read_weights."""
+    from .formats import e4m3_decode
+    nt, nq = n // TILE_N, k // (GROUP * QUAD)
+    blk = np.asarray(buf, np.uint8)[: nt * nq * 1152].reshape(nt, nq, 1152)
+    words = np.ascontiguousarray(blk[:, :, :1024]).view("<u4").reshape(nt, nq, 4, TILE_N, QUAD).astype(np.int64)
+    nib = (words[..., None] >> (4 * np.arange(8))) & 15                 # [nt][nq][kg][i][j][e]
+    codes = nib.transpose(0, 3, 1, 4, 2, 5).reshape(n, k)               # row (nt, i), channel (nq, j, kg, e)
+    meta = blk[:, :, 1024:].reshape(nt, nq, TILE_N, QUAD, 2)
+    zb = meta[..., 0].transpose(0, 2, 1, 3).reshape(n, k // GROUP)
+    sb = meta[..., 1].transpose(0, 2, 1, 3).reshape(n, k // GROUP)
     return codes, e4m3_decode(zb), e4m3_decode(sb)

@@ -19,6 +19,6 @@ def pytest_terminal_summary(terminalreporter):
     margins = getattr(sup, "MARGINS", None) if sup else None
     if not margins:
         return
-    terminalreporter.write_sep("-", "parity margins: worst |o_gpu - o_ref| / (1e-3 max|o_ref| + 1e-5)")
+    terminalreporter.write_sep("-", "parity margins: worst error / tolerance bound per case (attention: 1e-3 max|o_ref| + 1e-5)")
     for tag, worst in margins:
-        terminalreporter.write_line(f"{worst:7.3f}  {tag}")
+        terminalreporter.write_line(f"{worst:9.3g}  {tag}")

@@ -1,0 +1,205 @@
+"""GPU parity of the W4A4 linear layer with cross-loop residual activations against the
+float64 oracle (oracle/w4a4.py):
+
+* the packed weights (W and W R^T): every code and offset/scale byte against the oracle's
+  quantizer, codes allowed to differ only at inexact near-ties of the rounding;
+* the activation rows of every loop: the anchor loop's bytes likewise, each later loop's
+  coefficient c within one BF16 step of the oracle's (computed from the device's anchor
+  rows), its residual rows judged with the device's c;
+* the outputs: against the oracle's product of the device's own bytes, within the
+  float32 accumulation bound below, and against the oracle run end to end on the same
+  inputs (its own quantization) within 2e-3 of the largest output.
+
+Float32 bound of the product: per output the device adds at most 2 K/32 + 17 float32
+terms, each an exact product of FP16 operands or (for the offsets z_w X) a product with X
+split into two FP16 terms (2^-22 relative), so |y - y_ref| <= 3e-5 S with
+S = |W_hat| |x_hat| (+ |c| |y0| at the later loops); 2^-24 (2 * 4096/32 + 17) < 1.7e-5.
+"""
+import numpy as np
+import pytest
+import torch
+
+from looped_transformer_decode_amd import synth
+from oracle import w4a4 as W4
+
+from _support import record_margin, say
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (K, N, tokens, loops)
+    "k1024_n64_m3": (1024, 64, 3, 3),
+    "k2048_n128_m16": (2048, 128, 16, 4),
+    "k3072_n48_m1": (3072, 48, 1, 2),
+    "k4096_n32_m7": (4096, 32, 7, 3),
+}
+
+
+def _near_tie_ok(gpu_codes, ref_codes, vals, z, s, what):
+    """Codes equal except where the oracle's (v - z) / s lies within 1e-6 of a half-integer;
+    those are counted and stay below 1e-5 of the codes (plus one)."""
+    bad = gpu_codes != ref_codes
+    if not bad.any():
+        return 0
+    g = vals.shape[-1] // 32
+    t = (vals.reshape(vals.shape[:-1] + (g, 32)) - z[..., None]) / s[..., None]
+    t = t.reshape(vals.shape)
+    near = np.abs(t - (np.floor(t) + 0.5)) <= 1e-6 * np.maximum(1.0, np.abs(t))
+    assert np.all(near[bad]), f"{what}: {int((bad & ~near).sum())} codes differ away from a tie"
+    assert bad.sum() <= 1 + 1e-5 * bad.size, f"{what}: {int(bad.sum())} near-tie differences"
+    assert np.all(np.abs(gpu_codes[bad] - ref_codes[bad]) == 1)
+    return int(bad.sum())
+
+
+def _check_quantized(gpu, vals, what):
+    ref = W4.quantize(vals, 4, 32)
+    assert np.array_equal(gpu[1], ref[1]), f"{what}: offsets differ"
+    assert np.array_equal(gpu[2], ref[2]), f"{what}: scales differ"
+    return _near_tie_ok(gpu[0], ref[0], vals, ref[1], ref[2], what)
+
+
+def _run(B, K, N, M, L, inp, device, act_none=False, alias_y0=False):
+    cfg = B.w4a4_config(K, N, M)
+    wq = torch.zeros(B.rq_w4_weight_bytes(cfg), dtype=torch.uint8, device=device)
+    wrq = torch.zeros_like(wq)
+    B.rq_w4_quantize_weights(cfg, inp.w, None, wq)
+    B.rq_w4_quantize_weights(cfg, inp.w, inp.rot, wrq)
+    anchor = torch.zeros(B.rq_w4a4_act_bytes(cfg), dtype=torch.uint8, device=device)
+    ws = torch.zeros(B.rq_w4a4_workspace_bytes(cfg), dtype=torch.uint8, device=device)
+    y0 = torch.full((M, N), float("nan"), device=device)
+    out = []
+    for l in range(L):
+        act = None if act_none else torch.zeros(B.rq_w4a4_act_bytes(cfg), dtype=torch.uint8, device=device)
+        c = torch.full((M,), float("nan"), device=device)
+        y = y0 if (alias_y0 and l == 0) else torch.full((M, N), float("nan"), device=device)
+        say(f"[w4a4] K={K} N={N} M={M} loop {l}")
+        B.rq_w4a4_linear(cfg, wq if l == 0 else wrq, inp.x[l].contiguous(), l, anchor, act, inp.rot, c, y0, y, M, ws)
+        torch.cuda.synchronize()
+        out.append((None if act is None else act.cpu().numpy(), c.cpu().numpy().astype(np.float64),
+                    y.cpu().numpy().astype(np.float64)))
+    return cfg, wq.cpu().numpy(), wrq.cpu().numpy(), anchor.cpu().numpy(), y0.cpu().numpy().astype(np.float64), out
+
+
+def _verify(K, N, M, L, inp, res, check_weights=True, tag=""):
+    cfg, wq_b, wrq_b, anchor_b, y0_dev, out = res
+    w = inp.w.double().cpu().numpy()
+    rot = inp.rot.double().cpu().numpy()
+    xs = inp.x.double().cpu().numpy()
+    wq = W4.read_weights_fast(wq_b, N, K)
+    wrq = W4.read_weights_fast(wrq_b, N, K)
+    ties = 0
+    if check_weights:
+        ties += _check_quantized(wq, w, "weights")
+        ties += _check_quantized(wrq, W4.rotate_weights(w, rot), "rotated weights")
+    a = W4.read_act(anchor_b, M, K)
+    ties += _check_quantized(a, xs[0, :M], "anchor activations")
+    wh, wrh = W4.dequant(wq), W4.dequant(wrq)
+    ah = W4.dequant(a)
+    y0_ref = ah @ wh.T
+    s0 = np.abs(ah) @ np.abs(wh).T
+    worst = 0.0
+    for l in range(L):
+        act_b, c_dev, y_dev = out[l]
+        if l == 0:
+            assert np.all(c_dev == 1.0)
+            if act_b is not None:
+                assert np.array_equal(act_b[: anchor_b.size], anchor_b)
+            ref, bound = y0_ref, 3e-5 * s0
+            assert np.all(np.abs(y0_dev - y0_ref) <= 3e-5 * s0 + 1e-30)
+        else:
+            c_ref = W4.ls_coefficient(xs[l, :M], ah)[0]
+            # one BF16 step at c_ref (8 significant bits); an exact zero must stay zero
+            step = np.where(c_ref != 0, 2.0 ** (np.floor(np.log2(np.abs(np.where(c_ref != 0, c_ref, 1.0)))) - 7), 0.0)
+            assert np.all(np.abs(c_dev - c_ref) <= step), (l, c_dev, c_ref)
+            _, rq = W4.residual_activation(xs[l, :M], a, rot, c_override=c_dev)
+            if act_b is not None:
+                r_dev = W4.read_act(act_b, M, K)
+                r_vals = W4.rotate_blocks(xs[l, :M] - c_dev[:, None] * ah, rot)
+                ties += _check_quantized(r_dev, r_vals, f"loop {l} residual")
+                rq = r_dev
+            rh = W4.dequant(rq)
+            ref = c_dev[:, None] * y0_ref + rh @ wrh.T
+            bound = 3e-5 * (np.abs(c_dev)[:, None] * s0 + np.abs(rh) @ np.abs(wrh).T)
+        err = np.abs(y_dev - ref)
+        assert np.all(err <= bound + 1e-30), (l, float((err / (bound + 1e-30)).max()))
+        worst = max(worst, float((err / (bound + 1e-30)).max()))
+    # end to end against the oracle's own quantization of the same inputs
+    ys, cs, _ = W4.looped_linear(xs[:, :M], w, rot)
+    for l in range(L):
+        y_dev = out[l][2]
+        assert np.max(np.abs(y_dev - ys[l])) <= 2e-3 * np.max(np.abs(ys[l])) + 1e-6, l
+    say(f"[w4a4] {tag}: near-tie code differences {ties}, worst err/bound {worst:.3f}")
+    record_margin(f"w4a4 {tag} (float32 bound)", worst)
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_w4a4_loops(name):
+    from looped_transformer_decode_amd import binding as B
+    K, N, M, L = CASES[name]
+    wl = synth.W4A4Workload(name, K, N, M, L)
+    inp = synth.w4a4_inputs(wl, seed=31, device="cuda")
+    res = _run(B, K, N, M, L, inp, "cuda", alias_y0=(name == "k1024_n64_m3"))
+    _verify(K, N, M, L, inp, res, tag=name)
+
+
+def test_w4a4_rows_in_workspace():
+    """act = NULL keeps the residual rows in the workspace: same coefficients and outputs,
+    to the bit, as a call that is given the row buffer."""
+    from looped_transformer_decode_amd import binding as B
+    K, N, M, L = 3072, 48, 4, 3
+    inp = synth.w4a4_inputs(synth.W4A4Workload("ws", K, N, M, L), seed=37, device="cuda")
+    with_rows = _run(B, K, N, M, L, inp, "cuda")
+    without = _run(B, K, N, M, L, inp, "cuda", act_none=True)
+    for l in range(L):
+        assert np.array_equal(with_rows[5][l][1], without[5][l][1])
+        assert np.array_equal(with_rows[5][l][2], without[5][l][2])
+
+
+def test_w4a4_fewer_tokens_leave_rows_alone():
+    """n_tokens below max_tokens: rows past n_tokens of y stay untouched, and the result
+    for the first rows equals a call with exactly those tokens."""
+    from looped_transformer_decode_amd import binding as B
+    K, N = 2048, 64
+    wl = synth.W4A4Workload("partial", K, N, 16, 2)
+    inp = synth.w4a4_inputs(wl, seed=41, device="cuda")
+    cfg = B.w4a4_config(K, N, 16)
+    wq = torch.zeros(B.rq_w4_weight_bytes(cfg), dtype=torch.uint8, device="cuda")
+    B.rq_w4_quantize_weights(cfg, inp.w, None, wq)
+    anchor = torch.zeros(B.rq_w4a4_act_bytes(cfg), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(B.rq_w4a4_workspace_bytes(cfg), dtype=torch.uint8, device="cuda")
+    y0 = torch.full((16, N), float("nan"), device="cuda")
+    y = torch.full((16, N), -7.0, device="cuda")
+    B.rq_w4a4_linear(cfg, wq, inp.x[0].contiguous(), 0, anchor, None, None, None, y0, y, 5, ws)
+    torch.cuda.synchronize()
+    assert torch.all(y[5:] == -7.0) and torch.all(torch.isnan(y0[5:]))
+    cfg5 = B.w4a4_config(K, N, 5)
+    anchor5 = torch.zeros(B.rq_w4a4_act_bytes(cfg5), dtype=torch.uint8, device="cuda")
+    y5 = torch.zeros(5, N, device="cuda")
+    B.rq_w4a4_linear(cfg5, wq, inp.x[0, :5].contiguous(), 0, anchor5, None, None, None, y5, y5, 5,
+                     torch.zeros(B.rq_w4a4_workspace_bytes(cfg5), dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(y[:5], y5)
+    assert torch.equal(anchor[: anchor5.numel()], anchor5)
+
+
+def test_w4a4_zero_anchor():
+    """A zero anchor activation: offsets 0, c = 0 at the later loop, whose residual is R x."""
+    from looped_transformer_decode_amd import binding as B
+    K, N, M, L = 1024, 32, 2, 2
+    wl = synth.W4A4Workload("zero", K, N, M, L)
+    inp = synth.w4a4_inputs(wl, seed=43, device="cuda")
+    inp.x[0].zero_()
+    res = _run(B, K, N, M, L, inp, "cuda")
+    assert np.all(res[5][1][1] == 0.0)
+    assert np.all(res[4] == 0.0)
+    _verify(K, N, M, L, inp, res, tag="zero anchor")
+
+
+def test_w4a4_full_size():
+    """The benchmark's layer: K = 2048, N = 8192, 16 tokens, a group of 4 loops, every
+    output checked."""
+    from looped_transformer_decode_amd import binding as B
+    wl = synth.W4A4_WORKLOADS["ouro_up_b16"]
+    inp = synth.w4a4_inputs(wl, device="cuda")
+    res = _run(B, wl.in_features, wl.out_features, wl.tokens, wl.loops, inp, "cuda")
+    _verify(wl.in_features, wl.out_features, wl.tokens, wl.loops, inp, res, tag="full size ouro_up_b16")

@@ -183,3 +183,11 @@ def test_layout_round_trip(seed):
     a = W4.anchor_activation(rng.standard_normal((3, 256)))
     back = W4.read_act(W4.write_act(a), 3, 256)
     assert all(np.array_equal(u, v) for u, v in zip(a, back))
+
+
+def test_fast_weight_reader_equals_loops():
+    rng = np.random.default_rng(12)
+    q = W4.quantize_weights(rng.standard_normal((32, 256)) * 0.05)
+    buf = W4.write_weights(q)
+    a, b = W4.read_weights(buf, 32, 256), W4.read_weights_fast(buf, 32, 256)
+    assert all(np.array_equal(u, v) for u, v in zip(a, b))
