@@ -183,6 +183,98 @@ def cpu_baseline(wl, budget_s: float = 15.0, workers: int = 0):
     }
 
 
+
+def w4a4_bytes(wl, residual: bool) -> int:
+    """Algorithmic bytes of one loop-step of the W4A4 layer: the packed weights, the BF16
+    activations, the 4-bit activation rows written (and the anchor rows read at a residual
+    loop), the float32 output and the anchor product (written at the anchor loop, read at
+    the others)."""
+    K, N, M = wl.in_features, wl.out_features, wl.tokens
+    rows = M * (K // 2 + K // 16)
+    weights = N * K // 2 + N * (K // 32) * 2
+    return weights + M * K * 2 + rows * (2 if residual else 1) + 2 * M * N * 4
+
+
+def measure_w4a4(B, dev, sink, eager: bool = False) -> dict:
+    """The W4A4 layer with cross-loop residual activations at the Ouro-sized MLP up
+    projection (K 2048 -> N 8192) for a decode batch of 16: anchor and residual loop-steps
+    replayed from HIP graphs over cold weight copies (beyond the 256 MB Infinity Cache),
+    next to a plain load loop over the same weight bytes and a BF16 linear layer of the
+    same shape (hipBLASLt through torch) over cold BF16 weight copies."""
+    import torch
+    from looped_transformer_decode_amd import synth
+    wl = synth.W4A4_WORKLOADS["ouro_up_b16"]
+    K, N, M, L = wl.in_features, wl.out_features, wl.tokens, wl.loops
+    inp = synth.w4a4_inputs(wl, device=dev)
+    cfg = B.w4a4_config(K, N, M)
+    wb = B.rq_w4_weight_bytes(cfg)
+    wq = torch.empty(wb, dtype=torch.uint8, device=dev)
+    wrq = torch.empty_like(wq)
+    B.rq_w4_quantize_weights(cfg, inp.w, None, wq)
+    B.rq_w4_quantize_weights(cfg, inp.w, inp.rot, wrq)
+    n_rep = max(2, math.ceil(600e6 / (2 * wb)))
+    reps_a = [wq.clone() for _ in range(n_rep)]
+    reps_r = [wrq.clone() for _ in range(n_rep)]
+    anchor = torch.zeros(B.rq_w4a4_act_bytes(cfg), dtype=torch.uint8, device=dev)
+    act = torch.zeros_like(anchor)
+    ws = torch.zeros(B.rq_w4a4_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    y0 = torch.zeros(M, N, device=dev)
+    y = torch.zeros(M, N, device=dev)
+    xs = [inp.x[l].contiguous() for l in range(L)]
+    B.rq_w4a4_linear(cfg, wq, xs[0], 0, anchor, None, None, None, y0, y0, M, ws)
+    if eager:
+        # plain launches (for counter runs, which attribute per dispatch): a group of loops per replica
+        for i in range(n_rep):
+            B.rq_w4a4_linear(cfg, reps_a[i], xs[0], 0, anchor, None, None, None, y0, y0, M, ws)
+            for l in range(1, L):
+                B.rq_w4a4_linear(cfg, reps_r[i], xs[l], l, anchor, act, inp.rot, None, y0, y, M, ws)
+        torch.cuda.synchronize()
+        return {"workload": wl.name, "launch": "eager", "weight_replicas": n_rep}
+
+    def graph_ms(call, reps):
+        for i in range(2):
+            call(i)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(reps):
+                call(i + 2)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    reps = 3 * n_rep
+    ms_anchor = graph_ms(lambda i: B.rq_w4a4_linear(cfg, reps_a[i % n_rep], xs[0], 0, anchor, None, None, None,
+                                                    y0, y, M, ws), reps)
+    ms_resid = graph_ms(lambda i: B.rq_w4a4_linear(cfg, reps_r[i % n_rep], xs[1 + i % (L - 1)], 1 + i % (L - 1),
+                                                   anchor, act, inp.rot, None, y0, y, M, ws), reps)
+    ms_stream = graph_ms(lambda i: B.rq_stream_read(reps_a[i % n_rep], wb, sink), reps)
+    del reps_a, reps_r
+    w16 = inp.w.contiguous()
+    n16 = max(2, math.ceil(600e6 / w16.numel() / 2))
+    reps16 = [w16.clone() for _ in range(n16)]
+    out16 = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    ms_bf16 = graph_ms(lambda i: torch.matmul(xs[0], reps16[i % n16].t(), out=out16), 3 * n16)
+    del reps16
+    ba, br = w4a4_bytes(wl, False), w4a4_bytes(wl, True)
+    group_ms = ms_anchor + (L - 1) * ms_resid
+    return {"workload": wl.name, "in_features": K, "out_features": N, "tokens": M, "loops": L,
+            "weight_bytes": wb, "weight_replicas": n_rep,
+            "anchor_loop": {"bytes": ba, "ms": round(ms_anchor, 5), "gbps": round(ba / (ms_anchor * 1e-3) / 1e9, 1),
+                            "frac_of_hbm_peak": round(ba / (ms_anchor * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+            "residual_loop": {"bytes": br, "ms": round(ms_resid, 5), "gbps": round(br / (ms_resid * 1e-3) / 1e9, 1),
+                              "frac_of_hbm_peak": round(br / (ms_resid * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+            "group_of_loops_ms": round(group_ms, 5),
+            "stream_read_same_weight_bytes_ms": round(ms_stream, 5),
+            "bf16_linear_ms": round(ms_bf16, 5),
+            "speedup_vs_bf16_linear": round(ms_bf16 * L / group_ms, 3),
+            "timing": "HIP graph replay of back-to-back calls over cold weight copies, one event pair; "
+                      "each call = activation quantizer + GEMM kernels"}
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +289,7 @@ def main():
                     "(more bits far from the anchor)")
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-w4a4", action="store_true", help="skip the W4A4 layer measurement")
     ap.add_argument("--cpu-baseline-only", action="store_true",
                     help="time the CPU oracle on the workload and print its JSON (no GPU use)")
     ap.add_argument("--replicas", type=int, default=0)
@@ -649,6 +742,8 @@ def main():
                      + ", residual loop-step (split-K with the merge in its last workgroup)",
                      "algorithmic_bytes": round(roof_bytes), "source_digest": decode_source_digest(wl)},
     }
+    if not args.no_w4a4:
+        result["w4a4"] = measure_w4a4(B, dev, sink, eager=args.eager_only)
     if cpu_base is not None:
         result["cpu_baseline"] = cpu_base
     print(json.dumps(result))

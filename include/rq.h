@@ -337,7 +337,8 @@ rq_status rq_w4_quantize_weights(const rq_w4a4_config* cfg, const uint16_t* w, i
 
 /* rq_w4a4_linear - one loop of the layer for n_tokens tokens.
  *   weights    : packed W_hat at loop_local 0, packed W_R_hat at loop_local > 0.
- *   x          : device BF16 [n_tokens][x_stride] activations of this loop.
+ *   x          : device BF16 [n_tokens][x_stride] activations of this loop; 16-byte aligned,
+ *                x_stride a multiple of 8.
  *   loop_local : position of the loop in its group; 0 is the anchor loop.
  *   anchor     : device activation rows [max_tokens]: written at loop_local 0 (the 4-bit
  *                anchor), read at loop_local > 0.  Keep it across the group's loops.
@@ -350,8 +351,8 @@ rq_status rq_w4_quantize_weights(const rq_w4a4_config* cfg, const uint16_t* w, i
  *   y          : device float32 [n_tokens][out_features] output.
  * Arithmetic: the quantizers in float64 (codes as a float64 reference except inexact
  * near-ties; c within one BF16 step), the product on the matrix cores from exact FP16
- * operands with float32 accumulation.  Alignment: weights, anchor, act, rot, workspace
- * 16-byte aligned.  Two kernels are enqueued. */
+ * operands with float32 accumulation.  Alignment: weights, x, anchor, act, rot, workspace
+ * 16-byte aligned; y, y0 4-byte aligned.  Two kernels are enqueued. */
 rq_status rq_w4a4_linear(const rq_w4a4_config* cfg, const void* weights, const uint16_t* x, int64_t x_stride,
                          int32_t loop_local, void* anchor, void* act, const float* rot, float* c_out,
                          float* y0, float* y, int32_t n_tokens, void* workspace, size_t workspace_bytes,

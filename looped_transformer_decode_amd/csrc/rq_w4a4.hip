@@ -102,59 +102,111 @@ struct AArgs {
     int k, m;
 };
 
-constexpr int TQ = 4;           // tokens per activation-quantizer workgroup
+constexpr int TQ = 1;           // tokens per activation-quantizer workgroup
 
 // Sums over the 256 threads in a fixed order, TQ values per thread at once (every thread
-// gets the results).
-__device__ __forceinline__ void block_sum256(double (&v)[TQ], double (*red)[256]) {
+// gets the results): a butterfly inside each wave, then the 4 wave sums in order.
+__device__ __forceinline__ void block_sum256(double (&v)[TQ], double (*red)[4]) {
 #pragma unroll
-    for (int q = 0; q < TQ; ++q) red[q][threadIdx.x] = v[q];
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (threadIdx.x < s) {
+    for (int q = 0; q < TQ; ++q) {
 #pragma unroll
-            for (int q = 0; q < TQ; ++q) red[q][threadIdx.x] += red[q][threadIdx.x + s];
-        }
-        __syncthreads();
+        for (int o = 32; o > 0; o >>= 1) v[q] += shfl_xor_d(v[q], o);
     }
+    if ((threadIdx.x & 63) == 0) {
 #pragma unroll
-    for (int q = 0; q < TQ; ++q) v[q] = red[q][0];
+        for (int q = 0; q < TQ; ++q) red[q][threadIdx.x >> 6] = v[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < TQ; ++q) v[q] = ((red[q][0] + red[q][1]) + red[q][2]) + red[q][3];
     __syncthreads();
 }
 
-// grid (K / 128 channel blocks, ceil(M / 4) token quads), 256 threads.  Each workgroup
-// quantizes the 4 groups of its channel block for its 4 tokens; at a residual loop it
-// first forms each token's coefficient c from the whole row (every block computes the
-// same sums in the same order, so every block gets the same c) and rotates its block of
-// the residual (two outputs per thread, 128 float64 products each).
+// grid (K / 128 channel blocks, M tokens), 256 threads.  Each workgroup quantizes the 4
+// groups of its channel block for its token; at a residual loop it first forms the token's
+// coefficient c from the whole row (every block computes the same sums in the same order,
+// so every block gets the same c) and rotates its block of the residual (two threads per
+// output, 64 float64 products each).  The quantizer runs 16 threads per group, two values
+// each.
 template <bool RES>
 __global__ __launch_bounds__(256) void quantize_act_kernel(AArgs a) {
+    constexpr int GMAX = 4096 / GS;
     __shared__ double ys[TQ][RB];               // the block's values (x, or x - c a_hat)
-    __shared__ double rs[RES ? TQ : 1][RES ? RB : 1];   // the rotated residual
-    __shared__ float rt[RES ? RB : 1][RES ? RB : 1];    // rt[i][j] = R[j][i]
-    __shared__ double red[RES ? TQ : 1][RES ? 256 : 1];
+    __shared__ double rs[RES ? TQ : 1][RES ? RB : 1];          // the rotated residual
+    __shared__ double za[RES ? TQ : 1][RES ? GMAX : 1];        // anchor offsets and scales
+    __shared__ double sa[RES ? TQ : 1][RES ? GMAX : 1];
+    __shared__ double red[TQ][4];
+    __shared__ uint32_t cw[TQ][RB / 8];         // the block's code words
     const int t = threadIdx.x, b = blockIdx.x, m0 = blockIdx.y * TQ, K = a.k, G = K / GS;
     const int rowb = act_row_bytes(K);
     const int nq = min(TQ, a.m - m0);           // tokens of this workgroup
+    // every global load first, all in flight together: R, the anchor metadata, the row
+    // chunks for c (8 channels per step), and the block's own values
+    constexpr int RV = RES ? RB / 2 / 4 : 1;                     // float4 of R per thread: half a row
+    constexpr int CSTEP = RES ? 2 : 1;                           // row steps per token (K <= 4096)
+    float4 rv[RV];
+    uint32_t mbv[RES ? 2 : 1];
+    uint4 xc[TQ][CSTEP];
+    uint32_t cc[TQ][CSTEP];
+    uint32_t xb[1], cb[1];
+    if constexpr (RES) {
+        // thread t takes row t / 2 of R, columns 64 (t % 2) .. 64 (t % 2) + 63
+#pragma unroll
+        for (int k = 0; k < RV; ++k) rv[k] = reinterpret_cast<const float4*>(a.rot + RB * (t / 2) + 64 * (t & 1))[k];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int e = t + 256 * k, q = e / G, g = e % G;
+            mbv[k] = (e < TQ * G && q < nq)
+                         ? reinterpret_cast<const uint16_t*>(a.anchor + (size_t)(m0 + q) * rowb + K / 2)[g] : 0u;
+        }
+#pragma unroll
+        for (int q = 0; q < TQ; ++q) {
+            const int mq = m0 + min(q, nq - 1);
+#pragma unroll
+            for (int st = 0; st < CSTEP; ++st) {
+                const int e0 = min(8 * t + 2048 * st, K - 8);
+                xc[q][st] = *reinterpret_cast<const uint4*>(a.x + (int64_t)mq * a.ldx + e0);
+                cc[q][st] = *reinterpret_cast<const uint32_t*>(a.anchor + (size_t)mq * rowb + e0 / 2);
+            }
+        }
+    }
+    {
+        const int ch = RB * b + (t % RB);                  // threads t < 128 use their value
+        xb[0] = a.x[(int64_t)m0 * a.ldx + ch];
+        cb[0] = RES ? a.anchor[(size_t)m0 * rowb + ch / 2] : 0u;
+    }
+
     double c[TQ];
 #pragma unroll
     for (int q = 0; q < TQ; ++q) c[q] = 1.0;
     if constexpr (RES) {
-        for (int e = t; e < RB * RB; e += 256) rt[e % RB][e / RB] = a.rot[e];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int e = t + 256 * k;
+            if (e < TQ * G) {
+                za[e / G][e % G] = e4m3_value(mbv[k] & 0xFFu);
+                sa[e / G][e % G] = e4m3_value(mbv[k] >> 8);
+            }
+        }
+        __syncthreads();
         // c = <x, a_hat> / <a_hat, a_hat> over the whole row
         double num[TQ], den[TQ];
 #pragma unroll
         for (int q = 0; q < TQ; ++q) {
             num[q] = den[q] = 0.0;
-            if (q < nq) {
-                const uint16_t* xr = a.x + (int64_t)(m0 + q) * a.ldx;
-                const uint8_t* arow = a.anchor + (size_t)(m0 + q) * rowb;
-                for (int e = t; e < K; e += 256) {
-                    const uint32_t code = (arow[e / 2] >> (4 * (e & 1))) & 15u;
-                    const uint32_t mb = reinterpret_cast<const uint16_t*>(arow + K / 2)[e / GS];
-                    const double ah = e4m3_value(mb & 0xFFu) + (double)code * e4m3_value(mb >> 8);
-                    num[q] = fma((double)bf16_to_f32(xr[e]), ah, num[q]);
-                    den[q] = fma(ah, ah, den[q]);
+#pragma unroll
+            for (int st = 0; st < CSTEP; ++st) {
+                const int e0 = 8 * t + 2048 * st;
+                if (q < nq && e0 < K) {
+                    const double z = za[q][e0 / GS], sc = sa[q][e0 / GS];
+                    const uint32_t xw[4] = {xc[q][st].x, xc[q][st].y, xc[q][st].z, xc[q][st].w};
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const double ah = z + (double)((cc[q][st] >> (4 * k)) & 15u) * sc;
+                        const double xk = (double)(k & 1 ? bf16hi(xw[k / 2]) : bf16lo(xw[k / 2]));
+                        num[q] = fma(xk, ah, num[q]);
+                        den[q] = fma(ah, ah, den[q]);
+                    }
                 }
             }
         }
@@ -164,61 +216,71 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(AArgs a) {
         for (int q = 0; q < TQ; ++q) c[q] = bf16_round(den[q] > 0.0 ? num[q] / den[q] : 0.0);
     }
     // the block's values: x, or x - c a_hat
-    for (int e = t; e < TQ * RB; e += 256) {
-        const int q = e / RB, i = e % RB, ch = RB * b + i;
-        double v = 0.0;
-        if (q < nq) {
-            v = (double)bf16_to_f32(a.x[(int64_t)(m0 + q) * a.ldx + ch]);
-            if constexpr (RES) {
-                const uint8_t* arow = a.anchor + (size_t)(m0 + q) * rowb;
-                const uint32_t code = (arow[ch / 2] >> (4 * (ch & 1))) & 15u;
-                const uint32_t mb = reinterpret_cast<const uint16_t*>(arow + K / 2)[ch / GS];
-                v -= c[q] * (e4m3_value(mb & 0xFFu) + (double)code * e4m3_value(mb >> 8));
-            }
+    if (t < RB) {
+        const int ch = RB * b + t;
+        double v = (double)bf16_to_f32(xb[0]);
+        if constexpr (RES) {
+            const uint32_t code = (cb[0] >> (4 * (ch & 1))) & 15u;
+            v -= c[0] * (za[0][ch / GS] + (double)code * sa[0][ch / GS]);
         }
-        ys[q][i] = v;
+        ys[0][t] = v;
     }
     __syncthreads();
     const double (*src)[RB] = ys;
     if constexpr (RES) {
-        // r_j = sum_i R[j][i] y_i: thread t -> token t / 64, outputs 2 (t % 64), 2 (t % 64) + 1
-        const int q = t / 64, j = 2 * (t % 64);
-        double r0 = 0.0, r1 = 0.0;
-        for (int i = 0; i < RB; ++i) {
-            r0 = fma((double)rt[i][j], ys[q][i], r0);
-            r1 = fma((double)rt[i][j + 1], ys[q][i], r1);
+        // r_j = sum_i R[j][i] y_i: threads 2 j and 2 j + 1 take i < 64 and i >= 64 (the R values
+        // already in their registers), each as 4 partial sums over i mod 4 (independent
+        // chains); the halves are added by both threads (a + b == b + a), the partial sums in
+        // a fixed order
+        const int j = t / 2, h = t & 1;
+        double p[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int k = 0; k < RV; ++k) {
+            const int i = 64 * h + 4 * k;
+            p[0] = fma((double)rv[k].x, ys[0][i], p[0]);
+            p[1] = fma((double)rv[k].y, ys[0][i + 1], p[1]);
+            p[2] = fma((double)rv[k].z, ys[0][i + 2], p[2]);
+            p[3] = fma((double)rv[k].w, ys[0][i + 3], p[3]);
         }
-        rs[q][j] = r0;
-        rs[q][j + 1] = r1;
+        double r = (p[0] + p[1]) + (p[2] + p[3]);
+        r += shfl_xor_d(r, 1);
+        if (h == 0) rs[0][j] = r;
         __syncthreads();
         src = rs;
     }
-    // quantize: thread t < 16 -> token t / 4, group t % 4 of the block
-    if (t < TQ * 4 && t / 4 < nq) {
-        const int q = t / 4, jg = t % 4, g = 4 * b + jg, m = m0 + q;
-        const double* v = &src[q][GS * jg];
-        double lo = v[0], hi = v[0];
-        for (int e = 1; e < GS; ++e) {
-            lo = fmin(lo, v[e]);
-            hi = fmax(hi, v[e]);
+    // quantize: group (t / 16) = (token q, group jg of the block), values 2u, 2u + 1 (u = t % 16)
+    if (t < TQ * 64) {
+        const int grp = t / 16, u = t % 16, q = grp / 4, jg = grp % 4;
+        const double v0 = src[q][GS * jg + 2 * u], v1 = src[q][GS * jg + 2 * u + 1];
+        double lo = fmin(v0, v1), hi = fmax(v0, v1);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            lo = fmin(lo, shfl_xor_d(lo, o));
+            hi = fmax(hi, shfl_xor_d(hi, o));
         }
         const QOut qo = group_params(lo, hi, 4);
-        uint8_t* row = a.act + (size_t)m * rowb;
-        double sum = 0.0;
-        for (int w = 0; w < 4; ++w) {
-            uint32_t word = 0;
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t code = group_code(v[8 * w + e], qo, 4);
-                word |= code << (4 * e);
-                sum += qo.z + (double)code * qo.s;
-            }
-            reinterpret_cast<uint32_t*>(row + 16 * g)[w] = word;
-            if (a.act2) reinterpret_cast<uint32_t*>(a.act2 + (size_t)m * rowb + 16 * g)[w] = word;
+        const uint32_t c0 = group_code(v0, qo, 4), c1 = group_code(v1, qo, 4);
+        double sum = (qo.z + (double)c0 * qo.s) + (qo.z + (double)c1 * qo.s);
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) sum += shfl_xor_d(sum, o);
+        // byte u of the group's 16 code bytes; four neighbouring lanes form one word
+        uint32_t byte = (c0 | (c1 << 4)) << (8 * (u & 3));
+        byte |= (uint32_t)__shfl_xor((int)byte, 1, kWave);
+        byte |= (uint32_t)__shfl_xor((int)byte, 2, kWave);
+        if ((u & 3) == 0) cw[q][4 * jg + u / 4] = byte;
+        if (u == 0 && q < nq) {
+            const int g = 4 * b + jg, m = m0 + q;
+            const uint16_t mb = (uint16_t)(qo.zb | (qo.sb << 8));
+            reinterpret_cast<uint16_t*>(a.act + (size_t)m * rowb + K / 2)[g] = mb;
+            if (a.act2) reinterpret_cast<uint16_t*>(a.act2 + (size_t)m * rowb + K / 2)[g] = mb;
+            a.xsum[(size_t)m * G + g] = (float)sum;
         }
-        const uint16_t mb = (uint16_t)(qo.zb | (qo.sb << 8));
-        reinterpret_cast<uint16_t*>(row + K / 2)[g] = mb;
-        if (a.act2) reinterpret_cast<uint16_t*>(a.act2 + (size_t)m * rowb + K / 2)[g] = mb;
-        a.xsum[(size_t)m * G + g] = (float)sum;
+    }
+    __syncthreads();
+    if (t < TQ * 16 && t / 16 < nq) {
+        const int q = t / 16, wd = t % 16, m = m0 + q;
+        reinterpret_cast<uint32_t*>(a.act + (size_t)m * rowb + 64 * b)[wd] = cw[q][wd];
+        if (a.act2) reinterpret_cast<uint32_t*>(a.act2 + (size_t)m * rowb + 64 * b)[wd] = cw[q][wd];
     }
     if (b == 0 && t < nq) {
         a.c[m0 + t] = (float)c[t];
@@ -244,28 +306,30 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask) {
     asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(kMagic2));
     return r;
 }
-// (1024 + v, 1024 + v') -> (v, v') exactly
-__device__ __forceinline__ h2 unmagic(uint32_t r) {
-    return __builtin_bit_cast(h2, r) - (h2){(_Float16)1024.0f, (_Float16)1024.0f};
-}
 
-// 8 channels (nibble e = channel e) of a code word times scale s, in the MFMA K order
-// [0,4,1,5,2,6,3,7]; every value is exact in FP16 (4-bit code x 4-significant-bit E4M3
-// scale, magnitude in [2^-9, 6720]).  Odd channel pairs come out of the mask as 16 q and
-// are scaled by s / 16 (an exact power-of-two step, still a normal FP16 value).
-__device__ __forceinline__ h8 scaled_codes(uint32_t w, _Float16 s) {
-    const uint32_t w8 = w >> 8;
-    const _Float16 s16 = s * (_Float16)0.0625f;
-    const h2 p0 = unmagic(and_or(w, 0x000F000Fu)) * (h2){s, s};
-    const h2 p1 = unmagic(and_or(w, 0x00F000F0u)) * (h2){s16, s16};
-    const h2 p2 = unmagic(and_or(w8, 0x000F000Fu)) * (h2){s, s};
-    const h2 p3 = unmagic(and_or(w8, 0x00F000F0u)) * (h2){s16, s16};
+// (offset, scale) of a group from its two E4M3 bytes, as exact FP16 values
+__device__ __forceinline__ h2 meta_h2(uint32_t mb) { return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(mb, 1.0f, false); }
+
+// 8 channels (nibble e = channel e) of a code word times the group scale s, in the MFMA K
+// order [0,4,1,5,2,6,3,7].  Each channel pair is moved to bits 4..7 and 20..23 and OR-ed
+// into FP16 1024, giving 1024 + 16 q; one fused multiply-add (1024 + 16 q)(s / 16) - 64 s
+// then yields q s exactly (q s has at most 8 significant bits and lies in [2^-9, 6720];
+// s / 16 and 64 s <= 28672 are exact FP16 values).  sv = (s/16, s/16), cv = (-64 s, -64 s).
+__device__ __forceinline__ h8 scaled_codes(uint32_t w, h2 sv, h2 cv) {
+    const h2 p0 = __builtin_elementwise_fma(__builtin_bit_cast(h2, and_or(w << 4, 0x00F000F0u)), sv, cv);
+    const h2 p1 = __builtin_elementwise_fma(__builtin_bit_cast(h2, and_or(w, 0x00F000F0u)), sv, cv);
+    const h2 p2 = __builtin_elementwise_fma(__builtin_bit_cast(h2, and_or(w >> 4, 0x00F000F0u)), sv, cv);
+    const h2 p3 = __builtin_elementwise_fma(__builtin_bit_cast(h2, and_or(w >> 8, 0x00F000F0u)), sv, cv);
     return (h8){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
+__device__ __forceinline__ h2 sv_of(_Float16 s) { return (h2){s, s} * (h2){(_Float16)0.0625f, (_Float16)0.0625f}; }
+__device__ __forceinline__ h2 cv_of(_Float16 s) { return (h2){s, s} * (h2){(_Float16)-64.0f, (_Float16)-64.0f}; }
 
 __device__ __forceinline__ f32x4 mfma(h8 a, h8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
-// one workgroup (8 waves) per tile of 16 output rows; wave w covers the GW groups
+constexpr int NTW = 2;          // row tiles per GEMM workgroup (they share the activation operands)
+
+// one workgroup (8 waves) per pair of 16-row tiles; wave w covers the GW groups
 // [w GW, (w + 1) GW) of the input channels, the waves' products are summed in LDS.
 // MFMA operands: A row = token (lane l16), B column = output row of the tile (lane l16),
 // K = the 32 channels of one group (8 per lane quarter kg).
@@ -273,88 +337,121 @@ template <int GW, bool RES>
 __global__ __launch_bounds__(512) void gemm_kernel(GArgs a) {
     constexpr int NQ = GW / 4;                  // weight quads per wave
     static_assert(GW % 4 == 0 && GW <= 16, "groups per wave");
-    __shared__ f32x4 red[8][64];
+    __shared__ f32x4 red[NTW][8][64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l16 = lane & 15, kg = lane >> 4;
-    const int nt = blockIdx.x, K = a.k, G = K / GS;
+    const int tiles = a.n / TN, K = a.k, G = K / GS;
+    const int nt0 = NTW * blockIdx.x;
+    const bool two = nt0 + 1 < tiles;           // uniform over the workgroup
 
-    // weights of the wave's quads: row l16 of the tile, quarter kg, 4 groups per quad
-    const uint8_t* wt = a.w + ((size_t)nt * (K / RB) + (size_t)w * NQ) * QB;
-    u4 wc[NQ];
-    uint2 wm[NQ];
+    // every load first: the weights of the wave's quads for both tiles (row l16, quarter
+    // kg, 4 groups per quad; a missing second tile reads the first again), the token's
+    // code words and metadata, and X / 32 of the lane's local groups 4 kg .. 4 kg + 3
+    u4 wc[NTW][NQ];
+    uint2 wm[NTW][NQ];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        wc[q] = *reinterpret_cast<const u4*>(wt + q * QB + 16 * (16 * kg + l16));
-        wm[q] = *reinterpret_cast<const uint2*>(wt + q * QB + 1024 + 8 * l16);
+    for (int u = 0; u < NTW; ++u) {
+        const uint8_t* wt = a.w + ((size_t)(two ? nt0 + u : nt0) * (K / RB) + (size_t)w * NQ) * QB;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            wc[u][q] = *reinterpret_cast<const u4*>(wt + q * QB + 16 * (16 * kg + l16));
+            wm[u][q] = *reinterpret_cast<const uint2*>(wt + q * QB + 1024 + 8 * l16);
+        }
     }
-
-    // activation operands of token l16 (zero rows past the last token)
+    // lanes past the last token read the last token's row and zero it
     const bool mok = l16 < a.m;
     const int rowb = act_row_bytes(K);
-    const uint8_t* arow = a.act + (size_t)(mok ? l16 : 0) * rowb;
+    const int mrow = mok ? l16 : a.m - 1;
+    const uint8_t* arow = a.act + (size_t)mrow * rowb;
+    uint32_t aw[GW], am[GW];
+#pragma unroll
+    for (int gl = 0; gl < GW; ++gl) {
+        aw[gl] = *reinterpret_cast<const uint32_t*>(arow + 16 * (w * GW + gl) + 4 * kg);
+        am[gl] = reinterpret_cast<const uint16_t*>(arow + K / 2)[w * GW + gl];
+    }
+    float xq[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xq[j] = a.xsum[(size_t)mrow * G + w * GW + min(4 * kg + j, GW - 1)];
+    // the epilogue's operands (waves 0 and 1 store the two tiles): c and the anchor product
+    float ce[4] = {0.f, 0.f, 0.f, 0.f}, y0e[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (RES) {
+        if (w < NTW && (w == 0 || two)) {
+            const int n = (nt0 + w) * TN + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = min(4 * kg + r, a.m - 1);
+                ce[r] = a.c[m];
+                y0e[r] = a.y0_in[(size_t)m * a.n + n];
+            }
+        }
+    }
+
+    // activation operands: s_x q_x (exact FP16) and the broadcast offset z_x
     h8 a1[GW], a2[GW];
 #pragma unroll
     for (int gl = 0; gl < GW; ++gl) {
-        const int g = w * GW + gl;
-        const uint32_t word = mok ? *reinterpret_cast<const uint32_t*>(arow + 16 * g + 4 * kg) : 0u;
-        const uint32_t mb = mok ? reinterpret_cast<const uint16_t*>(arow + K / 2)[g] : 0u;
-        const _Float16 zx = (_Float16)e4m3_to_f32(mb & 0xFFu), sx = (_Float16)e4m3_to_f32(mb >> 8);
-        a1[gl] = scaled_codes(word, sx);
-        a2[gl] = (h8){zx, zx, zx, zx, zx, zx, zx, zx};
+        const h2 zs = meta_h2(mok ? am[gl] : 0u);
+        a1[gl] = scaled_codes(mok ? aw[gl] : 0u, sv_of(zs.y), cv_of(zs.y));
+        a2[gl] = (h8){zs.x, zs.x, zs.x, zs.x, zs.x, zs.x, zs.x, zs.x};
     }
     // z_w X terms: K' position 8 kg + e <-> local group 4 kg + e / 2, FP16 hi (e even) / lo
     // (e odd) of X / 32 on the token side, 32 z_w on the weight side (powers of two: exact)
-    h8 ax = {}, bx = {};
+    h8 ax;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int gl = 4 * kg + e / 2;
-        if (gl < GW && mok) {
-            const float xv = a.xsum[(size_t)l16 * G + w * GW + gl] * (1.f / 32.f);
-            const _Float16 hi = (_Float16)xv;
-            ax[e] = (e & 1) ? (_Float16)(xv - (float)hi) : hi;
-        }
-    }
-    {
-        // the lane's quarter kg holds the zero points of the wave's quad kg
-        uint2 mq = {0u, 0u};
-#pragma unroll
-        for (int q = 0; q < NQ; ++q)
-            if (q == kg) mq = wm[q];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int j = e / 2;
-            const uint32_t mb = (j < 2 ? mq.x : mq.y) >> (16 * (j & 1));
-            if (kg < NQ) bx[e] = (_Float16)(32.f * e4m3_to_f32(mb & 0xFFu));
-        }
+        const float xv = (gl < GW && mok) ? xq[e / 2] * (1.f / 32.f) : 0.f;
+        const _Float16 hi = (_Float16)xv;
+        ax[e] = (e & 1) ? (_Float16)(xv - (float)hi) : hi;
     }
 
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
+    for (int u = 0; u < NTW; ++u) {
+        h8 bx;
+        {
+            // the lane's quarter kg holds the offsets of the wave's quad kg
+            uint2 mq = wm[u][0];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t mb = ((j < 2) ? wm[q].x : wm[q].y) >> (16 * (j & 1));
-            const _Float16 sw = (_Float16)e4m3_to_f32((mb >> 8) & 0xFFu);
-            const h8 b = scaled_codes(wc[q][j], sw);
-            acc = mfma(a1[4 * q + j], b, acc);
-            acc = mfma(a2[4 * q + j], b, acc);
+            for (int q = 1; q < NQ; ++q)
+                if (q == kg) mq = wm[u][q];
+#pragma unroll
+            for (int jp = 0; jp < 2; ++jp) {
+                const uint32_t word = jp ? mq.y : mq.x;
+                const h2 m0 = meta_h2(word & 0xFFFFu), m1 = meta_h2(word >> 16);
+                const _Float16 z0 = kg < NQ ? m0.x * (_Float16)32.0f : (_Float16)0.0f;
+                const _Float16 z1 = kg < NQ ? m1.x * (_Float16)32.0f : (_Float16)0.0f;
+                bx[4 * jp + 0] = z0;
+                bx[4 * jp + 1] = z0;
+                bx[4 * jp + 2] = z1;
+                bx[4 * jp + 3] = z1;
+            }
         }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t mb = ((j < 2) ? wm[u][q].x : wm[u][q].y) >> (16 * (j & 1));
+                const _Float16 sw = meta_h2(mb & 0xFFFFu).y;
+                const h8 b = scaled_codes(wc[u][q][j], sv_of(sw), cv_of(sw));
+                acc = mfma(a1[4 * q + j], b, acc);
+                acc = mfma(a2[4 * q + j], b, acc);
+            }
+        }
+        red[u][w][lane] = mfma(ax, bx, acc);
     }
-    acc = mfma(ax, bx, acc);
-
-    red[w][lane] = acc;
     __syncthreads();
-    if (w == 0) {
-        f32x4 v = red[0][lane];
+    if (w < NTW && (w == 0 || two)) {
+        f32x4 v = red[w][0][lane];
 #pragma unroll
-        for (int i = 1; i < 8; ++i) v += red[i][lane];
-        const int n = nt * TN + l16;
+        for (int i = 1; i < 8; ++i) v += red[w][i][lane];
+        const int n = (nt0 + w) * TN + l16;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int m = 4 * kg + r;
             if (m < a.m) {
                 const size_t o = (size_t)m * a.n + n;
                 if constexpr (RES) {
-                    a.y[o] = a.c[m] * a.y0_in[o] + v[r];
+                    a.y[o] = ce[r] * y0e[r] + v[r];
                 } else {
                     a.y[o] = v[r];
                     if (a.y0_out) a.y0_out[o] = v[r];
@@ -366,7 +463,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(GArgs a) {
 
 template <int GW>
 static void launch_gemm(const GArgs& g, bool res, hipStream_t st) {
-    const dim3 grid(g.n / TN);
+    const dim3 grid((g.n / TN + NTW - 1) / NTW);
     if (res) hipLaunchKernelGGL((gemm_kernel<GW, true>), grid, dim3(512), 0, st, g);
     else hipLaunchKernelGGL((gemm_kernel<GW, false>), grid, dim3(512), 0, st, g);
 }
@@ -424,7 +521,7 @@ rq_status rq_w4a4_linear(const rq_w4a4_config* cfg, const void* weights, const u
         n_tokens > cfg->max_tokens || x_stride < cfg->in_features || (loop_local > 0 && !rot))
         return RQ_ERR_INVALID_ARG;
     if (!w4_aligned16(weights) || !w4_aligned16(anchor) || (act && !w4_aligned16(act)) ||
-        (rot && !w4_aligned16(rot)) || (reinterpret_cast<uintptr_t>(x) & 1u) ||
+        (rot && !w4_aligned16(rot)) || !w4_aligned16(x) || (x_stride % 8) != 0 ||
         (reinterpret_cast<uintptr_t>(y) & 3u) || (reinterpret_cast<uintptr_t>(y0) & 3u))
         return RQ_ERR_MISALIGNED;
     if (!workspace || workspace_bytes < rq_w4a4_workspace_bytes(cfg) || !w4_aligned16(workspace))

@@ -80,3 +80,17 @@ def test_loop_step_bytes_with_per_loop_widths():
     assert per == [74, 42, 42, 72]
     assert [bench.algorithmic_bytes(wl, l, False) for l in range(4)] == \
         [2 * (72 + 74) * ht, 2 * (72 + 42) * ht, 2 * (72 + 42) * ht, 2 * 72 * ht]
+
+
+def test_w4a4_bytes_match_the_layouts():
+    """The W4A4 loop-step byte counts against the oracle's layouts: packed weights, the BF16
+    activations, activation rows (written; and the anchor rows read at a residual loop),
+    and the float32 output and anchor product."""
+    import bench
+    from looped_transformer_decode_amd import synth
+    from oracle import w4a4 as W4
+    wl = synth.W4A4_WORKLOADS["ouro_up_b16"]
+    K, N, M = wl.in_features, wl.out_features, wl.tokens
+    base = W4.weight_bytes(N, K) + M * K * 2 + W4.act_bytes(M, K) + 2 * M * N * 4
+    assert bench.w4a4_bytes(wl, False) == base
+    assert bench.w4a4_bytes(wl, True) == base + W4.act_bytes(M, K)
