@@ -90,7 +90,11 @@ size_t rq_cache_bytes(const rq_config* cfg);
  * one arrival counter per (batch row, query head).  The caller allocates it and fills it
  * with zeros once before its first use; every call leaves the counters at zero again, so
  * the same workspace serves any number of later calls (and HIP graph replays) as long as
- * they do not overlap in time and nothing else writes to it. */
+ * they do not overlap in time and nothing else writes to it.  A call whose kernel does not
+ * run to its end (a device fault, which also leaves the HIP context unusable) may leave
+ * counters above zero, and later calls on that workspace would then merge wrong records:
+ * after any RQ_ERR_HIP or device error, fill the workspace with zeros again (or allocate a
+ * new one in the new context) before the next call. */
 size_t rq_workspace_bytes(const rq_config* cfg);
 
 /* Shape of one loop's uncompressed BF16 cache for the baseline decode kernel. */
