@@ -195,15 +195,16 @@ def w4a4_bytes(wl, residual: bool) -> int:
     return weights + M * K * 2 + rows * (2 if residual else 1) + 2 * M * N * 4
 
 
-def measure_w4a4(B, dev, sink, eager: bool = False) -> dict:
-    """The W4A4 layer with cross-loop residual activations at the Ouro-sized MLP up
-    projection (K 2048 -> N 8192) for a decode batch of 16: anchor and residual loop-steps
-    replayed from HIP graphs over cold weight copies (beyond the 256 MB Infinity Cache),
-    next to a plain load loop over the same weight bytes and a BF16 linear layer of the
-    same shape (hipBLASLt through torch) over cold BF16 weight copies."""
+def measure_w4a4(B, dev, sink, eager: bool = False, name: str = "ouro_up_b16") -> dict:
+    """The W4A4 layer with cross-loop residual activations at one MLP up projection
+    (ouro_up_b16: K 2048 -> N 8192 for a decode batch of 16; huginn_up_b8: K 4096 -> N 16384
+    for a batch of 8): anchor and residual loop-steps replayed from HIP graphs over cold
+    weight copies (beyond the 256 MB Infinity Cache), next to a plain load loop over the
+    same weight bytes and a BF16 linear layer of the same shape (hipBLASLt through torch)
+    over cold BF16 weight copies."""
     import torch
     from looped_transformer_decode_amd import synth
-    wl = synth.W4A4_WORKLOADS["ouro_up_b16"]
+    wl = synth.W4A4_WORKLOADS[name]
     K, N, M, L = wl.in_features, wl.out_features, wl.tokens, wl.loops
     inp = synth.w4a4_inputs(wl, device=dev)
     cfg = B.w4a4_config(K, N, M)
@@ -744,6 +745,7 @@ def main():
     }
     if not args.no_w4a4:
         result["w4a4"] = measure_w4a4(B, dev, sink, eager=args.eager_only)
+        result["w4a4_huginn"] = measure_w4a4(B, dev, sink, eager=args.eager_only, name="huginn_up_b8")
     if cpu_base is not None:
         result["cpu_baseline"] = cpu_base
     print(json.dumps(result))

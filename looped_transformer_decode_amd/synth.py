@@ -196,6 +196,8 @@ class W4A4Workload:
 W4A4_WORKLOADS = {
     # the MLP's up projection (4x width) for a decode batch of 16, one group of 4 loops
     "ouro_up_b16": W4A4Workload("ouro_up_b16", 2048, 8192, 16, 4),
+    # the same for a Huginn-sized block (model width 4096) at its decode batch of 8
+    "huginn_up_b8": W4A4Workload("huginn_up_b8", 4096, 16384, 8, 4),
     # a small case the float64 oracle checks in full
     "tiny_w4a4": W4A4Workload("tiny_w4a4", 1024, 64, 3, 3),
 }

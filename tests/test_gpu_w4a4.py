@@ -195,11 +195,12 @@ def test_w4a4_zero_anchor():
     _verify(K, N, M, L, inp, res, tag="zero anchor")
 
 
-def test_w4a4_full_size():
-    """The benchmark's layer: K = 2048, N = 8192, 16 tokens, a group of 4 loops, every
-    output checked."""
+@pytest.mark.parametrize("name", ["ouro_up_b16", "huginn_up_b8"])
+def test_w4a4_full_size(name):
+    """The benchmark's layers (K = 2048, N = 8192, 16 tokens; K = 4096, N = 16384, 8 tokens),
+    a group of 4 loops, every output checked."""
     from looped_transformer_decode_amd import binding as B
-    wl = synth.W4A4_WORKLOADS["ouro_up_b16"]
+    wl = synth.W4A4_WORKLOADS[name]
     inp = synth.w4a4_inputs(wl, device="cuda")
     res = _run(B, wl.in_features, wl.out_features, wl.tokens, wl.loops, inp, "cuda")
-    _verify(wl.in_features, wl.out_features, wl.tokens, wl.loops, inp, res, tag="full size ouro_up_b16")
+    _verify(wl.in_features, wl.out_features, wl.tokens, wl.loops, inp, res, tag=f"full size {name}")
