@@ -327,37 +327,43 @@ __device__ __forceinline__ h2 cv_of(_Float16 s) { return (h2){s, s} * (h2){(_Flo
 
 __device__ __forceinline__ f32x4 mfma(h8 a, h8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
-constexpr int NTW = 2;          // row tiles per GEMM workgroup (they share the activation operands)
-
-// one workgroup (8 waves) per pair of 16-row tiles; wave w covers the GW groups
-// [w GW, (w + 1) GW) of the input channels, the waves' products are summed in LDS.
-// MFMA operands: A row = token (lane l16), B column = output row of the tile (lane l16),
-// K = the 32 channels of one group (8 per lane quarter kg).
-template <int GW, bool RES>
-__global__ __launch_bounds__(512) void gemm_kernel(GArgs a) {
+// A workgroup of NW waves (NW * GW * 32 = K channels; wave w covers the GW groups
+// [w GW, (w + 1) GW)) builds the activation operands once and then walks over steps of NTW
+// 16-row tiles (step blockIdx.x, + gridDim.x, ...), loading the next step's weights into a
+// second register buffer while it multiplies the current one; the waves' products of a
+// step are summed in LDS (two buffers, one barrier per step).  MFMA operands: A row = token
+// (lane l16), B column = output row of the tile (lane l16), K = the 32 channels of a group.
+template <int GW, int NW, int NTW, bool RES>
+__global__ __launch_bounds__(NW * 64) void gemm_kernel(GArgs a) {
     constexpr int NQ = GW / 4;                  // weight quads per wave
     static_assert(GW % 4 == 0 && GW <= 16, "groups per wave");
-    __shared__ f32x4 red[NTW][8][64];
+    __shared__ f32x4 red[2][NTW][NW][64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l16 = lane & 15, kg = lane >> 4;
     const int tiles = a.n / TN, K = a.k, G = K / GS;
-    const int nt0 = NTW * blockIdx.x;
-    const bool two = nt0 + 1 < tiles;           // uniform over the workgroup
+    const int pairs = (tiles + NTW - 1) / NTW;
 
-    // every load first: the weights of the wave's quads for both tiles (row l16, quarter
-    // kg, 4 groups per quad; a missing second tile reads the first again), the token's
-    // code words and metadata, and X / 32 of the lane's local groups 4 kg .. 4 kg + 3
-    u4 wc[NTW][NQ];
-    uint2 wm[NTW][NQ];
+    // the weights of pair p: row l16 of each tile, quarter kg, 4 groups per quad (a missing
+    // second tile reads the first again)
+    auto load_w = [&](int p, u4 (&wc)[NTW][NQ], uint2 (&wm)[NTW][NQ]) {
+        const int nt0 = NTW * p;
+        const bool two = nt0 + 1 < tiles;
 #pragma unroll
-    for (int u = 0; u < NTW; ++u) {
-        const uint8_t* wt = a.w + ((size_t)(two ? nt0 + u : nt0) * (K / RB) + (size_t)w * NQ) * QB;
+        for (int u = 0; u < NTW; ++u) {
+            const uint8_t* wt = a.w + ((size_t)(two ? nt0 + u : nt0) * (K / RB) + (size_t)w * NQ) * QB;
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            wc[u][q] = *reinterpret_cast<const u4*>(wt + q * QB + 16 * (16 * kg + l16));
-            wm[u][q] = *reinterpret_cast<const uint2*>(wt + q * QB + 1024 + 8 * l16);
+            for (int q = 0; q < NQ; ++q) {
+                wc[u][q] = *reinterpret_cast<const u4*>(wt + q * QB + 16 * (16 * kg + l16));
+                wm[u][q] = *reinterpret_cast<const uint2*>(wt + q * QB + 1024 + 8 * l16);
+            }
         }
-    }
-    // lanes past the last token read the last token's row and zero it
+    };
+    u4 wcA[NTW][NQ], wcB[NTW][NQ];
+    uint2 wmA[NTW][NQ], wmB[NTW][NQ];
+    int p = blockIdx.x;                         // the grid never exceeds the pair count
+    load_w(p, wcA, wmA);
+
+    // activation operands of token l16; lanes past the last token read the last token's
+    // row (every load unconditional, so all are in flight together) and zero it
     const bool mok = l16 < a.m;
     const int rowb = act_row_bytes(K);
     const int mrow = mok ? l16 : a.m - 1;
@@ -371,27 +377,15 @@ __global__ __launch_bounds__(512) void gemm_kernel(GArgs a) {
     float xq[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) xq[j] = a.xsum[(size_t)mrow * G + w * GW + min(4 * kg + j, GW - 1)];
-    // the epilogue's operands (waves 0 and 1 store the two tiles): c and the anchor product
-    float ce[4] = {0.f, 0.f, 0.f, 0.f}, y0e[4] = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (RES) {
-        if (w < NTW && (w == 0 || two)) {
-            const int n = (nt0 + w) * TN + l16;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = min(4 * kg + r, a.m - 1);
-                ce[r] = a.c[m];
-                y0e[r] = a.y0_in[(size_t)m * a.n + n];
-            }
-        }
-    }
-
-    // activation operands: s_x q_x (exact FP16) and the broadcast offset z_x
-    h8 a1[GW], a2[GW];
+    // s_x q_x as exact FP16 operands; z_x kept as one packed pair per group and broadcast
+    // into the 8-wide operand at each use (fewer registers than holding the operands)
+    h8 a1[GW];
+    uint32_t zx2[GW];
 #pragma unroll
     for (int gl = 0; gl < GW; ++gl) {
         const h2 zs = meta_h2(mok ? am[gl] : 0u);
         a1[gl] = scaled_codes(mok ? aw[gl] : 0u, sv_of(zs.y), cv_of(zs.y));
-        a2[gl] = (h8){zs.x, zs.x, zs.x, zs.x, zs.x, zs.x, zs.x, zs.x};
+        zx2[gl] = __builtin_bit_cast(uint32_t, (h2){zs.x, zs.x});
     }
     // z_w X terms: K' position 8 kg + e <-> local group 4 kg + e / 2, FP16 hi (e even) / lo
     // (e odd) of X / 32 on the token side, 32 z_w on the weight side (powers of two: exact)
@@ -404,68 +398,113 @@ __global__ __launch_bounds__(512) void gemm_kernel(GArgs a) {
         ax[e] = (e & 1) ? (_Float16)(xv - (float)hi) : hi;
     }
 
+    // one pair: products, the waves' sums in LDS buffer `it & 1`, waves 0 and 1 store a tile each
+    auto pair = [&](int p, int it, const u4 (&wc)[NTW][NQ], const uint2 (&wm)[NTW][NQ]) {
+        const int nt0 = NTW * p;
+        const bool two = nt0 + 1 < tiles;
+        const bool storer = w < NTW && (w == 0 || two);
+        float ce[4] = {0.f, 0.f, 0.f, 0.f}, y0e[4] = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (RES) {
+            if (storer) {
+                const int n = (nt0 + w) * TN + l16;
 #pragma unroll
-    for (int u = 0; u < NTW; ++u) {
-        h8 bx;
-        {
-            // the lane's quarter kg holds the offsets of the wave's quad kg
-            uint2 mq = wm[u][0];
-#pragma unroll
-            for (int q = 1; q < NQ; ++q)
-                if (q == kg) mq = wm[u][q];
-#pragma unroll
-            for (int jp = 0; jp < 2; ++jp) {
-                const uint32_t word = jp ? mq.y : mq.x;
-                const h2 m0 = meta_h2(word & 0xFFFFu), m1 = meta_h2(word >> 16);
-                const _Float16 z0 = kg < NQ ? m0.x * (_Float16)32.0f : (_Float16)0.0f;
-                const _Float16 z1 = kg < NQ ? m1.x * (_Float16)32.0f : (_Float16)0.0f;
-                bx[4 * jp + 0] = z0;
-                bx[4 * jp + 1] = z0;
-                bx[4 * jp + 2] = z1;
-                bx[4 * jp + 3] = z1;
-            }
-        }
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t mb = ((j < 2) ? wm[u][q].x : wm[u][q].y) >> (16 * (j & 1));
-                const _Float16 sw = meta_h2(mb & 0xFFFFu).y;
-                const h8 b = scaled_codes(wc[u][q][j], sv_of(sw), cv_of(sw));
-                acc = mfma(a1[4 * q + j], b, acc);
-                acc = mfma(a2[4 * q + j], b, acc);
-            }
-        }
-        red[u][w][lane] = mfma(ax, bx, acc);
-    }
-    __syncthreads();
-    if (w < NTW && (w == 0 || two)) {
-        f32x4 v = red[w][0][lane];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) v += red[w][i][lane];
-        const int n = (nt0 + w) * TN + l16;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int m = 4 * kg + r;
-            if (m < a.m) {
-                const size_t o = (size_t)m * a.n + n;
-                if constexpr (RES) {
-                    a.y[o] = ce[r] * y0e[r] + v[r];
-                } else {
-                    a.y[o] = v[r];
-                    if (a.y0_out) a.y0_out[o] = v[r];
+                for (int r = 0; r < 4; ++r) {
+                    const int m = min(4 * kg + r, a.m - 1);
+                    ce[r] = a.c[m];
+                    y0e[r] = a.y0_in[(size_t)m * a.n + n];
                 }
             }
         }
+#pragma unroll
+        for (int u = 0; u < NTW; ++u) {
+            h8 bx;
+            {
+                // the lane's quarter kg holds the offsets of the wave's quad kg
+                uint2 mq = wm[u][0];
+#pragma unroll
+                for (int q = 1; q < NQ; ++q)
+                    if (q == kg) mq = wm[u][q];
+#pragma unroll
+                for (int jp = 0; jp < 2; ++jp) {
+                    const uint32_t word = jp ? mq.y : mq.x;
+                    const h2 m0 = meta_h2(word & 0xFFFFu), m1 = meta_h2(word >> 16);
+                    const _Float16 z0 = kg < NQ ? m0.x * (_Float16)32.0f : (_Float16)0.0f;
+                    const _Float16 z1 = kg < NQ ? m1.x * (_Float16)32.0f : (_Float16)0.0f;
+                    bx[4 * jp + 0] = z0;
+                    bx[4 * jp + 1] = z0;
+                    bx[4 * jp + 2] = z1;
+                    bx[4 * jp + 3] = z1;
+                }
+            }
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t mb = ((j < 2) ? wm[u][q].x : wm[u][q].y) >> (16 * (j & 1));
+                    const _Float16 sw = meta_h2(mb & 0xFFFFu).y;
+                    const h8 b = scaled_codes(wc[u][q][j], sv_of(sw), cv_of(sw));
+                    const uint32_t zz = zx2[4 * q + j];
+                    acc = mfma(a1[4 * q + j], b, acc);
+                    acc = mfma(__builtin_bit_cast(h8, (u4){zz, zz, zz, zz}), b, acc);
+                }
+            }
+            red[it & 1][u][w][lane] = mfma(ax, bx, acc);
+        }
+        __syncthreads();
+        if (storer) {
+            f32x4 v = red[it & 1][w][0][lane];
+#pragma unroll
+            for (int i = 1; i < NW; ++i) v += red[it & 1][w][i][lane];
+            const int n = (nt0 + w) * TN + l16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 4 * kg + r;
+                if (m < a.m) {
+                    const size_t o = (size_t)m * a.n + n;
+                    if constexpr (RES) {
+                        a.y[o] = ce[r] * y0e[r] + v[r];
+                    } else {
+                        a.y[o] = v[r];
+                        if (a.y0_out) a.y0_out[o] = v[r];
+                    }
+                }
+            }
+        }
+    };
+
+    // ping-pong over the workgroup's pairs: multiply with one buffer while the other loads
+    for (int it = 0;; it += 2) {
+        const int pb = p + gridDim.x;
+        if (pb < pairs) load_w(pb, wcB, wmB);
+        pair(p, it, wcA, wmA);
+        if (pb >= pairs) break;
+        const int pa = pb + gridDim.x;
+        if (pa < pairs) load_w(pa, wcA, wmA);
+        pair(pb, it + 1, wcB, wmB);
+        if (pa >= pairs) break;
+        p = pa;
     }
 }
 
-template <int GW>
+static int w4_cu_count() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || n <= 0)
+        n = 256;
+    return n;
+}
+
+// two tiles per step while the registers allow (they share the activation operands), one
+// at K >= 3072
+template <int GW, int NW>
 static void launch_gemm(const GArgs& g, bool res, hipStream_t st) {
-    const dim3 grid((g.n / TN + NTW - 1) / NTW);
-    if (res) hipLaunchKernelGGL((gemm_kernel<GW, true>), grid, dim3(512), 0, st, g);
-    else hipLaunchKernelGGL((gemm_kernel<GW, false>), grid, dim3(512), 0, st, g);
+    constexpr int NTW = GW <= 8 ? 2 : 1;
+    const int steps = (g.n / TN + NTW - 1) / NTW;
+    const int cus = w4_cu_count();
+    const dim3 grid(steps < cus ? steps : cus);
+    if (res) hipLaunchKernelGGL((gemm_kernel<GW, NW, NTW, true>), grid, dim3(NW * 64), 0, st, g);
+    else hipLaunchKernelGGL((gemm_kernel<GW, NW, NTW, false>), grid, dim3(NW * 64), 0, st, g);
 }
 
 }  // namespace w4
@@ -543,11 +582,12 @@ rq_status rq_w4a4_linear(const rq_w4a4_config* cfg, const void* weights, const u
 
     w4::GArgs g{static_cast<const uint8_t*>(weights), act_rows, xsum, cbuf, y0, res ? nullptr : y0, y, m,
                 cfg->out_features, k};
-    switch (k / 256) {
-        case 4: w4::launch_gemm<4>(g, res, stream); break;
-        case 8: w4::launch_gemm<8>(g, res, stream); break;
-        case 12: w4::launch_gemm<12>(g, res, stream); break;
-        default: w4::launch_gemm<16>(g, res, stream); break;
+    // 8 waves per workgroup, each covering K / 256 groups
+    switch (k) {
+        case 1024: w4::launch_gemm<4, 8>(g, res, stream); break;
+        case 2048: w4::launch_gemm<8, 8>(g, res, stream); break;
+        case 3072: w4::launch_gemm<12, 8>(g, res, stream); break;
+        default: w4::launch_gemm<16, 8>(g, res, stream); break;
     }
     return hipGetLastError() == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
