@@ -212,6 +212,7 @@ static rq_status quantize_impl(const rq_config* cfg, void* cache, const int32_t*
     // a few tokens: one per workgroup; groups longer than the per-loop-count instantiations
     // (L > 8, shared anchor) always take the one-loop-per-workgroup kernel below the bulk size
     a.tokens_per_wg = (n_tokens <= 8 || (!g.chained && g.L > 8)) ? 1 : 32;
+    a.n_cu = device_cu_count();
     return launch_pack(a, stream) == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }
 

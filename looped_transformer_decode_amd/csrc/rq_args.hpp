@@ -16,6 +16,7 @@ struct PackArgs {
     int batch;
     int n_tokens;
     int tokens_per_wg;          // tokens handled by one workgroup (it keeps its row of R)
+    int n_cu;                   // compute units of the device (choice of the drain kernel)
 };
 
 // The split-K merge that the last workgroup of each (batch row, query head) performs.

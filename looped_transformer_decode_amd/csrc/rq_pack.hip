@@ -178,8 +178,11 @@ __device__ __forceinline__ void rotate_all(const float (&rhalf)[D / 2], const do
 // instantiation serves every group length.
 // The coefficient follows the configuration's rule: least squares <x, ref>/<ref, ref> or
 // the norm ratio sqrt(<x, x>/<ref, ref>), both rounded to BF16.
+// The SPLIT kernel is held to three waves per SIMD (144 VGPRs, no spills): at batch 16 its
+// 1536 workgroups then run in two rounds instead of three (per-step pack 25 -> 22 us); four
+// or more waves per SIMD spill and are slower.
 template <int D, int G, int LR, bool SPLIT>
-__global__ __launch_bounds__(2 * D) void rq_pack_kernel(PackArgs a) {
+__global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(SPLIT ? 3 : 1))) void rq_pack_kernel(PackArgs a) {
     const int LRr = SPLIT ? a.geo.L - 1 : LR;         // residual loops of the group
     const int L = LRr + 1;
     constexpr int NL = SPLIT ? 1 : LR;                 // residual loops of this workgroup
@@ -301,6 +304,123 @@ __global__ __launch_bounds__(2 * D) void rq_pack_kernel(PackArgs a) {
                 __syncthreads();
             }
         }
+    }
+}
+
+// ---- per-step drain with R in LDS: every residual loop of one token per workgroup
+//
+// The kernel above holds half a row of R per thread in registers, which allows at most
+// three of its workgroups per CU.  Here one workgroup of 2 D threads per (token, batch row,
+// KV head, K|V) stages R in LDS (66 KB at d = 128, so two workgroups per CU) and takes every
+// residual loop of the group, rotated side by side: the Ouro-sized drain at batch 16 is 512
+// workgroups, one round on 256 CUs, where one loop per workgroup needs 1536.  The anchor
+// quantizer, the c reductions, the rotation (the same two chains per half row, the pair
+// adding its halves) and the quantizers are the float64 steps of the kernel above in the
+// same order, so the bytes it writes are identical.
+// R rows are padded to d + 4 floats, so the 8 channels of a 16-lane group of a 128-bit LDS
+// read start in 8 different 4-bank groups (the two halves of a channel share one: a two-way
+// conflict on the R reads, which are 1/7 of the rotation's LDS reads at three loops).
+template <int D>
+__device__ __forceinline__ int rlds_slot(int row, int c4) { return row * ((D + 4) / 4) + c4; }
+
+// r = sum_k R[i][k] y[k] with R in LDS: the same two chains per half row and the same order as
+// rotate_rows.  One base address per operand, so every read takes its step as an immediate
+// offset.
+template <int D>
+__device__ __forceinline__ double rotate_row_lds(const f32x4* rs, int i, const double* y, int p) {
+    constexpr int H = D / 2;
+    const f32x4* rrow = rs + rlds_slot<D>(i, p * (H / 4));
+    const double* yb = y + H * p;
+    double r0 = 0.0, r1 = 0.0;
+#pragma unroll
+    for (int k = 0; k < H; k += 4) {
+        if (k % 16 == 0) __builtin_amdgcn_sched_barrier(0);
+        const f32x4 rv = rrow[k / 4];
+        r0 = fma((double)rv.x, yb[k], r0);
+        r1 = fma((double)rv.y, yb[k + 1], r1);
+        r0 = fma((double)rv.z, yb[k + 2], r0);
+        r1 = fma((double)rv.w, yb[k + 3], r1);
+    }
+    return pair_sum(r0 + r1);
+}
+
+template <int D, int G, int LR>
+__global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(2))) void rq_drain_kernel(PackArgs a) {
+    constexpr int NT = 2 * D;
+    constexpr int NR = D * D / 4 / NT;                // float4 of R per thread
+    const Geom& Gm = a.geo;
+    const int L = LR + 1;
+    const int i = threadIdx.x >> 1, p = threadIdx.x & 1;
+    int wg = blockIdx.x;
+    const int x = wg & 1;
+    wg >>= 1;
+    const int h = wg % Gm.hkv;
+    wg /= Gm.hkv;
+    const int b = wg % a.batch;
+    const int t = wg / a.batch;
+    const int slot = a.pos[b] + t;
+    if (t >= a.n_tokens || slot < 0 || slot >= Gm.max_ctx) return;   // the whole workgroup
+    const int tile = slot / kTile, jj = slot % kTile;
+    const int loop0 = a.group_idx * L;
+    const bool norm_ratio = Gm.scale_rule == 1;
+
+    __shared__ f32x4 rs[D * (D + 4) / 4];
+    __shared__ double sh_y[LR][D];
+    __shared__ double red[LR + 1][NT / 64];
+
+    // every global load first: R (landed in LDS after the anchor quantizer), the loops' inputs
+    const f32x4* R4 = reinterpret_cast<const f32x4*>(a.rot + (int64_t)(h * 2 + x) * D * D);
+    f32x4 rv[NR];
+#pragma unroll
+    for (int e = 0; e < NR; ++e) rv[e] = R4[threadIdx.x + e * NT];
+    double xv[LR + 1];                                 // residual loops, then the anchor
+    const uint16_t* src = a.pending + t * a.st[0] + b * a.st[1] + x * a.st[3] + h * a.st[4] + i;
+#pragma unroll
+    for (int l = 0; l <= LR; ++l) xv[l] = (double)bf16_to_f32(src[(int64_t)l * a.st[2]]);
+
+    const QOut qa = quantize_lane<G>(xv[LR], Gm.ba);
+    {
+        uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + L - 1, tile);
+        store_codes(pl + jj * Gm.a_row, qa.code, Gm.ba);
+        store_meta(pl + kTile * Gm.a_row + jj * Gm.m_row, qa, Gm.g);
+    }
+    const double a_hat = qa.z + qa.code * qa.s;
+#pragma unroll
+    for (int e = 0; e < NR; ++e) {
+        const int idx = threadIdx.x + e * NT;
+        rs[rlds_slot<D>(idx / (D / 4), idx % (D / 4))] = rv[e];
+    }
+
+    double sums[LR + 1];
+#pragma unroll
+    for (int l = 0; l < LR; ++l) sums[l] = xv[l] * (norm_ratio ? xv[l] : a_hat);
+    sums[LR] = a_hat * a_hat;
+    block_sum<NT, LR + 1>(sums, red);                  // its barriers also publish rs
+    double cs[LR];
+#pragma unroll
+    for (int l = 0; l < LR; ++l) {
+        const double q = sums[l] / sums[LR];
+        cs[l] = bf16_round(sums[LR] > 0.0 ? (norm_ratio ? sqrt(q) : q) : 0.0);
+        if (p == 0) sh_y[l][i] = xv[l] - cs[l] * a_hat;
+    }
+    __syncthreads();
+    // one loop at a time: with the loops side by side the scheduler hoists every LDS read of
+    // the rotation and spills
+    double rl[LR];
+#pragma unroll
+    for (int l = 0; l < LR; ++l) {
+        __builtin_amdgcn_sched_barrier(0);
+        rl[l] = rotate_row_lds<D>(rs, i, sh_y[l], p);
+    }
+    QOut qr[LR];
+#pragma unroll
+    for (int l = 0; l < LR; ++l) qr[l] = quantize_lane<G>(rl[l], Gm.rbits(l));
+#pragma unroll
+    for (int l = 0; l < LR; ++l) {
+        uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + l, tile);
+        store_codes(pl + jj * Gm.rrow(l), qr[l].code, Gm.rbits(l));
+        store_meta(pl + kTile * Gm.rrow(l) + jj * Gm.m_row, qr[l], Gm.g);
+        store_c(pl + kTile * (Gm.rrow(l) + Gm.m_row), jj, cs[l]);
     }
 }
 
@@ -589,10 +709,34 @@ static hipError_t launch_dgs(const PackArgs& a, int nwg, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// one residual loop per workgroup for a few tokens with a shared anchor (the per-step drain)
+// every residual loop of one token per workgroup with R in LDS (shared anchor, up to 8 loops)
+template <int D, int G>
+static hipError_t launch_drain(const PackArgs& a, int nwg, hipStream_t stream) {
+    const dim3 grid(nwg), block(2 * D);
+    switch (a.geo.L - 1) {
+        case 1: hipLaunchKernelGGL((rq_drain_kernel<D, G, 1>), grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((rq_drain_kernel<D, G, 2>), grid, block, 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((rq_drain_kernel<D, G, 3>), grid, block, 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((rq_drain_kernel<D, G, 4>), grid, block, 0, stream, a); break;
+        case 5: hipLaunchKernelGGL((rq_drain_kernel<D, G, 5>), grid, block, 0, stream, a); break;
+        case 6: hipLaunchKernelGGL((rq_drain_kernel<D, G, 6>), grid, block, 0, stream, a); break;
+        case 7: hipLaunchKernelGGL((rq_drain_kernel<D, G, 7>), grid, block, 0, stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// A few tokens with a shared anchor (the per-step drain), one token per workgroup.  One residual
+// loop per workgroup has the shortest chain (10.4 us for the Ouro-sized drain at batch 4, against
+// 12.9 us with every loop and R in LDS) while its workgroups fit one round at three per CU; past
+// that the kernel with R in LDS runs (batch 16: 16.8 us in one round, against 21.5 us in two).
 template <int D, int G>
 static hipError_t launch_dg(const PackArgs& a, int nwg, hipStream_t stream) {
-    if (!a.geo.chained && a.tokens_per_wg == 1) return launch_dgs<D, G, true>(a, nwg, stream);
+    if (!a.geo.chained && a.tokens_per_wg == 1) {
+        const int64_t split_wgs = (int64_t)nwg * (a.geo.L - 1);
+        if (a.geo.L <= 8 && split_wgs > 3LL * (a.n_cu > 0 ? a.n_cu : 256)) return launch_drain<D, G>(a, nwg, stream);
+        return launch_dgs<D, G, true>(a, nwg, stream);
+    }
     return launch_dgs<D, G, false>(a, nwg, stream);
 }
 
