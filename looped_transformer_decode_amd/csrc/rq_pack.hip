@@ -19,39 +19,6 @@
 namespace rq {
 
 
-// ---- cross-lane steps on float64 values
-
-template <int CTRL>
-__device__ __forceinline__ double dpp_d(double v) {
-    const uint64_t u = (uint64_t)__double_as_longlong(v);
-    const int lo = __builtin_amdgcn_update_dpp((int)(uint32_t)u, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
-    const int hi = __builtin_amdgcn_update_dpp((int)(uint32_t)(u >> 32), (int)(uint32_t)(u >> 32), CTRL, 0xF,
-                                               0xF, false);
-    return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
-}
-
-// reduction over aligned groups of NL lanes (a power of two up to 64); every lane of the
-// group gets the same value (both lanes of a pair combine the same two operands)
-template <int NL, int M = 1, class Op>
-__device__ __forceinline__ double lanes_reduce(double v, Op op) {
-    if constexpr (M >= NL) {
-        return v;
-    } else if constexpr (M == 16 || M == 32) {
-        const uint64_t u = (uint64_t)__double_as_longlong(v);
-        const int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
-        const auto rl = (M == 16) ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
-                                  : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
-        const auto rh = (M == 16) ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
-                                  : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
-        const double p = __longlong_as_double((long long)(((uint64_t)(uint32_t)rh[0] << 32) | (uint32_t)rl[0]));
-        const double q = __longlong_as_double((long long)(((uint64_t)(uint32_t)rh[1] << 32) | (uint32_t)rl[1]));
-        return lanes_reduce<NL, 2 * M>(op(p, q), op);
-    } else {
-        constexpr int CTRL = M == 1 ? kDppQuadXor1 : M == 2 ? kDppQuadXor2 : M == 4 ? kDppRowHalfMirror : kDppRowMirror;
-        return lanes_reduce<NL, 2 * M>(op(v, dpp_d<CTRL>(v)), op);
-    }
-}
-
 // min / max over aligned groups of NL = 16, 32 or 64 lanes, result in every lane
 template <int NL>
 __device__ __forceinline__ double group_min(double v) {
@@ -66,7 +33,7 @@ __device__ __forceinline__ double group_max(double v) {
 __device__ __forceinline__ double pair_sum(double v) { return v + dpp_d<kDppQuadXor1>(v); }
 
 // ---- the group quantizer (two lanes per channel, groups of G consecutive channels);
-// QOut, group_params and group_code are in rq_quant.hpp
+// QOut, group_params, group_code and lanes_reduce are in rq_quant.hpp
 
 template <int G>
 __device__ __forceinline__ QOut quantize_lane(double x, int bits) {

@@ -4,12 +4,47 @@
 // [0, n].  n s has at most 8 significant bits and z + n s is a multiple of 2^-9 below
 // 2^13, so the covering test is exact; the candidate scale from an approximate quotient
 // is off by at most one grid step and is corrected by that test.  The code divides
-// exactly as a float64 reference does.
+// exactly as a float64 reference does.  The float64 lane reductions the quantizers use for
+// group extremes and dot products live here too.
 #pragma once
 
+#include "rq_common.hpp"
 #include "rq_fp8.hpp"
 
 namespace rq {
+
+// Cross-lane steps on float64 values (DPP inside a 16-lane row, lane swaps across rows).
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp((int)(uint32_t)u, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp((int)(uint32_t)(u >> 32), (int)(uint32_t)(u >> 32), CTRL, 0xF,
+                                               0xF, false);
+    return __longlong_as_double((long long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo));
+}
+
+// reduction over aligned groups of NL lanes (a power of two up to 64); every lane of the
+// group gets the same value (both lanes of a pair combine the same two operands)
+template <int NL, int M = 1, class Op>
+__device__ __forceinline__ double lanes_reduce(double v, Op op) {
+    if constexpr (M >= NL) {
+        return v;
+    } else if constexpr (M == 16 || M == 32) {
+        const uint64_t u = (uint64_t)__double_as_longlong(v);
+        const int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
+        const auto rl = (M == 16) ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                                  : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+        const auto rh = (M == 16) ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                                  : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+        const double p = __longlong_as_double((long long)(((uint64_t)(uint32_t)rh[0] << 32) | (uint32_t)rl[0]));
+        const double q = __longlong_as_double((long long)(((uint64_t)(uint32_t)rh[1] << 32) | (uint32_t)rl[1]));
+        return lanes_reduce<NL, 2 * M>(op(p, q), op);
+    } else {
+        constexpr int CTRL = M == 1 ? kDppQuadXor1 : M == 2 ? kDppQuadXor2 : M == 4 ? kDppRowHalfMirror : kDppRowMirror;
+        return lanes_reduce<NL, 2 * M>(op(v, dpp_d<CTRL>(v)), op);
+    }
+}
 
 struct QOut {
     uint32_t code, zb, sb;

@@ -104,21 +104,28 @@ struct AArgs {
 
 constexpr int TQ = 1;           // tokens per activation-quantizer workgroup
 
-// Sums over the 256 threads in a fixed order, TQ values per thread at once (every thread
-// gets the results): a butterfly inside each wave, then the 4 wave sums in order.
-__device__ __forceinline__ void block_sum256(double (&v)[TQ], double (*red)[4]) {
+// Sums over the 256 threads of two values in a fixed order, both reduced side by side (every
+// thread gets the results): DPP and lane swaps inside each wave, then the 4 wave sums in order.
+__device__ __forceinline__ void block_sum256(double (&u)[TQ], double (&v)[TQ], double (*red)[4]) {
+    const auto add = [](double p, double q) { return p + q; };
 #pragma unroll
     for (int q = 0; q < TQ; ++q) {
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) v[q] += shfl_xor_d(v[q], o);
+        u[q] = lanes_reduce<kWave>(u[q], add);
+        v[q] = lanes_reduce<kWave>(v[q], add);
     }
     if ((threadIdx.x & 63) == 0) {
 #pragma unroll
-        for (int q = 0; q < TQ; ++q) red[q][threadIdx.x >> 6] = v[q];
+        for (int q = 0; q < TQ; ++q) {
+            red[2 * q][threadIdx.x >> 6] = u[q];
+            red[2 * q + 1][threadIdx.x >> 6] = v[q];
+        }
     }
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < TQ; ++q) v[q] = ((red[q][0] + red[q][1]) + red[q][2]) + red[q][3];
+    for (int q = 0; q < TQ; ++q) {
+        u[q] = ((red[2 * q][0] + red[2 * q][1]) + red[2 * q][2]) + red[2 * q][3];
+        v[q] = ((red[2 * q + 1][0] + red[2 * q + 1][1]) + red[2 * q + 1][2]) + red[2 * q + 1][3];
+    }
     __syncthreads();
 }
 
@@ -135,7 +142,7 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(AArgs a) {
     __shared__ double rs[RES ? TQ : 1][RES ? RB : 1];          // the rotated residual
     __shared__ double za[RES ? TQ : 1][RES ? GMAX : 1];        // anchor offsets and scales
     __shared__ double sa[RES ? TQ : 1][RES ? GMAX : 1];
-    __shared__ double red[TQ][4];
+    __shared__ double red[2 * TQ][4];
     __shared__ uint32_t cw[TQ][RB / 8];         // the block's code words
     const int t = threadIdx.x, b = blockIdx.x, m0 = blockIdx.y * TQ, K = a.k, G = K / GS;
     const int rowb = act_row_bytes(K);
@@ -210,8 +217,7 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(AArgs a) {
                 }
             }
         }
-        block_sum256(num, red);
-        block_sum256(den, red);
+        block_sum256(num, den, red);
 #pragma unroll
         for (int q = 0; q < TQ; ++q) c[q] = bf16_round(den[q] > 0.0 ? num[q] / den[q] : 0.0);
     }
@@ -243,7 +249,7 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(AArgs a) {
             p[3] = fma((double)rv[k].w, ys[0][i + 3], p[3]);
         }
         double r = (p[0] + p[1]) + (p[2] + p[3]);
-        r += shfl_xor_d(r, 1);
+        r += dpp_d<kDppQuadXor1>(r);
         if (h == 0) rs[0][j] = r;
         __syncthreads();
         src = rs;
@@ -252,21 +258,16 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(AArgs a) {
     if (t < TQ * 64) {
         const int grp = t / 16, u = t % 16, q = grp / 4, jg = grp % 4;
         const double v0 = src[q][GS * jg + 2 * u], v1 = src[q][GS * jg + 2 * u + 1];
-        double lo = fmin(v0, v1), hi = fmax(v0, v1);
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-            lo = fmin(lo, shfl_xor_d(lo, o));
-            hi = fmax(hi, shfl_xor_d(hi, o));
-        }
+        const double lo = lanes_reduce<16>(fmin(v0, v1), [](double p, double q) { return fmin(p, q); });
+        const double hi = lanes_reduce<16>(fmax(v0, v1), [](double p, double q) { return fmax(p, q); });
         const QOut qo = group_params(lo, hi, 4);
         const uint32_t c0 = group_code(v0, qo, 4), c1 = group_code(v1, qo, 4);
-        double sum = (qo.z + (double)c0 * qo.s) + (qo.z + (double)c1 * qo.s);
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) sum += shfl_xor_d(sum, o);
+        const double sum = lanes_reduce<16>((qo.z + (double)c0 * qo.s) + (qo.z + (double)c1 * qo.s),
+                                            [](double p, double q) { return p + q; });
         // byte u of the group's 16 code bytes; four neighbouring lanes form one word
         uint32_t byte = (c0 | (c1 << 4)) << (8 * (u & 3));
-        byte |= (uint32_t)__shfl_xor((int)byte, 1, kWave);
-        byte |= (uint32_t)__shfl_xor((int)byte, 2, kWave);
+        byte |= (uint32_t)xshfl_i<1>((int)byte);
+        byte |= (uint32_t)xshfl_i<2>((int)byte);
         if ((u & 3) == 0) cw[q][4 * jg + u / 4] = byte;
         if (u == 0 && q < nq) {
             const int g = 4 * b + jg, m = m0 + q;
