@@ -91,6 +91,8 @@ inline size_t workspace_bytes(int max_batch, int hq, int d) {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- number formats
 

@@ -396,11 +396,11 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(2))) void
 // For a prefilled context the token-at-a-time chain above leaves the chip idle.  Here a
 // workgroup takes kBulkTokens tokens: the quantizers and the c dot products run one token
 // per wave (lane = D/64 consecutive channels), and the rotations of all residual loops of
-// all its tokens form one product R Y (D x D times D x (tokens x loops)) read from LDS
-// with register tiles.  Same float64 arithmetic and the same decisions as the kernel
-// above; only the order of the additions inside the dot products differs.
+// all its tokens form one product R Y (D x D times D x (tokens x loops)) on the float64
+// matrix cores.  Same float64 arithmetic and the same decisions as the kernel above; only
+// the order of the additions inside the dot products differs.
 constexpr int kBulkTokens = 16;
-// threads per workgroup: 8 waves (two per SIMD, to hide each other's latency) at D = 128
+// threads per workgroup: 8 waves at D = 128 (one 16-row tile of R each), two workgroups per CU
 template <int D>
 constexpr int bulk_threads() { return D == 128 ? 512 : 256; }
 
@@ -458,14 +458,13 @@ __device__ __forceinline__ void quantize_row(const double (&x)[CPL], double (&xh
 // LB = min(L - 1, 3) residual loops per product; the loop count itself comes from the
 // configuration, so one instantiation serves every group length of at least LB + 1.
 template <int D, int G, int LB>
-__global__ __launch_bounds__(bulk_threads<D>()) void rq_pack_bulk_kernel(PackArgs a) {
+__global__ __launch_bounds__(bulk_threads<D>()) __attribute__((amdgpu_waves_per_eu(4))) void rq_pack_bulk_kernel(PackArgs a) {
     constexpr int kBulkThreads = bulk_threads<D>();
     constexpr int TK = kBulkTokens, NW = kBulkThreads / kWave;
     constexpr int CPL = D / kWave;                    // channels per lane
     constexpr int NCOL = TK * LB;                     // columns of Y: (token, loop)
-    constexpr int RB = D / 4, CB = kBulkThreads / RB, CPT = NCOL / CB;
-    static_assert(NCOL % CB == 0 && CPT >= 1 && TK % NW == 0, "register tile, tokens per wave");
-    constexpr int RS = D + 4;                         // padded LDS row of R (floats)
+    static_assert(D / 16 == NW && TK % NW == 0, "one 16-row tile of R per wave, tokens per wave");
+    constexpr int YS = D + 2;                         // padded LDS row of Y (doubles)
     const Geom& Gm = a.geo;
     const int LR = Gm.L - 1, L = Gm.L;
     const bool norm_ratio = Gm.scale_rule == 1;
@@ -479,17 +478,18 @@ __global__ __launch_bounds__(bulk_threads<D>()) void rq_pack_bulk_kernel(PackArg
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int loop0 = a.group_idx * L;
 
-    __shared__ __attribute__((aligned(16))) float rs[D * RS];      // R, row-major
-    __shared__ __attribute__((aligned(16))) double yt[D][NCOL];    // Y, then R Y: [channel][column]
+    __shared__ __attribute__((aligned(16))) double yt[NCOL][YS];   // Y, then R Y: [column][channel]
     __shared__ double ah[TK][D];                                   // dequantized anchors
     __shared__ double aa[TK];                                      // <a_hat, a_hat>
     __shared__ uint16_t xs[LB][TK][D];                             // BF16 inputs of the loops at hand
 
-    const float* R = a.rot + (int64_t)(h * 2 + x) * D * D;
-    for (int idx = threadIdx.x; idx < D * D / 4; idx += kBulkThreads) {
-        const int i = idx / (D / 4), k4 = idx % (D / 4);
-        *reinterpret_cast<float4*>(&rs[i * RS + 4 * k4]) = reinterpret_cast<const float4*>(R)[idx];
-    }
+    // The A operand of the rotation product: this lane's part of the 16 rows of R that its wave
+    // multiplies (row 16 w + lane % 16, channels (D/4) (lane / 16) ..), read from global memory
+    // (L2) right before each product and never staged in LDS: that leaves room for two
+    // workgroups per CU (79 KB of LDS, 94 VGPRs), whose latency-bound phases overlap.
+    const int i16 = lane & 15, kq = lane >> 4;
+    const f32x4* rp = reinterpret_cast<const f32x4*>(a.rot + (int64_t)(h * 2 + x) * D * D +
+                                                     (int64_t)(16 * w + i16) * D + (D / 4) * kq);
 
     const int p0 = a.pos[b] + t0;
     auto valid = [&](int tok) {
@@ -584,40 +584,42 @@ __global__ __launch_bounds__(bulk_threads<D>()) void rq_pack_bulk_kernel(PackArg
                         (uint16_t)(__float_as_uint((float)cl) >> 16);
                 }
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) yt[CPL * lane + c][tok * LB + li] = xl[c] - cl * xh[c];
+                for (int c = 0; c < CPL; ++c) yt[tok * LB + li][CPL * lane + c] = xl[c] - cl * xh[c];
             }
         }
         __syncthreads();
-        // ---- r = R y for every column: thread tile of 4 rows x CPT columns
+        // ---- r = R y for every column on the matrix cores (v_mfma_f64_16x16x4_f64): wave w
+        // takes the 16 rows 16 w .. of R and every 16-column tile of Y.  The sum over the
+        // channels is split over the four K slots of the product, slot kq taking channels
+        // (D/4) kq + s at step s, so that each lane reads its R row and its Y column as
+        // contiguous runs (R from registers, Y from LDS).  Lane layout (measured with an in-bounds probe): A[i][k] in lane
+        // i + 16 k, B[k][j] in lane j + 16 k, D[i][j] in lane j + 16 (i % 4), element i / 4.
         {
-            const int r0 = 4 * (threadIdx.x / CB), c0 = (threadIdx.x % CB) * CPT;
-            double acc[4][CPT];
+            f32x4 ra[D / 16];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+            for (int q = 0; q < D / 16; ++q) ra[q] = rp[q];
+            f64x4 acc[LB];
 #pragma unroll
-                for (int j = 0; j < CPT; ++j) acc[e][j] = 0.0;
-            for (int k4 = 0; k4 < D / 4; ++k4) {
-                float4 rr[4];
+            for (int c = 0; c < LB; ++c) acc[c] = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) rr[e] = *reinterpret_cast<const float4*>(&rs[(r0 + e) * RS + 4 * k4]);
+            for (int q = 0; q < D / 16; ++q) {
+                const f32x4 rv = ra[q];
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    double yv[CPT];
-#pragma unroll
-                    for (int j = 0; j < CPT; ++j) yv[j] = yt[4 * k4 + kk][c0 + j];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const double re = (double)(kk == 0 ? rr[e].x : kk == 1 ? rr[e].y : kk == 2 ? rr[e].z : rr[e].w);
-#pragma unroll
-                        for (int j = 0; j < CPT; ++j) acc[e][j] = fma(re, yv[j], acc[e][j]);
-                    }
+                for (int c = 0; c < LB; ++c) {
+                    const double* yb = &yt[16 * c + i16][(D / 4) * kq + 4 * q];
+                    const f64x2 y01 = *reinterpret_cast<const f64x2*>(yb);
+                    const f64x2 y23 = *reinterpret_cast<const f64x2*>(yb + 2);
+                    acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)rv.x, y01.x, acc[c], 0, 0, 0);
+                    acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)rv.y, y01.y, acc[c], 0, 0, 0);
+                    acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)rv.z, y23.x, acc[c], 0, 0, 0);
+                    acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64((double)rv.w, y23.y, acc[c], 0, 0, 0);
                 }
             }
-            __syncthreads();                          // every thread has read Y
+            __syncthreads();                          // every wave has read Y
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+            for (int c = 0; c < LB; ++c)
 #pragma unroll
-                for (int j = 0; j < CPT; ++j) yt[r0 + e][c0 + j] = acc[e][j];
+                for (int e = 0; e < 4; ++e) yt[16 * c + i16][16 * w + 4 * e + kq] = acc[c][e];
         }
         __syncthreads();
         // ---- residual codes, one token per wave
@@ -630,7 +632,7 @@ __global__ __launch_bounds__(bulk_threads<D>()) void rq_pack_bulk_kernel(PackArg
                 const int l = lb0 + li;
                 double r[CPL], rh[CPL];
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) r[c] = yt[CPL * lane + c][tok * LB + li];
+                for (int c = 0; c < CPL; ++c) r[c] = yt[tok * LB + li][CPL * lane + c];
                 const int lq = l < LR ? l : 0;            // a loop past the group's last is not stored
                 uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + lq, tile);
                 if (Gm.rbits(lq) == 4) quantize_row<G, CPL, 4>(r, rh, pl, Gm.rrow(lq), Gm.m_row, jj, ok && l < LR, lane);
