@@ -68,3 +68,30 @@ def test_drain_kernels_agree(name):
             check_pack_block(device_block(one_call, ocfg, b, h), sub, xs, rot[h], N_TOK, stats)
     say(f"[drain] case={name} stats={stats}")
     assert_stats(stats, wl.group)
+
+
+def test_drain_through_block_tables():
+    """The LDS drain kernel through a shuffled block table: the gathered bytes equal the
+    contiguous drain of the same tokens."""
+    from looped_transformer_decode_amd import binding as B
+    from test_gpu_paged import gather
+    wl, batch, hkv = CASES["d128g32_L4"]
+    wl = wl.with_(batch=batch, ctx=N_TOK, chained=False, n_kv_heads=hkv, n_q_heads=hkv)
+    inp = synth.generate(wl, seed=607, device="cuda")
+    cfg = B.config_for(wl)
+    ocfg = oracle_cfg(wl)
+    n_tiles = (cfg.max_ctx + 63) // 64
+    n_blocks = batch * n_tiles + 3
+    table_np = np.random.default_rng(5).permutation(n_blocks)[: batch * n_tiles].reshape(batch, n_tiles)
+    table = torch.from_numpy(table_np.astype(np.int32)).to("cuda")
+    bb = B.rq_paged_block_bytes(cfg)
+    pool = torch.zeros(n_blocks * bb, dtype=torch.uint8, device="cuda")
+    flat = torch.zeros(B.rq_cache_bytes(cfg), dtype=torch.uint8, device="cuda")
+    pos = torch.zeros(batch, dtype=torch.int32, device="cuda")
+    say(f"[drain] paged: batch={batch} hkv={hkv} blocks={n_blocks}")
+    kv = inp.kv[0]
+    B.rq_quantize_token_paged(cfg, pool, n_blocks, table, kv, 0, pos, inp.rot, batch, N_TOK,
+                              pending_strides=pending_strides(kv))
+    B.rq_quantize_token(cfg, flat, kv, 0, pos, inp.rot, batch, N_TOK, pending_strides=pending_strides(kv))
+    torch.cuda.synchronize()
+    assert np.array_equal(gather(pool.cpu().numpy(), table_np, ocfg, bb), flat.cpu().numpy())
