@@ -288,9 +288,11 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
         }
     }
     __syncthreads();
-    // group sums of q and u (for the offsets z), one thread per (plane, query, group)
-    if (threadIdx.x < 2 * G * NG) {
-        const int pl = threadIdx.x / (G * NG), g = (threadIdx.x / NG) % G, gi = threadIdx.x % NG;
+    // group sums of q and u (for the offsets z), one thread per (plane, query, group), on the
+    // upper waves (the lower four build the key operands below at the same time)
+    if (threadIdx.x >= NT - 2 * G * NG) {
+        const int tq = threadIdx.x - (NT - 2 * G * NG);
+        const int pl = tq / (G * NG), g = (tq / NG) % G, gi = tq % NG;
         const float* src = pl ? sm.su[g] : sm.sq[g];
         float s = 0.f, off = 0.f;
         if (pl == 0 || NRES > 0) {
