@@ -94,11 +94,13 @@ __device__ __forceinline__ h8 b_magic_crumbs(uint32_t w) {
     return pack_h8(and_or(w, 0x00030003u), and_or(w, 0x000C000Cu), and_or(w, 0x00300030u), and_or(w, 0x00C000C0u));
 }
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// the (offset, scale) pair of a group: bytes 2 p and 2 p + 1 of a metadata word, one conversion
-__device__ __forceinline__ f32x2 fp8_pair(uint32_t word, int p) {
-    return p ? __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true) : __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+__device__ __forceinline__ float fp8(uint32_t word, int byte) {
+    switch (byte) {
+        case 0: return __builtin_amdgcn_cvt_f32_fp8((int)word, 0);
+        case 1: return __builtin_amdgcn_cvt_f32_fp8((int)word, 1);
+        case 2: return __builtin_amdgcn_cvt_f32_fp8((int)word, 2);
+        default: return __builtin_amdgcn_cvt_f32_fp8((int)word, 3);
+    }
 }
 
 __device__ __forceinline__ f32x4 mfma(h8 a, h8 b, f32x4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
@@ -394,8 +396,7 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
                 const uint32_t mw = gi < 2 ? am.x : am.y;
-                const f32x2 zs = fp8_pair(mw, gi & 1);
-                part_a += zs.x * Qs[gi] + zs.y * (da[gi] - Ca[gi]);
+                part_a += fp8(mw, 2 * (gi & 1)) * Qs[gi] + fp8(mw, 2 * (gi & 1) + 1) * (da[gi] - Ca[gi]);
             }
             float coef = 1.f, part_r = 0.f;
             if constexpr (NRES > 0) {
@@ -403,8 +404,7 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi) {
                     const uint32_t mw = gi < 2 ? rm.x : rm.y;
-                    const f32x2 zs = fp8_pair(mw, gi & 1);
-                    part_r += zs.x * Us[gi] + zs.y * (dr[gi] - Cu[gi]);
+                    part_r += fp8(mw, 2 * (gi & 1)) * Us[gi] + fp8(mw, 2 * (gi & 1) + 1) * (dr[gi] - Cu[gi]);
                 }
                 coef = bf16_to_f32(*reinterpret_cast<const uint16_t*>(sp + RES_OFF + RC + RM + t * 2));
             }
@@ -466,8 +466,7 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
                 const uint32_t mw = gi < 2 ? vam.x : vam.y;
-                const f32x2 zsa = fp8_pair(mw, gi & 1);
-                const float za = zsa.x, sa = zsa.y;
+                const float za = fp8(mw, 2 * (gi & 1)), sa = fp8(mw, 2 * (gi & 1) + 1);
                 zA[gi] += pc * za;
                 const float wa = pc * sa * mult;
                 // the anchor weight as two FP16 terms (about 22 significant bits): the anchor part
@@ -479,8 +478,7 @@ __global__ __launch_bounds__(NT) void rq_decode_gqa_kernel(DecodeArgs a) {
                 }
                 if constexpr (NRES > 0) {
                     const uint32_t rw = gi < 2 ? vrm.x : vrm.y;
-                    const f32x2 zsr = fp8_pair(rw, gi & 1);
-                    const float zr = zsr.x, sr = zsr.y;
+                    const float zr = fp8(rw, 2 * (gi & 1)), sr = fp8(rw, 2 * (gi & 1) + 1);
                     zR[gi] += p * zr;
                     const float wr = p * sr * mult;
                     if (q_ok) sm.wbuf[w][2][gi][qs][pos] = (_Float16)wr;
