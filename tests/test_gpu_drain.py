@@ -95,3 +95,31 @@ def test_drain_through_block_tables():
     B.rq_quantize_token(cfg, flat, kv, 0, pos, inp.rot, batch, N_TOK, pending_strides=pending_strides(kv))
     torch.cuda.synchronize()
     assert np.array_equal(gather(pool.cpu().numpy(), table_np, ocfg, bb), flat.cpu().numpy())
+
+
+def test_drain_past_max_ctx():
+    """Tokens whose slot lies past max_ctx are skipped by the LDS drain kernel as by the
+    one-loop kernel: 8 tokens from slot max_ctx - 3, in one call and one call per token, give
+    the same bytes, and the slots before the first token stay untouched."""
+    from looped_transformer_decode_amd import binding as B
+    wl, batch, hkv = CASES["d128g32_L4"]
+    wl = wl.with_(batch=batch, ctx=N_TOK, chained=False, n_kv_heads=hkv, n_q_heads=hkv)
+    inp = synth.generate(wl, seed=608, device="cuda")
+    cfg = B.config_for(wl)
+    p0 = cfg.max_ctx - 3
+    one_call = torch.full((B.rq_cache_bytes(cfg),), 0x5A, dtype=torch.uint8, device="cuda")
+    per_tok = one_call.clone()
+    untouched = one_call.clone()
+    kv = inp.kv[0]
+    say(f"[drain] past max_ctx: first slot {p0}, max_ctx {cfg.max_ctx}")
+    B.rq_quantize_token(cfg, one_call, kv, 0, torch.full((batch,), p0, dtype=torch.int32, device="cuda"), inp.rot,
+                        batch, N_TOK, pending_strides=pending_strides(kv))
+    for t in range(N_TOK):
+        kt = inp.kv[0, :, :, :, :, t:t + 1]
+        B.rq_quantize_token(cfg, per_tok, kt, 0, torch.full((batch,), p0 + t, dtype=torch.int32, device="cuda"),
+                            inp.rot, batch, 1, pending_strides=pending_strides(kt))
+    torch.cuda.synchronize()
+    assert torch.equal(one_call, per_tok)
+    # only the three token rows at slots p0 .. max_ctx - 1 changed: the rest of every tile keeps 0x5A
+    changed = int((one_call != untouched).sum())
+    assert 0 < changed <= 3 * batch * hkv * 2 * (72 + 3 * (40 + 2)), changed
