@@ -421,44 +421,62 @@ __device__ __forceinline__ uint32_t lanes_or(uint32_t v) {
     }
 }
 
-// Quantize the CPL channels of this lane (channels CPL*lane + c of one token, one wave per
-// token) with groups of G channels; store codes and metadata into token row jj of `tile`
-// when `store`; return the dequantized values.
-template <int G, int CPL, int BITS>
-__device__ __forceinline__ void quantize_row(const double (&x)[CPL], double (&xhat)[CPL], uint8_t* tile, int row_bytes,
-                                             int m_row, int jj, bool store, int lane) {
+// Quantize the CPL channels of this lane (channels CPL*lane + c) of S tokens at once (one
+// wave holds S tokens; their chains are independent, so the compiler interleaves them) with
+// groups of G channels; store codes and metadata into token row jj[t] of tile[t] where
+// store[t]; return the dequantized values.
+template <int G, int CPL, int BITS, int S>
+__device__ __forceinline__ void quantize_rows(const double (&x)[S][CPL], double (&xhat)[S][CPL], uint8_t* const (&tile)[S],
+                                              int row_bytes, int m_row, const int (&jj)[S], const bool (&store)[S],
+                                              int lane) {
     constexpr int GL = G / CPL;                       // lanes per group
-    double lo = x[0], hi = x[0];
-#pragma unroll
-    for (int c = 1; c < CPL; ++c) {
-        lo = fmin(lo, x[c]);
-        hi = fmax(hi, x[c]);
-    }
-    lo = lanes_reduce<GL>(lo, [](double p, double q) { return fmin(p, q); });
-    hi = lanes_reduce<GL>(hi, [](double p, double q) { return fmax(p, q); });
-    const QOut o = group_params(lo, hi, BITS);
     constexpr int PER = 32 / BITS;                    // channels per code word
-    uint32_t word = 0;
+    double lo[S], hi[S];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        const uint32_t code = group_code(x[c], o, BITS);
-        xhat[c] = o.z + (double)code * o.s;
-        word |= code << (((CPL * lane + c) % PER) * BITS);
+    for (int t = 0; t < S; ++t) {
+        lo[t] = hi[t] = x[t][0];
+#pragma unroll
+        for (int c = 1; c < CPL; ++c) {
+            lo[t] = fmin(lo[t], x[t][c]);
+            hi[t] = fmax(hi[t], x[t][c]);
+        }
     }
-    word = lanes_or<PER / CPL>(word);
-    if (store) {
-        if ((CPL * lane) % PER == 0)
-            reinterpret_cast<uint32_t*>(tile + (int64_t)jj * row_bytes)[(CPL * lane) / PER] = word;
-        if ((CPL * lane) % G == 0)
-            reinterpret_cast<uint16_t*>(tile + (int64_t)kTile * row_bytes + (int64_t)jj * m_row)[(CPL * lane) / G] =
-                (uint16_t)(o.zb | (o.sb << 8));
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+        lo[t] = lanes_reduce<GL>(lo[t], [](double p, double q) { return fmin(p, q); });
+        hi[t] = lanes_reduce<GL>(hi[t], [](double p, double q) { return fmax(p, q); });
+    }
+    QOut o[S];
+    uint32_t word[S];
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+        o[t] = group_params(lo[t], hi[t], BITS);
+        word[t] = 0;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const uint32_t code = group_code(x[t][c], o[t], BITS);
+            xhat[t][c] = o[t].z + (double)code * o[t].s;
+            word[t] |= code << (((CPL * lane + c) % PER) * BITS);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < S; ++t) word[t] = lanes_or<PER / CPL>(word[t]);
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+        if (store[t]) {
+            if ((CPL * lane) % PER == 0)
+                reinterpret_cast<uint32_t*>(tile[t] + (int64_t)jj[t] * row_bytes)[(CPL * lane) / PER] = word[t];
+            if ((CPL * lane) % G == 0)
+                reinterpret_cast<uint16_t*>(tile[t] + (int64_t)kTile * row_bytes + (int64_t)jj[t] * m_row)[(CPL * lane) / G] =
+                    (uint16_t)(o[t].zb | (o[t].sb << 8));
+        }
     }
 }
 
 // LB = min(L - 1, 3) residual loops per product; the loop count itself comes from the
 // configuration, so one instantiation serves every group length of at least LB + 1.
 template <int D, int G, int LB>
-__global__ __launch_bounds__(bulk_threads<D>()) __attribute__((amdgpu_waves_per_eu(4))) void rq_pack_bulk_kernel(PackArgs a) {
+__global__ __launch_bounds__(bulk_threads<D>()) __attribute__((amdgpu_waves_per_eu(D == 128 ? 4 : 3))) void rq_pack_bulk_kernel(PackArgs a) {
     constexpr int kBulkThreads = bulk_threads<D>();
     constexpr int TK = kBulkTokens, NW = kBulkThreads / kWave;
     constexpr int CPL = D / kWave;                    // channels per lane
@@ -527,26 +545,53 @@ __global__ __launch_bounds__(bulk_threads<D>()) __attribute__((amdgpu_waves_per_
     };
     const auto add = [](double p, double q) { return p + q; };
 
-    // ---- anchors: one token per wave
+    // the S = TK / NW tokens of this wave (tokens t NW + w), taken SB at a time side by side
+    constexpr int S = TK / NW, SB = S < 2 ? S : 2;
+    int jjs[S], tiles[S];
+    bool oks[S];
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+        const int tok = t * NW + w;
+        oks[t] = valid(tok);                          // wave-uniform
+        const int slot = oks[t] ? p0 + tok : 0;
+        tiles[t] = slot / kTile;
+        jjs[t] = slot % kTile;
+    }
+
+    // ---- anchors, SB of the wave's tokens side by side
     stage_x(L - 1, 1);
     __syncthreads();
-    for (int s = 0; s < TK / NW; ++s) {
-        const int tok = s * NW + w;
-        const bool ok = valid(tok);                   // wave-uniform
-        const int slot = ok ? p0 + tok : 0, tile = slot / kTile, jj = slot % kTile;
-        double xa[CPL], xh[CPL];
-        load_x(0, tok, xa);
-        uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + L - 1, tile);
-        if (Gm.ba == 4) quantize_row<G, CPL, 4>(xa, xh, pl, Gm.a_row, Gm.m_row, jj, ok, lane);
-        else quantize_row<G, CPL, 2>(xa, xh, pl, Gm.a_row, Gm.m_row, jj, ok, lane);
-        double ss = 0.0;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            ss = fma(xh[c], xh[c], ss);
-            ah[tok][CPL * lane + c] = xh[c];
+    for (int tb = 0; tb < S; tb += SB) {
+        double xa[SB][CPL], xh[SB][CPL];
+        uint8_t* pl[SB];
+        int jb[SB];
+        bool ob[SB];
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+            load_x(0, (tb + u) * NW + w, xa[u]);
+            pl[u] = a.cache + Gm.tile_offset(b, h, x, loop0 + L - 1, tiles[tb + u]);
+            jb[u] = jjs[tb + u];
+            ob[u] = oks[tb + u];
         }
-        ss = lanes_reduce<kWave>(ss, add);
-        if (lane == 0) aa[tok] = ss;
+        if (Gm.ba == 4) quantize_rows<G, CPL, 4, SB>(xa, xh, pl, Gm.a_row, Gm.m_row, jb, ob, lane);
+        else quantize_rows<G, CPL, 2, SB>(xa, xh, pl, Gm.a_row, Gm.m_row, jb, ob, lane);
+        double ss[SB];
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+            ss[u] = 0.0;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                ss[u] = fma(xh[u][c], xh[u][c], ss[u]);
+                ah[(tb + u) * NW + w][CPL * lane + c] = xh[u][c];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < SB; ++u) ss[u] = lanes_reduce<kWave>(ss[u], add);
+        if (lane == 0) {
+#pragma unroll
+            for (int u = 0; u < SB; ++u) aa[(tb + u) * NW + w] = ss[u];
+        }
     }
 
     for (int lb0 = 0; lb0 < LR; lb0 += LB) {
@@ -554,37 +599,57 @@ __global__ __launch_bounds__(bulk_threads<D>()) __attribute__((amdgpu_waves_per_
         __syncthreads();                              // ah and aa written; xs and yt free
         stage_x(lb0, LB < LR - lb0 ? LB : LR - lb0);
         __syncthreads();
-        for (int s = 0; s < TK / NW; ++s) {
-            const int tok = s * NW + w;
-            const bool ok = valid(tok);
-            const int slot = ok ? p0 + tok : 0, tile = slot / kTile, jj = slot % kTile;
-            double xh[CPL];
+        {
+            // the dot products of SB tokens' loops first, then their reductions side by side;
+            // the inputs are read again from LDS for y, rather than held in registers
+            const auto lok = [&](int t, int li) { return oks[t] && lb0 + li < LR; };
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) xh[c] = ah[tok][CPL * lane + c];
-            const double na = aa[tok];
+            for (int tb = 0; tb < S; tb += SB) {
+                double dot[SB][LB];
 #pragma unroll
-            for (int li = 0; li < LB; ++li) {
-                const int l = lb0 + li;
-                const bool lok = ok && l < LR;
-                double xl[CPL];
-                load_x(li, tok, xl);
-                if (!lok) {
+                for (int u = 0; u < SB; ++u) {
+                    const int tok = (tb + u) * NW + w;
+                    double xh[CPL];
 #pragma unroll
-                    for (int c = 0; c < CPL; ++c) xl[c] = 0.0;
-                }
-                double dot = 0.0;
+                    for (int c = 0; c < CPL; ++c) xh[c] = ah[tok][CPL * lane + c];
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) dot = fma(xl[c], norm_ratio ? xl[c] : xh[c], dot);
-                dot = lanes_reduce<kWave>(dot, add);
-                const double qn = dot / na;
-                const double cl = bf16_round(na > 0.0 ? (norm_ratio ? sqrt(qn) : qn) : 0.0);
-                if (lok && lane == 0) {
-                    uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + l, tile);
-                    reinterpret_cast<uint16_t*>(pl + (int64_t)kTile * (Gm.rrow(l) + Gm.m_row))[jj] =
-                        (uint16_t)(__float_as_uint((float)cl) >> 16);
+                    for (int li = 0; li < LB; ++li) {
+                        double xl[CPL];
+                        load_x(li, tok, xl);
+                        dot[u][li] = 0.0;
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c) dot[u][li] = fma(xl[c], norm_ratio ? xl[c] : xh[c], dot[u][li]);
+                        if (!lok(tb + u, li)) dot[u][li] = 0.0;
+                    }
                 }
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) yt[tok * LB + li][CPL * lane + c] = xl[c] - cl * xh[c];
+                for (int u = 0; u < SB; ++u)
+#pragma unroll
+                    for (int li = 0; li < LB; ++li) dot[u][li] = lanes_reduce<kWave>(dot[u][li], add);
+#pragma unroll
+                for (int u = 0; u < SB; ++u) {
+                    const int t = tb + u, tok = t * NW + w;
+                    const double na = aa[tok];
+                    double xh[CPL];
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) xh[c] = ah[tok][CPL * lane + c];
+#pragma unroll
+                    for (int li = 0; li < LB; ++li) {
+                        const int l = lb0 + li;
+                        const double qn = dot[u][li] / na;
+                        const double cl = bf16_round(na > 0.0 ? (norm_ratio ? sqrt(qn) : qn) : 0.0);
+                        if (lok(t, li) && lane == 0) {
+                            uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + l, tiles[t]);
+                            reinterpret_cast<uint16_t*>(pl + (int64_t)kTile * (Gm.rrow(l) + Gm.m_row))[jjs[t]] =
+                                (uint16_t)(__float_as_uint((float)cl) >> 16);
+                        }
+                        double xl[CPL];
+                        load_x(li, tok, xl);
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c)
+                            yt[tok * LB + li][CPL * lane + c] = (lok(t, li) ? xl[c] : 0.0) - cl * xh[c];
+                    }
+                }
             }
         }
         __syncthreads();
@@ -592,8 +657,9 @@ __global__ __launch_bounds__(bulk_threads<D>()) __attribute__((amdgpu_waves_per_
         // takes the 16 rows 16 w .. of R and every 16-column tile of Y.  The sum over the
         // channels is split over the four K slots of the product, slot kq taking channels
         // (D/4) kq + s at step s, so that each lane reads its R row and its Y column as
-        // contiguous runs (R from registers, Y from LDS).  Lane layout (measured with an in-bounds probe): A[i][k] in lane
-        // i + 16 k, B[k][j] in lane j + 16 k, D[i][j] in lane j + 16 (i % 4), element i / 4.
+        // contiguous runs (R loaded into registers, Y from LDS).  Lane layout (measured with
+        // an in-bounds probe): A[i][k] in lane i + 16 k, B[k][j] in lane j + 16 k, D[i][j] in
+        // lane j + 16 (i % 4), element i / 4.
         {
             f32x4 ra[D / 16];
 #pragma unroll
@@ -622,21 +688,27 @@ __global__ __launch_bounds__(bulk_threads<D>()) __attribute__((amdgpu_waves_per_
                 for (int e = 0; e < 4; ++e) yt[16 * c + i16][16 * w + 4 * e + kq] = acc[c][e];
         }
         __syncthreads();
-        // ---- residual codes, one token per wave
-        for (int s = 0; s < TK / NW; ++s) {
-            const int tok = s * NW + w;
-            const bool ok = valid(tok);
-            const int slot = ok ? p0 + tok : 0, tile = slot / kTile, jj = slot % kTile;
+        // ---- residual codes, SB of the wave's tokens side by side
 #pragma unroll
-            for (int li = 0; li < LB; ++li) {
-                const int l = lb0 + li;
-                double r[CPL], rh[CPL];
+        for (int li = 0; li < LB; ++li) {
+            const int l = lb0 + li;
+            const int lq = l < LR ? l : 0;                // a loop past the group's last is not stored
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) r[c] = yt[tok * LB + li][CPL * lane + c];
-                const int lq = l < LR ? l : 0;            // a loop past the group's last is not stored
-                uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + lq, tile);
-                if (Gm.rbits(lq) == 4) quantize_row<G, CPL, 4>(r, rh, pl, Gm.rrow(lq), Gm.m_row, jj, ok && l < LR, lane);
-                else quantize_row<G, CPL, 2>(r, rh, pl, Gm.rrow(lq), Gm.m_row, jj, ok && l < LR, lane);
+            for (int tb = 0; tb < S; tb += SB) {
+                double r[SB][CPL], rh[SB][CPL];
+                uint8_t* pl[SB];
+                int jb[SB];
+                bool st[SB];
+#pragma unroll
+                for (int u = 0; u < SB; ++u) {
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) r[u][c] = yt[((tb + u) * NW + w) * LB + li][CPL * lane + c];
+                    pl[u] = a.cache + Gm.tile_offset(b, h, x, loop0 + lq, tiles[tb + u]);
+                    jb[u] = jjs[tb + u];
+                    st[u] = oks[tb + u] && l < LR;
+                }
+                if (Gm.rbits(lq) == 4) quantize_rows<G, CPL, 4, SB>(r, rh, pl, Gm.rrow(lq), Gm.m_row, jb, st, lane);
+                else quantize_rows<G, CPL, 2, SB>(r, rh, pl, Gm.rrow(lq), Gm.m_row, jb, st, lane);
             }
         }
     }
