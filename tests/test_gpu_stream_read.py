@@ -1,7 +1,7 @@
 """The measuring stick rq_stream_read reads every 16-byte unit of the buffer it is given once:
 with the sink cleared, the XOR of all sink words equals the XOR of every 32-bit word of the
 buffer (random contents, so a unit skipped or read twice changes the fold).  Sizes cover one
-unit, a ragged tail within a workgroup's slab, and a buffer split over the most workgroups."""
+unit, a ragged tail within a workgroup's slab, and a buffer split over every workgroup (two per CU)."""
 import numpy as np
 import pytest
 import torch
