@@ -319,7 +319,7 @@ rq_status rq_kv_project(const rq_config* cfg, const uint16_t* x, int64_t x_strid
 typedef struct rq_w4a4_config {
     int32_t in_features;      /* K: 1024, 2048, 3072 or 4096 */
     int32_t out_features;     /* N: a positive multiple of 16 */
-    int32_t max_tokens;       /* tokens per call: 1..16 */
+    int32_t max_tokens;       /* tokens per call: 1..64 (the product runs in tiles of 16) */
 } rq_w4a4_config;
 
 /* Bytes of one packed weight matrix (N K / 2 + N K / 16), of max_tokens activation rows

@@ -103,6 +103,8 @@ struct AArgs {
 };
 
 constexpr int TQ = 1;           // tokens per activation-quantizer workgroup
+constexpr int TM = 16;          // tokens per GEMM workgroup (one MFMA tile of rows)
+constexpr int kMaxTokens = 64;
 
 // Sums over the 256 threads of two values in a fixed order, both reduced side by side (every
 // thread gets the results): DPP and lane swaps inside each wave, then the 4 wave sums in order.
@@ -335,8 +337,20 @@ __device__ __forceinline__ f32x4 mfma(h8 a, h8 b, f32x4 c) { return __builtin_am
 // step are summed in LDS (two buffers, one barrier per step).  MFMA operands: A row = token
 // (lane l16), B column = output row of the tile (lane l16), K = the 32 channels of a group.
 template <int GW, int NW, int NTW, bool RES>
-__global__ __launch_bounds__(NW * 64) void gemm_kernel(GArgs a) {
+__global__ __launch_bounds__(NW * 64) void gemm_kernel(GArgs g) {
     constexpr int NQ = GW / 4;                  // weight quads per wave
+    // this workgroup's tile of up to 16 tokens (blockIdx.y): the arguments shifted to its rows
+    GArgs a = g;
+    {
+        const int m0 = TM * blockIdx.y;
+        a.m = min(TM, g.m - m0);
+        a.act += (size_t)m0 * act_row_bytes(g.k);
+        a.xsum += (size_t)m0 * (g.k / GS);
+        a.c += m0;
+        if (a.y0_in) a.y0_in += (size_t)m0 * g.n;
+        if (a.y0_out) a.y0_out += (size_t)m0 * g.n;
+        a.y += (size_t)m0 * g.n;
+    }
     static_assert(GW % 4 == 0 && GW <= 16, "groups per wave");
     __shared__ f32x4 red[2][NTW][NW][64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l16 = lane & 15, kg = lane >> 4;
@@ -497,13 +511,17 @@ static int w4_cu_count() {
 }
 
 // two tiles per step while the registers allow (they share the activation operands), one
-// at K >= 3072
+// at K >= 3072.  More than 16 tokens: one row of workgroups per 16-token tile (each reads
+// the weights; the tiles after the first mostly from the Infinity Cache), about one
+// workgroup per CU in all.
 template <int GW, int NW>
 static void launch_gemm(const GArgs& g, bool res, hipStream_t st) {
     constexpr int NTW = GW <= 8 ? 2 : 1;
     const int steps = (g.n / TN + NTW - 1) / NTW;
+    const int tiles_m = (g.m + TM - 1) / TM;
     const int cus = w4_cu_count();
-    const dim3 grid(steps < cus ? steps : cus);
+    const int per_tile = cus / tiles_m > 0 ? cus / tiles_m : 1;
+    const dim3 grid(steps < per_tile ? steps : per_tile, tiles_m);
     if (res) hipLaunchKernelGGL((gemm_kernel<GW, NW, NTW, true>), grid, dim3(NW * 64), 0, st, g);
     else hipLaunchKernelGGL((gemm_kernel<GW, NW, NTW, false>), grid, dim3(NW * 64), 0, st, g);
 }
@@ -514,7 +532,7 @@ static bool w4_cfg_ok(const rq_w4a4_config* cfg) {
     if (!cfg) return false;
     const int k = cfg->in_features;
     return (k == 1024 || k == 2048 || k == 3072 || k == 4096) && cfg->out_features > 0 &&
-           cfg->out_features % w4::TN == 0 && cfg->max_tokens >= 1 && cfg->max_tokens <= 16;
+           cfg->out_features % w4::TN == 0 && cfg->max_tokens >= 1 && cfg->max_tokens <= w4::kMaxTokens;
 }
 static bool w4_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 static size_t w4_round256(size_t b) { return (b + 255) & ~(size_t)255; }

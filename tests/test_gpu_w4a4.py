@@ -32,6 +32,9 @@ CASES = {
     "k2048_n128_m16": (2048, 128, 16, 4),
     "k3072_n48_m1": (3072, 48, 1, 2),
     "k4096_n32_m7": (4096, 32, 7, 3),
+    # more than one 16-token tile of the product
+    "k2048_n64_m40": (2048, 64, 40, 3),
+    "k1024_n48_m64": (1024, 48, 64, 2),
 }
 
 
