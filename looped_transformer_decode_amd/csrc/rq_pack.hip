@@ -279,14 +279,14 @@ __global__ __launch_bounds__(2 * D) __attribute__((amdgpu_waves_per_eu(SPLIT ? 3
 // The kernel above holds half a row of R per thread in registers, which allows at most
 // three of its workgroups per CU.  Here one workgroup of 2 D threads per (token, batch row,
 // KV head, K|V) stages R in LDS (66 KB at d = 128, so two workgroups per CU) and takes every
-// residual loop of the group, rotated side by side: the Ouro-sized drain at batch 16 is 512
-// workgroups, one round on 256 CUs, where one loop per workgroup needs 1536.  The anchor
-// quantizer, the c reductions, the rotation (the same two chains per half row, the pair
-// adding its halves) and the quantizers are the float64 steps of the kernel above in the
-// same order, so the bytes it writes are identical.
+// residual loop of the group (quantized side by side, rotated one loop at a time): the
+// Ouro-sized drain at batch 16 is 512 workgroups, one round on 256 CUs, where one loop per
+// workgroup needs 1536.  The anchor quantizer, the c reductions, the rotation (the same two
+// chains per half row, the pair adding its halves) and the quantizers are the float64 steps
+// of the kernel above in the same order, so the bytes it writes are identical.
 // R rows are padded to d + 4 floats, so the 8 channels of a 16-lane group of a 128-bit LDS
 // read start in 8 different 4-bank groups (the two halves of a channel share one: a two-way
-// conflict on the R reads, which are 1/7 of the rotation's LDS reads at three loops).
+// conflict on the R reads, which are a third of the rotation's LDS reads).
 template <int D>
 __device__ __forceinline__ int rlds_slot(int row, int c4) { return row * ((D + 4) / 4) + c4; }
 
