@@ -317,7 +317,10 @@ rq_status rq_kv_project(const rq_config* cfg, const uint16_t* x, int64_t x_strid
  * Activations: one row per token of K/2 code bytes (channel 2 i in the low nibble of byte
  * i, 2 i + 1 in the high one) then K/16 metadata bytes (offset, scale per group). */
 typedef struct rq_w4a4_config {
-    int32_t in_features;      /* K: 1024, 2048, 3072 or 4096 */
+    int32_t in_features;      /* K: a multiple of 128 up to 16384 (1024, 2048, 3072 and 4096 take
+                                 the fastest path; others run in slices of up to 4096 channels
+                                 whose partial products a second kernel adds, which the
+                                 workspace holds) */
     int32_t out_features;     /* N: a positive multiple of 16 */
     int32_t max_tokens;       /* tokens per call: 1..64 (the product runs in tiles of 16) */
 } rq_w4a4_config;
@@ -356,7 +359,8 @@ rq_status rq_w4_quantize_weights(const rq_w4a4_config* cfg, const uint16_t* w, i
  * Arithmetic: the quantizers in float64 (codes as a float64 reference except inexact
  * near-ties; c within one BF16 step), the product on the matrix cores from exact FP16
  * operands with float32 accumulation.  Alignment: weights, x, anchor, act, rot, workspace
- * 16-byte aligned; y, y0 4-byte aligned.  Two kernels are enqueued. */
+ * 16-byte aligned; y, y0 4-byte aligned.  Two kernels are enqueued (three when K is above
+ * 4096 and not 1024, 2048, 3072 or 4096). */
 rq_status rq_w4a4_linear(const rq_w4a4_config* cfg, const void* weights, const uint16_t* x, int64_t x_stride,
                          int32_t loop_local, void* anchor, void* act, const float* rot, float* c_out,
                          float* y0, float* y, int32_t n_tokens, void* workspace, size_t workspace_bytes,

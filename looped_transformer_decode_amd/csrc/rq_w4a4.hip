@@ -105,6 +105,7 @@ struct AArgs {
 constexpr int TQ = 1;           // tokens per activation-quantizer workgroup
 constexpr int TM = 16;          // tokens per GEMM workgroup (one MFMA tile of rows)
 constexpr int kMaxTokens = 64;
+constexpr int kMaxK = 16384;    // input channels
 
 // Sums over the 256 threads of two values in a fixed order, both reduced side by side (every
 // thread gets the results): DPP and lane swaps inside each wave, then the 4 wave sums in order.
@@ -137,9 +138,9 @@ __device__ __forceinline__ void block_sum256(double (&u)[TQ], double (&v)[TQ], d
 // so every block gets the same c) and rotates its block of the residual (two threads per
 // output, 64 float64 products each).  The quantizer runs 16 threads per group, two values
 // each.
-template <bool RES>
+template <bool RES, int CST>
 __global__ __launch_bounds__(256) void quantize_act_kernel(AArgs a) {
-    constexpr int GMAX = 4096 / GS;
+    constexpr int GMAX = kMaxK / GS;
     __shared__ double ys[TQ][RB];               // the block's values (x, or x - c a_hat)
     __shared__ double rs[RES ? TQ : 1][RES ? RB : 1];          // the rotated residual
     __shared__ double za[RES ? TQ : 1][RES ? GMAX : 1];        // anchor offsets and scales
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(256) void quantize_act_kernel(AArgs a) {
     // every global load first, all in flight together: R, the anchor metadata, the row
     // chunks for c (8 channels per step), and the block's own values
     constexpr int RV = RES ? RB / 2 / 4 : 1;                     // float4 of R per thread: half a row
-    constexpr int CSTEP = RES ? 2 : 1;                           // row steps per token (K <= 4096)
+    constexpr int CSTEP = RES ? CST : 1;                         // row steps of 2048 channels per token
     float4 rv[RV];
     uint32_t mbv[RES ? 2 : 1];
     uint4 xc[TQ][CSTEP];
@@ -301,6 +302,7 @@ struct GArgs {
     const float* y0_in;         // residual loops: the anchor product
     float* y0_out;              // anchor loop: the product kept for the group's later loops
     float* y;                   // [M][N]
+    float* part;                // split K: [splits][M][N] partial sums (the epilogue then runs apart), else null
     int m, n, k;
 };
 
@@ -336,7 +338,10 @@ __device__ __forceinline__ f32x4 mfma(h8 a, h8 b, f32x4 c) { return __builtin_am
 // second register buffer while it multiplies the current one; the waves' products of a
 // step are summed in LDS (two buffers, one barrier per step).  MFMA operands: A row = token
 // (lane l16), B column = output row of the tile (lane l16), K = the 32 channels of a group.
-template <int GW, int NW, int NTW, bool RES>
+// MASK: a general K.  The workgroups of split blockIdx.z take the NW NQ quads from quad
+// blockIdx.z NW NQ on; a wave's quads past the row are read at the last quad (in bounds) and
+// multiplied by zero activation operands.
+template <int GW, int NW, int NTW, bool RES, bool MASK>
 __global__ __launch_bounds__(NW * 64) void gemm_kernel(GArgs g) {
     constexpr int NQ = GW / 4;                  // weight quads per wave
     // this workgroup's tile of up to 16 tokens (blockIdx.y): the arguments shifted to its rows
@@ -350,12 +355,18 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GArgs g) {
         if (a.y0_in) a.y0_in += (size_t)m0 * g.n;
         if (a.y0_out) a.y0_out += (size_t)m0 * g.n;
         a.y += (size_t)m0 * g.n;
+        if (a.part) a.part += ((size_t)blockIdx.z * g.m + m0) * g.n;
     }
     static_assert(GW % 4 == 0 && GW <= 16, "groups per wave");
     __shared__ f32x4 red[2][NTW][NW][64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l16 = lane & 15, kg = lane >> 4;
     const int tiles = a.n / TN, K = a.k, G = K / GS;
     const int pairs = (tiles + NTW - 1) / NTW;
+    const int KQ = K / RB;                      // quads of a row
+    const int wq0 = (MASK ? (int)blockIdx.z * NW * NQ : 0) + w * NQ;   // first quad of this wave
+    const auto quad = [&](int q) { return MASK ? min(wq0 + q, KQ - 1) : wq0 + q; };
+    const auto grp = [&](int gl) { return MASK ? min(4 * wq0 + gl, G - 1) : 4 * wq0 + gl; };
+    const auto gvalid = [&](int gl) { return !MASK || 4 * wq0 + gl < G; };
 
     // the weights of pair p: row l16 of each tile, quarter kg, 4 groups per quad (a missing
     // second tile reads the first again)
@@ -364,11 +375,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GArgs g) {
         const bool two = nt0 + 1 < tiles;
 #pragma unroll
         for (int u = 0; u < NTW; ++u) {
-            const uint8_t* wt = a.w + ((size_t)(two ? nt0 + u : nt0) * (K / RB) + (size_t)w * NQ) * QB;
+            const uint8_t* wt = a.w + (size_t)(two ? nt0 + u : nt0) * KQ * QB;
 #pragma unroll
             for (int q = 0; q < NQ; ++q) {
-                wc[u][q] = *reinterpret_cast<const u4*>(wt + q * QB + 16 * (16 * kg + l16));
-                wm[u][q] = *reinterpret_cast<const uint2*>(wt + q * QB + 1024 + 8 * l16);
+                const uint8_t* wq = wt + (size_t)quad(q) * QB;
+                wc[u][q] = *reinterpret_cast<const u4*>(wq + 16 * (16 * kg + l16));
+                wm[u][q] = *reinterpret_cast<const uint2*>(wq + 1024 + 8 * l16);
             }
         }
     };
@@ -386,20 +398,21 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GArgs g) {
     uint32_t aw[GW], am[GW];
 #pragma unroll
     for (int gl = 0; gl < GW; ++gl) {
-        aw[gl] = *reinterpret_cast<const uint32_t*>(arow + 16 * (w * GW + gl) + 4 * kg);
-        am[gl] = reinterpret_cast<const uint16_t*>(arow + K / 2)[w * GW + gl];
+        aw[gl] = *reinterpret_cast<const uint32_t*>(arow + 16 * grp(gl) + 4 * kg);
+        am[gl] = reinterpret_cast<const uint16_t*>(arow + K / 2)[grp(gl)];
     }
     float xq[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xq[j] = a.xsum[(size_t)mrow * G + w * GW + min(4 * kg + j, GW - 1)];
+    for (int j = 0; j < 4; ++j) xq[j] = a.xsum[(size_t)mrow * G + grp(min(4 * kg + j, GW - 1))];
     // s_x q_x as exact FP16 operands; z_x kept as one packed pair per group and broadcast
     // into the 8-wide operand at each use (fewer registers than holding the operands)
     h8 a1[GW];
     uint32_t zx2[GW];
 #pragma unroll
     for (int gl = 0; gl < GW; ++gl) {
-        const h2 zs = meta_h2(mok ? am[gl] : 0u);
-        a1[gl] = scaled_codes(mok ? aw[gl] : 0u, sv_of(zs.y), cv_of(zs.y));
+        const bool ok = mok && gvalid(gl);
+        const h2 zs = meta_h2(ok ? am[gl] : 0u);
+        a1[gl] = scaled_codes(ok ? aw[gl] : 0u, sv_of(zs.y), cv_of(zs.y));
         zx2[gl] = __builtin_bit_cast(uint32_t, (h2){zs.x, zs.x});
     }
     // z_w X terms: K' position 8 kg + e <-> local group 4 kg + e / 2, FP16 hi (e even) / lo
@@ -408,7 +421,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GArgs g) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int gl = 4 * kg + e / 2;
-        const float xv = (gl < GW && mok) ? xq[e / 2] * (1.f / 32.f) : 0.f;
+        const float xv = (gl < GW && mok && gvalid(gl)) ? xq[e / 2] * (1.f / 32.f) : 0.f;
         const _Float16 hi = (_Float16)xv;
         ax[e] = (e & 1) ? (_Float16)(xv - (float)hi) : hi;
     }
@@ -420,7 +433,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GArgs g) {
         const bool storer = w < NTW && (w == 0 || two);
         float ce[4] = {0.f, 0.f, 0.f, 0.f}, y0e[4] = {0.f, 0.f, 0.f, 0.f};
         if constexpr (RES) {
-            if (storer) {
+            if (storer && !a.part) {
                 const int n = (nt0 + w) * TN + l16;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -477,7 +490,9 @@ __global__ __launch_bounds__(NW * 64) void gemm_kernel(GArgs g) {
                 const int m = 4 * kg + r;
                 if (m < a.m) {
                     const size_t o = (size_t)m * a.n + n;
-                    if constexpr (RES) {
+                    if (a.part) {
+                        a.part[o] = v[r];
+                    } else if constexpr (RES) {
                         a.y[o] = ce[r] * y0e[r] + v[r];
                     } else {
                         a.y[o] = v[r];
@@ -513,25 +528,48 @@ static int w4_cu_count() {
 // two tiles per step while the registers allow (they share the activation operands), one
 // at K >= 3072.  More than 16 tokens: one row of workgroups per 16-token tile (each reads
 // the weights; the tiles after the first mostly from the Infinity Cache), about one
-// workgroup per CU in all.
-template <int GW, int NW>
-static void launch_gemm(const GArgs& g, bool res, hipStream_t st) {
+// workgroup per CU in all.  A general K: `splits` slices of up to 4096 channels
+// (blockIdx.z), whose partial products a second kernel adds in order.
+template <int GW, int NW, bool MASK>
+static void launch_gemm(const GArgs& g, bool res, int splits, hipStream_t st) {
     constexpr int NTW = GW <= 8 ? 2 : 1;
     const int steps = (g.n / TN + NTW - 1) / NTW;
     const int tiles_m = (g.m + TM - 1) / TM;
     const int cus = w4_cu_count();
-    const int per_tile = cus / tiles_m > 0 ? cus / tiles_m : 1;
-    const dim3 grid(steps < per_tile ? steps : per_tile, tiles_m);
-    if (res) hipLaunchKernelGGL((gemm_kernel<GW, NW, NTW, true>), grid, dim3(NW * 64), 0, st, g);
-    else hipLaunchKernelGGL((gemm_kernel<GW, NW, NTW, false>), grid, dim3(NW * 64), 0, st, g);
+    const int per_tile = cus / (tiles_m * splits) > 0 ? cus / (tiles_m * splits) : 1;
+    const dim3 grid(steps < per_tile ? steps : per_tile, tiles_m, splits);
+    if (res) hipLaunchKernelGGL((gemm_kernel<GW, NW, NTW, true, MASK>), grid, dim3(NW * 64), 0, st, g);
+    else hipLaunchKernelGGL((gemm_kernel<GW, NW, NTW, false, MASK>), grid, dim3(NW * 64), 0, st, g);
 }
+
+// the split-K epilogue: y = c y0 + sum of the splits' partial products (in split order) at a
+// residual loop, y = y0 = the sum at the anchor loop
+template <bool RES>
+__global__ __launch_bounds__(256) void splitk_epilogue_kernel(GArgs g, int splits) {
+    const int64_t total = (int64_t)g.m * g.n;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= total) return;
+    float v = 0.f;
+    for (int s = 0; s < splits; ++s) v += g.part[s * total + i];
+    if constexpr (RES) {
+        g.y[i] = g.c[i / g.n] * g.y0_in[i] + v;
+    } else {
+        g.y[i] = v;
+        if (g.y0_out) g.y0_out[i] = v;
+    }
+}
+
+// channels per split of a general K
+constexpr int kSplitK = 4096;
+inline int splits_of(int k) { return (k + kSplitK - 1) / kSplitK; }
+inline bool fast_k(int k) { return k == 1024 || k == 2048 || k == 3072 || k == 4096; }
 
 }  // namespace w4
 
 static bool w4_cfg_ok(const rq_w4a4_config* cfg) {
     if (!cfg) return false;
     const int k = cfg->in_features;
-    return (k == 1024 || k == 2048 || k == 3072 || k == 4096) && cfg->out_features > 0 &&
+    return k >= w4::RB && k <= w4::kMaxK && k % w4::RB == 0 && cfg->out_features > 0 &&
            cfg->out_features % w4::TN == 0 && cfg->max_tokens >= 1 && cfg->max_tokens <= w4::kMaxTokens;
 }
 static bool w4_aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -553,11 +591,19 @@ size_t rq_w4a4_act_bytes(const rq_w4a4_config* cfg) {
     return (size_t)cfg->max_tokens * (cfg->in_features / 2 + cfg->in_features / 16);
 }
 
-size_t rq_w4a4_workspace_bytes(const rq_w4a4_config* cfg) {
-    if (!w4_cfg_ok(cfg)) return 0;
+// workspace: X [max_tokens][K/32], c [max_tokens], activation rows, and with a split K the
+// partial products [splits][max_tokens][N]
+static size_t w4_part_offset(const rq_w4a4_config* cfg) {
     const size_t m = cfg->max_tokens, k = cfg->in_features;
     return w4_round256(m * (k / w4::GS) * sizeof(float)) + w4_round256(m * sizeof(float)) +
            w4_round256(rq_w4a4_act_bytes(cfg));
+}
+
+size_t rq_w4a4_workspace_bytes(const rq_w4a4_config* cfg) {
+    if (!w4_cfg_ok(cfg)) return 0;
+    const int k = cfg->in_features, splits = w4::fast_k(k) ? 1 : w4::splits_of(k);
+    const size_t part = splits > 1 ? w4_round256((size_t)splits * cfg->max_tokens * cfg->out_features * sizeof(float)) : 0;
+    return w4_part_offset(cfg) + part;
 }
 
 rq_status rq_w4_quantize_weights(const rq_w4a4_config* cfg, const uint16_t* w, int64_t w_stride, const float* rot,
@@ -595,18 +641,38 @@ rq_status rq_w4a4_linear(const rq_w4a4_config* cfg, const void* weights, const u
     uint8_t* act2 = (!res && act && act != anchor) ? static_cast<uint8_t*>(act) : nullptr;
     w4::AArgs qa{x, x_stride, static_cast<const uint8_t*>(anchor), act_rows, act2, rot, cbuf, c_out, xsum, k, m};
     const dim3 qgrid(k / w4::RB, (m + w4::TQ - 1) / w4::TQ);
-    if (res) hipLaunchKernelGGL((w4::quantize_act_kernel<true>), qgrid, dim3(256), 0, stream, qa);
-    else hipLaunchKernelGGL((w4::quantize_act_kernel<false>), qgrid, dim3(256), 0, stream, qa);
+    // row steps of 2048 channels for the c sums
+    if (res) {
+        if (k <= 2048) hipLaunchKernelGGL((w4::quantize_act_kernel<true, 1>), qgrid, dim3(256), 0, stream, qa);
+        else if (k <= 4096) hipLaunchKernelGGL((w4::quantize_act_kernel<true, 2>), qgrid, dim3(256), 0, stream, qa);
+        else if (k <= 8192) hipLaunchKernelGGL((w4::quantize_act_kernel<true, 4>), qgrid, dim3(256), 0, stream, qa);
+        else hipLaunchKernelGGL((w4::quantize_act_kernel<true, 8>), qgrid, dim3(256), 0, stream, qa);
+    } else {
+        hipLaunchKernelGGL((w4::quantize_act_kernel<false, 1>), qgrid, dim3(256), 0, stream, qa);
+    }
     if (hipGetLastError() != hipSuccess) return RQ_ERR_HIP;
 
-    w4::GArgs g{static_cast<const uint8_t*>(weights), act_rows, xsum, cbuf, y0, res ? nullptr : y0, y, m,
+    w4::GArgs g{static_cast<const uint8_t*>(weights), act_rows, xsum, cbuf, y0, res ? nullptr : y0, y, nullptr, m,
                 cfg->out_features, k};
-    // 8 waves per workgroup, each covering K / 256 groups
-    switch (k) {
-        case 1024: w4::launch_gemm<4, 8>(g, res, stream); break;
-        case 2048: w4::launch_gemm<8, 8>(g, res, stream); break;
-        case 3072: w4::launch_gemm<12, 8>(g, res, stream); break;
-        default: w4::launch_gemm<16, 8>(g, res, stream); break;
+    if (w4::fast_k(k)) {
+        // 8 waves per workgroup, each covering K / 256 groups
+        switch (k) {
+            case 1024: w4::launch_gemm<4, 8, false>(g, res, 1, stream); break;
+            case 2048: w4::launch_gemm<8, 8, false>(g, res, 1, stream); break;
+            case 3072: w4::launch_gemm<12, 8, false>(g, res, 1, stream); break;
+            default: w4::launch_gemm<16, 8, false>(g, res, 1, stream); break;
+        }
+        return hipGetLastError() == hipSuccess ? RQ_OK : RQ_ERR_HIP;
+    }
+    const int splits = w4::splits_of(k);
+    if (splits > 1) g.part = reinterpret_cast<float*>(ws + w4_part_offset(cfg));
+    w4::launch_gemm<16, 8, true>(g, res, splits, stream);
+    if (hipGetLastError() != hipSuccess) return RQ_ERR_HIP;
+    if (splits > 1) {
+        const int64_t total = (int64_t)m * cfg->out_features;
+        const dim3 egrid((unsigned)((total + 255) / 256));
+        if (res) hipLaunchKernelGGL((w4::splitk_epilogue_kernel<true>), egrid, dim3(256), 0, stream, g, splits);
+        else hipLaunchKernelGGL((w4::splitk_epilogue_kernel<false>), egrid, dim3(256), 0, stream, g, splits);
     }
     return hipGetLastError() == hipSuccess ? RQ_OK : RQ_ERR_HIP;
 }

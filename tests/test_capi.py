@@ -315,3 +315,26 @@ def test_kv_project_binding_rejects_wrong_shapes(B):
         B.rq_kv_project(cfg, x, w, 0, k, k, pend, 3)
     with pytest.raises(ValueError):
         B.rq_kv_project(cfg, x.float(), w, 0, k, k, pend, 2)
+
+
+@pytest.mark.parametrize("k", [128, 640, 1024, 2048, 3072, 4096, 5632, 8192, 16384])
+def test_w4a4_sizes_follow_the_layouts(B, k):
+    """Weight and activation bytes of any K that is a multiple of 128 up to 16384 follow the
+    oracle's layouts; the workspace holds X, c, the activation rows and, for a K off the four
+    fast sizes that needs more than one 4096-channel slice, the slices' partial products."""
+    from oracle import w4a4 as W4
+    n, m = 48, 10
+    cfg = B.w4a4_config(k, n, m)
+    assert B.rq_w4_weight_bytes(cfg) == W4.weight_bytes(n, k)
+    assert B.rq_w4a4_act_bytes(cfg) == W4.act_bytes(m, k)
+    r = lambda b: (b + 255) // 256 * 256
+    base = r(m * (k // 32) * 4) + r(m * 4) + r(W4.act_bytes(m, k))
+    splits = 1 if k in (1024, 2048, 3072, 4096) else -(-k // 4096)
+    assert B.rq_w4a4_workspace_bytes(cfg) == base + (r(splits * m * n * 4) if splits > 1 else 0)
+
+
+@pytest.mark.parametrize("k,n,m", [(0, 16, 1), (64, 16, 1), (1000, 16, 1), (16512, 16, 1), (1024, 8, 1),
+                                   (1024, 16, 0), (1024, 16, 65)])
+def test_w4a4_invalid_sizes_have_no_size(B, k, n, m):
+    cfg = B.w4a4_config(k, n, m)
+    assert B.rq_w4_weight_bytes(cfg) == 0 and B.rq_w4a4_workspace_bytes(cfg) == 0
