@@ -276,6 +276,82 @@ def measure_w4a4(B, dev, sink, eager: bool = False, name: str = "ouro_up_b16") -
             "timing": "HIP graph replay of back-to-back calls over cold weight copies, one event pair; "
                       "each call = activation quantizer + GEMM kernels"}
 
+def measure_loop_steps(B, dev, name: str, splits: int = 0) -> dict:
+    """Residual and anchor loop-steps of a second workload (the batch-4 case beside the batch-16
+    default), each launched back to back over cold cache replicas with one event pair per
+    repeat, and the BF16 kernel's loop-step on the same K/V."""
+    import torch
+    from looped_transformer_decode_amd import synth
+    wl = synth.WORKLOADS[name]
+    L, d, T, Bt = wl.loops_per_group, wl.head_dim, wl.ctx, wl.batch
+    inp = synth.generate(wl, seed=20261202, device=dev)
+    cfg = B.config_for(wl)
+    cache_bytes = B.rq_cache_bytes(cfg)
+    cache = torch.zeros(cache_bytes, dtype=torch.uint8, device=dev)
+    pos0 = torch.zeros(Bt, dtype=torch.int32, device=dev)
+    for grp in range(wl.n_groups):
+        st = inp.kv[grp].stride()
+        B.rq_quantize_token(cfg, cache, inp.kv[grp], grp, pos0, inp.rot, Bt, T,
+                            pending_strides=(st[4], st[2], st[0], st[1], st[3]))
+    n_rep = max(2, min(16, math.ceil(1.6e9 / cache_bytes)))
+    caches = [cache] + [cache.clone() for _ in range(n_rep - 1)]
+    q = [inp.q[i].contiguous() for i in range(L)]
+    k_cur = [inp.kv[0, i, 0, :, :, T].contiguous() for i in range(L)]
+    v_cur = [inp.kv[0, i, 1, :, :, T].contiguous() for i in range(L)]
+    ctx_len = torch.full((Bt,), T, dtype=torch.int32, device=dev)
+    ws = torch.zeros(B.rq_workspace_bytes(cfg), dtype=torch.uint8, device=dev)
+    out = torch.empty(Bt, wl.n_q_heads, d, dtype=torch.float32, device=dev)
+    sc = synth.sm_scale(d)
+    stream = torch.cuda.current_stream()
+
+    def back_to_back(loops, calls):
+        reps = []
+        for r in range(4):                        # the first repeat warms up
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(calls):
+                loop = loops[i % len(loops)]
+                B.rq_decode_attention(cfg, caches[i % n_rep], loop, q[loop], k_cur[loop], v_cur[loop], None, ctx_len,
+                                      T, inp.rot, sc, out, ws, Bt, n_splits=splits, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            reps.append(e0.elapsed_time(e1) / calls)
+        return sum(reps[1:]) / 3
+
+    res_ms = back_to_back(list(range(L - 1)), 6 * n_rep)
+    anc_ms = back_to_back([L - 1], 2 * n_rep)
+    res_bytes = algorithmic_bytes(wl, 0, False)
+    anc_bytes = algorithmic_bytes(wl, L - 1, False)
+    bcfg = B.bf16_config_for(wl)
+    bws = torch.zeros(B.rq_bf16_workspace_bytes(bcfg), dtype=torch.uint8, device=dev)
+    Ks = [inp.kv[0, l, 0] for l in range(L)]
+    Vs = [inp.kv[0, l, 1] for l in range(L)]
+    bre = []
+    for r in range(4):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(2 * L):
+            l = i % L
+            B.rq_bf16_decode_attention(bcfg, Ks[l], Vs[l], q[l], k_cur[l], v_cur[l], False, ctx_len, T, sc, out, bws,
+                                       Bt, n_splits=splits, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bre.append(e0.elapsed_time(e1) / (2 * L))
+    bf16_ms = sum(bre[1:]) / 3
+    return {"workload": name, "batch": Bt, "ctx": T, "cache_replicas": n_rep,
+            "residual_loop_step": {"bytes": res_bytes, "ms": round(res_ms, 4),
+                                   "gbps": round(res_bytes / (res_ms * 1e-3) / 1e9, 1),
+                                   "frac_of_hbm_peak": round(res_bytes / (res_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+            "anchor_loop_step": {"bytes": anc_bytes, "ms": round(anc_ms, 4),
+                                 "gbps": round(anc_bytes / (anc_ms * 1e-3) / 1e9, 1),
+                                 "frac_of_hbm_peak": round(anc_bytes / (anc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+            "bf16": {"bytes": bf16_bytes(wl), "ms_per_loop_step": round(bf16_ms, 4),
+                     "gbps": round(bf16_bytes(wl) / (bf16_ms * 1e-3) / 1e9, 1),
+                     "speedup_rq_residual_vs_bf16": round(bf16_ms / res_ms, 3)},
+            "timing": "HIP events around back-to-back loop-steps over cold cache replicas (mean of 3 repeats "
+                      "after one warm-up repeat); BF16 loop-steps back to back on the same K/V"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -291,6 +367,8 @@ def main():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-w4a4", action="store_true", help="skip the W4A4 layer measurement")
+    ap.add_argument("--no-batch4", action="store_true",
+                    help="skip the batch-4 loop-steps measured beside the default batch-16 workload")
     ap.add_argument("--cpu-baseline-only", action="store_true",
                     help="time the CPU oracle on the workload and print its JSON (no GPU use)")
     ap.add_argument("--replicas", type=int, default=0)
@@ -648,6 +726,14 @@ def main():
     proj_step_ovl = step_graph_ms(True)
     del wreps
 
+    # the batch-4 case beside the default batch-16 workload (before the roofline timing, so
+    # that the roofline's dispatches stay the last decode dispatches of the run)
+    batch4 = None
+    if args.workload == DEFAULT_WORKLOAD and not variant and not args.chained and not args.no_batch4:
+        print("[bench] batch-4 loop-steps", file=sys.stderr, flush=True)
+        batch4 = measure_loop_steps(B, dev, "ouro_b4_t8192", args.splits)
+        torch.cuda.empty_cache()
+
     # roofline timing: back-to-back residual loop-steps over the cold replicas, one event
     # pair around all of them (launches overlap the previous kernel, as in a decode step)
     roof_calls = 6 * n_rep
@@ -743,6 +829,8 @@ def main():
                      + ", residual loop-step (split-K with the merge in its last workgroup)",
                      "algorithmic_bytes": round(roof_bytes), "source_digest": decode_source_digest(wl)},
     }
+    if batch4 is not None:
+        result["ouro_b4_t8192"] = batch4
     if not args.no_w4a4:
         result["w4a4"] = measure_w4a4(B, dev, sink, eager=args.eager_only)
         result["w4a4_huginn"] = measure_w4a4(B, dev, sink, eager=args.eager_only, name="huginn_up_b8")
