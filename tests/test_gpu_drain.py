@@ -123,3 +123,48 @@ def test_drain_past_max_ctx():
     # only the three token rows at slots p0 .. max_ctx - 1 changed: the rest of every tile keeps 0x5A
     changed = int((one_call != untouched).sum())
     assert 0 < changed <= 3 * batch * hkv * 2 * (72 + 3 * (40 + 2)), changed
+
+
+@pytest.mark.parametrize("kind", ["zero", "constant", "large", "zero_anchor"])
+def test_drain_kernels_agree_on_edge_inputs(kind):
+    """Degenerate inputs through both drain kernels: all zeros (zero anchor, c = 0, zero ranges),
+    one constant per vector (zero group ranges, the smallest scale), values near the E4M3 range
+    (offsets at -448, scales near 448) and a zero anchor under nonzero loops (c = 0, the residual
+    is R x).  The bytes must be identical and the encoding follow the oracle's rules."""
+    from looped_transformer_decode_amd import binding as B
+    wl, batch, hkv = CASES["d128g32_L4"]
+    wl = wl.with_(batch=batch, ctx=N_TOK, chained=False, n_kv_heads=hkv, n_q_heads=hkv)
+    inp = synth.generate(wl, seed=609, device="cuda")
+    kv = inp.kv
+    if kind == "zero":
+        kv.zero_()
+    elif kind == "constant":
+        kv.copy_(torch.linspace(-3.0, 3.0, kv.shape[5], device="cuda").view(1, 1, 1, 1, 1, -1, 1).expand_as(kv))
+    elif kind == "large":
+        kv.copy_((kv.float().clamp(-1.0, 1.0) * 380.0).to(kv.dtype))
+    else:
+        kv[:, wl.loops_per_group - 1].zero_()
+    cfg = B.config_for(wl)
+    ocfg = oracle_cfg(wl)
+    one_call = torch.zeros(B.rq_cache_bytes(cfg), dtype=torch.uint8, device="cuda")
+    per_tok = torch.zeros_like(one_call)
+    say(f"[drain] edge inputs: {kind}")
+    k0 = kv[0]
+    B.rq_quantize_token(cfg, one_call, k0, 0, torch.zeros(batch, dtype=torch.int32, device="cuda"), inp.rot, batch,
+                        N_TOK, pending_strides=pending_strides(k0))
+    for t in range(N_TOK):
+        kt = kv[0, :, :, :, :, t:t + 1]
+        B.rq_quantize_token(cfg, per_tok, kt, 0, torch.full((batch,), t, dtype=torch.int32, device="cuda"), inp.rot,
+                            batch, 1, pending_strides=pending_strides(kt))
+    torch.cuda.synchronize()
+    assert torch.equal(one_call, per_tok)
+    kvd = kv.double().cpu().numpy()
+    rot = inp.rot.double().cpu().numpy()
+    stats = new_stats()
+    _, sub = sub_cache(np.zeros(0, np.uint8), ocfg, 0, 0)
+    for b in range(batch):
+        for h in range(0, hkv, 5):
+            xs = [[kvd[0, :, x, b, h, :N_TOK] for x in range(2)]]
+            check_pack_block(device_block(one_call, ocfg, b, h), sub, xs, rot[h], N_TOK, stats)
+    say(f"[drain] edge {kind} stats={stats}")
+    assert_stats(stats, wl.group)
