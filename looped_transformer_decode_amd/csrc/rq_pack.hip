@@ -714,6 +714,234 @@ __global__ __launch_bounds__(bulk_threads<D>()) __attribute__((amdgpu_waves_per_
     }
 }
 
+// ---- bulk pack of the chained layout: many tokens per workgroup
+//
+// Chained: loop l is stored against the rebuilt loop l + 1 (the anchor closes the chain), so
+// the loops run one after the other, each with two products on the float64 matrix cores over
+// the workgroup's 16 tokens: r = R y, then the rebuilt loop c ref + R^T r_hat, which is the
+// next loop's reference.  The coefficient and quantizer phases run one token per wave as in
+// the kernel above.  Same float64 steps and decisions as the token-at-a-time kernel; only the
+// order of the additions inside the products differs.
+template <int D, int G>
+__global__ __launch_bounds__(bulk_threads<D>()) __attribute__((amdgpu_waves_per_eu(D == 128 ? 4 : 3)))
+void rq_pack_bulk_chained_kernel(PackArgs a) {
+    constexpr int kBulkThreads = bulk_threads<D>();
+    constexpr int TK = kBulkTokens, NW = kBulkThreads / kWave;
+    constexpr int CPL = D / kWave;                    // channels per lane
+    static_assert(D / 16 == NW && TK % NW == 0, "one 16-row tile of R per wave, tokens per wave");
+    constexpr int YS = D + 2;                         // padded LDS row of Y (doubles)
+    const Geom& Gm = a.geo;
+    const int L = Gm.L;
+    const bool norm_ratio = Gm.scale_rule == 1;
+    int wg = blockIdx.x;
+    const int x = wg & 1;
+    wg >>= 1;
+    const int h = wg % Gm.hkv;
+    wg /= Gm.hkv;
+    const int b = wg % a.batch;
+    const int t0 = (wg / a.batch) * TK;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int loop0 = a.group_idx * L;
+
+    __shared__ __attribute__((aligned(16))) double yt[TK][YS];     // y, then R y, then r_hat: [token][channel]
+    __shared__ double ref[TK][D];                                  // reference of the loop at hand
+    __shared__ double cs[TK];                                      // its coefficient per token
+    __shared__ uint16_t xs[TK][D];                                 // BF16 inputs of the loop at hand
+
+    // A operands: rows 16 w + lane % 16 of R (channels (D/4) (lane / 16) + s, contiguous) for
+    // r = R y, and the same rows of R^T (R[(D/4) (lane / 16) + s][16 w + lane % 16], one
+    // float per step) for R^T r_hat, both read from L2 right before their product
+    const int i16 = lane & 15, kq = lane >> 4;
+    const float* Rm = a.rot + (int64_t)(h * 2 + x) * D * D;
+    const f32x4* rp = reinterpret_cast<const f32x4*>(Rm + (int64_t)(16 * w + i16) * D + (D / 4) * kq);
+    const float* rtp = Rm + (int64_t)((D / 4) * kq) * D + 16 * w + i16;
+
+    const int p0 = a.pos[b] + t0;
+    auto valid = [&](int tok) {
+        const int slot = p0 + tok;
+        return t0 + tok < a.n_tokens && slot >= 0 && slot < Gm.max_ctx;
+    };
+    constexpr int PE = TK * D / kBulkThreads;         // elements per thread
+    auto stage_x = [&](int l) {
+        uint16_t v[PE];
+#pragma unroll
+        for (int e = 0; e < PE; ++e) {
+            const int idx = e * kBulkThreads + threadIdx.x, i = idx % D, tok = idx / D;
+            v[e] = valid(tok) ? a.pending[(int64_t)(t0 + tok) * a.st[0] + (int64_t)b * a.st[1] + (int64_t)l * a.st[2] +
+                                          (int64_t)x * a.st[3] + (int64_t)h * a.st[4] + i]
+                              : (uint16_t)0;
+        }
+#pragma unroll
+        for (int e = 0; e < PE; ++e) {
+            const int idx = e * kBulkThreads + threadIdx.x;
+            xs[idx / D][idx % D] = v[e];
+        }
+    };
+    auto load_x = [&](int tok, double (&v)[CPL]) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) v[c] = (double)bf16_to_f32(xs[tok][CPL * lane + c]);
+    };
+    const auto add = [](double p, double q) { return p + q; };
+    // one 16 x 16 output tile per wave: D[i][j] = sum_k A[i][k] Y[k][j] with B from yt
+    auto product = [&](const auto& a_of) {
+        f64x4 acc = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int q = 0; q < D / 16; ++q) {
+            const double* yb = &yt[i16][(D / 4) * kq + 4 * q];
+            const f64x2 y01 = *reinterpret_cast<const f64x2*>(yb);
+            const f64x2 y23 = *reinterpret_cast<const f64x2*>(yb + 2);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a_of(4 * q), y01.x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a_of(4 * q + 1), y01.y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a_of(4 * q + 2), y23.x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a_of(4 * q + 3), y23.y, acc, 0, 0, 0);
+        }
+        return acc;
+    };
+
+    constexpr int S = TK / NW, SB = S < 2 ? S : 2;
+    int jjs[S], tiles[S];
+    bool oks[S];
+#pragma unroll
+    for (int t = 0; t < S; ++t) {
+        const int tok = t * NW + w;
+        oks[t] = valid(tok);
+        const int slot = oks[t] ? p0 + tok : 0;
+        tiles[t] = slot / kTile;
+        jjs[t] = slot % kTile;
+    }
+
+    // ---- anchors: the first reference
+    stage_x(L - 1);
+    __syncthreads();
+#pragma unroll
+    for (int tb = 0; tb < S; tb += SB) {
+        double xa[SB][CPL], xh[SB][CPL];
+        uint8_t* pl[SB];
+        int jb[SB];
+        bool ob[SB];
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
+            load_x((tb + u) * NW + w, xa[u]);
+            pl[u] = a.cache + Gm.tile_offset(b, h, x, loop0 + L - 1, tiles[tb + u]);
+            jb[u] = jjs[tb + u];
+            ob[u] = oks[tb + u];
+        }
+        if (Gm.ba == 4) quantize_rows<G, CPL, 4, SB>(xa, xh, pl, Gm.a_row, Gm.m_row, jb, ob, lane);
+        else quantize_rows<G, CPL, 2, SB>(xa, xh, pl, Gm.a_row, Gm.m_row, jb, ob, lane);
+#pragma unroll
+        for (int u = 0; u < SB; ++u)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) ref[(tb + u) * NW + w][CPL * lane + c] = xh[u][c];
+    }
+
+    for (int l = L - 2; l >= 0; --l) {
+        __syncthreads();                              // ref written; xs and yt free
+        stage_x(l);
+        __syncthreads();
+        // ---- c and y = x - c ref
+#pragma unroll
+        for (int tb = 0; tb < S; tb += SB) {
+            double dot[SB], nn[SB];
+#pragma unroll
+            for (int u = 0; u < SB; ++u) {
+                const int tok = (tb + u) * NW + w;
+                double xl[CPL];
+                load_x(tok, xl);
+                dot[u] = nn[u] = 0.0;
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    const double rf = ref[tok][CPL * lane + c];
+                    dot[u] = fma(xl[c], norm_ratio ? xl[c] : rf, dot[u]);
+                    nn[u] = fma(rf, rf, nn[u]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < SB; ++u) {
+                dot[u] = lanes_reduce<kWave>(dot[u], add);
+                nn[u] = lanes_reduce<kWave>(nn[u], add);
+            }
+#pragma unroll
+            for (int u = 0; u < SB; ++u) {
+                const int t = tb + u, tok = t * NW + w;
+                const double qn = dot[u] / nn[u];
+                const double cl = bf16_round(nn[u] > 0.0 ? (norm_ratio ? sqrt(qn) : qn) : 0.0);
+                if (lane == 0) {
+                    cs[tok] = cl;
+                    if (oks[t]) {
+                        uint8_t* pl = a.cache + Gm.tile_offset(b, h, x, loop0 + l, tiles[t]);
+                        reinterpret_cast<uint16_t*>(pl + (int64_t)kTile * (Gm.rrow(l) + Gm.m_row))[jjs[t]] =
+                            (uint16_t)(__float_as_uint((float)cl) >> 16);
+                    }
+                }
+                double xl[CPL];
+                load_x(tok, xl);
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) yt[tok][CPL * lane + c] = xl[c] - cl * ref[tok][CPL * lane + c];
+            }
+        }
+        __syncthreads();
+        // ---- r = R y (R is read again each loop: held across the loops it would spill)
+        {
+            const f32x4* rpl = rp;
+            asm volatile("" : "+v"(rpl));
+            f32x4 ra[D / 16];
+#pragma unroll
+            for (int q = 0; q < D / 16; ++q) ra[q] = rpl[q];
+            const f64x4 acc = product([&](int s) { return (double)ra[s / 4][s % 4]; });
+            __syncthreads();                          // every wave has read y
+#pragma unroll
+            for (int e = 0; e < 4; ++e) yt[i16][16 * w + 4 * e + kq] = acc[e];
+        }
+        __syncthreads();
+        // ---- residual codes; r_hat replaces r in yt (each wave its own tokens' rows)
+#pragma unroll
+        for (int tb = 0; tb < S; tb += SB) {
+            double r[SB][CPL], rh[SB][CPL];
+            uint8_t* pl[SB];
+            int jb[SB];
+            bool st[SB];
+#pragma unroll
+            for (int u = 0; u < SB; ++u) {
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) r[u][c] = yt[(tb + u) * NW + w][CPL * lane + c];
+                pl[u] = a.cache + Gm.tile_offset(b, h, x, loop0 + l, tiles[tb + u]);
+                jb[u] = jjs[tb + u];
+                st[u] = oks[tb + u];
+            }
+            if (Gm.rbits(l) == 4) quantize_rows<G, CPL, 4, SB>(r, rh, pl, Gm.rrow(l), Gm.m_row, jb, st, lane);
+            else quantize_rows<G, CPL, 2, SB>(r, rh, pl, Gm.rrow(l), Gm.m_row, jb, st, lane);
+#pragma unroll
+            for (int u = 0; u < SB; ++u)
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) yt[(tb + u) * NW + w][CPL * lane + c] = rh[u][c];
+        }
+        if (l == 0) break;                            // no later loop needs the rebuilt loop 0
+        __syncthreads();
+        // ---- the next reference: c ref + R^T r_hat
+        {
+            const float* rtl = rtp;
+            asm volatile("" : "+v"(rtl));
+            float rt[D / 4];
+#pragma unroll
+            for (int s = 0; s < D / 4; ++s) rt[s] = rtl[(int64_t)s * D];
+            const f64x4 acc = product([&](int s) { return (double)rt[s]; });
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                double& rf = ref[i16][16 * w + 4 * e + kq];
+                rf = cs[i16] * rf + acc[e];
+            }
+        }
+    }
+}
+
+template <int D, int G>
+static hipError_t launch_bulk_chained(const PackArgs& a, int nwg, hipStream_t stream) {
+    const int LR = a.geo.L - 1;
+    if (LR < 1 || LR > kMaxLoops - 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((rq_pack_bulk_chained_kernel<D, G>), dim3(nwg), dim3(bulk_threads<D>()), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int D, int G>
 static hipError_t launch_bulk(const PackArgs& a, int nwg, hipStream_t stream) {
     constexpr int kBulkThreads = bulk_threads<D>();
@@ -790,8 +1018,13 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t stream) {
     if (!a.cache || !a.pending || !a.pos || !a.rot || a.batch < 1 || a.n_tokens < 1 || a.tokens_per_wg < 1 ||
         (a.geo.g != 16 && a.geo.g != 32) || (a.geo.d != 64 && a.geo.d != 128))
         return hipErrorInvalidValue;
-    if (!a.geo.chained && a.n_tokens >= kBulkTokens) {
+    if (a.n_tokens >= kBulkTokens) {
         const int nwg = (a.n_tokens + kBulkTokens - 1) / kBulkTokens * a.batch * a.geo.hkv * 2;
+        if (a.geo.chained) {
+            if (a.geo.d == 128)
+                return a.geo.g == 32 ? launch_bulk_chained<128, 32>(a, nwg, stream) : launch_bulk_chained<128, 16>(a, nwg, stream);
+            return a.geo.g == 32 ? launch_bulk_chained<64, 32>(a, nwg, stream) : launch_bulk_chained<64, 16>(a, nwg, stream);
+        }
         if (a.geo.d == 128) return a.geo.g == 32 ? launch_bulk<128, 32>(a, nwg, stream) : launch_bulk<128, 16>(a, nwg, stream);
         return a.geo.g == 32 ? launch_bulk<64, 32>(a, nwg, stream) : launch_bulk<64, 16>(a, nwg, stream);
     }

@@ -1,8 +1,10 @@
-"""GPU parity of the many-token pack path (16 tokens per workgroup, used for 16 or more
-tokens with a shared anchor) on the cases the default workloads do not reach: 2, 6 and
-8 loops per anchor group (one, two and three residual batches of the rotation product,
-the last one partial), head_dim 64 and 128, INT4 and INT2 anchors, a token count that is
-not a multiple of 16, and a start slot so close to max_ctx that the last tokens have no
+"""GPU parity of the many-token pack paths (16 tokens per workgroup, used for 16 or more
+tokens) on the cases the default workloads do not reach.  Shared anchor: 2, 6 and 8 loops
+per anchor group (one, two and three residual batches of the rotation product, the last
+one partial), head_dim 64 and 128, INT4 and INT2 anchors.  Chained: 2, 3 and 4 loops per
+group (one to three links of the chain), head_dim 64 and 128, g = 16 and 32, both
+coefficient rules, a start slot that is not a multiple of 16.  Both: a token count that
+is not a multiple of 16, and a start slot so close to max_ctx that the last tokens have no
 slot (they must be skipped: nothing written, nothing else touched).  Every stored code,
 FP8 offset/scale and c is checked against the float64 oracle under the parity rules."""
 import numpy as np
@@ -22,6 +24,12 @@ U = "uniform(0.8,1.0)"
 CASES = {
     # name: (workload, batch, tokens, n_kv_heads, first slot, max_ctx or None)
     "L2_d128g32": (W["ouro_b4_t8192"].with_(loops_per_group=2, loop_scale=U), 2, 100, 2, 0, None),
+    "chained_L2_d128g32": (W["ouro_b4_t8192"].with_(loops_per_group=2, loop_scale=U, chained=True), 2, 100, 2, 0,
+                           None),
+    "chained_L3_d64g16_offset": (W["tiny_d64_t256"].with_(group=16, loops_per_group=3, loop_scale=U, chained=True), 2,
+                                 45, 2, 5, None),
+    "chained_L4_d128g32_past_max_ctx": (W["ouro_b4_t8192"].with_(chained=True), 2, 50, 1, 51, 96),
+    "chained_norm_ratio_d64g32": (W["tiny_d64_t256"].with_(scale_rule=1, chained=True), 1, 70, 2, 0, None),
     "L6_d128g16int2": (W["int2g16_b4_t16384"].with_(loops_per_group=6, loop_scale=U), 1, 70, 2, 0, None),
     "L8_d64": (W["tiny_d64_t256"].with_(loops_per_group=8, loop_scale=U), 1, 40, 2, 0, None),
     "past_max_ctx": (W["ouro_b4_t8192"], 2, 50, 1, 51, 96),
