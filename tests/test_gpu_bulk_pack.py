@@ -14,8 +14,8 @@ import torch
 from looped_transformer_decode_amd import synth
 from oracle import residualquant as RQ
 
-from _support import (assert_stats, check_encoding, device_block, gpu_pack, new_stats, oracle_cfg, say,
-                      slice_enc, sub_cache)
+from _support import (assert_stats, check_encoding, device_block, gpu_pack, new_stats, oracle_cfg, pending_strides,
+                      say, slice_enc, sub_cache)
 
 pytestmark = pytest.mark.gpu
 
@@ -67,4 +67,42 @@ def test_bulk_pack_parity(name):
                         head = slice_enc(enc, slice(0, pos0))
                         assert not np.any(head.anchor[0]) and not np.any(head.anchor[1])
     say(f"[bulk] case={name} stats={stats}")
+    assert_stats(stats, wl.group)
+
+
+@pytest.mark.parametrize("chained", [False, True], ids=["shared", "chained"])
+def test_bulk_pack_rows_start_at_their_own_slots(chained):
+    """Each batch row packs from its own first slot (pos[b]): row 0 from slot 0, row 1 from
+    slot 37, so that its 40 tokens straddle a 64-token tile boundary.  Every stored value is
+    checked against the oracle, and the slots before a row's first one stay untouched."""
+    from looped_transformer_decode_amd import binding as B
+    wl = W["ouro_b4_t8192"].with_(batch=2, ctx=40, n_kv_heads=2, n_q_heads=2, chained=chained)
+    T, starts = 40, [0, 37]
+    max_ctx = max(starts) + T
+    say(f"[bulk] rows from slots {starts}, {T} tokens, chained={chained}")
+    inp = synth.generate(wl, seed=331, device="cuda")
+    cfg = B.config_for(wl, max_ctx=max_ctx)
+    ocfg = oracle_cfg(wl, max_ctx=max_ctx)
+    cache = torch.zeros(B.rq_cache_bytes(cfg), dtype=torch.uint8, device="cuda")
+    pos = torch.tensor(starts, dtype=torch.int32, device="cuda")
+    for grp in range(wl.n_groups):
+        B.rq_quantize_token(cfg, cache, inp.kv[grp], grp, pos, inp.rot, wl.batch, T,
+                            pending_strides=pending_strides(inp.kv[grp]))
+    torch.cuda.synchronize()
+    kv = inp.kv.double().cpu().numpy()
+    rot = inp.rot.double().cpu().numpy()
+    stats = new_stats()
+    for b, p0 in enumerate(starts):
+        for h in range(wl.n_kv_heads):
+            block = device_block(cache, ocfg, b, h)
+            _, sub = sub_cache(np.zeros(0, np.uint8), ocfg, b, h)
+            lay = RQ.Layout(sub)
+            for k in range(wl.n_groups):
+                for x in range(2):
+                    enc = RQ.read_tokens(block, lay, 0, 0, x, k, p0 + T)
+                    check_encoding(slice_enc(enc, slice(p0, p0 + T)), kv[k, :, x, b, h, :T], rot[h, x], sub, stats)
+                    if p0 > 0:
+                        head = slice_enc(enc, slice(0, p0))
+                        assert not np.any(head.anchor[0]) and not np.any(head.anchor[1])
+    say(f"[bulk] rows from their own slots stats={stats}")
     assert_stats(stats, wl.group)
