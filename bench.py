@@ -100,9 +100,13 @@ def bulk_in_bytes(wl) -> int:
 
 
 def rotation_fma(wl) -> int:
-    """Float64 FMAs of the residual rotations R y in a bulk pack of the whole context."""
-    n_res = wl.n_groups * (wl.loops_per_group - 1)
-    return wl.batch * wl.ctx * wl.n_kv_heads * 2 * n_res * wl.head_dim * wl.head_dim
+    """Float64 FMAs of the d x d products in a bulk pack of the whole context: R y of every
+    residual vector, and in the chained layout also the rebuilt reference c ref + R^T r_hat
+    of every residual loop but the group's first (the last loop stored needs no successor)."""
+    n_prod = wl.n_groups * (wl.loops_per_group - 1)
+    if wl.chained:
+        n_prod += wl.n_groups * (wl.loops_per_group - 2)
+    return wl.batch * wl.ctx * wl.n_kv_heads * 2 * n_prod * wl.head_dim * wl.head_dim
 
 
 def _oracle_worker(args):

@@ -53,6 +53,8 @@ def test_bulk_pack_and_rotation_counts():
     assert bench.bulk_in_bytes(wl) == wl.batch * wl.ctx * 4 * 2 * wl.n_kv_heads * wl.head_dim * 2
     # one d x d product per residual vector
     assert bench.rotation_fma(wl) == wl.batch * wl.ctx * wl.n_kv_heads * 2 * 3 * wl.head_dim ** 2
+    # chained: loops 2 and 1 also rebuild their reference for loops 1 and 0 (R^T r_hat)
+    assert bench.rotation_fma(wl.with_(chained=True)) == wl.batch * wl.ctx * wl.n_kv_heads * 2 * 5 * wl.head_dim ** 2
 
 
 def test_more_than_one_gpu_is_refused():
