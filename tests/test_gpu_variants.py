@@ -1,7 +1,8 @@
 """GPU parity of the precision, group-length and scale-rule settings on the same kernels:
 uniform INT4 (4-bit anchors and 4-bit residuals), the mixed INT2/4 at g = 16, loop groups
 of 8 and 16, the norm-ratio coefficient (shared and chained), the grouped-query kernel
-with two query heads per KV head, and residual widths per loop (4 bits far from the
+with two query heads per KV head, the chained layout with two and four query heads per KV
+head (one workgroup per query head) and with two anchor groups, and residual widths per loop (4 bits far from the
 anchor, 2 bits near it; with grouped queries the 2-bit loops run on the grouped kernel and
 the 4-bit ones on the one-query kernel).  Each case packs a
 ragged context (the many-token kernel), decodes every loop (or a spread of loops for the
@@ -33,6 +34,10 @@ CASES = {
                                 [80], 2, 4, [0, 7, 14, 15, 16, 30, 31]),
     "norm_ratio_d128g32": (W["ouro_b4_t8192"].with_(scale_rule=1), False, 3, [64, 1, 150], 2, 2, None),
     "norm_ratio_chained_int2g16": (W["int2g16_b4_t16384"].with_(scale_rule=1), True, 2, [65, 130], 2, 2, None),
+    # chained with grouped queries (the one-query kernel once per query head) and two anchor groups
+    "chained_gqa2_two_groups_d128g32": (W["ouro_b4_t8192"].with_(n_groups=2, loop_scale=U), True, 2, [130, 77], 2, 4,
+                                        None),
+    "chained_gqa4_int2g16": (W["int2g16_b4_t16384"], True, 2, [100, 190], 2, 8, None),
     "norm_ratio_int4_uniform_d64": (W["tiny_d64_t256"].with_(scale_rule=1, resid_bits=4), False, 1, [200], 2, 2,
                                     None),
     "widths_422_d128g32": (W["ouro_b4_t8192"].with_(resid_bits_loop=(4, 2, 2)), False, 3, [0, 70, 200], 2, 2, None),
